@@ -1,0 +1,161 @@
+"""CPU oracle for the block-diffusion denoise step (fp64, plain loops).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package; the GPU library and
+its Python binding never do, and the two share no code.
+
+The arithmetic lives in ``bd_oracle.c`` (compiled with gcc, no fast-math);
+this module only builds it, loads it with ctypes and marshals numpy arrays.
+Each wrapper names the passage its C function follows.
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "bd_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16 = 0, 1
+BIDIR, CAUSAL = 0, 1
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP over independent query rows, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int
+        lib.bdo_attention.argtypes = [i32] * 8 + [ctypes.c_double] + [P] * 7
+        lib.bdo_attention.restype = None
+        lib.bdo_confidence_row.argtypes = [i32, P, P, P, P, P]
+        lib.bdo_commit_k.argtypes = [i32, i32, i32]
+        lib.bdo_commit_k.restype = i32
+        lib.bdo_confidence_commit.argtypes = [i32, i32, i32, i32, ctypes.c_float] + [P] * 7
+        lib.bdo_spec_verify.argtypes = [i32, i32, i32, P, P, P, P]
+        lib.bdo_kv_append.argtypes = [i32] * 6 + [P] * 7
+        lib.bdo_num_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def num_threads() -> int:
+    return int(_load().bdo_num_threads())
+
+
+def attention(q, k_blk, v_blk, k_cache, v_cache, prefix, mode, scale=None):
+    """Block attention of Fast-dVLM's causal-context decoding (Fast-dVLM write-up,
+    sections 4.1 and 5.3; summary page Fig. 3): returns float64 [n][D][Hq][d]."""
+    lib = _load()
+    n, D, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dtype = F32 if q.dtype == np.float32 else BF16
+    el = np.float32 if dtype == F32 else np.uint16
+    arrs = [_c(a, el) for a in (q, k_blk, v_blk, k_cache, v_cache)]
+    assert k_blk.shape == (n, D, Hkv, d) and v_blk.shape == (n, D, Hkv, d)
+    assert k_cache.shape == (n, Hkv, cap, d) and v_cache.shape == (n, Hkv, d, cap)
+    prefix = _c(prefix, np.int32)
+    assert prefix.shape == (n,) and np.all(prefix >= 0) and np.all(prefix <= cap)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n, D, Hq, d), dtype=np.float64)
+    lib.bdo_attention(n, D, Hq, Hkv, d, cap, dtype, int(mode), float(scale),
+                      *[_ptr(a) for a in arrs], _ptr(prefix), _ptr(out))
+    return out
+
+
+def confidence_row(x):
+    """Confidence and greedy token of one logits row (DiffusionVL notes, cached block
+    decoding: confidence = model probability of the chosen token).
+    Returns (conf, argmax, lse, p2) with conf, lse, p2 in float64."""
+    lib = _load()
+    x = _c(x, np.float32)
+    conf, lse, p2 = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    a = ctypes.c_int32()
+    lib.bdo_confidence_row(x.size, _ptr(x), ctypes.byref(conf), ctypes.byref(a),
+                           ctypes.byref(lse), ctypes.byref(p2))
+    return conf.value, a.value, lse.value, p2.value
+
+
+def commit_k(D, S, n_masked):
+    """k = min(ceil(D/S), |M|) (DiffusionVL notes, Algorithm 1)."""
+    return int(_load().bdo_commit_k(int(D), int(S), int(n_masked)))
+
+
+def confidence_commit(logits, masked, tokens, S, tau):
+    """One denoising step's confidence + dynamic commit (DiffusionVL notes, cached
+    block decoding and Algorithm 1).  ``masked`` and ``tokens`` are updated in place
+    (copies are returned too).  Returns dict(conf, argmax, committed, n_committed,
+    masked, tokens)."""
+    lib = _load()
+    n_req, D, V = logits.shape
+    logits = _c(logits, np.float32)
+    masked = np.array(masked, dtype=np.uint8, copy=True, order="C")
+    tokens = np.array(tokens, dtype=np.int32, copy=True, order="C")
+    conf = np.zeros((n_req, D), np.float64)
+    amax = np.zeros((n_req, D), np.int32)
+    committed = np.zeros((n_req, D), np.uint8)
+    ncom = np.zeros(n_req, np.int32)
+    lib.bdo_confidence_commit(n_req, D, V, int(S), ctypes.c_float(tau), _ptr(logits), _ptr(masked),
+                              _ptr(tokens), _ptr(conf), _ptr(amax), _ptr(committed), _ptr(ncom))
+    return dict(conf=conf, argmax=amax, committed=committed, n_committed=ncom,
+                masked=masked, tokens=tokens)
+
+
+def spec_verify(logits, draft):
+    """Longest accepted draft prefix (Fast-dVLM write-up, section 5.3, linear
+    speculative decoding).  Returns (accepted_len int32[n_req], argmax int32[n_req][D])."""
+    lib = _load()
+    n_req, D, V = logits.shape
+    logits = _c(logits, np.float32)
+    draft = _c(draft, np.int32)
+    L = np.zeros(n_req, np.int32)
+    amax = np.zeros((n_req, D), np.int32)
+    lib.bdo_spec_verify(n_req, D, V, _ptr(logits), _ptr(draft), _ptr(L), _ptr(amax))
+    return L, amax
+
+
+def kv_append(k_cache, v_cache, prefix, k_blk, v_blk, n_accept=None):
+    """Append accepted block K/V to the cache (Fast-dVLM write-up, section 5.3: crop
+    the cache to the accepted prefix; DiffusionVL notes: a finished block joins the
+    history cache).  Returns new (k_cache, v_cache, prefix, err)."""
+    lib = _load()
+    n, Hkv, cap, d = k_cache.shape
+    D = k_blk.shape[1]
+    dtype = F32 if k_cache.dtype == np.float32 else BF16
+    k_cache = np.array(k_cache, copy=True, order="C")
+    v_cache = np.array(v_cache, copy=True, order="C")
+    prefix = np.array(prefix, dtype=np.int32, copy=True)
+    kb = np.ascontiguousarray(k_blk)
+    vb = np.ascontiguousarray(v_blk)
+    na = None if n_accept is None else _c(n_accept, np.int32)
+    err = np.zeros(1, np.int32)
+    lib.bdo_kv_append(n, D, Hkv, d, cap, dtype, _ptr(k_cache), _ptr(v_cache), _ptr(prefix),
+                      _ptr(kb), _ptr(vb), _ptr(na), _ptr(err))
+    return k_cache, v_cache, prefix, int(err[0])

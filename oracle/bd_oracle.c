@@ -1,0 +1,287 @@
+/*
+ * CPU oracle for one block-diffusion denoising step and its speculative
+ * verify / append companion.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, plain reference that
+ * the GPU library is checked against.  Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg may build, load or call it;
+ * the GPU library never does, and the two share no code.
+ *
+ * Everything is computed in double precision with plain loops: no BLAS,
+ * no intrinsics, no fast-math.  bf16 inputs (raw 16-bit patterns) and
+ * fp32 inputs are widened to double exactly.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [FD]  "Fast-dVLM: block diffusion ..." write-up (itsolotime.com),
+ *        section 4.1 (causal-context attention: noisy block attends to
+ *        itself bidirectionally and to every earlier clean position incl.
+ *        vision; clean tokens stay causal), section 5.1 (each block opens
+ *        with an AR step), section 5.3 (linear self-speculative decoding:
+ *        bidirectional draft, causal verify, accept the longest matching
+ *        prefix, crop the KV cache).
+ *  [FD2] Fast-dVLM summary page (signal-papers), Fig. 3 caption
+ *        (M_N2N is block-diagonal; vision tokens only in the clean stream).
+ *  [DV]  "DiffusionVL" notes (papernotes.org), "cached block decoding"
+ *        design item and Algorithm 1 as restated there: confidence is the
+ *        model probability of the chosen token; static commit takes the
+ *        k = min(ceil(D/S), |M|) most confident masked positions; the
+ *        dynamic rule also commits every masked position whose confidence
+ *        is greater than tau; committed tokens stay as context; a finished
+ *        block joins the KV cache.
+ *
+ * Readings where the pages are silent (each also listed in the design
+ * notes): scale 1/sqrt(d) is passed in; GQA head h uses KV head
+ * h / (Hq/Hkv); Q and K are already position-encoded; the greedy token is
+ * the argmax with the lowest index on ties; "greater than tau" is strict;
+ * positions are ranked by (confidence desc, index asc); the commit decision
+ * is taken on confidences rounded to fp32, the precision the GPU decides in.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define BDO_F32 0
+#define BDO_BF16 1
+#define BDO_BIDIR 0
+#define BDO_CAUSAL 1
+
+static double widen(const void *base, int dtype, size_t idx) {
+    if (dtype == BDO_F32) return (double)((const float *)base)[idx];
+    uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+int bdo_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Block attention ([FD] 4.1, 5.3; [FD2] Fig. 3).
+ *
+ * Key sequence of item n: positions 0..P-1 come from the frozen cache,
+ * positions P..P+D-1 are this step's block slots 0..D-1.
+ * Query (slot i, head h) may attend to key position j when
+ *   j < P                      (every earlier clean position, vision included), or
+ *   BIDIR:  P <= j < P + D     (the whole current block), or
+ *   CAUSAL: P <= j <= P + i    (the block up to and including itself).
+ * o = sum_j w_j v_j / sum_j w_j,  w_j = exp(s_j - max s),  s_j = scale * <q, k_j>.
+ *
+ * Layouts: q [n][D][Hq][d], k_blk/v_blk [n][D][Hkv][d],
+ * k_cache [n][Hkv][cap][d], v_cache [n][Hkv][d][cap] (transposed),
+ * out [n][D][Hq][d] double.
+ */
+void bdo_attention(int n, int D, int Hq, int Hkv, int d, int cap, int dtype, int mode,
+                   double scale, const void *q, const void *k_blk, const void *v_blk,
+                   const void *k_cache, const void *v_cache, const int32_t *prefix_len,
+                   double *out) {
+    const int group = Hq / Hkv;
+    long total = (long)n * D * Hq;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (long u = 0; u < total; ++u) {
+        const int it = (int)(u / ((long)D * Hq));
+        const int i = (int)((u / Hq) % D);
+        const int h = (int)(u % Hq);
+        const int g = h / group;
+        const int P = prefix_len[it];
+        const int nkeys = P + D;
+        double *s = (double *)malloc(sizeof(double) * (size_t)(nkeys > 0 ? nkeys : 1));
+        const size_t qoff = (((size_t)it * D + i) * Hq + h) * (size_t)d;
+        double m = -INFINITY;
+        for (int j = 0; j < nkeys; ++j) {
+            int allowed = (j < P) || (mode == BDO_BIDIR) || (j - P <= i);
+            if (!allowed) { s[j] = -INFINITY; continue; }
+            double acc = 0.0;
+            for (int t = 0; t < d; ++t) {
+                double kv;
+                if (j < P)
+                    kv = widen(k_cache, dtype, (((size_t)it * Hkv + g) * cap + j) * (size_t)d + t);
+                else
+                    kv = widen(k_blk, dtype, (((size_t)it * D + (j - P)) * Hkv + g) * (size_t)d + t);
+                acc += widen(q, dtype, qoff + t) * kv;
+            }
+            s[j] = scale * acc;
+            if (s[j] > m) m = s[j];
+        }
+        double denom = 0.0;
+        for (int j = 0; j < nkeys; ++j) {
+            s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
+            denom += s[j];
+        }
+        for (int t = 0; t < d; ++t) {
+            double acc = 0.0;
+            for (int j = 0; j < nkeys; ++j) {
+                if (s[j] == 0.0) continue;
+                double vv;
+                if (j < P)
+                    vv = widen(v_cache, dtype, (((size_t)it * Hkv + g) * d + t) * (size_t)cap + j);
+                else
+                    vv = widen(v_blk, dtype, (((size_t)it * D + (j - P)) * Hkv + g) * (size_t)d + t);
+                acc += s[j] * vv;
+            }
+            out[qoff + t] = acc / denom;
+        }
+        free(s);
+    }
+}
+
+/*
+ * Confidence of one row of logits ([DV] cached block decoding: the
+ * confidence of a position is the model probability of the token chosen
+ * for it).  Greedy choice a = first index of the maximum (values compared
+ * exactly); conf = 1 / sum_v exp(x_v - x_a); lse = x_a + log(sum).
+ * p2 = probability of the best token other than a (diagnostic).
+ */
+void bdo_confidence_row(int V, const float *x, double *conf, int32_t *argmax, double *lse,
+                        double *p2) {
+    int a = 0;
+    for (int v = 1; v < V; ++v)
+        if (x[v] > x[a]) a = v;
+    double m = (double)x[a];
+    double z = 0.0;
+    for (int v = 0; v < V; ++v) z += exp((double)x[v] - m);
+    double second = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if (v != a && (double)x[v] > second) second = (double)x[v];
+    *argmax = a;
+    *conf = 1.0 / z;
+    if (lse) *lse = m + log(z);
+    if (p2) *p2 = exp(second - m) / z;
+}
+
+/* k = min(ceil(D / S), |M|)  ([DV] Algorithm 1 as restated in the notes). */
+int bdo_commit_k(int D, int S, int n_masked) {
+    int k = (D + S - 1) / S;
+    return k < n_masked ? k : n_masked;
+}
+
+/* a ranks before b: higher fp32 confidence first, lower index on equal confidence. */
+static int ranks_before(float ca, int ia, float cb, int ib) {
+    return (ca > cb) || (ca == cb && ia < ib);
+}
+
+/*
+ * One denoising step's confidence + commit for n_req requests ([DV]
+ * cached block decoding; Algorithm 1; dynamic rule).
+ *   M = masked positions; for i in M: (conf_i, a_i) from the row's logits.
+ *   k = min(ceil(D/S), |M|); T = the k positions of M ranked first;
+ *   H = { i in M : conf_i > tau };  commit C = T u H:
+ *   tokens[i] = a_i, masked[i] = 0, committed[i] = 1.
+ * Positions outside M are not read and never change.
+ * conf_out (double, NaN outside M) and argmax_out (-1 outside M) report
+ * the fp64 values; the ranking and threshold use them rounded to fp32.
+ */
+void bdo_confidence_commit(int n_req, int D, int V, int S, float tau, const float *logits,
+                           uint8_t *masked, int32_t *tokens, double *conf_out,
+                           int32_t *argmax_out, uint8_t *committed_out,
+                           int32_t *n_committed_out) {
+    double *conf = (double *)malloc(sizeof(double) * (size_t)D);
+    float *c32 = (float *)malloc(sizeof(float) * (size_t)D);
+    int32_t *amax = (int32_t *)malloc(sizeof(int32_t) * (size_t)D);
+    uint8_t *take = (uint8_t *)malloc((size_t)D);
+    for (int r = 0; r < n_req; ++r) {
+        int n_m = 0;
+        for (int i = 0; i < D; ++i) {
+            conf[i] = NAN;
+            amax[i] = -1;
+            take[i] = 0;
+            if (masked[(size_t)r * D + i]) {
+                ++n_m;
+                bdo_confidence_row(V, logits + ((size_t)r * D + i) * (size_t)V, &conf[i], &amax[i],
+                                   NULL, NULL);
+            }
+            c32[i] = (float)conf[i];
+        }
+        int k = bdo_commit_k(D, S, n_m);
+        for (int i = 0; i < D; ++i) {
+            if (!masked[(size_t)r * D + i]) continue;
+            int rank = 0;
+            for (int j = 0; j < D; ++j)
+                if (j != i && masked[(size_t)r * D + j] && ranks_before(c32[j], j, c32[i], i)) ++rank;
+            if (rank < k || c32[i] > tau) take[i] = 1;
+        }
+        int cnt = 0;
+        for (int i = 0; i < D; ++i) {
+            size_t o = (size_t)r * D + i;
+            if (conf_out) conf_out[o] = conf[i];
+            if (argmax_out) argmax_out[o] = amax[i];
+            if (committed_out) committed_out[o] = take[i];
+            if (take[i]) {
+                tokens[o] = amax[i];
+                masked[o] = 0;
+                ++cnt;
+            }
+        }
+        if (n_committed_out) n_committed_out[r] = cnt;
+    }
+    free(conf);
+    free(c32);
+    free(amax);
+    free(take);
+}
+
+/*
+ * Speculative verify ([FD] 5.3, linear variant): row i of the causal
+ * pass gives the AR prediction for draft slot i (greedy, lowest index on
+ * ties); L = first i whose prediction differs from draft[i], or D if all
+ * agree.
+ */
+void bdo_spec_verify(int n_req, int D, int V, const float *logits, const int32_t *draft,
+                     int32_t *accepted_len, int32_t *argmax_out) {
+    for (int r = 0; r < n_req; ++r) {
+        int L = D;
+        for (int i = 0; i < D; ++i) {
+            const float *x = logits + ((size_t)r * D + i) * (size_t)V;
+            int a = 0;
+            for (int v = 1; v < V; ++v)
+                if (x[v] > x[a]) a = v;
+            if (argmax_out) argmax_out[(size_t)r * D + i] = a;
+            if (L == D && a != draft[(size_t)r * D + i]) L = i;
+        }
+        accepted_len[r] = L;
+    }
+}
+
+/*
+ * Append the accepted block K/V to the frozen cache ([FD] 5.3: crop the
+ * cache to the accepted prefix; [DV] a finished block joins the history
+ * cache).  For item it with L = n_accept[it] (D when n_accept is NULL):
+ * cache slots P..P+L-1 receive block slots 0..L-1 bit for bit and
+ * prefix_len[it] becomes P+L.  If P+L exceeds cap the item is left
+ * untouched and *err is set to 1.
+ */
+void bdo_kv_append(int n, int D, int Hkv, int d, int cap, int dtype, void *k_cache, void *v_cache,
+                   int32_t *prefix_len, const void *k_blk, const void *v_blk,
+                   const int32_t *n_accept, int32_t *err) {
+    size_t es = dtype == BDO_F32 ? 4 : 2;
+    for (int it = 0; it < n; ++it) {
+        int P = prefix_len[it];
+        int L = n_accept ? n_accept[it] : D;
+        if (L < 0 || L > D || P + L > cap) {
+            if (err) *err = 1;
+            continue;
+        }
+        for (int t = 0; t < L; ++t)
+            for (int g = 0; g < Hkv; ++g)
+                for (int e = 0; e < d; ++e) {
+                    size_t src = (((size_t)it * D + t) * Hkv + g) * (size_t)d + e;
+                    size_t kdst = (((size_t)it * Hkv + g) * cap + (P + t)) * (size_t)d + e;
+                    size_t vdst = (((size_t)it * Hkv + g) * d + e) * (size_t)cap + (P + t);
+                    memcpy((char *)k_cache + kdst * es, (const char *)k_blk + src * es, es);
+                    memcpy((char *)v_cache + vdst * es, (const char *)v_blk + src * es, es);
+                }
+        prefix_len[it] = P + L;
+    }
+}

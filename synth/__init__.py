@@ -1,0 +1,7 @@
+"""Seeded synthetic workloads shared by the CPU oracle tests, the GPU parity tests and the benchmark.
+
+Holds configuration data and random draws only; no part of the step's arithmetic lives here.
+"""
+from .configs import BF16, BIDIR, CAUSAL, CONFIGS, F32, seed_of  # noqa: F401
+from .gen import (bf16_bits_to_f32, cache_capacity, config_step, f32_to_bf16_bits,  # noqa: F401
+                  fresh_logits, make_step, params_for)

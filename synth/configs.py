@@ -1,0 +1,60 @@
+"""The five step workloads, as plain data.
+
+Each entry fixes the shapes and value distributions of one synthetic
+block-diffusion step.  The geometries follow the Qwen2.5-VL-3B / 7B
+attention shapes that the Fast-dVLM write-up builds on (itsolotime.com
+"Fast-dVLM" page, introduction: a Qwen2.5-VL-3B base) and the block sizes
+8 / 16 / 32 that both pages discuss (Fast-dVLM page, sections 4.2 and 5.3,
+Fig. 6; DiffusionVL notes, "cached block decoding", default training block
+D = 8).
+
+Distribution strings read as variance: ``sigma2 = 4`` means standard
+deviation 2.  Nothing here computes any part of the method.
+"""
+
+F32 = 0
+BF16 = 1
+
+BIDIR = 0   # denoise step: the whole current block is visible to each slot
+CAUSAL = 1  # verify step: slot i sees the block only up to itself
+
+CONFIGS = {
+    1: dict(
+        name="tiny: 1 item, 2q/1kv heads, d64, fp32, prefix 64, D=8 (4 masked), V=1000",
+        n_items=1, n_req=1, Hq=2, Hkv=1, d=64, dtype=F32, mode=BIDIR,
+        prefix=("fixed", 64), D=8, n_masked=4, V=1000, logit_sigma2=3.0,
+        plant=None, S=8, tau=0.9,
+    ),
+    2: dict(
+        name="3B single layer: 16q/2kv, d128, bf16, prefix 1024 (768 vision + 256 text), "
+             "D=8 all masked, V=151936 with a +8 planted peak",
+        n_items=1, n_req=1, Hq=16, Hkv=2, d=128, dtype=BF16, mode=BIDIR,
+        prefix=("fixed", 1024), D=8, n_masked=8, V=151936, logit_sigma2=4.0,
+        plant="peak8", S=8, tau=0.9,
+    ),
+    3: dict(
+        name="3B long-reasoning step: 36 layers x (16q/2kv, d128, bf16, prefix 4096), "
+             "D=16 with 8 committed, V=151936, S=16, tau=0.9",
+        n_items=36, n_req=1, Hq=16, Hkv=2, d=128, dtype=BF16, mode=BIDIR,
+        prefix=("fixed", 4096), D=16, n_masked=8, V=151936, logit_sigma2=4.0,
+        plant=None, S=16, tau=0.9,
+    ),
+    4: dict(
+        name="3B self-speculative verify: 16q/2kv, d128, bf16, prefix 2048, D=16 draft, "
+             "causal, V=151936, geometric(0.3) accepted prefix, then append",
+        n_items=1, n_req=1, Hq=16, Hkv=2, d=128, dtype=BF16, mode=CAUSAL,
+        prefix=("fixed", 2048), D=16, n_masked=16, V=151936, logit_sigma2=4.0,
+        plant="geom0.3", S=16, tau=0.9,
+    ),
+    5: dict(
+        name="7B batched step: 8 requests, prefixes U{2048..8192}, 28q/4kv, d128, bf16, "
+             "D=32 all masked, V=152064, S=8, tau=0.8",
+        n_items=8, n_req=8, Hq=28, Hkv=4, d=128, dtype=BF16, mode=BIDIR,
+        prefix=("uniform", 2048, 8192), D=32, n_masked=32, V=152064, logit_sigma2=4.0,
+        plant=None, S=8, tau=0.8,
+    ),
+}
+
+
+def seed_of(cfg_id: int) -> int:
+    return 1000 + int(cfg_id)

@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs for one block-diffusion step.
+
+This module draws numbers and lays them out in the byte layouts that the
+C-ABI library and the CPU oracle both read.  It holds none of the step's
+arithmetic (no attention, no softmax, no ranking): only random draws, the
+bf16 rounding of those draws, placement in memory, and the planting of
+chosen logit peaks.
+
+Layouts (row-major, innermost last):
+
+    q        [n][D][Hq][d]        this step's queries for every block slot
+    k_blk    [n][D][Hkv][d]       this step's block keys
+    v_blk    [n][D][Hkv][d]       this step's block values
+    k_cache  [n][Hkv][cap][d]     frozen keys of the prompt and finished blocks
+    v_cache  [n][Hkv][d][cap]     frozen values, stored transposed (d-major)
+    prefix   int32[n]             valid cache length per item
+    logits   f32 [n_req][D][V]
+    masked   u8  [n_req][D]       1 = still [MASK]
+    tokens   i32 [n_req][D]       committed ids; -1 at masked slots
+    draft    i32 [n_req][D]       draft ids to verify (speculative configs)
+
+Cache slots at and beyond ``prefix`` are filled with NaN bit patterns, so
+a kernel that reads past the valid prefix cannot go unnoticed.
+
+Draw order for a step (one Generator(PCG64(seed)) per step): prefix
+lengths, Q, K cache, V cache, block K, block V, the masked set, committed
+token ids, logits, then plants.
+"""
+
+import numpy as np
+
+from .configs import BF16, CONFIGS, F32, seed_of
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round to nearest, ties to even); return the raw 16-bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = ((b >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((b + rounding) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 patterns to float32 exactly."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal(rng, shape, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == BF16 else x
+
+
+def cache_capacity(max_prefix: int, D: int) -> int:
+    """Room for the longest prefix plus one appended block, rounded up to 64 slots."""
+    return ((max_prefix + D + 63) // 64) * 64
+
+
+def params_for(cfg_id: int, **overrides) -> dict:
+    p = dict(CONFIGS[cfg_id])
+    p.update(overrides)
+    return p
+
+
+def make_step(p: dict, seed: int, plant_L=None) -> dict:
+    """Draw one step's inputs for parameter dict ``p`` (a config, possibly overridden).
+
+    ``plant_L`` forces the accepted-prefix length of a speculative plant
+    (used for the L = 0 and L = D edge cases).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n, D, Hq, Hkv, d = p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"]
+    dtype = p["dtype"]
+    kind = p["prefix"][0]
+    if kind == "fixed":
+        prefix = np.full(n, p["prefix"][1], dtype=np.int32)
+    elif kind == "uniform":
+        lo, hi = p["prefix"][1], p["prefix"][2]
+        prefix = rng.integers(lo, hi + 1, size=n, dtype=np.int64).astype(np.int32)
+    elif kind == "list":
+        prefix = np.asarray(p["prefix"][1], dtype=np.int32)
+        assert prefix.shape == (n,)
+    else:
+        raise ValueError(kind)
+    max_prefix = int(prefix.max()) if n else 0
+    cap = p.get("cap") or cache_capacity(max_prefix, D)
+    elem = np.uint16 if dtype == BF16 else np.float32
+    nan = BF16_NAN if dtype == BF16 else np.float32(np.nan)
+
+    q = _normal(rng, (n, D, Hq, d), dtype)
+    k_cache = np.full((n, Hkv, cap, d), nan, dtype=elem)
+    v_cache = np.full((n, Hkv, d, cap), nan, dtype=elem)
+    for it in range(n):
+        P = int(prefix[it])
+        k_cache[it, :, :P, :] = _normal(rng, (Hkv, P, d), dtype)
+    for it in range(n):
+        P = int(prefix[it])
+        v_nat = _normal(rng, (Hkv, P, d), dtype)
+        v_cache[it, :, :, :P] = np.swapaxes(v_nat, 1, 2)
+    k_blk = _normal(rng, (n, D, Hkv, d), dtype)
+    v_blk = _normal(rng, (n, D, Hkv, d), dtype)
+
+    n_req, V = p["n_req"], p["V"]
+    masked = np.zeros((n_req, D), dtype=np.uint8)
+    tokens = np.full((n_req, D), -1, dtype=np.int32)
+    for r in range(n_req):
+        perm = rng.permutation(D)
+        masked[r, perm[: p["n_masked"]]] = 1
+    for r in range(n_req):
+        ids = rng.integers(0, V, size=D, dtype=np.int64).astype(np.int32)
+        tokens[r] = np.where(masked[r] == 1, -1, ids)
+
+    std = np.float32(np.sqrt(p["logit_sigma2"]))
+    logits = rng.standard_normal(size=(n_req, D, V), dtype=np.float32) * std
+
+    out = dict(params=p, seed=seed, cap=cap, prefix=prefix, q=q, k_cache=k_cache,
+               v_cache=v_cache, k_blk=k_blk, v_blk=v_blk, masked=masked, tokens=tokens,
+               logits=logits)
+
+    plant = p.get("plant")
+    if plant == "peak8":
+        for r in range(n_req):
+            for i in range(D):
+                v_star = int(rng.integers(0, V))
+                logits[r, i, v_star] = logits[r, i].max() + np.float32(8.0)
+    elif plant == "geom0.3":
+        draft = rng.integers(0, V, size=(n_req, D), dtype=np.int64).astype(np.int32)
+        Ls = np.zeros(n_req, dtype=np.int32)
+        for r in range(n_req):
+            L = int(rng.geometric(0.3)) - 1  # P(L = l) = 0.3 * 0.7**l, l >= 0
+            if plant_L is not None:
+                L = int(plant_L)
+            L = min(L, D)
+            Ls[r] = L
+            for i in range(L):
+                logits[r, i, draft[r, i]] = logits[r, i].max() + np.float32(8.0)
+            if L < D:
+                logits[r, L, draft[r, L]] = logits[r, L].min() - np.float32(1.0)
+        out["draft"] = draft
+        out["planted_L"] = Ls
+    return out
+
+
+def fresh_logits(p: dict, rng: np.random.Generator) -> np.ndarray:
+    """Logits for a later denoising step of the same block (no plant)."""
+    std = np.float32(np.sqrt(p["logit_sigma2"]))
+    return rng.standard_normal(size=(p["n_req"], p["D"], p["V"]), dtype=np.float32) * std
+
+
+def config_step(cfg_id: int, **overrides) -> dict:
+    """The canonical seeded step of a config (seed 1000 + config number)."""
+    return make_step(params_for(cfg_id, **overrides), seed_of(cfg_id))

@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against something it does not share code with:
+a dense attention mask built from the pages' three mask rules and evaluated
+by torch's SDPA in float64, library routines (scipy ``logsumexp``, numpy
+``argmax``), closed forms, brute force over all choices on tiny inputs,
+invariants, and the worked example printed on the pages
+(``tests/golden/commit_k.json``).
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+from synth import BF16, BIDIR, CAUSAL, F32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _widen(a):
+    return synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def _rand(rng, shape, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return synth.f32_to_bf16_bits(x) if dtype == BF16 else x
+
+
+def _pack_cache(k_seq, v_seq, cap, dtype):
+    """k_seq/v_seq: [Hkv][P][d] -> cache layouts [1][Hkv][cap][d] and [1][Hkv][d][cap] (NaN tail)."""
+    Hkv, P, d = k_seq.shape
+    el = np.uint16 if dtype == BF16 else np.float32
+    nan = synth.gen.BF16_NAN if dtype == BF16 else np.float32(np.nan)
+    kc = np.full((1, Hkv, cap, d), nan, el)
+    vc = np.full((1, Hkv, d, cap), nan, el)
+    kc[0, :, :P, :] = k_seq
+    vc[0, :, :, :P] = np.swapaxes(v_seq, 1, 2)
+    return kc, vc
+
+
+def _sdpa(q, k, v, mask, group):
+    """torch SDPA in float64; q [Hq][Lq][d], k/v [Hkv][Lk][d], mask [Lq][Lk] bool."""
+    qt = torch.from_numpy(q)[None]
+    kt = torch.from_numpy(k).repeat_interleave(group, dim=0)[None]
+    vt = torch.from_numpy(v).repeat_interleave(group, dim=0)[None]
+    m = None if mask is None else torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m)[0].numpy()
+
+
+# ---------------------------------------------------------------------------
+# Attention: two-stream training mask (Fast-dVLM write-up section 4.1; summary
+# page Fig. 3) evaluated densely, versus the oracle's per-block inference form.
+# ---------------------------------------------------------------------------
+
+def _two_stream_mask(n_vis, n_txt, D, B):
+    """Mask over [noisy stream w ; clean stream x] built from the three rules:
+    M_N2N block-diagonal among noisy tokens; M_N2C noisy block b sees vision,
+    prompt text and clean blocks before b; M_C2C clean tokens causal.  Clean
+    tokens never see noisy ones.  Vision lives only in the clean stream."""
+    Ln = B * D
+    Lp = n_vis + n_txt
+    Lc = Lp + B * D
+    L = Ln + Lc
+    mask = np.zeros((L, L), dtype=bool)
+    for b in range(B):
+        rows = slice(b * D, (b + 1) * D)
+        mask[rows, b * D:(b + 1) * D] = True                # M_N2N
+        mask[rows, Ln:Ln + Lp] = True                        # M_N2C: vision + prompt
+        mask[rows, Ln + Lp:Ln + Lp + b * D] = True           # M_N2C: earlier clean blocks
+    for c in range(Lc):
+        mask[Ln + c, Ln:Ln + c + 1] = True                   # M_C2C
+    return mask
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("Hq,Hkv,d", [(2, 1, 8), (4, 2, 16), (6, 3, 8)])
+def test_attention_matches_two_stream_dense_mask(dtype, Hq, Hkv, d):
+    rng = np.random.Generator(np.random.PCG64(7 + Hq + d))
+    n_vis, n_txt, D, B = 5, 3, 4, 3
+    Ln, Lp = B * D, n_vis + n_txt
+    Lc = Lp + B * D
+    L = Ln + Lc
+    group = Hq // Hkv
+    Q = _rand(rng, (Hq, L, d), dtype)
+    K = _rand(rng, (Hkv, L, d), dtype)
+    V = _rand(rng, (Hkv, L, d), dtype)
+    ref = _sdpa(_widen(Q), _widen(K), _widen(V), _two_stream_mask(n_vis, n_txt, D, B), group)
+    for b in range(B):
+        P = Lp + b * D
+        cap = P + D + 3
+        ctx = slice(Ln, Ln + P)                               # clean positions before block b
+        kc, vc = _pack_cache(K[:, ctx], V[:, ctx], cap, dtype)
+        # Noisy block b: denoise attention (bidirectional inside the block).
+        nz = slice(b * D, (b + 1) * D)
+        q = np.ascontiguousarray(np.swapaxes(Q[:, nz], 0, 1))[None]
+        kb = np.ascontiguousarray(np.swapaxes(K[:, nz], 0, 1))[None]
+        vb = np.ascontiguousarray(np.swapaxes(V[:, nz], 0, 1))[None]
+        out = oracle.attention(q, kb, vb, kc, vc, np.array([P], np.int32), BIDIR)
+        np.testing.assert_allclose(out[0], np.swapaxes(ref[:, nz], 0, 1), rtol=0, atol=1e-12)
+        # Clean block b: the causal (verify / AR) pass over the filled block.
+        cl = slice(Ln + P, Ln + P + D)
+        q = np.ascontiguousarray(np.swapaxes(Q[:, cl], 0, 1))[None]
+        kb = np.ascontiguousarray(np.swapaxes(K[:, cl], 0, 1))[None]
+        vb = np.ascontiguousarray(np.swapaxes(V[:, cl], 0, 1))[None]
+        out = oracle.attention(q, kb, vb, kc, vc, np.array([P], np.int32), CAUSAL)
+        np.testing.assert_allclose(out[0], np.swapaxes(ref[:, cl], 0, 1), rtol=0, atol=1e-12)
+
+
+def _random_step(rng, n, D, Hq, Hkv, d, P, dtype, cap=None):
+    prefix = np.asarray(P, np.int32)
+    cap = cap or int(prefix.max()) + D + 5
+    q = _rand(rng, (n, D, Hq, d), dtype)
+    kb = _rand(rng, (n, D, Hkv, d), dtype)
+    vb = _rand(rng, (n, D, Hkv, d), dtype)
+    el = np.uint16 if dtype == BF16 else np.float32
+    nan = synth.gen.BF16_NAN if dtype == BF16 else np.float32(np.nan)
+    kc = np.full((n, Hkv, cap, d), nan, el)
+    vc = np.full((n, Hkv, d, cap), nan, el)
+    for it in range(n):
+        p = int(prefix[it])
+        kc[it, :, :p] = _rand(rng, (Hkv, p, d), dtype)
+        vc[it, :, :, :p] = _rand(rng, (Hkv, d, p), dtype)
+    return q, kb, vb, kc, vc, prefix
+
+
+def _keys_natural(kc, vc, kb, vb, it, P):
+    """Key/value sequences [Hkv][P+D][d] of item ``it`` in natural layout."""
+    k = np.concatenate([kc[it, :, :P], np.swapaxes(kb[it], 0, 1)], axis=1)
+    v = np.concatenate([np.swapaxes(vc[it, :, :, :P], 1, 2), np.swapaxes(vb[it], 0, 1)], axis=1)
+    return k, v
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_single_slot_is_textbook_decode(dtype):
+    """D = 1: the block step is ordinary single-query decode over P + 1 keys
+    (each block opens with one AR step: Fast-dVLM write-up, section 5.1)."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    n, Hq, Hkv, d = 3, 4, 2, 16
+    q, kb, vb, kc, vc, prefix = _random_step(rng, n, 1, Hq, Hkv, d, [0, 9, 40], dtype)
+    o_c = oracle.attention(q, kb, vb, kc, vc, prefix, CAUSAL)
+    o_b = oracle.attention(q, kb, vb, kc, vc, prefix, BIDIR)
+    np.testing.assert_array_equal(o_c, o_b)
+    for it in range(n):
+        k, v = _keys_natural(kc, vc, kb, vb, it, int(prefix[it]))
+        ref = _sdpa(np.swapaxes(_widen(q[it]), 0, 1), _widen(k), _widen(v), None, Hq // Hkv)
+        np.testing.assert_allclose(o_c[it], np.swapaxes(ref, 0, 1), rtol=0, atol=1e-12)
+
+
+def test_empty_prefix_bidir_is_full_attention_over_block():
+    rng = np.random.Generator(np.random.PCG64(12))
+    q, kb, vb, kc, vc, prefix = _random_step(rng, 1, 6, 4, 1, 8, [0], F32)
+    out = oracle.attention(q, kb, vb, kc, vc, prefix, BIDIR)
+    ref = _sdpa(np.swapaxes(_widen(q[0]), 0, 1), _widen(np.swapaxes(kb[0], 0, 1)),
+                _widen(np.swapaxes(vb[0], 0, 1)), None, 4)
+    np.testing.assert_allclose(out[0], np.swapaxes(ref, 0, 1), rtol=0, atol=1e-12)
+
+
+def test_causal_with_cache_is_chunked_prefill():
+    """CAUSAL with a cache equals causal attention over the concatenated sequence (rows of the block)."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    D, P = 5, 17
+    q, kb, vb, kc, vc, prefix = _random_step(rng, 1, D, 2, 2, 8, [P], F32)
+    out = oracle.attention(q, kb, vb, kc, vc, prefix, CAUSAL)
+    k, v = _keys_natural(kc, vc, kb, vb, 0, P)
+    mask = np.tril(np.ones((P + D, P + D), bool))[P:]
+    ref = _sdpa(np.swapaxes(_widen(q[0]), 0, 1), _widen(k), _widen(v), mask, 1)
+    np.testing.assert_allclose(out[0], np.swapaxes(ref, 0, 1), rtol=0, atol=1e-12)
+
+
+def test_attention_invariants():
+    rng = np.random.Generator(np.random.PCG64(14))
+    n, D, Hq, Hkv, d = 2, 4, 4, 2, 8
+    q, kb, vb, kc, vc, prefix = _random_step(rng, n, D, Hq, Hkv, d, [20, 33], F32)
+    base = oracle.attention(q, kb, vb, kc, vc, prefix, BIDIR)
+    assert np.all(np.isfinite(base)), "NaN canaries past the prefix must never be read"
+    # Constant values give that constant, whatever the scores.
+    vc2, vb2 = vc.copy(), vb.copy()
+    for it in range(n):
+        vc2[it, :, :, :prefix[it]] = 0.75
+    vb2[:] = 0.75
+    const = oracle.attention(q, kb, vb2, kc, vc2, prefix, BIDIR)
+    np.testing.assert_allclose(const, 0.75, rtol=0, atol=1e-14)
+    # Permuting prefix positions (keys with their values) changes nothing.
+    kc3, vc3 = kc.copy(), vc.copy()
+    for it in range(n):
+        P = int(prefix[it])
+        perm = rng.permutation(P)
+        kc3[it, :, :P] = kc[it, :, perm].swapaxes(0, 1)
+        vc3[it, :, :, :P] = vc[it, :, :, perm].transpose(1, 2, 0)
+    perm_out = oracle.attention(q, kb, vb, kc3, vc3, prefix, BIDIR)
+    np.testing.assert_allclose(perm_out, base, rtol=0, atol=1e-12)
+    # CAUSAL differs from BIDIR only in the block: the last slot sees the whole block either way.
+    caus = oracle.attention(q, kb, vb, kc, vc, prefix, CAUSAL)
+    np.testing.assert_allclose(caus[:, D - 1], base[:, D - 1], rtol=0, atol=1e-13)
+    assert not np.allclose(caus[:, 0], base[:, 0])
+
+
+def test_gqa_grouping_is_contiguous():
+    """Heads 0..G-1 share KV head 0 (contiguous grouping): with identical queries per
+    group, every head of a group must give the same output and the groups differ."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    q, kb, vb, kc, vc, prefix = _random_step(rng, 1, 3, 6, 2, 8, [10], F32)
+    q[:, :, :, :] = q[:, :, :1, :]
+    out = oracle.attention(q, kb, vb, kc, vc, prefix, BIDIR)
+    np.testing.assert_array_equal(out[:, :, 1], out[:, :, 0])
+    np.testing.assert_array_equal(out[:, :, 2], out[:, :, 0])
+    np.testing.assert_array_equal(out[:, :, 4], out[:, :, 3])
+    assert not np.allclose(out[:, :, 3], out[:, :, 0])
+
+
+# ---------------------------------------------------------------------------
+# Confidence (DiffusionVL notes, cached block decoding: confidence is the
+# probability of the chosen token).
+# ---------------------------------------------------------------------------
+
+def test_confidence_matches_logsumexp_and_argmax():
+    rng = np.random.Generator(np.random.PCG64(21))
+    for V, sig in [(2, 1.0), (1000, math.sqrt(3)), (151936, 2.0)]:
+        x = (rng.standard_normal(V, dtype=np.float32) * np.float32(sig))
+        conf, a, lse, p2 = oracle.confidence_row(x)
+        assert a == int(np.argmax(x))
+        ref_lse = scipy.special.logsumexp(x.astype(np.float64))
+        assert abs(lse - ref_lse) <= 1e-12 * max(1.0, abs(ref_lse))
+        assert abs(conf - math.exp(float(x[a]) - ref_lse)) <= 1e-14
+        xs = np.sort(x.astype(np.float64))
+        assert abs(p2 - math.exp(xs[-2] - ref_lse)) <= 1e-14
+
+
+def test_confidence_closed_forms():
+    V = 50
+    conf, a, _, _ = oracle.confidence_row(np.full(V, 0.3, np.float32))
+    assert a == 0 and abs(conf - 1.0 / V) < 1e-15
+    x = np.full(V, -1.0, np.float32)
+    x[17] = 2.0
+    conf, a, _, _ = oracle.confidence_row(x)
+    ref = math.exp(2.0) / (math.exp(2.0) + (V - 1) * math.exp(-1.0))
+    assert a == 17 and abs(conf - ref) < 1e-15
+    # Shift invariance (integer logits keep the shift exact in fp32).
+    rng = np.random.Generator(np.random.PCG64(22))
+    xi = rng.integers(-20, 20, size=300).astype(np.float32)
+    c0, a0, _, _ = oracle.confidence_row(xi)
+    c1, a1, _, _ = oracle.confidence_row(xi + np.float32(64.0))
+    assert a0 == a1 and abs(c0 - c1) < 1e-15
+    # Ties go to the lowest index.
+    x = np.zeros(10, np.float32)
+    x[[7, 3, 9]] = 5.0
+    assert oracle.confidence_row(x)[1] == 3
+
+
+# ---------------------------------------------------------------------------
+# Commit rule (DiffusionVL notes, Algorithm 1 and the dynamic rule).
+# ---------------------------------------------------------------------------
+
+def test_commit_k_matches_pages_worked_example():
+    with open(os.path.join(GOLDEN, "commit_k.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert oracle.commit_k(c["D"], c["S"], c["n_masked"]) == c["k"], c
+
+
+def _brute_commit(conf32, masked, k, tau):
+    """Top-k by exhaustive search: the unique k-subset of M whose every member
+    outranks every non-member under (confidence desc, index asc); plus {c > tau}."""
+    M = [i for i in range(len(masked)) if masked[i]]
+    before = lambda a, b: conf32[a] > conf32[b] or (conf32[a] == conf32[b] and a < b)
+    tops = [set(T) for T in itertools.combinations(M, k)
+            if all(before(t, u) for t in T for u in M if u not in T)]
+    assert len(tops) == 1
+    return tops[0] | {i for i in M if conf32[i] > np.float32(tau)}
+
+
+def _logits_for_conf(rng, D, V):
+    return (rng.standard_normal((1, D, V), dtype=np.float32) * np.float32(1.5))
+
+
+@pytest.mark.parametrize("D", [1, 2, 3, 4, 5, 6])
+def test_commit_brute_force_small_blocks(D):
+    rng = np.random.Generator(np.random.PCG64(30 + D))
+    V = 7
+    for trial in range(60):
+        logits = _logits_for_conf(rng, D, V)
+        if trial % 5 == 0:                       # force exact confidence ties
+            logits[0, :] = logits[0, 0]
+        masked = rng.integers(0, 2, size=(1, D)).astype(np.uint8)
+        tokens = np.where(masked == 1, -1, 5).astype(np.int32)
+        S = int(rng.integers(1, D + 2))
+        tau = float(rng.choice([0.2, 0.35, 0.5, 0.9, 1.0]))
+        r = oracle.confidence_commit(logits, masked, tokens, S, tau)
+        conf32 = r["conf"][0].astype(np.float32)
+        k = min(-(-D // S), int(masked.sum()))
+        want = _brute_commit(conf32, masked[0], k, tau)
+        got = set(np.nonzero(r["committed"][0])[0].tolist())
+        assert got == want, (trial, conf32, masked, k, tau)
+        for i in range(D):
+            if masked[0, i]:
+                assert r["argmax"][0, i] == int(np.argmax(logits[0, i]))
+            else:
+                assert r["tokens"][0, i] == tokens[0, i] and np.isnan(r["conf"][0, i])
+
+
+def test_commit_threshold_is_strict():
+    """'greater than tau': a confidence exactly equal to tau is not taken by the threshold."""
+    D, V = 4, 2
+    logits = np.zeros((1, D, V), np.float32)       # rows 1..3: conf exactly 0.5
+    logits[0, 0] = [10.0, 0.0]                     # row 0 wins the single top-k slot
+    masked = np.ones((1, D), np.uint8)
+    tokens = np.full((1, D), -1, np.int32)
+    r = oracle.confidence_commit(logits, masked, tokens, S=4, tau=0.5)
+    assert r["committed"][0].tolist() == [1, 0, 0, 0]
+    r = oracle.confidence_commit(logits, masked, tokens, S=4, tau=0.4999)
+    assert r["committed"][0].tolist() == [1, 1, 1, 1]
+
+
+def _run_block(p, seed, logits0, masked, tokens):
+    """Multi-step denoising of one block with fresh logits per step."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    steps, history = 0, []
+    logits = logits0
+    while masked.sum() > 0:
+        before_tokens = tokens.copy()
+        before_masked = masked.copy()
+        r = oracle.confidence_commit(logits, masked, tokens, p["S"], p["tau"])
+        masked, tokens = r["masked"], r["tokens"]
+        steps += 1
+        history.append((before_masked, before_tokens, r))
+        logits = synth.fresh_logits(p, rng)
+        assert steps <= p["S"] + 1
+    return steps, history
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_multistep_invariants(cfg):
+    """Committed tokens stay fixed; each step commits at least min(k, |M|);
+    a block finishes within S steps (DiffusionVL notes, cached block decoding)."""
+    s = synth.config_step(cfg)
+    p = s["params"]
+    steps, hist = _run_block(p, 99, s["logits"], s["masked"].copy(), s["tokens"].copy())
+    assert steps <= p["S"]
+    for before_m, before_t, r in hist:
+        for rq in range(p["n_req"]):
+            nm = int(before_m[rq].sum())
+            k = oracle.commit_k(p["D"], p["S"], nm)
+            assert int(r["n_committed"][rq]) >= k
+            keep = before_m[rq] == 0
+            np.testing.assert_array_equal(r["tokens"][rq][keep], before_t[rq][keep])
+            assert np.all(r["masked"][rq][keep] == 0)
+    if cfg == 2:
+        # Planted +8 peaks put most confidences near 0.93-0.98 (> tau = 0.9): most of
+        # the block commits in the first step through the threshold rule.
+        first = hist[0][2]
+        assert int(first["n_committed"][0]) >= 6 and steps <= 2
+        c32 = first["conf"][0].astype(np.float32)
+        for i in range(p["D"]):
+            if first["committed"][0, i] and c32[i] <= np.float32(p["tau"]):
+                assert c32[i] == c32.max()
+
+
+def test_threshold_off_gives_closed_form_step_count():
+    """With tau >= 1 nothing passes the threshold: exactly ceil(|M0| / ceil(D/S)) steps."""
+    for (D, S, nm) in [(8, 8, 8), (8, 4, 8), (16, 16, 8), (32, 8, 32), (16, 5, 11)]:
+        p = synth.params_for(1, D=D, S=S, n_masked=nm, tau=1.0, V=64)
+        s = synth.make_step(p, seed=5)
+        steps, _ = _run_block(p, 6, s["logits"], s["masked"].copy(), s["tokens"].copy())
+        k = -(-D // S)
+        assert steps == -(-nm // k), (D, S, nm, steps)
+
+
+# ---------------------------------------------------------------------------
+# Speculative verify and KV append (Fast-dVLM write-up, section 5.3).
+# ---------------------------------------------------------------------------
+
+def test_verify_recovers_planted_prefix():
+    for seed in range(40):
+        s = synth.make_step(synth.params_for(4, V=3000, prefix=("fixed", 8)), seed)
+        L, amax = oracle.spec_verify(s["logits"], s["draft"])
+        assert L[0] == s["planted_L"][0], seed
+        np.testing.assert_array_equal(amax[0], np.argmax(s["logits"][0], axis=1))
+    for forced in (0, 16):
+        s = synth.make_step(synth.params_for(4, V=3000, prefix=("fixed", 8)), 3, plant_L=forced)
+        L, _ = oracle.spec_verify(s["logits"], s["draft"])
+        assert L[0] == forced
+
+
+def test_verify_brute_force():
+    rng = np.random.Generator(np.random.PCG64(41))
+    for _ in range(50):
+        n, D, V = 3, 5, 4
+        logits = rng.integers(0, 3, size=(n, D, V)).astype(np.float32)   # many ties
+        draft = rng.integers(0, V, size=(n, D)).astype(np.int32)
+        L, _ = oracle.spec_verify(logits, draft)
+        for r in range(n):
+            want = D
+            for i in range(D):
+                if int(np.argmax(logits[r, i])) != draft[r, i]:
+                    want = i
+                    break
+            assert L[r] == want
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_kv_append_is_bitwise_and_bounded(dtype):
+    rng = np.random.Generator(np.random.PCG64(51))
+    n, D, Hq, Hkv, d = 3, 6, 4, 2, 8
+    q, kb, vb, kc, vc, prefix = _random_step(rng, n, D, Hq, Hkv, d, [5, 0, 9], dtype, cap=16)
+    acc = np.array([2, 6, 0], np.int32)
+    kc2, vc2, p2, err = oracle.kv_append(kc, vc, prefix, kb, vb, acc)
+    assert err == 0 and p2.tolist() == [7, 6, 9]
+    for it in range(n):
+        P, L = int(prefix[it]), int(acc[it])
+        np.testing.assert_array_equal(kc2[it, :, P:P + L], np.swapaxes(kb[it, :L], 0, 1))
+        np.testing.assert_array_equal(vc2[it, :, :, P:P + L], np.transpose(vb[it, :L], (1, 2, 0)))
+        untouched_k = np.ones(kc.shape[2], bool)
+        untouched_k[P:P + L] = False
+        bits = lambda a: np.ascontiguousarray(a).view(np.uint8)
+        np.testing.assert_array_equal(bits(kc2[it][:, untouched_k]), bits(kc[it][:, untouched_k]))
+        np.testing.assert_array_equal(bits(vc2[it][:, :, untouched_k]), bits(vc[it][:, :, untouched_k]))
+    # Overflow: that item is skipped and the error word is set.
+    kc3, vc3, p3, err = oracle.kv_append(kc, vc, np.array([12, 0, 0], np.int32), kb, vb, None)
+    assert err == 1 and p3.tolist() == [12, 6, 6]
+    assert kc3[0].view(np.uint8).tobytes() == kc[0].view(np.uint8).tobytes()
