@@ -1,0 +1,166 @@
+/*
+ * bd.h - C ABI of the block-diffusion denoise-step library (libbd.so, gfx950).
+ *
+ * One denoising step of a block-diffusion VLM decoder, plus the companion
+ * calls of linear self-speculative decoding.  The operations follow:
+ *
+ *  [FD]  "Fast-dVLM" write-up (itsolotime.com): section 4.1 (causal-context
+ *        attention: a noisy block attends to itself bidirectionally and to
+ *        every earlier clean position, vision included), section 5.1 (each
+ *        block opens with an AR step), section 5.3 (linear self-speculative
+ *        decoding: bidirectional draft, causal verify, accept the longest
+ *        prefix that matches the AR prediction, crop the KV cache).
+ *  [FD2] Fast-dVLM summary page, Fig. 3 caption (M_N2N block-diagonal mask).
+ *  [DV]  "DiffusionVL" notes (papernotes.org): cached block decoding and
+ *        Algorithm 1 as restated there (confidence = probability of the
+ *        chosen token; commit the k = min(ceil(D/S), |M|) most confident
+ *        masked positions plus, under the dynamic rule, every masked
+ *        position whose confidence is greater than tau; committed tokens stay
+ *        as context; a finished block joins the KV cache).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except `stream` and the descriptors is a DEVICE
+ *    pointer, 16-byte aligned, owned by the caller.  The library allocates no
+ *    memory and keeps no state beyond a thread-local last HIP error.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and performs no host synchronisation.  Lengths that change on
+ *    the device (prefix lengths, accepted lengths) stay on the device.
+ *  - Host-side validation happens before anything is launched: on a bad
+ *    argument the call returns a non-zero bd_status and touches nothing.
+ *    BD_E_LAUNCH means the HIP runtime rejected a launch (bd_last_hip_error()).
+ *  - Workspaces: size them with the matching *_workspace_bytes() call and
+ *    zero-fill them once before first use.  Each call leaves the counter area
+ *    it uses zeroed again, so a workspace can be reused by later calls on the
+ *    same stream.  Calls that overlap in time must not share a workspace.
+ *  - bf16 data is raw 16-bit storage (round-to-nearest-even when produced).
+ *    Accumulation is fp32.  Results do not depend on scheduling: every
+ *    reduction runs in a fixed order.
+ *
+ * Layouts (row-major, innermost index last):
+ *    q, out     [n][D][Hq][d]        queries / outputs of every block slot
+ *    k_blk,v_blk[n][D][Hkv][d]       this step's block keys / values
+ *    k_cache    [n][Hkv][cap][d]     frozen keys of prompt and finished blocks
+ *    v_cache    [n][Hkv][d][cap]     frozen values, stored d-major (transposed)
+ *    prefix_len int32[n]             valid cache length of each item (device)
+ *    logits     f32[n_req][D][V]
+ *    masked     u8[n_req][D]         1 = still [MASK]
+ *    tokens     i32[n_req][D]        committed token ids
+ */
+#ifndef BD_H
+#define BD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t bd_status;
+#define BD_OK 0
+#define BD_E_NULL 1      /* a required pointer is NULL */
+#define BD_E_SHAPE 2     /* a size is out of range or inconsistent */
+#define BD_E_DTYPE 3     /* unknown or unsupported dtype */
+#define BD_E_PARAM 4     /* unknown mode, S < 1, NaN tau or scale, ... */
+#define BD_E_WORKSPACE 5 /* workspace missing or too small */
+#define BD_E_LAUNCH 6    /* the HIP runtime rejected a launch */
+
+enum { BD_F32 = 0, BD_BF16 = 1 };
+enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1 };
+
+/* Shape of one block-attention call.
+ *  n_items    independent (request, layer) items, >= 1
+ *  D          block length, 1..64
+ *  Hq, Hkv    query / KV heads, Hq % Hkv == 0; head h uses KV head h / (Hq/Hkv)
+ *  d          head dim, 64 or 128
+ *  cap        cache capacity in tokens, a multiple of 8
+ *  dtype      BD_BF16 (MFMA path) or BD_F32 (vector path)
+ *  mode       BD_BLOCK_BIDIR or BD_BLOCK_CAUSAL
+ *  max_prefix host-side upper bound of every prefix_len[i], 0..cap; sizes the grid
+ *  scale      softmax scale (normally 1/sqrt(d)); finite and > 0 */
+typedef struct {
+    int32_t n_items, D, Hq, Hkv, d, cap, dtype, mode, max_prefix;
+    float scale;
+} bd_attn_desc;
+
+/* Shape of one confidence + commit call.
+ *  n_req >= 1, D 1..64, V >= 2, S >= 1 denoising steps per block,
+ *  tau threshold (not NaN; tau >= 1 disables the threshold rule). */
+typedef struct {
+    int32_t n_req, D, V, S;
+    float tau;
+} bd_commit_desc;
+
+/* Workspace bytes bd_attn_step needs for `desc` (0 if none); SIZE_MAX if desc is invalid. */
+size_t bd_attn_workspace_bytes(const bd_attn_desc *desc);
+
+/* Block attention of one denoising step ([FD] 4.1, 5.1, 5.3; [FD2] Fig. 3).
+ * For item i with P = prefix_len[i], slot s < D and head h (KV head g):
+ *   keys/values are cache positions 0..P-1 followed by block slots 0..D-1;
+ *   BD_BLOCK_BIDIR  : slot s sees all P + D of them (denoise step);
+ *   BD_BLOCK_CAUSAL : slot s sees cache 0..P-1 and block slots 0..s (verify / AR step);
+ *   out = softmax(scale * q k^T) v over the visible keys.
+ * Cache positions >= P are never read.  `out` has the input dtype.
+ * Preconditions (device): 0 <= prefix_len[i] <= max_prefix.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH. */
+bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_blk,
+                       const void *v_blk, const void *k_cache, const void *v_cache,
+                       const int32_t *prefix_len, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Workspace bytes bd_confidence_commit needs; SIZE_MAX if desc is invalid. */
+size_t bd_commit_workspace_bytes(const bd_commit_desc *desc);
+
+/* Confidence + commit of one denoising step ([DV] cached block decoding, Algorithm 1).
+ * For each request r and masked slot i (masked[r][i] == 1):
+ *   a_i = argmax_v logits[r][i][v] (lowest index on ties), conf_i = softmax(logits[r][i])[a_i];
+ *   k = min(ceil(D/S), |M|); T = the k masked slots first in (conf desc, index asc);
+ *   commit C = T u { i in M : conf_i > tau }: tokens[r][i] = a_i, masked[r][i] = 0.
+ * Rows of unmasked slots are not read; their tokens and masked flags do not change.
+ * masked and tokens are updated in place.  Optional outputs (NULL to skip):
+ *   conf f32[n_req][D] (NaN at unmasked slots), argmax i32[n_req][D] (-1 at unmasked),
+ *   committed u8[n_req][D] (1 where committed now), n_committed i32[n_req].
+ * NaN logits are not supported (results unspecified).
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH. */
+bd_status bd_confidence_commit(const bd_commit_desc *desc, const float *logits, uint8_t *masked,
+                               int32_t *tokens, float *conf, int32_t *argmax, uint8_t *committed,
+                               int32_t *n_committed, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Workspace bytes bd_spec_verify needs; SIZE_MAX if the sizes are invalid. */
+size_t bd_verify_workspace_bytes(int32_t n_req, int32_t D, int32_t V);
+
+/* Speculative verify ([FD] 5.3, linear variant).  Row i of request r holds the
+ * causal pass's logits for draft slot i (the caller aligns rows and slots).
+ *   a_i = argmax_v logits[r][i][v] (lowest index on ties);
+ *   accepted_len[r] = first i with a_i != draft[r][i], or D if none.
+ * argmax (optional, i32[n_req][D]) receives every a_i, so a caller can take
+ * a_L as the next token.  All D rows are read.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_WORKSPACE, BD_E_LAUNCH. */
+bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logits,
+                         const int32_t *draft, int32_t *accepted_len, int32_t *argmax,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Append accepted block K/V to the cache ([FD] 5.3: crop the cache to the accepted
+ * prefix; [DV] a finished block joins the history cache).  Uses n_items, D, Hkv, d,
+ * cap and dtype of `desc`.  For item i with P = prefix_len[i] and
+ * L = n_accept ? n_accept[i] : D (device values): cache slots P..P+L-1 receive block
+ * slots 0..L-1 bit for bit (keys row-wise, values into the d-major layout) and
+ * prefix_len[i] becomes P + L.  Nothing else is written.  If L is outside 0..D or
+ * P + L > cap, item i is left untouched and *dev_err (optional device int32) is set to 1.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_LAUNCH. */
+bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache,
+                       int32_t *prefix_len, const void *k_blk, const void *v_blk,
+                       const int32_t *n_accept, int32_t *dev_err, void *stream);
+
+/* Static description of a status code. */
+const char *bd_status_string(bd_status status);
+
+/* hipError_t value of the last failed launch on the calling thread (0 if none). */
+int32_t bd_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BD_H */

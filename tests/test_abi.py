@@ -1,0 +1,133 @@
+"""The C ABI on the host: every symbol that include/bd.h declares is exported by
+libbd.so, and argument validation rejects bad calls before anything is launched
+(no GPU needed: validation returns before the first HIP call)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bd.h")
+
+
+@pytest.fixture(scope="module")
+def bd():
+    from vlm_decoding_amd import bd as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(bd_[a-z_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ["bd_attn_step", "bd_confidence_commit", "bd_spec_verify", "bd_kv_append"]:
+        assert must in names
+    assert len(names) >= 9
+
+
+def test_library_exports_every_declared_symbol(bd):
+    lib = ctypes.CDLL(bd.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def _attn(bd, **kw):
+    base = dict(n_items=36, D=16, Hq=16, Hkv=2, d=128, cap=4160, dtype=1, mode=0, max_prefix=4096, scale=0.0884)
+    base.update(kw)
+    return bd.BdAttnDesc(*[base[f] for f, _ in bd.BdAttnDesc._fields_])
+
+
+BAD_ATTN = [
+    (dict(d=96), "BD_E_SHAPE"), (dict(D=0), "BD_E_SHAPE"), (dict(D=65), "BD_E_SHAPE"),
+    (dict(Hq=15), "BD_E_SHAPE"), (dict(Hkv=0), "BD_E_SHAPE"), (dict(cap=4161), "BD_E_SHAPE"),
+    (dict(max_prefix=5000), "BD_E_SHAPE"), (dict(max_prefix=-1), "BD_E_SHAPE"), (dict(n_items=0), "BD_E_SHAPE"),
+    (dict(dtype=7), "BD_E_DTYPE"), (dict(mode=2), "BD_E_PARAM"), (dict(scale=float("nan")), "BD_E_PARAM"),
+    (dict(scale=0.0), "BD_E_PARAM"), (dict(scale=float("inf")), "BD_E_PARAM"),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_ATTN)
+def test_attn_validation(bd, kw, code):
+    desc = _attn(bd, **kw)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    st = bd.lib.bd_attn_step(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 30, None)
+    assert st == getattr(bd, code)
+    assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
+
+
+def test_attn_null_and_workspace_errors(bd):
+    desc = _attn(bd)
+    fake = 1 << 20
+    assert bd.lib.bd_attn_step(None, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 30, None) == bd.BD_E_NULL
+    assert bd.lib.bd_attn_step(ctypes.byref(desc), None, fake, fake, fake, fake, fake, fake, fake, 1 << 30, None) == bd.BD_E_NULL
+    need = bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc))
+    assert 0 < need < bd.SIZE_MAX
+    assert bd.lib.bd_attn_step(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, fake, need - 1, None) == bd.BD_E_WORKSPACE
+    assert bd.lib.bd_attn_step(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, None, need, None) == bd.BD_E_WORKSPACE
+    assert bd.lib.bd_attn_step(ctypes.byref(desc), fake + 2, fake, fake, fake, fake, fake, fake, fake, need, None) == bd.BD_E_PARAM
+
+
+def test_single_split_needs_no_workspace(bd):
+    desc = _attn(bd, n_items=1, max_prefix=63, cap=128)
+    assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == 0
+    desc32 = _attn(bd, dtype=0)
+    assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc32)) == 0
+
+
+BAD_COMMIT = [
+    (dict(n_req=0), "BD_E_SHAPE"), (dict(D=0), "BD_E_SHAPE"), (dict(D=65), "BD_E_SHAPE"), (dict(V=1), "BD_E_SHAPE"),
+    (dict(S=0), "BD_E_PARAM"), (dict(tau=float("nan")), "BD_E_PARAM"),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_COMMIT)
+def test_commit_validation(bd, kw, code):
+    base = dict(n_req=1, D=16, V=151936, S=16, tau=0.9)
+    base.update(kw)
+    desc = bd.BdCommitDesc(base["n_req"], base["D"], base["V"], base["S"], base["tau"])
+    fake = 1 << 20
+    st = bd.lib.bd_confidence_commit(ctypes.byref(desc), fake, fake, fake, None, None, None, None, fake, 1 << 30, None)
+    assert st == getattr(bd, code)
+    assert bd.lib.bd_commit_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
+
+
+def test_commit_null_and_workspace(bd):
+    desc = bd.BdCommitDesc(1, 16, 151936, 16, 0.9)
+    fake = 1 << 20
+    need = bd.lib.bd_commit_workspace_bytes(ctypes.byref(desc))
+    assert 0 < need < bd.SIZE_MAX
+    assert bd.lib.bd_confidence_commit(ctypes.byref(desc), None, fake, fake, None, None, None, None, fake, need, None) == bd.BD_E_NULL
+    assert bd.lib.bd_confidence_commit(ctypes.byref(desc), fake, fake, fake, None, None, None, None, fake, need - 1, None) == bd.BD_E_WORKSPACE
+    # tau >= 1 is legal (the threshold rule is then off); inf too.
+    ok = bd.BdCommitDesc(1, 16, 151936, 16, math.inf)
+    assert bd.lib.bd_commit_workspace_bytes(ctypes.byref(ok)) == need
+
+
+def test_verify_and_append_validation(bd):
+    fake = 1 << 20
+    assert bd.lib.bd_verify_workspace_bytes(1, 0, 100) == bd.SIZE_MAX
+    need = bd.lib.bd_verify_workspace_bytes(1, 16, 151936)
+    assert bd.lib.bd_spec_verify(1, 16, 151936, fake, None, fake, None, fake, need, None) == bd.BD_E_NULL
+    assert bd.lib.bd_spec_verify(1, 16, 151936, fake, fake, fake, None, fake, need - 1, None) == bd.BD_E_WORKSPACE
+    assert bd.lib.bd_spec_verify(1, 65, 151936, fake, fake, fake, None, fake, need, None) == bd.BD_E_SHAPE
+    desc = _attn(bd, dtype=5)
+    assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_DTYPE
+    desc = _attn(bd, cap=100)
+    assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_SHAPE
+    desc = _attn(bd)
+    assert bd.lib.bd_kv_append(ctypes.byref(desc), None, fake, fake, fake, fake, None, None, None) == bd.BD_E_NULL
+
+
+def test_status_strings(bd):
+    for code in range(7):
+        assert bd.lib.bd_status_string(code)
+    assert bd.lib.bd_status_string(99) == b"unknown status"
+    assert bd.lib.bd_last_hip_error() == 0

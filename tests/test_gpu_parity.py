@@ -1,0 +1,345 @@
+"""GPU parity: libbd.so (through its C ABI) against the fp64 CPU oracle.
+
+Bars:
+  * bf16 / fp32 attention: max |gpu - oracle| <= 2e-2 and, per item,
+    ||gpu - oracle||_2 / ||oracle||_2 <= 1e-2.
+  * confidences: |gpu - oracle| <= 1e-5 absolute.
+  * greedy tokens, committed sets, accepted lengths, appended bytes: exact.
+    A commit decision is excluded (and counted) only where the oracle's own
+    fp64 values put it within 1e-4 of a tie: the k-th / (k+1)-th confidence
+    boundary, or the threshold tau.  The GPU's committed set must in addition
+    equal the rule applied exactly to the GPU's own confidences.
+"""
+
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import BF16, BIDIR, CAUSAL, F32
+
+pytestmark = pytest.mark.gpu
+
+ATTN_MAX_ABS = 2e-2
+ATTN_REL = 1e-2
+CONF_ABS = 1e-5
+FRAGILE = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    from vlm_decoding_amd import bd, step  # raises if libbd.so is missing
+    return dict(torch=torch, bd=bd, step=step)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _out_host(dev, ds):
+    dev["torch"].cuda.synchronize()
+    a = ds.out.cpu().numpy()
+    if ds.dtype == BF16:
+        return synth.bf16_bits_to_f32(a.view(np.uint16)).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _check_attention(got, ref, label):
+    assert np.all(np.isfinite(got)), label + ": non-finite output"
+    err = np.abs(got - ref)
+    max_abs = float(err.max())
+    rels = [float(np.linalg.norm((got[i] - ref[i]).ravel()) / np.linalg.norm(ref[i].ravel()))
+            for i in range(ref.shape[0])]
+    _say("%s: max_abs=%.3g max_rel_l2=%.3g" % (label, max_abs, max(rels)))
+    assert max_abs <= ATTN_MAX_ABS, (label, max_abs)
+    assert max(rels) <= ATTN_REL, (label, max(rels))
+
+
+def _run_attention(dev, step_np, mode=None, label=""):
+    ds = dev["step"].DeviceStep(step_np)
+    p = step_np["params"]
+    mode = p["mode"] if mode is None else mode
+    _say("attention %s n=%d D=%d Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s" % (
+        label, p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"], p["dtype"], mode,
+        np.unique(step_np["prefix"])[:8].tolist()))
+    ds.attn(mode=mode)
+    got = _out_host(dev, ds)
+    ref = oracle.attention(step_np["q"], step_np["k_blk"], step_np["v_blk"], step_np["k_cache"],
+                           step_np["v_cache"], step_np["prefix"], mode)
+    _check_attention(got, ref, label)
+    return ds, got
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_attention_configs(dev, cfg):
+    """Every configuration at its full size, every output element against the oracle."""
+    _run_attention(dev, synth.config_step(cfg), label="cfg%d" % cfg)
+
+
+ATTN_CASES = [
+    # (label, overrides)  -- small shapes spanning several tiles and ragged tails
+    ("tail_only_P0", dict(prefix=("fixed", 0))),
+    ("P_lt_tile", dict(prefix=("fixed", 37))),
+    ("P_exact_tiles", dict(prefix=("fixed", 256))),
+    ("P_ragged", dict(prefix=("list", [1, 63, 64, 65, 200, 511, 640, 1000]), n_items=8)),
+    ("D1_decode", dict(D=1, prefix=("fixed", 300))),
+    ("D3_rows_pad", dict(D=3, prefix=("fixed", 129))),
+    ("D64_two_row_blocks", dict(D=64, prefix=("fixed", 130))),
+    ("G7_rows224", dict(Hq=28, Hkv=4, D=32, prefix=("list", [70, 500]), n_items=2)),
+    ("d64_bf16", dict(d=64, prefix=("fixed", 333))),
+    ("many_items", dict(n_items=40, prefix=("fixed", 150))),
+]
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("label,ov", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_attention_edge_cases(dev, label, ov, mode):
+    base = dict(n_items=2, Hq=16, Hkv=2, d=128, dtype=BF16, D=16, n_masked=8, V=1000, plant=None)
+    base.update(ov)
+    p = synth.params_for(3, **base)
+    _run_attention(dev, synth.make_step(p, seed=zlib.crc32(label.encode()) % 10000), mode=mode, label=label)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+def test_attention_fp32_vector_path(dev, d, mode):
+    p = synth.params_for(1, d=d, n_items=3, prefix=("list", [0, 70, 129]), Hq=6, Hkv=2, D=5)
+    _run_attention(dev, synth.make_step(p, seed=77), mode=mode, label="fp32_d%d" % d)
+
+
+def test_attention_deterministic_and_workspace_reuse(dev):
+    """Bitwise-identical results over repeated calls on one workspace (the split
+    merge runs in a fixed order and the ticket counters reset themselves)."""
+    torch = dev["torch"]
+    s = synth.config_step(3)
+    ds = dev["step"].DeviceStep(s)
+    ds.attn()
+    torch.cuda.synchronize()
+    first = ds.out.clone()
+    for _ in range(3):
+        ds.out.zero_()
+        ds.attn()
+    torch.cuda.synchronize()
+    assert torch.equal(first, ds.out)
+
+
+def test_attention_rejects_bad_arguments_before_launch(dev):
+    bd = dev["bd"]
+    ds = dev["step"].DeviceStep(synth.config_step(2))
+    bad = bd.attn_desc(1, 8, 16, 2, 96, ds.cap, BF16, BIDIR, 1024)
+    with pytest.raises(bd.BdError) as e:
+        bd.bd_attn_step(bad, ds.q, ds.k_blk, ds.v_blk, ds.k_cache, ds.v_cache, ds.prefix, ds.out, ds.attn_ws)
+    assert e.value.status == bd.BD_E_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# Confidence + commit
+# ---------------------------------------------------------------------------
+
+def _rule_commit(conf32, masked, k, tau):
+    """Top-k by (conf desc, index asc) plus {conf > tau}, on fp32 values."""
+    idx = [i for i in range(len(masked)) if masked[i]]
+    order = sorted(idx, key=lambda i: (-float(conf32[i]), i))
+    take = set(order[:k]) | {i for i in idx if conf32[i] > np.float32(tau)}
+    return take
+
+
+def _fragile(conf64, masked, k, tau):
+    """Positions whose commit decision sits within 1e-4 of a tie in the oracle's values."""
+    idx = [i for i in range(len(masked)) if masked[i]]
+    frag = set()
+    for i in idx:
+        if abs(conf64[i] - tau) < FRAGILE:
+            frag.add(i)
+    if 0 < k < len(idx):
+        order = sorted(idx, key=lambda i: (-conf64[i], i))
+        kth, nxt = conf64[order[k - 1]], conf64[order[k]]
+        if kth - nxt < FRAGILE:
+            frag |= {i for i in idx if abs(conf64[i] - kth) < FRAGILE or abs(conf64[i] - nxt) < FRAGILE}
+    return frag
+
+
+def _compare_commit(dev, ds, p, masked_in, tokens_in, logits_np, label):
+    torch = dev["torch"]
+    torch.cuda.synchronize()
+    ref = oracle.confidence_commit(logits_np, masked_in, tokens_in, p["S"], p["tau"])
+    g_conf = ds.conf.cpu().numpy()
+    g_arg = ds.argmax.cpu().numpy()
+    g_com = ds.committed.cpu().numpy()
+    g_ncom = ds.n_committed.cpu().numpy()
+    g_mask = ds.masked.cpu().numpy()
+    g_tok = ds.tokens.cpu().numpy()
+    excluded = 0
+    for r in range(p["n_req"]):
+        m = masked_in[r].astype(bool)
+        nm = int(m.sum())
+        k = min(-(-p["D"] // p["S"]), nm)
+        assert np.all(np.isnan(g_conf[r][~m])) and np.all(g_arg[r][~m] == -1)
+        if nm:
+            err = np.abs(g_conf[r][m].astype(np.float64) - ref["conf"][r][m])
+            assert err.max() <= CONF_ABS, (label, r, err.max())
+            np.testing.assert_array_equal(g_arg[r][m], ref["argmax"][r][m])
+        # The GPU applies the rule exactly to its own fp32 confidences ...
+        own = _rule_commit(g_conf[r], m, k, p["tau"])
+        assert set(np.nonzero(g_com[r])[0].tolist()) == own, (label, r)
+        # ... and agrees with the oracle wherever the decision is not within 1e-4 of a tie.
+        frag = _fragile(ref["conf"][r], m, k, p["tau"])
+        excluded += len(frag)
+        for i in range(p["D"]):
+            if i in frag:
+                continue
+            assert g_com[r, i] == ref["committed"][r, i], (label, r, i)
+            assert g_mask[r, i] == ref["masked"][r, i]
+            assert g_tok[r, i] == ref["tokens"][r, i]
+        assert g_ncom[r] == int(g_com[r].sum())
+        untouched = ~m
+        np.testing.assert_array_equal(g_tok[r][untouched], tokens_in[r][untouched])
+        np.testing.assert_array_equal(g_mask[r][untouched], 0)
+    return excluded, ref
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_confidence_commit_configs(dev, cfg):
+    s = synth.config_step(cfg)
+    p = s["params"]
+    _say("confidence_commit cfg%d n_req=%d D=%d V=%d" % (cfg, p["n_req"], p["D"], p["V"]))
+    ds = dev["step"].DeviceStep(s)
+    ds.confidence_commit()
+    excl, _ = _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], "cfg%d" % cfg)
+    _say("cfg%d excluded fragile decisions: %d" % (cfg, excl))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_multistep_block_parity(dev, cfg):
+    """The whole S-step loop of one block: at every step both sides start from the
+    oracle's state, decide, and must agree (DiffusionVL notes, Algorithm 1)."""
+    torch = dev["torch"]
+    s = synth.config_step(cfg)
+    p = s["params"]
+    ds = dev["step"].DeviceStep(s)
+    rng = np.random.Generator(np.random.PCG64(4242 + cfg))
+    masked, tokens, logits = s["masked"].copy(), s["tokens"].copy(), s["logits"]
+    steps, excluded = 0, 0
+    while masked.sum() > 0:
+        _say("cfg%d step %d masked=%d" % (cfg, steps + 1, int(masked.sum())))
+        ds.masked.copy_(torch.from_numpy(masked))
+        ds.tokens.copy_(torch.from_numpy(tokens))
+        lg = torch.from_numpy(np.ascontiguousarray(logits)).cuda()
+        ds.confidence_commit(logits=lg)
+        e, ref = _compare_commit(dev, ds, p, masked, tokens, logits, "cfg%d step%d" % (cfg, steps + 1))
+        excluded += e
+        masked, tokens = ref["masked"], ref["tokens"]
+        steps += 1
+        logits = synth.fresh_logits(p, rng)
+    assert steps <= p["S"]
+    _say("cfg%d finished in %d steps, excluded %d" % (cfg, steps, excluded))
+
+
+COMMIT_CASES = [
+    ("none_masked", dict(n_masked=0)),
+    ("one_masked", dict(n_masked=1)),
+    ("D64_k", dict(D=64, n_masked=50, S=5)),
+    ("tau_ge_1", dict(tau=1.0)),
+    ("tau_low", dict(tau=0.01)),
+    ("V_odd", dict(V=1001)),
+    ("V_small", dict(V=2)),
+    ("many_req", dict(n_req=12, n_items=1, D=8, n_masked=5, V=5000)),
+]
+
+
+@pytest.mark.parametrize("label,ov", COMMIT_CASES, ids=[c[0] for c in COMMIT_CASES])
+def test_confidence_commit_edge_cases(dev, label, ov):
+    base = dict(n_items=1, n_req=3, D=16, n_masked=9, V=20000, S=4, tau=0.05, logit_sigma2=1.0,
+                prefix=("fixed", 8), Hq=2, Hkv=1, d=64, dtype=F32)
+    base.update(ov)
+    p = synth.params_for(1, **base)
+    s = synth.make_step(p, seed=len(label) * 31)
+    _say("confidence_commit %s" % label)
+    ds = dev["step"].DeviceStep(s)
+    ds.confidence_commit()
+    _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], label)
+
+
+def test_confidence_ties_and_equal_rows(dev):
+    """Exact ties: equal logits give conf 1/V and token 0; equal confidences rank by index."""
+    torch = dev["torch"]
+    p = synth.params_for(1, n_req=1, D=6, n_masked=6, V=4096, S=3, tau=2.0, prefix=("fixed", 8),
+                         Hq=2, Hkv=1, d=64, dtype=F32)
+    s = synth.make_step(p, seed=5)
+    s["logits"][:] = 0.25
+    s["logits"][0, 4, [100, 7, 4000]] = 3.0
+    ds = dev["step"].DeviceStep(s)
+    ds.confidence_commit()
+    torch.cuda.synchronize()
+    conf = ds.conf.cpu().numpy()[0]
+    arg = ds.argmax.cpu().numpy()[0]
+    assert arg.tolist() == [0, 0, 0, 0, 7, 0]
+    assert abs(conf[0] - 1.0 / 4096) < 1e-9
+    assert ds.committed.cpu().numpy()[0].tolist() == [1, 0, 0, 0, 1, 0]   # k = 2: slot 4, then slot 0
+
+
+# ---------------------------------------------------------------------------
+# Speculative verify and KV append
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_verify_then_append_cfg4(dev, seed):
+    torch = dev["torch"]
+    forced = {0: 0, 1: 16}.get(seed)
+    s = synth.make_step(synth.params_for(4), synth.seed_of(4) + seed, plant_L=forced)
+    p = s["params"]
+    _say("verify+append cfg4 seed=%d planted L=%d" % (seed, int(s["planted_L"][0])))
+    ds = dev["step"].DeviceStep(s)
+    ds.attn()
+    L_gpu = ds.verify()
+    ds.append(n_accept=L_gpu)
+    torch.cuda.synchronize()
+    L_ref, amax_ref = oracle.spec_verify(s["logits"], s["draft"])
+    assert int(L_gpu.cpu()[0]) == int(L_ref[0]) == int(s["planted_L"][0])
+    np.testing.assert_array_equal(ds.argmax.cpu().numpy(), amax_ref)
+    kc, vc, pref, err = oracle.kv_append(s["k_cache"], s["v_cache"], s["prefix"], s["k_blk"], s["v_blk"], L_ref)
+    assert err == 0 and int(ds.dev_err.cpu()[0]) == 0
+    np.testing.assert_array_equal(ds.prefix.cpu().numpy(), pref)
+    assert ds.k_cache.cpu().numpy().view(np.uint16).tobytes() == kc.tobytes()
+    assert ds.v_cache.cpu().numpy().view(np.uint16).tobytes() == vc.tobytes()
+
+
+def test_verify_ragged_requests(dev):
+    torch = dev["torch"]
+    p = synth.params_for(4, n_req=6, n_items=1, D=13, V=3001, prefix=("fixed", 8))
+    s = synth.make_step(p, seed=9)
+    ds = dev["step"].DeviceStep(s)
+    L = ds.verify()
+    torch.cuda.synchronize()
+    L_ref, amax_ref = oracle.spec_verify(s["logits"], s["draft"])
+    np.testing.assert_array_equal(L.cpu().numpy(), L_ref)
+    np.testing.assert_array_equal(L_ref, s["planted_L"])
+    np.testing.assert_array_equal(ds.argmax.cpu().numpy(), amax_ref)
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+def test_append_overflow_and_partial(dev, dtype):
+    torch = dev["torch"]
+    p = synth.params_for(1, n_items=3, D=8, dtype=dtype, prefix=("list", [10, 0, 50]), Hq=4, Hkv=2,
+                         d=64, cap=64)
+    s = synth.make_step(p, seed=3)
+    ds = dev["step"].DeviceStep(s)
+    acc = np.array([3, 8, 8], np.int32)     # item 2: 50 + 8 > 56? no: cap 64 -> fits
+    acc[2] = 8
+    s_prefix = s["prefix"].copy()
+    s_prefix[2] = 60                        # 60 + 8 > 64: overflow for item 2
+    ds.prefix.copy_(torch.from_numpy(s_prefix))
+    ds.append(n_accept=torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+    kc, vc, pref, err = oracle.kv_append(s["k_cache"], s["v_cache"], s_prefix, s["k_blk"], s["v_blk"], acc)
+    assert err == 1 and int(ds.dev_err.cpu()[0]) == 1
+    np.testing.assert_array_equal(ds.prefix.cpu().numpy(), pref)
+    el = np.uint16 if dtype == BF16 else np.float32
+    assert ds.k_cache.cpu().numpy().view(el).tobytes() == kc.tobytes()
+    assert ds.v_cache.cpu().numpy().view(el).tobytes() == vc.tobytes()

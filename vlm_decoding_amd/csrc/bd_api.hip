@@ -1,0 +1,187 @@
+// C-ABI entry points of libbd: host-side validation, workspace sizing and launch.
+// Every check runs before any HIP call, so invalid arguments are reported
+// without touching the device (and can be exercised on a machine without a GPU).
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/bd.h"
+#include "bd_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bd_status check_attn_desc(const bd_attn_desc *d) {
+    if (!d) return BD_E_NULL;
+    if (d->dtype != BD_F32 && d->dtype != BD_BF16) return BD_E_DTYPE;
+    if (d->mode != BD_BLOCK_BIDIR && d->mode != BD_BLOCK_CAUSAL) return BD_E_PARAM;
+    if (!(d->scale > 0.f) || !isfinite(d->scale)) return BD_E_PARAM;
+    if (d->n_items < 1 || d->D < 1 || d->D > 64) return BD_E_SHAPE;
+    if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return BD_E_SHAPE;
+    if (d->d != 64 && d->d != 128) return BD_E_SHAPE;
+    if (d->cap < 1 || d->cap % 8 != 0) return BD_E_SHAPE;
+    if (d->max_prefix < 0 || d->max_prefix > d->cap) return BD_E_SHAPE;
+    // Index arithmetic in the kernels uses 32-bit ints for per-item quantities.
+    if ((int64_t)d->D * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
+    return BD_OK;
+}
+
+bd_status check_commit_desc(const bd_commit_desc *d) {
+    if (!d) return BD_E_NULL;
+    if (d->n_req < 1 || d->D < 1 || d->D > 64 || d->V < 2) return BD_E_SHAPE;
+    if ((int64_t)d->n_req * d->D > (1 << 24)) return BD_E_SHAPE;
+    if (d->S < 1 || isnan(d->tau)) return BD_E_PARAM;
+    return BD_OK;
+}
+
+bd_status check_rows(int32_t n_req, int32_t D, int32_t V) {
+    if (n_req < 1 || D < 1 || D > 64 || V < 2) return BD_E_SHAPE;
+    if ((int64_t)n_req * D > (1 << 24)) return BD_E_SHAPE;
+    return BD_OK;
+}
+
+bd_status launched(hipError_t e) {
+    if (e != hipSuccess) {
+        g_last_hip_error = (int32_t)e;
+        return BD_E_LAUNCH;
+    }
+    return BD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bd_attn_workspace_bytes(const bd_attn_desc *desc) {
+    if (check_attn_desc(desc) != BD_OK) return SIZE_MAX;
+    const bd::AttnPlan pl = bd::plan_attention(desc->n_items, desc->D, desc->Hq, desc->Hkv, desc->d,
+                                               desc->dtype, desc->max_prefix);
+    return pl.ws_bytes;
+}
+
+bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_blk, const void *v_blk,
+                       const void *k_cache, const void *v_cache, const int32_t *prefix_len, void *out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    bd_status st = check_attn_desc(desc);
+    if (st != BD_OK) return st;
+    if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !prefix_len || !out) return BD_E_NULL;
+    if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return BD_E_PARAM;
+    const bd::AttnPlan pl = bd::plan_attention(desc->n_items, desc->D, desc->Hq, desc->Hkv, desc->d,
+                                               desc->dtype, desc->max_prefix);
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+        return BD_E_WORKSPACE;
+    bd::AttnArgs a{};
+    a.q = q;
+    a.k_blk = k_blk;
+    a.v_blk = v_blk;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.prefix = prefix_len;
+    a.out = out;
+    a.ws = workspace;
+    a.n = desc->n_items;
+    a.D = desc->D;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.d = desc->d;
+    a.cap = desc->cap;
+    a.mode = desc->mode;
+    a.scale = desc->scale;
+    hipStream_t s = (hipStream_t)stream;
+    return launched(pl.mfma ? bd::launch_attention_mfma(pl, a, s) : bd::launch_attention_vec(a, desc->dtype, s));
+}
+
+size_t bd_commit_workspace_bytes(const bd_commit_desc *desc) {
+    if (check_commit_desc(desc) != BD_OK) return SIZE_MAX;
+    return bd::plan_rows(desc->n_req, desc->D, desc->V).ws_bytes;
+}
+
+bd_status bd_confidence_commit(const bd_commit_desc *desc, const float *logits, uint8_t *masked,
+                               int32_t *tokens, float *conf, int32_t *argmax, uint8_t *committed,
+                               int32_t *n_committed, void *workspace, size_t workspace_bytes, void *stream) {
+    bd_status st = check_commit_desc(desc);
+    if (st != BD_OK) return st;
+    if (!logits || !masked || !tokens) return BD_E_NULL;
+    if (!aligned16(logits)) return BD_E_PARAM;
+    const bd::RowPlan pl = bd::plan_rows(desc->n_req, desc->D, desc->V);
+    if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) return BD_E_WORKSPACE;
+    bd::RowArgs a{};
+    a.logits = logits;
+    a.masked = masked;
+    a.tokens = tokens;
+    a.conf = conf;
+    a.argmax = argmax;
+    a.committed = committed;
+    a.n_committed = n_committed;
+    a.ws = workspace;
+    a.n_req = desc->n_req;
+    a.D = desc->D;
+    a.V = desc->V;
+    a.S = desc->S;
+    a.tau = desc->tau;
+    return launched(bd::launch_confidence_commit(pl, a, (hipStream_t)stream));
+}
+
+size_t bd_verify_workspace_bytes(int32_t n_req, int32_t D, int32_t V) {
+    if (check_rows(n_req, D, V) != BD_OK) return SIZE_MAX;
+    return bd::plan_rows(n_req, D, V).ws_bytes;
+}
+
+bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logits, const int32_t *draft,
+                         int32_t *accepted_len, int32_t *argmax, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    bd_status st = check_rows(n_req, D, V);
+    if (st != BD_OK) return st;
+    if (!logits || !draft || !accepted_len) return BD_E_NULL;
+    if (!aligned16(logits)) return BD_E_PARAM;
+    const bd::RowPlan pl = bd::plan_rows(n_req, D, V);
+    if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) return BD_E_WORKSPACE;
+    bd::RowArgs a{};
+    a.logits = logits;
+    a.draft = draft;
+    a.accepted_len = accepted_len;
+    a.argmax = argmax;
+    a.ws = workspace;
+    a.n_req = n_req;
+    a.D = D;
+    a.V = V;
+    a.S = 1;
+    return launched(bd::launch_spec_verify(pl, a, (hipStream_t)stream));
+}
+
+bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache, int32_t *prefix_len,
+                       const void *k_blk, const void *v_blk, const int32_t *n_accept, int32_t *dev_err,
+                       void *stream) {
+    if (!desc) return BD_E_NULL;
+    if (desc->dtype != BD_F32 && desc->dtype != BD_BF16) return BD_E_DTYPE;
+    if (desc->n_items < 1 || desc->D < 1 || desc->D > 64 || desc->Hkv < 1) return BD_E_SHAPE;
+    if (desc->d != 64 && desc->d != 128) return BD_E_SHAPE;
+    if (desc->cap < 1 || desc->cap % 8 != 0) return BD_E_SHAPE;
+    if (!k_cache || !v_cache || !prefix_len || !k_blk || !v_blk) return BD_E_NULL;
+    return launched(bd::launch_kv_append(desc->n_items, desc->D, desc->Hkv, desc->d, desc->cap,
+                                         desc->dtype == BD_F32 ? 4 : 2, k_cache, v_cache, prefix_len, k_blk,
+                                         v_blk, n_accept, dev_err, (hipStream_t)stream));
+}
+
+const char *bd_status_string(bd_status s) {
+    switch (s) {
+        case BD_OK: return "ok";
+        case BD_E_NULL: return "a required pointer is NULL";
+        case BD_E_SHAPE: return "a size is out of range or inconsistent";
+        case BD_E_DTYPE: return "unknown or unsupported dtype";
+        case BD_E_PARAM: return "invalid parameter (mode, S, tau, scale or alignment)";
+        case BD_E_WORKSPACE: return "workspace missing, misaligned or too small";
+        case BD_E_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        default: return "unknown status";
+    }
+}
+
+int32_t bd_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

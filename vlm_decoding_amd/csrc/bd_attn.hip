@@ -1,0 +1,556 @@
+// Block attention of one denoising / verify step on gfx950.
+//
+// Operation (Fast-dVLM write-up, section 4.1 and 5.3; summary page Fig. 3):
+// the D slots of the current block attend to the frozen cache positions
+// 0..P-1 and to the block itself, bidirectionally (denoise) or causally
+// (verify / AR step).  GQA: the Hq/Hkv query heads sharing one KV head are
+// processed together as D * Hq/Hkv "grouped rows" against one K/V stream.
+//
+// MFMA path (bf16, d = 64 or 128).  One workgroup owns one (item, KV head,
+// row block, key split).  Each wave owns 32 grouped rows and computes
+//     S^T = K . Q^T        (v_mfma_f32_32x32x16_bf16, keys x rows)
+//     O^T += V^T . P^T     (same instruction, d x rows)
+// so that each lane holds one query row: the softmax max is an in-lane
+// reduction plus one exchange between the two 32-lane halves.  K rows are
+// fed to the first MFMA in a permuted order so that the eight scores a lane
+// holds for each 16-key chunk are eight consecutive keys; the second MFMA
+// then reads its V^T operand as one 16-byte LDS load per lane from the
+// d-major value tile.  K and V^T tiles (64 keys) are staged through LDS in
+// two buffers with XOR swizzles that keep 16-lane groups conflict-free.
+// The online softmax (Milakov & Gimelshein, "Online normalizer calculation
+// for softmax", 2018) only rescales when the running maximum grows by more
+// than 2^8, which keeps every exponent <= 2^8 and is exact after the final
+// normalisation.  The cached prefix is split across workgroups (split-K);
+// the last workgroup of a unit to finish merges the (m, l, o) partials in
+// split order, so results do not depend on scheduling.
+#include "bd_common.h"
+#include "bd_internal.h"
+
+namespace bd {
+namespace {
+
+constexpr int TK = kTileKeys;
+
+struct MfmaParams {
+    const uint16_t *q, *kb, *vb, *kc, *vc;
+    const int32_t *prefix;
+    uint16_t *out;
+    float *ws_o;
+    float2 *ws_ml;
+    int *ws_cnt;
+    int n, D, Hq, Hkv, G, cap, mode;
+    int R, row_blocks, max_splits, tiles_per_split, total_logical;
+    float c;  // scale * log2(e)
+};
+
+// Row permutation of the K operand: A-row rho (= lane % 32) of a 32-key block
+// loads key pi(rho), which makes output register i of half h hold key
+// 16 * (i / 8) + 8 * h + (i % 8).
+__device__ __forceinline__ int key_perm(int rho) {
+    int q = rho >> 3, h = (rho >> 2) & 1, e = rho & 3;
+    return ((q >> 1) << 4) + (h << 3) + ((q & 1) << 2) + e;
+}
+
+// 16-byte-unit XOR swizzles of the LDS tiles.
+template <int HD>
+__device__ __forceinline__ int k_swz(int key) {
+    // K tile rows are HD*2 bytes = HD/8 units; 16 units span all LDS banks.
+    return (HD == 128) ? (key & 15) : ((key >> 1) & 7);
+}
+__device__ __forceinline__ int v_swz(int dd) { return (dd >> 1) & 7; }  // V^T rows: 8 units
+
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int KU = HD / 8;          // 16-byte units per K row
+    constexpr int K_UNITS = TK * KU;
+    constexpr int V_UNITS = HD * (TK / 8);
+    constexpr int LK = (K_UNITS + NT - 1) / NT;
+    constexpr int LV = (V_UNITS + NT - 1) / NT;
+    constexpr int KC = HD / 16;         // d-chunks of the first MFMA
+    constexpr int MB = HD / 32;         // d-blocks of the second MFMA
+    constexpr int RPG = NW * 32;        // rows per workgroup
+
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][TK * HD];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][HD * TK];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+
+    // XCD-aware decode: consecutive logical ids (the splits of one unit) share an XCD.
+    const int nb = gridDim.x;
+    const int logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
+    if (logical >= p.total_logical) return;
+    const int unit = logical / p.max_splits;
+    const int split = logical - unit * p.max_splits;
+    const int rb = unit % p.row_blocks;
+    const int pair = unit / p.row_blocks;
+    const int g = pair % p.Hkv;
+    const int it = pair / p.Hkv;
+
+    // Prefix lengths are clamped into [0, cap] so that no access leaves the cache.
+    const int P = min(max(p.prefix[it], 0), p.cap);
+    const int P64 = P & ~(TK - 1);
+    const int nbulk = P64 / TK;
+    // A prefix above the host's max_prefix widens the splits instead of
+    // overrunning the workspace (every workgroup of the unit agrees on tps).
+    const int tps = max(p.tiles_per_split, (nbulk + p.max_splits - 1) / p.max_splits);
+    const int nsplit = max(1, (nbulk + tps - 1) / tps);
+    if (split >= nsplit) return;
+    const int t0 = split * tps;
+    const int nb_split = max(0, min(nbulk, t0 + tps) - t0);
+    const bool last = split == nsplit - 1;
+    const int tail_len = last ? (P - P64) + p.D : 0;
+    const int ntiles = nb_split + (tail_len + TK - 1) / TK;
+
+    const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD;   // [cap][HD]
+    const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap;   // [HD][cap]
+
+    // This lane's query row.
+    const int r_local = w * 32 + col;
+    const int r = rb * RPG + r_local;
+    const bool row_valid = r < p.R;
+    const bool wave_active = rb * RPG + w * 32 < p.R;
+    const int slot = r / p.G;
+    const int head = g * p.G + (r - slot * p.G);
+
+    bf16x8 qf[KC];
+    {
+        const uint16_t *qp = p.q + (((size_t)it * p.D + slot) * p.Hq + head) * HD + half * 8;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            if (row_valid)
+                qf[kc] = *reinterpret_cast<const bf16x8 *>(qp + kc * 16);
+            else
+                qf[kc] = bf16x8{};
+        }
+    }
+
+    floatx16 o[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) o[mb] = floatx16{};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    u32x4 kreg[LK], vreg[LV];
+    auto load_bulk = [&](int t) {
+        const int key0 = t * TK;
+#pragma unroll
+        for (int j = 0; j < LK; ++j) {
+            const int u = tid + j * NT;
+            if (K_UNITS % NT == 0 || u < K_UNITS) {
+                const int key = u / KU, lu = u % KU;
+                kreg[j] = *reinterpret_cast<const u32x4 *>(p.kc + kc_base + (size_t)(key0 + key) * HD + lu * 8);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < LV; ++j) {
+            const int u = tid + j * NT;
+            if (V_UNITS % NT == 0 || u < V_UNITS) {
+                const int dd = u >> 3, lu = u & 7;
+                vreg[j] = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + key0 + lu * 8);
+            }
+        }
+    };
+    auto store_bulk = [&](int st) {
+#pragma unroll
+        for (int j = 0; j < LK; ++j) {
+            const int u = tid + j * NT;
+            if (K_UNITS % NT == 0 || u < K_UNITS) {
+                const int key = u / KU, lu = u % KU;
+                *reinterpret_cast<u32x4 *>(&lds_k[st][key * HD + ((lu ^ k_swz<HD>(key)) << 3)]) = kreg[j];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < LV; ++j) {
+            const int u = tid + j * NT;
+            if (V_UNITS % NT == 0 || u < V_UNITS) {
+                const int dd = u >> 3, lu = u & 7;
+                *reinterpret_cast<u32x4 *>(&lds_v[st][dd * TK + ((lu ^ v_swz(dd)) << 3)]) = vreg[j];
+            }
+        }
+    };
+    // Tail tiles: the last P % 64 cache positions followed by the D block slots,
+    // zero-filled past the end.  Element-wise; at most two tiles per unit.
+    auto load_tail = [&](int st, int tt) {
+        for (int e = tid; e < TK * HD; e += NT) {
+            const int key = e / HD, dd = e % HD;
+            const int j = tt * TK + key;
+            uint16_t val = 0;
+            if (j < tail_len) {
+                const int pos = P64 + j;
+                val = pos < P ? p.kc[kc_base + (size_t)pos * HD + dd]
+                              : p.kb[(((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + dd];
+            }
+            lds_k[st][key * HD + ((((dd >> 3) ^ k_swz<HD>(key))) << 3) + (dd & 7)] = val;
+        }
+        for (int e = tid; e < HD * TK; e += NT) {
+            const int dd = e / TK, key = e % TK;
+            const int j = tt * TK + key;
+            uint16_t val = 0;
+            if (j < tail_len) {
+                const int pos = P64 + j;
+                val = pos < P ? p.vc[vc_base + (size_t)dd * p.cap + pos]
+                              : p.vb[(((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + dd];
+            }
+            lds_v[st][dd * TK + (((key >> 3) ^ v_swz(dd)) << 3) + (key & 7)] = val;
+        }
+    };
+
+    auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */) {
+        const uint16_t *Kt = lds_k[st];
+        const uint16_t *Vt = lds_v[st];
+        floatx16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = floatx16{};
+            const int key = kb * 32 + key_perm(col);
+            const int sw = k_swz<HD>(key);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+                const int lu = kc * 2 + half;
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&Kt[key * HD + ((lu ^ sw) << 3)]);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+            }
+        }
+        if (tt >= 0) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = tt * TK + kb * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+                    bool ok = j < tail_len;
+                    if (p.mode == 1) {
+                        const int pos = P64 + j;
+                        ok = ok && (pos < P || pos - P <= slot);
+                    }
+                    if (!ok) s[kb][i] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = fmaxf(mx, bd_swap_halves(mx));
+        const float mx2 = mx * p.c;
+        const bool need = mx2 > m_run + 8.0f;
+        if (bd_wave_any(need)) {
+            const float m_new = need ? mx2 : m_run;
+            const float alpha = need ? bd_exp2(m_run - m_new) : 1.0f;
+            l_run *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+            m_run = m_new;
+        }
+        const float msub = (m_run == -INFINITY) ? 0.f : m_run;
+        float lsum = 0.f;
+        bf16x8 pb[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = bd_exp2(fmaf(s[kb][i], p.c, -msub));
+                lsum += pv;
+                pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
+            }
+        l_run += lsum;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int dd = mb * 32 + col;
+            const int sw = v_swz(dd);
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const int lu = c4 * 2 + half;
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&Vt[dd * TK + ((lu ^ sw) << 3)]);
+                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c4], o[mb], 0, 0, 0);
+            }
+        }
+    };
+
+    if (nb_split > 0) load_bulk(t0);
+    for (int tl = 0; tl < ntiles; ++tl) {
+        const int st = tl & 1;
+        if (tl < nb_split)
+            store_bulk(st);
+        else
+            load_tail(st, tl - nb_split);
+        __syncthreads();
+        if (tl + 1 < nb_split) load_bulk(t0 + tl + 1);
+        if (wave_active) compute(st, tl < nb_split ? -1 : tl - nb_split);
+    }
+
+    const float l_tot = l_run + bd_swap_halves(l_run);
+    // Output element mapping of the O^T accumulators: block mb, register i of
+    // half h holds d = mb*32 + 8*(i/4) + 4*h + (i%4) of this lane's row.
+    if (nsplit == 1) {
+        if (row_valid) {
+            const float inv = 1.0f / l_tot;
+            uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int dd = mb * 32 + 8 * i4 + 4 * half;
+                    uint2 v;
+                    v.x = bd_f32_to_bf16(o[mb][4 * i4 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 1] * inv) << 16);
+                    v.y = bd_f32_to_bf16(o[mb][4 * i4 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 3] * inv) << 16);
+                    *reinterpret_cast<uint2 *>(op + dd) = v;
+                }
+        }
+        return;
+    }
+
+    const size_t part = (size_t)unit * p.max_splits;
+    if (wave_active) {
+        float *wo = p.ws_o + ((part + split) * RPG + r_local) * HD;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int dd = mb * 32 + 8 * i4 + 4 * half;
+                *reinterpret_cast<float4 *>(wo + dd) =
+                    make_float4(o[mb][4 * i4], o[mb][4 * i4 + 1], o[mb][4 * i4 + 2], o[mb][4 * i4 + 3]);
+            }
+        if (half == 0) p.ws_ml[(part + split) * RPG + r_local] = make_float2(m_run, l_tot);
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&p.ws_cnt[unit], 1) == nsplit - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (wave_active) {
+        float M = -INFINITY;
+        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, p.ws_ml[(part + sp) * RPG + r_local].x);
+        float L = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) o[mb] = floatx16{};
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const float2 ml = p.ws_ml[(part + sp) * RPG + r_local];
+            const float wgt = (ml.x == -INFINITY) ? 0.f : bd_exp2(ml.x - M);
+            L += wgt * ml.y;
+            const float *wo = p.ws_o + ((part + sp) * RPG + r_local) * HD;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int dd = mb * 32 + 8 * i4 + 4 * half;
+                    const float4 v = *reinterpret_cast<const float4 *>(wo + dd);
+                    o[mb][4 * i4 + 0] += wgt * v.x;
+                    o[mb][4 * i4 + 1] += wgt * v.y;
+                    o[mb][4 * i4 + 2] += wgt * v.z;
+                    o[mb][4 * i4 + 3] += wgt * v.w;
+                }
+        }
+        if (row_valid) {
+            const float inv = 1.0f / L;
+            uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const int dd = mb * 32 + 8 * i4 + 4 * half;
+                    uint2 v;
+                    v.x = bd_f32_to_bf16(o[mb][4 * i4 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 1] * inv) << 16);
+                    v.y = bd_f32_to_bf16(o[mb][4 * i4 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 3] * inv) << 16);
+                    *reinterpret_cast<uint2 *>(op + dd) = v;
+                }
+        }
+    }
+    if (tid == 0) p.ws_cnt[unit] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// Vector path: one wave per (item, slot, head) query row, keys 64 at a time
+// across lanes, values accumulated with lanes over d.  Used for fp32 inputs.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float ld(const T *p, size_t i);
+template <>
+__device__ __forceinline__ float ld<float>(const float *p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t *p, size_t i) { return bd_bf16_to_f32(p[i]); }
+__device__ __forceinline__ void st(float *p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void st(uint16_t *p, size_t i, float v) { p[i] = bd_f32_to_bf16(v); }
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, const T *vb, const T *kc,
+                                                       const T *vc, const int32_t *prefix, T *out, int n,
+                                                       int D, int Hq, int Hkv, int cap, int mode, float scale) {
+    constexpr int PER = HD / 64;
+    __shared__ float qs[4][HD];
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    const long u = (long)blockIdx.x * 4 + w;
+    const bool active = u < (long)n * D * Hq;
+    const int it = active ? (int)(u / ((long)D * Hq)) : 0;
+    const int slot = (int)((u / Hq) % D);
+    const int h = (int)(u % Hq);
+    const int g = h / (Hq / Hkv);
+    const size_t qoff = (((size_t)it * D + slot) * Hq + h) * HD;
+    for (int t = lane; t < HD; t += 64) qs[w][t] = active ? ld(q, qoff + t) : 0.f;
+    __syncthreads();
+    if (!active) return;
+    const int P = min(max(prefix[it], 0), cap);
+    const int nk = P + D;
+    const size_t kc_base = ((size_t)it * Hkv + g) * cap * HD;
+    const size_t vc_base = ((size_t)it * Hkv + g) * HD * cap;
+    float m = -INFINITY, l = 0.f, o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+    for (int base = 0; base < nk; base += 64) {
+        const int key = base + lane;
+        const bool valid = key < nk && (mode == 0 || key < P || key - P <= slot);
+        float s = -INFINITY;
+        if (valid) {
+            float acc = 0.f;
+            if (key < P) {
+                for (int t = 0; t < HD; ++t) acc = fmaf(qs[w][t], ld(kc, kc_base + (size_t)key * HD + t), acc);
+            } else {
+                const size_t kbo = (((size_t)it * D + (key - P)) * Hkv + g) * HD;
+                for (int t = 0; t < HD; ++t) acc = fmaf(qs[w][t], ld(kb, kbo + t), acc);
+            }
+            s = acc * scale;
+        }
+        float mx = s;
+        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const float m_new = fmaxf(m, mx);
+        const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+        const float pv = valid ? expf(s - m_new) : 0.f;
+        float ps = pv;
+        for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off, 64);
+        l = l * alpha + ps;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] *= alpha;
+        m = m_new;
+        const int kmax = min(64, nk - base);
+        for (int kk = 0; kk < kmax; ++kk) {
+            const float pk = __shfl(pv, kk, 64);
+            if (pk == 0.f) continue;
+            const int key2 = base + kk;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+                const int dd = lane + 64 * e;
+                const float vv = key2 < P ? ld(vc, vc_base + (size_t)dd * cap + key2)
+                                          : ld(vb, (((size_t)it * D + (key2 - P)) * Hkv + g) * HD + dd);
+                o[e] = fmaf(pk, vv, o[e]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) st(out, qoff + lane + 64 * e, o[e] / l);
+}
+
+}  // namespace
+
+AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix) {
+    AttnPlan pl{};
+    pl.mfma = (dtype == 1);
+    pl.rows = D * (Hq / Hkv);
+    if (!pl.mfma) {
+        pl.grid = (int)(((long)n * D * Hq + 3) / 4);
+        pl.ws_bytes = 0;
+        return pl;
+    }
+    pl.nw = pl.rows <= 128 ? 4 : 8;
+    pl.rows_per_group = pl.nw * 32;
+    pl.row_blocks = (pl.rows + pl.rows_per_group - 1) / pl.rows_per_group;
+    pl.units = n * Hkv * pl.row_blocks;
+    const int ntiles_max = max_prefix / kTileKeys;
+    const int want = std::max(1, (kTargetGroups + pl.units - 1) / pl.units);
+    pl.tiles_per_split = std::max(1, (ntiles_max + want - 1) / want);
+    pl.max_splits = std::max(1, (ntiles_max + pl.tiles_per_split - 1) / pl.tiles_per_split);
+    const long total = (long)pl.units * pl.max_splits;
+    pl.grid = (int)((total + 7) / 8 * 8);
+    if (pl.max_splits > 1) {
+        size_t off = 0;
+        auto take = [&](size_t bytes) {
+            size_t o = off;
+            off += (bytes + 255) / 256 * 256;
+            return o;
+        };
+        const size_t parts = (size_t)pl.units * pl.max_splits * pl.rows_per_group;
+        pl.ws_cnt_off = take(sizeof(int) * (size_t)pl.units);
+        pl.ws_ml_off = take(sizeof(float) * 2 * parts);
+        pl.ws_o_off = take(sizeof(float) * (size_t)d * parts);
+        pl.ws_bytes = off;
+    }
+    return pl;
+}
+
+hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStream_t s) {
+    MfmaParams p{};
+    p.q = (const uint16_t *)a.q;
+    p.kb = (const uint16_t *)a.k_blk;
+    p.vb = (const uint16_t *)a.v_blk;
+    p.kc = (const uint16_t *)a.k_cache;
+    p.vc = (const uint16_t *)a.v_cache;
+    p.prefix = a.prefix;
+    p.out = (uint16_t *)a.out;
+    char *ws = (char *)a.ws;
+    p.ws_cnt = pl.max_splits > 1 ? (int *)(ws + pl.ws_cnt_off) : nullptr;
+    p.ws_ml = pl.max_splits > 1 ? (float2 *)(ws + pl.ws_ml_off) : nullptr;
+    p.ws_o = pl.max_splits > 1 ? (float *)(ws + pl.ws_o_off) : nullptr;
+    p.n = a.n;
+    p.D = a.D;
+    p.Hq = a.Hq;
+    p.Hkv = a.Hkv;
+    p.G = a.Hq / a.Hkv;
+    p.cap = a.cap;
+    p.mode = a.mode;
+    p.R = pl.rows;
+    p.row_blocks = pl.row_blocks;
+    p.max_splits = pl.max_splits;
+    p.tiles_per_split = pl.tiles_per_split;
+    p.total_logical = pl.units * pl.max_splits;
+    p.c = a.scale * BD_LOG2E;
+    dim3 grid(pl.grid), block(pl.nw * 64);
+    if (a.d == 128) {
+        if (pl.nw == 4)
+            hipLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_mfma_kernel<128, 8>), grid, block, 0, s, p);
+    } else {
+        if (pl.nw == 4)
+            hipLaunchKernelGGL((attn_mfma_kernel<64, 4>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((attn_mfma_kernel<64, 8>), grid, block, 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {
+    const long rows = (long)a.n * a.D * a.Hq;
+    dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (dtype == 0) {
+        auto *q = (const float *)a.q;
+        if (a.d == 128)
+            hipLaunchKernelGGL((attn_vec_kernel<float, 128>), grid, block, 0, s, q, (const float *)a.k_blk,
+                               (const float *)a.v_blk, (const float *)a.k_cache, (const float *)a.v_cache,
+                               a.prefix, (float *)a.out, a.n, a.D, a.Hq, a.Hkv, a.cap, a.mode, a.scale);
+        else
+            hipLaunchKernelGGL((attn_vec_kernel<float, 64>), grid, block, 0, s, q, (const float *)a.k_blk,
+                               (const float *)a.v_blk, (const float *)a.k_cache, (const float *)a.v_cache,
+                               a.prefix, (float *)a.out, a.n, a.D, a.Hq, a.Hkv, a.cap, a.mode, a.scale);
+    } else {
+        auto *q = (const uint16_t *)a.q;
+        if (a.d == 128)
+            hipLaunchKernelGGL((attn_vec_kernel<uint16_t, 128>), grid, block, 0, s, q, (const uint16_t *)a.k_blk,
+                               (const uint16_t *)a.v_blk, (const uint16_t *)a.k_cache,
+                               (const uint16_t *)a.v_cache, a.prefix, (uint16_t *)a.out, a.n, a.D, a.Hq,
+                               a.Hkv, a.cap, a.mode, a.scale);
+        else
+            hipLaunchKernelGGL((attn_vec_kernel<uint16_t, 64>), grid, block, 0, s, q, (const uint16_t *)a.k_blk,
+                               (const uint16_t *)a.v_blk, (const uint16_t *)a.k_cache,
+                               (const uint16_t *)a.v_cache, a.prefix, (uint16_t *)a.out, a.n, a.D, a.Hq,
+                               a.Hkv, a.cap, a.mode, a.scale);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,69 @@
+// Internal launch interface between the C-ABI layer (bd_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bd {
+
+// ---- block attention -------------------------------------------------------
+constexpr int kTileKeys = 64;       // keys per LDS tile
+constexpr int kTargetGroups = 512;  // workgroups the split-K decomposition aims for
+
+struct AttnPlan {
+    bool mfma;            // bf16 MFMA path (else the fp32/any vector path)
+    int nw;               // waves per workgroup (MFMA path)
+    int rows;             // grouped query rows per (item, KV head) = D * Hq/Hkv
+    int rows_per_group;   // rows one workgroup covers (32 * nw)
+    int row_blocks;
+    int units;            // n_items * Hkv * row_blocks
+    int tiles_per_split;
+    int max_splits;
+    int grid;             // workgroups launched
+    size_t ws_cnt_off, ws_ml_off, ws_o_off, ws_bytes;
+};
+
+struct AttnArgs {
+    const void *q, *k_blk, *v_blk, *k_cache, *v_cache;
+    const int32_t *prefix;
+    void *out;
+    void *ws;
+    int n, D, Hq, Hkv, d, cap, mode;
+    float scale;
+};
+
+AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix);
+hipError_t launch_attention_mfma(const AttnPlan &plan, const AttnArgs &a, hipStream_t s);
+hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s);
+
+// ---- confidence / verify ----------------------------------------------------
+struct RowPlan {
+    int rows, chunks, chunk_elems;
+    size_t part_off, rowres_off, cnt_off, ws_bytes;
+};
+RowPlan plan_rows(int n_req, int D, int V);
+
+struct RowArgs {
+    const float *logits;
+    uint8_t *masked;
+    int32_t *tokens;
+    float *conf;
+    int32_t *argmax;
+    uint8_t *committed;
+    int32_t *n_committed;
+    const int32_t *draft;
+    int32_t *accepted_len;
+    void *ws;
+    int n_req, D, V, S;
+    float tau;
+};
+hipError_t launch_confidence_commit(const RowPlan &plan, const RowArgs &a, hipStream_t s);
+hipError_t launch_spec_verify(const RowPlan &plan, const RowArgs &a, hipStream_t s);
+
+// ---- KV append --------------------------------------------------------------
+hipError_t launch_kv_append(int n, int D, int Hkv, int d, int cap, int elem_bytes, void *k_cache,
+                            void *v_cache, int32_t *prefix, const void *k_blk, const void *v_blk,
+                            const int32_t *n_accept, int32_t *dev_err, hipStream_t s);
+
+}  // namespace bd

@@ -1,0 +1,342 @@
+// Vocab-wide row reductions on gfx950: confidence + commit, and speculative verify.
+//
+// Confidence (DiffusionVL notes, cached block decoding): for each masked
+// slot the greedy token a = argmax_v x_v (lowest index on ties) and its
+// probability conf = 1 / sum_v exp(x_v - x_a).  Commit (Algorithm 1 and the
+// dynamic rule as restated there): the k = min(ceil(D/S), |M|) most
+// confident masked slots, plus every masked slot with conf > tau.
+// Verify (Fast-dVLM write-up, section 5.3, linear speculative decoding):
+// the accepted length is the first slot whose greedy token differs from
+// the draft.
+//
+// Each row is split into chunks of whole 1024-float strides; one 256-thread
+// workgroup streams one chunk with 16-byte loads, keeping a running
+// (max, index of first max, sum of exp(x - max)) per thread.  Partials are
+// combined in a fixed tree inside the workgroup, then across chunks by the
+// last workgroup of the row (atomic ticket) in chunk order; the last row of
+// a request runs the one-wave commit / verify tail.  No float atomics, so
+// results are identical run to run.
+#include "bd_common.h"
+#include "bd_internal.h"
+
+namespace bd {
+namespace {
+
+constexpr int NT = 256;
+
+struct Part {
+    float m;  // running maximum
+    float s;  // sum of exp(x - m)
+    int i;    // index of the first maximum
+};
+
+__device__ __forceinline__ Part combine(Part a, Part b) {
+    Part r;
+    const bool take_b = b.m > a.m || (b.m == a.m && b.i < a.i);
+    r.m = take_b ? b.m : a.m;
+    r.i = take_b ? b.i : a.i;
+    const float sa = a.m == -INFINITY ? 0.f : a.s * bd_exp2((a.m - r.m) * BD_LOG2E);
+    const float sb = b.m == -INFINITY ? 0.f : b.s * bd_exp2((b.m - r.m) * BD_LOG2E);
+    r.s = sa + sb;
+    return r;
+}
+
+template <bool WITH_SUM>
+__device__ __forceinline__ void push(Part &p, float x, int idx) {
+    if (x > p.m) {
+        if (WITH_SUM) p.s = p.s * bd_exp2((p.m - x) * BD_LOG2E) + 1.0f;
+        p.m = x;
+        p.i = idx;
+    } else if (WITH_SUM) {
+        p.s += bd_exp2((x - p.m) * BD_LOG2E);
+    }
+}
+
+__device__ __forceinline__ Part wave_reduce(Part p) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        Part o;
+        o.m = __shfl_xor(p.m, off, 64);
+        o.s = __shfl_xor(p.s, off, 64);
+        o.i = __shfl_xor(p.i, off, 64);
+        // Fixed operand order (lower lane first) keeps the tree deterministic.
+        p = ((threadIdx.x & off) == 0) ? combine(p, o) : combine(o, p);
+    }
+    return p;
+}
+
+struct RowParams {
+    const float *logits;
+    uint8_t *masked;
+    int32_t *tokens;
+    float *conf;
+    int32_t *argmax;
+    uint8_t *committed;
+    int32_t *n_committed;
+    const int32_t *draft;
+    int32_t *accepted_len;
+    float *part_m, *part_s;
+    int *part_i;
+    float *row_conf;
+    int *row_arg;
+    int *row_cnt, *req_cnt;
+    int n_req, D, V, S, chunks, chunk_elems;
+    float tau;
+};
+
+template <bool VERIFY>
+__global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
+    __shared__ Part s_part[NT / 64];
+    __shared__ int s_row_done, s_req_done, s_nm, s_mine;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int row = blockIdx.x / p.chunks;
+    const int chunk = blockIdx.x - row * p.chunks;
+    const int r = row / p.D;
+    const int slot = row - r * p.D;
+
+    if (!VERIFY) {
+        if (w == 0) {
+            const bool mk = lane < p.D && p.masked[(size_t)r * p.D + lane] != 0;
+            const unsigned long long b = __builtin_amdgcn_ballot_w64(mk);
+            if (lane == 0) {
+                s_nm = __popcll(b);
+                s_mine = (int)((b >> slot) & 1ull);
+            }
+        }
+        __syncthreads();
+        const int nm = s_nm;
+        if (!s_mine) {
+            // A request with nothing masked still reports an empty commit.
+            if (nm == 0 && slot == 0 && chunk == 0 && w == 0 && lane < p.D) {
+                const size_t o = (size_t)r * p.D + lane;
+                if (p.conf) p.conf[o] = __int_as_float(0x7fc00000);
+                if (p.argmax) p.argmax[o] = -1;
+                if (p.committed) p.committed[o] = 0;
+                if (p.n_committed && lane == 0) p.n_committed[r] = 0;
+            }
+            return;
+        }
+    }
+
+    // Stream this chunk of the row.
+    const float *x = p.logits + (size_t)row * p.V;
+    const int beg = chunk * p.chunk_elems;
+    const int end = min(p.V, beg + p.chunk_elems);
+    Part acc{-INFINITY, 0.f, 0x7fffffff};
+    if ((p.V & 3) == 0) {
+        constexpr int U = 4;
+        for (int e0 = beg + tid * 4; e0 < end; e0 += U * NT * 4) {
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * NT * 4;
+                if (e < end) v[u] = *reinterpret_cast<const float4 *>(x + e);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * NT * 4;
+                if (e < end) {
+                    push<!VERIFY>(acc, v[u].x, e);
+                    push<!VERIFY>(acc, v[u].y, e + 1);
+                    push<!VERIFY>(acc, v[u].z, e + 2);
+                    push<!VERIFY>(acc, v[u].w, e + 3);
+                }
+            }
+        }
+    } else {
+        for (int e = beg + tid; e < end; e += NT) push<!VERIFY>(acc, x[e], e);
+    }
+    acc = wave_reduce(acc);
+    if (lane == 0) s_part[w] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        Part t = s_part[0];
+#pragma unroll
+        for (int k = 1; k < NT / 64; ++k) t = combine(t, s_part[k]);
+        const size_t o = (size_t)row * p.chunks + chunk;
+        p.part_m[o] = t.m;
+        p.part_s[o] = t.s;
+        p.part_i[o] = t.i;
+        __threadfence();
+        s_row_done = atomicAdd(&p.row_cnt[row], 1) == p.chunks - 1;
+    }
+    __syncthreads();
+    if (!s_row_done) return;
+
+    // Last chunk of this row: merge the chunk partials in chunk order (fixed tree).
+    if (w == 0) {
+        __threadfence();
+        Part t{-INFINITY, 0.f, 0x7fffffff};
+        for (int c = lane; c < p.chunks; c += 64) {
+            const size_t o = (size_t)row * p.chunks + c;
+            Part q{p.part_m[o], p.part_s[o], p.part_i[o]};
+            t = (c == lane) ? q : combine(t, q);
+        }
+        t = wave_reduce(t);
+        if (lane == 0) {
+            p.row_conf[row] = VERIFY ? 0.f : 1.0f / t.s;
+            p.row_arg[row] = t.i;
+            p.row_cnt[row] = 0;
+            __threadfence();
+            const int need = VERIFY ? p.D : s_nm;
+            s_req_done = atomicAdd(&p.req_cnt[r], 1) == need - 1;
+        }
+    }
+    __syncthreads();
+    if (!s_req_done || w != 0) return;
+
+    // Last row of request r: one wave decides for the whole block.
+    __threadfence();
+    const size_t ob = (size_t)r * p.D;
+    if (VERIFY) {
+        const int a = lane < p.D ? p.row_arg[ob + lane] : 0;
+        const bool bad = lane < p.D && a != p.draft[ob + lane];
+        const unsigned long long b = __builtin_amdgcn_ballot_w64(bad);
+        if (lane < p.D && p.argmax) p.argmax[ob + lane] = a;
+        if (lane == 0) {
+            p.accepted_len[r] = b ? (__ffsll((long long)b) - 1) : p.D;
+            p.req_cnt[r] = 0;
+        }
+        return;
+    }
+    const bool mk = lane < p.D && p.masked[ob + lane] != 0;
+    const float cf = mk ? p.row_conf[ob + lane] : __int_as_float(0x7fc00000);
+    const int am = mk ? p.row_arg[ob + lane] : -1;
+    const int nm = s_nm;
+    const int k = min((p.D + p.S - 1) / p.S, nm);
+    int rank = 0;
+    for (int j = 0; j < p.D; ++j) {
+        const float cj = __shfl(cf, j, 64);
+        const int mj = __shfl((int)mk, j, 64);
+        if (mj && j != lane && (cj > cf || (cj == cf && j < lane))) ++rank;
+    }
+    const bool take = mk && (rank < k || cf > p.tau);
+    const unsigned long long tb = __builtin_amdgcn_ballot_w64(take);
+    if (lane < p.D) {
+        if (take) {
+            p.tokens[ob + lane] = am;
+            p.masked[ob + lane] = 0;
+        }
+        if (p.conf) p.conf[ob + lane] = cf;
+        if (p.argmax) p.argmax[ob + lane] = am;
+        if (p.committed) p.committed[ob + lane] = take ? 1 : 0;
+    }
+    if (lane == 0) {
+        if (p.n_committed) p.n_committed[r] = __popcll(tb);
+        p.req_cnt[r] = 0;
+    }
+}
+
+RowParams make_params(const RowPlan &pl, const RowArgs &a) {
+    RowParams p{};
+    p.logits = a.logits;
+    p.masked = a.masked;
+    p.tokens = a.tokens;
+    p.conf = a.conf;
+    p.argmax = a.argmax;
+    p.committed = a.committed;
+    p.n_committed = a.n_committed;
+    p.draft = a.draft;
+    p.accepted_len = a.accepted_len;
+    char *ws = (char *)a.ws;
+    const size_t np = (size_t)pl.rows * pl.chunks;
+    p.part_m = (float *)(ws + pl.part_off);
+    p.part_s = p.part_m + np;
+    p.part_i = (int *)(p.part_s + np);
+    p.row_conf = (float *)(ws + pl.rowres_off);
+    p.row_arg = (int *)(p.row_conf + pl.rows);
+    p.row_cnt = (int *)(ws + pl.cnt_off);
+    p.req_cnt = p.row_cnt + pl.rows;
+    p.n_req = a.n_req;
+    p.D = a.D;
+    p.V = a.V;
+    p.S = a.S;
+    p.chunks = pl.chunks;
+    p.chunk_elems = pl.chunk_elems;
+    p.tau = a.tau;
+    return p;
+}
+
+}  // namespace
+
+RowPlan plan_rows(int n_req, int D, int V) {
+    RowPlan pl{};
+    pl.rows = n_req * D;
+    const int strides = (V + 1023) / 1024;  // 1024-float strides per row
+    const int want = std::max(1, (2048 + pl.rows - 1) / pl.rows);
+    int chunks = std::min(strides, want);
+    const int per = (strides + chunks - 1) / chunks;
+    pl.chunk_elems = per * 1024;
+    pl.chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) / 256 * 256;
+        return o;
+    };
+    pl.part_off = take((size_t)pl.rows * pl.chunks * 12);
+    pl.rowres_off = take((size_t)pl.rows * 8);
+    pl.cnt_off = take((size_t)(pl.rows + n_req) * 4);
+    pl.ws_bytes = off;
+    return pl;
+}
+
+hipError_t launch_confidence_commit(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
+    RowParams p = make_params(pl, a);
+    hipLaunchKernelGGL((row_kernel<false>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_spec_verify(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
+    RowParams p = make_params(pl, a);
+    hipLaunchKernelGGL((row_kernel<true>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// KV append (Fast-dVLM write-up, section 5.3: crop the cache to the accepted
+// prefix; DiffusionVL notes: a finished block joins the history cache).
+// One workgroup per item; the prefix length is read on the device, so no
+// host round trip is needed between verify and append.
+// ---------------------------------------------------------------------------
+template <typename E>
+__global__ __launch_bounds__(256) void kv_append_kernel(int D, int Hkv, int d, int cap, E *k_cache, E *v_cache,
+                                                        int32_t *prefix, const E *k_blk, const E *v_blk,
+                                                        const int32_t *n_accept, int32_t *dev_err) {
+    const int it = blockIdx.x;
+    const int P = prefix[it];
+    const int L = n_accept ? n_accept[it] : D;
+    if (L < 0 || L > D || P < 0 || P + L > cap) {
+        if (threadIdx.x == 0 && dev_err) *dev_err = 1;
+        return;
+    }
+    const int per_t = Hkv * d;
+    for (int e = threadIdx.x; e < L * per_t; e += blockDim.x) {
+        const int t = e / per_t;
+        const int g = (e / d) % Hkv;
+        const int dd = e % d;
+        const size_t src = (((size_t)it * D + t) * Hkv + g) * d + dd;
+        k_cache[(((size_t)it * Hkv + g) * cap + (P + t)) * d + dd] = k_blk[src];
+        v_cache[(((size_t)it * Hkv + g) * d + dd) * cap + (P + t)] = v_blk[src];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) prefix[it] = P + L;
+}
+
+hipError_t launch_kv_append(int n, int D, int Hkv, int d, int cap, int elem_bytes, void *k_cache, void *v_cache,
+                            int32_t *prefix, const void *k_blk, const void *v_blk, const int32_t *n_accept,
+                            int32_t *dev_err, hipStream_t s) {
+    if (elem_bytes == 4)
+        hipLaunchKernelGGL((kv_append_kernel<uint32_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
+                           (uint32_t *)k_cache, (uint32_t *)v_cache, prefix, (const uint32_t *)k_blk,
+                           (const uint32_t *)v_blk, n_accept, dev_err);
+    else
+        hipLaunchKernelGGL((kv_append_kernel<uint16_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
+                           (uint16_t *)k_cache, (uint16_t *)v_cache, prefix, (const uint16_t *)k_blk,
+                           (const uint16_t *)v_blk, n_accept, dev_err);
+    return hipGetLastError();
+}
+
+}  // namespace bd

@@ -1,0 +1,104 @@
+"""Device buffers for one block-diffusion step, and the calls that run it.
+
+``DeviceStep`` uploads a host-side step (numpy arrays in the layouts of
+include/bd.h) to HBM once, sizes and zero-fills the workspaces, and exposes
+the library calls on those buffers.  torch supplies device memory and the
+stream; the arithmetic runs in libbd.so.
+"""
+
+import numpy as np
+import torch
+
+from . import bd
+
+_TORCH = {np.float32: torch.float32, np.uint16: torch.int16, np.uint8: torch.uint8,
+          np.int32: torch.int32}
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host(t: torch.Tensor, like=None) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if like is not None and like == np.uint16:
+        a = a.view(np.uint16)
+    return a
+
+
+class DeviceStep:
+    """One step's inputs resident in HBM, with outputs and workspaces."""
+
+    def __init__(self, step: dict, device="cuda"):
+        p = step["params"]
+        self.p = p
+        self.dtype = p["dtype"]
+        self.device = device
+        n, D, Hq, Hkv, d = p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"]
+        self.cap = int(step["cap"])
+        self.max_prefix = int(step["prefix"].max())
+        self.q = to_device(step["q"], device)
+        self.k_blk = to_device(step["k_blk"], device)
+        self.v_blk = to_device(step["v_blk"], device)
+        self.k_cache = to_device(step["k_cache"], device)
+        self.v_cache = to_device(step["v_cache"], device)
+        self.prefix = to_device(step["prefix"], device)
+        self.logits = to_device(step["logits"], device)
+        self.masked0 = to_device(step["masked"], device)
+        self.tokens0 = to_device(step["tokens"], device)
+        self.masked = self.masked0.clone()
+        self.tokens = self.tokens0.clone()
+        self.draft = to_device(step["draft"], device) if "draft" in step else None
+        self.out = torch.empty_like(self.q)
+        self.adesc = bd.attn_desc(n, D, Hq, Hkv, d, self.cap, self.dtype, p["mode"], self.max_prefix)
+        self.cdesc = bd.commit_desc(p["n_req"], D, p["V"], p["S"], p["tau"])
+        ab = bd.bd_attn_workspace_bytes(self.adesc)
+        cb = bd.bd_commit_workspace_bytes(self.cdesc)
+        vb = bd.bd_verify_workspace_bytes(p["n_req"], D, p["V"])
+        self.attn_ws = torch.zeros(max(ab, 16), dtype=torch.uint8, device=device)
+        self.commit_ws = torch.zeros(max(cb, 16), dtype=torch.uint8, device=device)
+        self.verify_ws = torch.zeros(max(vb, 16), dtype=torch.uint8, device=device)
+        nr = p["n_req"]
+        self.conf = torch.empty((nr, D), dtype=torch.float32, device=device)
+        self.argmax = torch.empty((nr, D), dtype=torch.int32, device=device)
+        self.committed = torch.empty((nr, D), dtype=torch.uint8, device=device)
+        self.n_committed = torch.empty((nr,), dtype=torch.int32, device=device)
+        self.accepted = torch.empty((nr,), dtype=torch.int32, device=device)
+        self.dev_err = torch.zeros((1,), dtype=torch.int32, device=device)
+
+    def reset_block_state(self):
+        self.masked.copy_(self.masked0)
+        self.tokens.copy_(self.tokens0)
+
+    def attn(self, mode=None, stream=None):
+        desc = self.adesc
+        if mode is not None and mode != desc.mode:
+            desc = bd.attn_desc(desc.n_items, desc.D, desc.Hq, desc.Hkv, desc.d, desc.cap, desc.dtype,
+                                mode, desc.max_prefix, desc.scale)
+        bd.bd_attn_step(desc, self.q, self.k_blk, self.v_blk, self.k_cache, self.v_cache, self.prefix,
+                        self.out, self.attn_ws, stream=stream)
+        return self.out
+
+    def confidence_commit(self, logits=None, stream=None):
+        bd.bd_confidence_commit(self.cdesc, self.logits if logits is None else logits, self.masked,
+                                self.tokens, self.conf, self.argmax, self.committed, self.n_committed,
+                                self.commit_ws, stream=stream)
+
+    def step(self, stream=None):
+        """One denoise step: block attention, then confidence + commit."""
+        self.attn(stream=stream)
+        self.confidence_commit(stream=stream)
+
+    def verify(self, logits=None, draft=None, stream=None):
+        p = self.p
+        bd.bd_spec_verify(p["n_req"], p["D"], p["V"], self.logits if logits is None else logits,
+                          self.draft if draft is None else draft, self.accepted, self.argmax,
+                          self.verify_ws, stream=stream)
+        return self.accepted
+
+    def append(self, n_accept=None, stream=None):
+        bd.bd_kv_append(self.adesc, self.k_cache, self.v_cache, self.prefix, self.k_blk, self.v_blk,
+                        n_accept, self.dev_err, stream=stream)
