@@ -1,0 +1,208 @@
+"""Throughput of one block-diffusion denoise step on one MI355X.
+
+Workload (the long-reasoning 3B-shape step): 36 independent layers of block
+attention (16 query / 2 KV heads, head dim 128, bf16, cached prefix 4096,
+block D = 16 with 8 slots still masked) in one bd_attn_step call, then one
+bd_confidence_commit over the 8 masked rows of a 16 x 151936 fp32 logits
+tensor (S = 16, tau = 0.9).  A "step" is exactly those two calls.  The
+commit mutates the block state, so each step starts from its own copy of
+the initial state (8 of 16 slots masked), prepared before timing.
+
+Inputs are seeded and synthetic.  Four independent input sets (~645 MB) are
+rotated so that no step finds its K/V in the 256 MB last-level cache: every
+step streams its bytes from HBM.
+
+Prints one JSON line (see the keys below).  ``roofline`` describes the
+attention kernel (the dominant one): algorithmic bytes per launch divided by
+its average duration from HIP events recorded on the launch stream during
+the timed steps.  ``cpu_baseline`` times the fp64 CPU oracle on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+CFG = 3
+N_SETS = 4
+HBM_PEAK_GBS = 8000.0
+METRIC = "denoise steps/sec + achieved HBM GB/s (%peak), 3B-shape block-16, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_cfg3_traffic.json")
+ATTN_SOURCES = ["vlm_decoding_amd/csrc/bd_attn.hip", "vlm_decoding_amd/csrc/bd_common.h",
+                "vlm_decoding_amd/csrc/bd_internal.h"]
+
+
+def algorithmic_bytes(p, prefix, n_masked):
+    """Bytes a step must move at least once: every K/V element of the prefix and the
+    block once per KV head, Q read, O written, and the masked rows' logits."""
+    n, D, Hq, Hkv, d = p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"]
+    kv = int(np.sum(prefix.astype(np.int64) + D)) * Hkv * d * 2 * 2
+    qo = n * D * Hq * d * 2 * 2
+    logits = n_masked * p["V"] * 4
+    state = D * (1 + 4) * 2 + D * (4 + 4 + 1) + 4   # masked/tokens in+out, conf/argmax/committed, count
+    return kv + qo, logits, state
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per attention launch from committed counter runs, if they still
+    describe the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != attn_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(step, budget_s):
+    """The fp64 oracle on the host cores: whole steps (36-layer attention, then
+    confidence + commit) repeated until ``budget_s`` of wall time has passed."""
+    import oracle
+    p = step["params"]
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        oracle.attention(step["q"], step["k_blk"], step["v_blk"], step["k_cache"], step["v_cache"],
+                         step["prefix"], p["mode"])
+        oracle.confidence_commit(step["logits"], step["masked"], step["tokens"], p["S"], p["tau"])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return dict(value=done / el, unit="steps/s", cores=oracle.num_threads(), kind="oracle",
+                sample="%d full step(s) of the same workload (36-layer attention + confidence/commit), "
+                       "%.1f s wall" % (done, el))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline (0 to skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from vlm_decoding_amd.step import DeviceStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    p = synth.params_for(CFG)
+    sets = []
+    host0 = None
+    for k in range(N_SETS):
+        s = synth.make_step(p, synth.seed_of(CFG) + 1000 * k)
+        if k == 0:
+            host0 = s
+        sets.append(DeviceStep(s))
+        print("input set %d uploaded" % k, file=sys.stderr, flush=True)
+    # The commit mutates the block state (masked flags, tokens), so every step
+    # gets its own copy of its set's initial state, prepared before timing: one
+    # 128-byte row per step (masked at bytes 0..15, tokens at 64..127).
+    total = args.warmup + args.steps
+    rows = np.zeros((N_SETS, 128), dtype=np.uint8)
+    for k, ds in enumerate(sets):
+        rows[k, :16] = ds.masked0.cpu().numpy().reshape(-1)
+        rows[k, 64:128] = ds.tokens0.cpu().numpy().reshape(-1).view(np.uint8)
+    state = torch.from_numpy(rows[np.arange(total) % N_SETS]).to("cuda")
+    torch.cuda.synchronize()
+
+    attn_bytes, logit_bytes, state_bytes = algorithmic_bytes(p, host0["prefix"], int(host0["masked"].sum()))
+    step_bytes = attn_bytes + logit_bytes + state_bytes
+    stream = torch.cuda.current_stream()
+
+    def one_step(i, ev=None):
+        ds = sets[i % N_SETS]
+        ds.masked = state[i, :16].view(1, 16)
+        ds.tokens = state[i, 64:128].view(torch.int32).view(1, 16)
+        if ev is not None:
+            ev[0].record(stream)
+        ds.attn()
+        if ev is not None:
+            ev[1].record(stream)
+        ds.confidence_commit()
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_avg_s = float(attn_ms.mean()) * 1e-3
+    achieved = attn_bytes / attn_avg_s / 1e9
+
+    tr = traffic_per_launch()
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=tr,
+                    kernel="bd_attn_step (attn_mfma_kernel<128,4> + attn_merge_kernel<128,4>)",
+                    kernel_avg_us=round(attn_avg_s * 1e6, 2),
+                    kernel_p10_p90_us=[round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
+                                       round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
+                    algorithmic_bytes_per_launch=attn_bytes)
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(host0, args.cpu_budget)
+
+    steps_per_s = args.steps / elapsed
+    out = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 1),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "3B-shape long-reasoning denoise step: 36 layers x block attention "
+                        "(16q/2kv heads, d128, bf16, prefix 4096, block D=16, 8 of 16 masked) + "
+                        "confidence/commit over 8 x 151936 fp32 logits (S=16, tau=0.9)",
+            "layers": p["n_items"], "prefix": 4096, "block": p["D"], "heads_q": p["Hq"], "heads_kv": p["Hkv"],
+            "head_dim": p["d"], "vocab": p["V"], "masked": int(host0["masked"].sum()), "S": p["S"],
+            "tau": p["tau"], "input_sets_rotated": N_SETS,
+        },
+        "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": step_bytes,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

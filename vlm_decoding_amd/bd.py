@@ -40,6 +40,10 @@ class BdError(RuntimeError):
 
 
 def _load():
+    # torch ships its own libamdhip64.so.7.  Load it first, so libbd.so binds to
+    # the same HIP runtime that owns torch's device memory and streams (both
+    # libraries carry the same soname; whichever loads first serves the process).
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError("libbd.so is not built (%s); run __graft_entry__.build() or "
                           "python vlm_decoding_amd/build.py" % LIB_PATH)

@@ -23,6 +23,8 @@
 // normalisation.  The cached prefix is split across workgroups (split-K);
 // the last workgroup of a unit to finish merges the (m, l, o) partials in
 // split order, so results do not depend on scheduling.
+#include <type_traits>
+
 #include "bd_common.h"
 #include "bd_internal.h"
 
@@ -37,7 +39,6 @@ struct MfmaParams {
     uint16_t *out;
     float *ws_o;
     float2 *ws_ml;
-    int *ws_cnt;
     int n, D, Hq, Hkv, G, cap, mode;
     int R, row_blocks, max_splits, tiles_per_split, total_logical;
     float c;  // scale * log2(e)
@@ -49,6 +50,13 @@ struct MfmaParams {
 __device__ __forceinline__ int key_perm(int rho) {
     int q = rho >> 3, h = (rho >> 2) & 1, e = rho & 3;
     return ((q >> 1) << 4) + (h << 3) + ((q & 1) << 2) + e;
+}
+
+// Splits of a unit with prefix P: about tiles_per_split bulk (64-key) tiles
+// each, at least one, at most max_splits.  Shared by the tile and merge kernels.
+__device__ __forceinline__ int unit_splits(int P, int tiles_per_split, int max_splits) {
+    const int nbulk = P / kTileKeys;
+    return min(max_splits, max(1, (nbulk + tiles_per_split - 1) / tiles_per_split));
 }
 
 // 16-byte-unit XOR swizzles of the LDS tiles.
@@ -71,9 +79,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     constexpr int MB = HD / 32;         // d-blocks of the second MFMA
     constexpr int RPG = NW * 32;        // rows per workgroup
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][TK * HD];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][HD * TK];
-    __shared__ int s_last;
+    // One array per stage: the tile loop below is unrolled by two so that every
+    // LDS access names a fixed array, which lets the compiler see that reads of
+    // one stage never alias the global->LDS copies in flight into the other.
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * HD];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * HD];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v0[HD * TK];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v1[HD * TK];
+    auto kbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * { return st ? lds_k1 : lds_k0; };
+    auto vbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * { return st ? lds_v1 : lds_v0; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -96,16 +110,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     const int P = min(max(p.prefix[it], 0), p.cap);
     const int P64 = P & ~(TK - 1);
     const int nbulk = P64 / TK;
-    // A prefix above the host's max_prefix widens the splits instead of
-    // overrunning the workspace (every workgroup of the unit agrees on tps).
-    const int tps = max(p.tiles_per_split, (nbulk + p.max_splits - 1) / p.max_splits);
-    const int nsplit = max(1, (nbulk + tps - 1) / tps);
+    // Splits per unit grow with the prefix (about tiles_per_split bulk tiles
+    // each) up to max_splits, so a prefix above the host's max_prefix widens the
+    // splits instead of overrunning the workspace.  Tiles are dealt out evenly,
+    // counting the tail tiles, which always belong to the last split.
+    const int ntail_all = (P - P64 + p.D + TK - 1) / TK;
+    const int nsplit = unit_splits(P, p.tiles_per_split, p.max_splits);
     if (split >= nsplit) return;
-    const int t0 = split * tps;
-    const int nb_split = max(0, min(nbulk, t0 + tps) - t0);
+    const int total_tiles = nbulk + ntail_all;
+    const int t0 = min(nbulk, (int)(((long)split * total_tiles) / nsplit));
     const bool last = split == nsplit - 1;
+    const int t1 = last ? nbulk : min(nbulk, (int)(((long)(split + 1) * total_tiles) / nsplit));
+    const int nb_split = t1 - t0;
     const int tail_len = last ? (P - P64) + p.D : 0;
-    const int ntiles = nb_split + (tail_len + TK - 1) / TK;
+    const int ntiles = nb_split + (last ? ntail_all : 0);
 
     const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD;   // [cap][HD]
     const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap;   // [HD][cap]
@@ -128,6 +146,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
             else
                 qf[kc] = bf16x8{};
         }
+        // Retire the Q loads here, before any tile copy is issued: otherwise the
+        // compiler re-waits for them (vmcnt(0)) inside the loop and so drains the
+        // tile prefetch every iteration.
+        bd_wait_vmcnt<0>();
     }
 
     floatx16 o[MB];
@@ -136,74 +158,92 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    u32x4 kreg[LK], vreg[LV];
-    auto load_bulk = [&](int t) {
+    // Bulk tiles are copied global -> LDS by the load units directly
+    // (global_load_lds_dwordx4): each instruction fills 64 consecutive 16-byte
+    // LDS slots, one per lane, so the XOR swizzle is applied by choosing every
+    // lane's source address.  No VGPRs hold tile data.
+    static_assert(K_UNITS % NT == 0 && V_UNITS % NT == 0, "tile units must split evenly over lanes");
+    auto issue_bulk = [&](int t, int st) __attribute__((always_inline)) {
         const int key0 = t * TK;
 #pragma unroll
         for (int j = 0; j < LK; ++j) {
-            const int u = tid + j * NT;
-            if (K_UNITS % NT == 0 || u < K_UNITS) {
-                const int key = u / KU, lu = u % KU;
-                kreg[j] = *reinterpret_cast<const u32x4 *>(p.kc + kc_base + (size_t)(key0 + key) * HD + lu * 8);
-            }
+            const int base = (j * NW + w) * 64;
+            const int slot = base + lane;
+            const int key = slot / KU, pu = slot % KU;
+            const int lu = pu ^ k_swz<HD>(key);
+            const uint16_t *src = p.kc + kc_base + (size_t)(key0 + key) * HD + lu * 8;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&kbuf(st)[base * 8], 16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < LV; ++j) {
-            const int u = tid + j * NT;
-            if (V_UNITS % NT == 0 || u < V_UNITS) {
-                const int dd = u >> 3, lu = u & 7;
-                vreg[j] = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + key0 + lu * 8);
-            }
-        }
-    };
-    auto store_bulk = [&](int st) {
-#pragma unroll
-        for (int j = 0; j < LK; ++j) {
-            const int u = tid + j * NT;
-            if (K_UNITS % NT == 0 || u < K_UNITS) {
-                const int key = u / KU, lu = u % KU;
-                *reinterpret_cast<u32x4 *>(&lds_k[st][key * HD + ((lu ^ k_swz<HD>(key)) << 3)]) = kreg[j];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < LV; ++j) {
-            const int u = tid + j * NT;
-            if (V_UNITS % NT == 0 || u < V_UNITS) {
-                const int dd = u >> 3, lu = u & 7;
-                *reinterpret_cast<u32x4 *>(&lds_v[st][dd * TK + ((lu ^ v_swz(dd)) << 3)]) = vreg[j];
-            }
+            const int base = (j * NW + w) * 64;
+            const int slot = base + lane;
+            const int dd = slot >> 3, pu = slot & 7;
+            const int lu = pu ^ v_swz(dd);
+            const uint16_t *src = p.vc + vc_base + (size_t)dd * p.cap + key0 + lu * 8;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 8], 16, 0, 0);
         }
     };
     // Tail tiles: the last P % 64 cache positions followed by the D block slots,
-    // zero-filled past the end.  Element-wise; at most two tiles per unit.
-    auto load_tail = [&](int st, int tt) {
-        for (int e = tid; e < TK * HD; e += NT) {
-            const int key = e / HD, dd = e % HD;
+    // zero past the end (at most two tiles, always in the unit's last split).
+    // Every 16-byte unit is gathered into registers first (all loads in flight
+    // together), then written to LDS with the same swizzle as the bulk tiles.
+    auto load_tail = [&](int st, int tt) __attribute__((always_inline)) {
+        u32x4 kr[LK], vr[LV];
+#pragma unroll
+        for (int i = 0; i < LK; ++i) {
+            const int u = tid + i * NT;
+            const int key = u / KU, lu = u % KU;
             const int j = tt * TK + key;
-            uint16_t val = 0;
+            const int pos = P64 + j;
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
             if (j < tail_len) {
-                const int pos = P64 + j;
-                val = pos < P ? p.kc[kc_base + (size_t)pos * HD + dd]
-                              : p.kb[(((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + dd];
+                const uint16_t *src = pos < P ? p.kc + kc_base + (size_t)pos * HD + lu * 8
+                                              : p.kb + (((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + lu * 8;
+                v = *reinterpret_cast<const u32x4 *>(src);
             }
-            lds_k[st][key * HD + ((((dd >> 3) ^ k_swz<HD>(key))) << 3) + (dd & 7)] = val;
+            kr[i] = v;
         }
-        for (int e = tid; e < HD * TK; e += NT) {
-            const int dd = e / TK, key = e % TK;
-            const int j = tt * TK + key;
-            uint16_t val = 0;
-            if (j < tail_len) {
-                const int pos = P64 + j;
-                val = pos < P ? p.vc[vc_base + (size_t)dd * p.cap + pos]
-                              : p.vb[(((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + dd];
+#pragma unroll
+        for (int i = 0; i < LV; ++i) {
+            const int u = tid + i * NT;
+            const int dd = u >> 3, lu = u & 7;
+            const int j0 = tt * TK + lu * 8;
+            const int pos0 = P64 + j0;
+            u32x4 v;
+            if (j0 + 8 <= tail_len && pos0 + 8 <= P) {
+                v = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + pos0);
+            } else {
+                uint16_t e8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = j0 + e, pos = pos0 + e;
+                    e8[e] = j >= tail_len ? (uint16_t)0
+                            : pos < P    ? p.vc[vc_base + (size_t)dd * p.cap + pos]
+                                         : p.vb[(((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + dd];
+                }
+                v = u32x4{e8[0] | ((uint32_t)e8[1] << 16), e8[2] | ((uint32_t)e8[3] << 16),
+                          e8[4] | ((uint32_t)e8[5] << 16), e8[6] | ((uint32_t)e8[7] << 16)};
             }
-            lds_v[st][dd * TK + (((key >> 3) ^ v_swz(dd)) << 3) + (key & 7)] = val;
+            vr[i] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < LK; ++i) {
+            const int u = tid + i * NT;
+            const int key = u / KU, lu = u % KU;
+            *reinterpret_cast<u32x4 *>(kbuf(st) + key * HD + ((lu ^ k_swz<HD>(key)) << 3)) = kr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < LV; ++i) {
+            const int u = tid + i * NT;
+            const int dd = u >> 3, lu = u & 7;
+            *reinterpret_cast<u32x4 *>(vbuf(st) + dd * TK + ((lu ^ v_swz(dd)) << 3)) = vr[i];
         }
     };
 
-    auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */) {
-        const uint16_t *Kt = lds_k[st];
-        const uint16_t *Vt = lds_v[st];
+    auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */) __attribute__((always_inline)) {
+        const uint16_t *Kt = kbuf(st);
+        const uint16_t *Vt = vbuf(st);
         floatx16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -272,16 +312,31 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         }
     };
 
-    if (nb_split > 0) load_bulk(t0);
-    for (int tl = 0; tl < ntiles; ++tl) {
-        const int st = tl & 1;
-        if (tl < nb_split)
-            store_bulk(st);
-        else
-            load_tail(st, tl - nb_split);
-        __syncthreads();
-        if (tl + 1 < nb_split) load_bulk(t0 + tl + 1);
-        if (wave_active) compute(st, tl < nb_split ? -1 : tl - nb_split);
+    // Two LDS stages: tile tl+1 is in flight while tile tl is computed.
+    if (nb_split > 0)
+        issue_bulk(t0, 0);
+    else
+        load_tail(0, 0);
+    auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage)::value;
+        if (tl + 1 < ntiles) {
+            bd_barrier_lds();  // every wave is done with stage 1-ST (tile tl-1)
+            if (tl + 1 < nb_split) {
+                issue_bulk(t0 + tl + 1, 1 - ST);
+                bd_wait_vmcnt<LK + LV>();  // tile tl's copies have landed
+            } else {
+                load_tail(1 - ST, tl + 1 - nb_split);
+                bd_wait_vmcnt<0>();
+            }
+        } else {
+            bd_wait_vmcnt<0>();
+        }
+        bd_barrier_lds();  // tile tl is visible to every wave
+        if (wave_active) compute(ST, tl < nb_split ? -1 : tl - nb_split);
+    };
+    for (int tl = 0; tl < ntiles; tl += 2) {
+        step(std::integral_constant<int, 0>{}, tl);
+        if (tl + 1 < ntiles) step(std::integral_constant<int, 1>{}, tl + 1);
     }
 
     const float l_tot = l_run + bd_swap_halves(l_run);
@@ -305,64 +360,83 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         return;
     }
 
-    const size_t part = (size_t)unit * p.max_splits;
+    // Split-K partials: unnormalised o plus (m, l), stored lane-major so that
+    // every store of a wave covers one contiguous 1 KB span: quad q (4 floats)
+    // of thread t of split s of unit u lives at [(u * max_splits + s) * QUADS + q][t].
+    // The merge kernel reads them back with the same thread -> (row, d) mapping.
+    constexpr int QUADS = MB * 4;
     if (wave_active) {
-        float *wo = p.ws_o + ((part + split) * RPG + r_local) * HD;
+        const size_t base = ((size_t)unit * p.max_splits + split);
+        float4 *wo = reinterpret_cast<float4 *>(p.ws_o) + base * QUADS * NT + tid;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int dd = mb * 32 + 8 * i4 + 4 * half;
-                *reinterpret_cast<float4 *>(wo + dd) =
+            for (int i4 = 0; i4 < 4; ++i4)
+                wo[(size_t)(mb * 4 + i4) * NT] =
                     make_float4(o[mb][4 * i4], o[mb][4 * i4 + 1], o[mb][4 * i4 + 2], o[mb][4 * i4 + 3]);
-            }
-        if (half == 0) p.ws_ml[(part + split) * RPG + r_local] = make_float2(m_run, l_tot);
+        p.ws_ml[base * NT + tid] = make_float2(m_run, l_tot);
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&p.ws_cnt[unit], 1) == nsplit - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (wave_active) {
-        float M = -INFINITY;
-        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, p.ws_ml[(part + sp) * RPG + r_local].x);
-        float L = 0.f;
+}
+
+// Merge of the split-K partials (second launch; the kernel boundary orders
+// the partial stores before these loads).  Thread t of block (unit, q)
+// finishes output quad q of the row that thread t of the tile kernel owned:
+//   M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s o_s / sum_s w_s l_s,
+// summed in split order.  All loads of a thread are issued before use.
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_merge_kernel(MfmaParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int MB = HD / 32;
+    constexpr int QUADS = MB * 4;
+    constexpr int RPG = NW * 32;
+    constexpr int MAXS = kMaxSplits;
+    const int unit = blockIdx.x / QUADS;
+    const int q = blockIdx.x - unit * QUADS;
+    const int rb = unit % p.row_blocks;
+    const int pair = unit / p.row_blocks;
+    const int g = pair % p.Hkv;
+    const int it = pair / p.Hkv;
+    const int P = min(max(p.prefix[it], 0), p.cap);
+    const int nsplit = unit_splits(P, p.tiles_per_split, p.max_splits);
+    if (nsplit == 1) return;  // written directly by the tile kernel
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int r = rb * RPG + w * 32 + col;
+    if (r >= p.R) return;
+    const int slot = r / p.G;
+    const int head = g * p.G + (r - slot * p.G);
+    const size_t base = (size_t)unit * p.max_splits;
+    float2 ml[MAXS];
+    float4 v[MAXS];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) o[mb] = floatx16{};
-        for (int sp = 0; sp < nsplit; ++sp) {
-            const float2 ml = p.ws_ml[(part + sp) * RPG + r_local];
-            const float wgt = (ml.x == -INFINITY) ? 0.f : bd_exp2(ml.x - M);
-            L += wgt * ml.y;
-            const float *wo = p.ws_o + ((part + sp) * RPG + r_local) * HD;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int dd = mb * 32 + 8 * i4 + 4 * half;
-                    const float4 v = *reinterpret_cast<const float4 *>(wo + dd);
-                    o[mb][4 * i4 + 0] += wgt * v.x;
-                    o[mb][4 * i4 + 1] += wgt * v.y;
-                    o[mb][4 * i4 + 2] += wgt * v.z;
-                    o[mb][4 * i4 + 3] += wgt * v.w;
-                }
+    for (int s = 0; s < MAXS; ++s)
+        if (s < nsplit) {
+            ml[s] = p.ws_ml[(base + s) * NT + tid];
+            v[s] = reinterpret_cast<const float4 *>(p.ws_o)[((base + s) * QUADS + q) * NT + tid];
         }
-        if (row_valid) {
-            const float inv = 1.0f / L;
-            uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
+    float M = -INFINITY;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+    for (int s = 0; s < MAXS; ++s)
+        if (s < nsplit) M = fmaxf(M, ml[s].x);
+    float L = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const int dd = mb * 32 + 8 * i4 + 4 * half;
-                    uint2 v;
-                    v.x = bd_f32_to_bf16(o[mb][4 * i4 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 1] * inv) << 16);
-                    v.y = bd_f32_to_bf16(o[mb][4 * i4 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 3] * inv) << 16);
-                    *reinterpret_cast<uint2 *>(op + dd) = v;
-                }
+    for (int s = 0; s < MAXS; ++s)
+        if (s < nsplit) {
+            const float wgt = (ml[s].x == -INFINITY) ? 0.f : bd_exp2(ml[s].x - M);
+            L += wgt * ml[s].y;
+            acc.x += wgt * v[s].x;
+            acc.y += wgt * v[s].y;
+            acc.z += wgt * v[s].z;
+            acc.w += wgt * v[s].w;
         }
-    }
-    if (tid == 0) p.ws_cnt[unit] = 0;
+    const float inv = 1.0f / L;
+    const int mb = q >> 2, i4 = q & 3;
+    const int dd = mb * 32 + 8 * i4 + 4 * half;
+    uint2 o;
+    o.x = bd_f32_to_bf16(acc.x * inv) | ((uint32_t)bd_f32_to_bf16(acc.y * inv) << 16);
+    o.y = bd_f32_to_bf16(acc.z * inv) | ((uint32_t)bd_f32_to_bf16(acc.w * inv) << 16);
+    *reinterpret_cast<uint2 *>(p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD + dd) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -461,10 +535,12 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     pl.rows_per_group = pl.nw * 32;
     pl.row_blocks = (pl.rows + pl.rows_per_group - 1) / pl.rows_per_group;
     pl.units = n * Hkv * pl.row_blocks;
+    // Resident workgroups: two 4-wave or one 8-wave workgroup per CU (256 CUs).
+    const int slots = pl.nw == 4 ? 2 * kCUs : kCUs;
     const int ntiles_max = max_prefix / kTileKeys;
-    const int want = std::max(1, (kTargetGroups + pl.units - 1) / pl.units);
-    pl.tiles_per_split = std::max(1, (ntiles_max + want - 1) / want);
-    pl.max_splits = std::max(1, (ntiles_max + pl.tiles_per_split - 1) / pl.tiles_per_split);
+    const int want = std::max(1, slots / pl.units);
+    pl.max_splits = std::max(1, std::min(std::min(want, ntiles_max), kMaxSplits));
+    pl.tiles_per_split = std::max(1, (ntiles_max + pl.max_splits - 1) / pl.max_splits);
     const long total = (long)pl.units * pl.max_splits;
     pl.grid = (int)((total + 7) / 8 * 8);
     if (pl.max_splits > 1) {
@@ -474,10 +550,11 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
             off += (bytes + 255) / 256 * 256;
             return o;
         };
-        const size_t parts = (size_t)pl.units * pl.max_splits * pl.rows_per_group;
-        pl.ws_cnt_off = take(sizeof(int) * (size_t)pl.units);
-        pl.ws_ml_off = take(sizeof(float) * 2 * parts);
-        pl.ws_o_off = take(sizeof(float) * (size_t)d * parts);
+        // Per (unit, split): every thread of the workgroup stores d/2 floats of
+        // unnormalised output plus one (m, l) pair.
+        const size_t lanes = (size_t)pl.units * pl.max_splits * pl.nw * 64;
+        pl.ws_ml_off = take(sizeof(float) * 2 * lanes);
+        pl.ws_o_off = take(sizeof(float) * (size_t)(d / 2) * lanes);
         pl.ws_bytes = off;
     }
     return pl;
@@ -493,7 +570,6 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.prefix = a.prefix;
     p.out = (uint16_t *)a.out;
     char *ws = (char *)a.ws;
-    p.ws_cnt = pl.max_splits > 1 ? (int *)(ws + pl.ws_cnt_off) : nullptr;
     p.ws_ml = pl.max_splits > 1 ? (float2 *)(ws + pl.ws_ml_off) : nullptr;
     p.ws_o = pl.max_splits > 1 ? (float *)(ws + pl.ws_o_off) : nullptr;
     p.n = a.n;
@@ -509,19 +585,19 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.tiles_per_split = pl.tiles_per_split;
     p.total_logical = pl.units * pl.max_splits;
     p.c = a.scale * BD_LOG2E;
-    dim3 grid(pl.grid), block(pl.nw * 64);
+    dim3 block(pl.nw * 64);
+    const void *tile, *merge;
     if (a.d == 128) {
-        if (pl.nw == 4)
-            hipLaunchKernelGGL((attn_mfma_kernel<128, 4>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((attn_mfma_kernel<128, 8>), grid, block, 0, s, p);
+        tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4> : (const void *)attn_mfma_kernel<128, 8>;
+        merge = pl.nw == 4 ? (const void *)attn_merge_kernel<128, 4> : (const void *)attn_merge_kernel<128, 8>;
     } else {
-        if (pl.nw == 4)
-            hipLaunchKernelGGL((attn_mfma_kernel<64, 4>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((attn_mfma_kernel<64, 8>), grid, block, 0, s, p);
+        tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<64, 4> : (const void *)attn_mfma_kernel<64, 8>;
+        merge = pl.nw == 4 ? (const void *)attn_merge_kernel<64, 4> : (const void *)attn_merge_kernel<64, 8>;
     }
-    return hipGetLastError();
+    void *args[] = {&p};
+    hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
+    if (e != hipSuccess || pl.max_splits == 1) return e;
+    return hipLaunchKernel(merge, dim3(pl.units * (a.d / 8)), block, args, 0, s);
 }
 
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -26,6 +26,58 @@ __device__ __forceinline__ float bd_exp2(float x) { return __builtin_amdgcn_exp2
 // Value of lane (lane ^ 32): exchanges the two 32-lane halves of a wave.
 __device__ __forceinline__ float bd_swap_halves(float v) { return __shfl_xor(v, 32, 64); }
 
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void bd_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its outstanding global loads (unlike __syncthreads, whose fence drains
+// vmcnt).  Callers order global->LDS copies with bd_wait_vmcnt first.
+__device__ __forceinline__ void bd_barrier_lds() {
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ bool bd_wave_any(bool p) {
     return __builtin_amdgcn_ballot_w64(p) != 0;
+}
+
+// Cross-workgroup hand-off without whole-cache maintenance.  Partial results
+// are written with agent-scope relaxed atomic stores (write-through, "sc1")
+// and read back with agent-scope relaxed atomic loads (coherent reads).  The
+// writer waits for its stores to complete (s_waitcnt 0) before the workgroup
+// takes its ticket, so a device-scope fence (which would write back and
+// invalidate the whole L2) is never needed.
+__device__ __forceinline__ void bd_coherent_store2(float *p, float a, float b) {
+    const uint64_t v = ((uint64_t)__float_as_uint(b) << 32) | (uint64_t)__float_as_uint(a);
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 bd_coherent_load2(const float *p) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ void bd_coherent_store(float *p, float a) {
+    __hip_atomic_store(p, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void bd_coherent_store(int *p, int a) {
+    __hip_atomic_store(p, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float bd_coherent_load(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int bd_coherent_load(const int *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this thread issued has completed.
+__device__ __forceinline__ void bd_wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// Relaxed agent-scope ticket: returns the previous count.
+__device__ __forceinline__ int bd_ticket(int *counter) {
+    return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

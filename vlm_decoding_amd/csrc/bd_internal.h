@@ -9,7 +9,8 @@ namespace bd {
 
 // ---- block attention -------------------------------------------------------
 constexpr int kTileKeys = 64;       // keys per LDS tile
-constexpr int kTargetGroups = 512;  // workgroups the split-K decomposition aims for
+constexpr int kCUs = 256;           // compute units of an MI355X
+constexpr int kMaxSplits = 16;      // split-K pieces per unit (merge registers)
 
 struct AttnPlan {
     bool mfma;            // bf16 MFMA path (else the fp32/any vector path)
@@ -21,7 +22,7 @@ struct AttnPlan {
     int tiles_per_split;
     int max_splits;
     int grid;             // workgroups launched
-    size_t ws_cnt_off, ws_ml_off, ws_o_off, ws_bytes;
+    size_t ws_ml_off, ws_o_off, ws_bytes;
 };
 
 struct AttnArgs {
@@ -40,7 +41,7 @@ hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s);
 // ---- confidence / verify ----------------------------------------------------
 struct RowPlan {
     int rows, chunks, chunk_elems;
-    size_t part_off, rowres_off, cnt_off, ws_bytes;
+    size_t part_off, cnt_off, ws_bytes;
 };
 RowPlan plan_rows(int n_req, int D, int V);
 

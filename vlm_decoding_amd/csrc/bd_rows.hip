@@ -12,9 +12,9 @@
 // Each row is split into chunks of whole 1024-float strides; one 256-thread
 // workgroup streams one chunk with 16-byte loads, keeping a running
 // (max, index of first max, sum of exp(x - max)) per thread.  Partials are
-// combined in a fixed tree inside the workgroup, then across chunks by the
-// last workgroup of the row (atomic ticket) in chunk order; the last row of
-// a request runs the one-wave commit / verify tail.  No float atomics, so
+// combined in a fixed tree inside the workgroup; the last workgroup of a
+// request (one atomic ticket per request) merges every row's chunk partials
+// in chunk order and runs the one-wave commit / verify tail.  No float atomics, so
 // results are identical run to run.
 #include "bd_common.h"
 #include "bd_internal.h"
@@ -77,9 +77,7 @@ struct RowParams {
     int32_t *accepted_len;
     float *part_m, *part_s;
     int *part_i;
-    float *row_conf;
-    int *row_arg;
-    int *row_cnt, *req_cnt;
+    int *req_cnt;
     int n_req, D, V, S, chunks, chunk_elems;
     float tau;
 };
@@ -87,7 +85,10 @@ struct RowParams {
 template <bool VERIFY>
 __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     __shared__ Part s_part[NT / 64];
-    __shared__ int s_row_done, s_req_done, s_nm, s_mine;
+    __shared__ float s_conf[64];
+    __shared__ int s_arg[64];
+    __shared__ int s_done, s_nm;
+    __shared__ unsigned long long s_mask;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -95,25 +96,24 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     const int chunk = blockIdx.x - row * p.chunks;
     const int r = row / p.D;
     const int slot = row - r * p.D;
+    const size_t ob = (size_t)r * p.D;
 
     if (!VERIFY) {
         if (w == 0) {
-            const bool mk = lane < p.D && p.masked[(size_t)r * p.D + lane] != 0;
+            const bool mk = lane < p.D && p.masked[ob + lane] != 0;
             const unsigned long long b = __builtin_amdgcn_ballot_w64(mk);
             if (lane == 0) {
+                s_mask = b;
                 s_nm = __popcll(b);
-                s_mine = (int)((b >> slot) & 1ull);
             }
         }
         __syncthreads();
-        const int nm = s_nm;
-        if (!s_mine) {
+        if (!((s_mask >> slot) & 1ull)) {
             // A request with nothing masked still reports an empty commit.
-            if (nm == 0 && slot == 0 && chunk == 0 && w == 0 && lane < p.D) {
-                const size_t o = (size_t)r * p.D + lane;
-                if (p.conf) p.conf[o] = __int_as_float(0x7fc00000);
-                if (p.argmax) p.argmax[o] = -1;
-                if (p.committed) p.committed[o] = 0;
+            if (s_nm == 0 && slot == 0 && chunk == 0 && w == 0 && lane < p.D) {
+                if (p.conf) p.conf[ob + lane] = __int_as_float(0x7fc00000);
+                if (p.argmax) p.argmax[ob + lane] = -1;
+                if (p.committed) p.committed[ob + lane] = 0;
                 if (p.n_committed && lane == 0) p.n_committed[r] = 0;
             }
             return;
@@ -156,60 +156,58 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
 #pragma unroll
         for (int k = 1; k < NT / 64; ++k) t = combine(t, s_part[k]);
         const size_t o = (size_t)row * p.chunks + chunk;
-        p.part_m[o] = t.m;
-        p.part_s[o] = t.s;
-        p.part_i[o] = t.i;
-        __threadfence();
-        s_row_done = atomicAdd(&p.row_cnt[row], 1) == p.chunks - 1;
+        bd_coherent_store(p.part_m + o, t.m);
+        bd_coherent_store(p.part_s + o, t.s);
+        bd_coherent_store(p.part_i + o, t.i);
+        bd_wait_all_memory();
+        // One ticket per request: the last of its (rows x chunks) workgroups finishes it.
+        const int need = (VERIFY ? p.D : s_nm) * p.chunks;
+        s_done = bd_ticket(&p.req_cnt[r]) == need - 1;
     }
     __syncthreads();
-    if (!s_row_done) return;
+    if (!s_done) return;
 
-    // Last chunk of this row: merge the chunk partials in chunk order (fixed tree).
-    if (w == 0) {
-        __threadfence();
+    // Merge every participating row of request r, each in chunk order (fixed tree),
+    // one wave per row.
+    for (int i = w; i < p.D; i += NT / 64) {
+        const bool part = VERIFY || ((s_mask >> i) & 1ull);
+        if (!part) continue;
+        const size_t rw = ob + i;
         Part t{-INFINITY, 0.f, 0x7fffffff};
         for (int c = lane; c < p.chunks; c += 64) {
-            const size_t o = (size_t)row * p.chunks + c;
-            Part q{p.part_m[o], p.part_s[o], p.part_i[o]};
+            const size_t o = rw * p.chunks + c;
+            Part q{bd_coherent_load(p.part_m + o), bd_coherent_load(p.part_s + o), bd_coherent_load(p.part_i + o)};
             t = (c == lane) ? q : combine(t, q);
         }
         t = wave_reduce(t);
         if (lane == 0) {
-            p.row_conf[row] = VERIFY ? 0.f : 1.0f / t.s;
-            p.row_arg[row] = t.i;
-            p.row_cnt[row] = 0;
-            __threadfence();
-            const int need = VERIFY ? p.D : s_nm;
-            s_req_done = atomicAdd(&p.req_cnt[r], 1) == need - 1;
+            s_conf[i] = 1.0f / t.s;
+            s_arg[i] = t.i;
         }
     }
     __syncthreads();
-    if (!s_req_done || w != 0) return;
-
-    // Last row of request r: one wave decides for the whole block.
-    __threadfence();
-    const size_t ob = (size_t)r * p.D;
+    if (w != 0) return;
     if (VERIFY) {
-        const int a = lane < p.D ? p.row_arg[ob + lane] : 0;
+        const int a = lane < p.D ? s_arg[lane] : 0;
         const bool bad = lane < p.D && a != p.draft[ob + lane];
         const unsigned long long b = __builtin_amdgcn_ballot_w64(bad);
         if (lane < p.D && p.argmax) p.argmax[ob + lane] = a;
         if (lane == 0) {
             p.accepted_len[r] = b ? (__ffsll((long long)b) - 1) : p.D;
-            p.req_cnt[r] = 0;
+            bd_coherent_store(p.req_cnt + r, 0);
         }
         return;
     }
-    const bool mk = lane < p.D && p.masked[ob + lane] != 0;
-    const float cf = mk ? p.row_conf[ob + lane] : __int_as_float(0x7fc00000);
-    const int am = mk ? p.row_arg[ob + lane] : -1;
+    // Commit (one wave, one lane per slot).
+    const bool mk = lane < p.D && ((s_mask >> lane) & 1ull);
+    const float cf = mk ? s_conf[lane] : __int_as_float(0x7fc00000);
+    const int am = mk ? s_arg[lane] : -1;
     const int nm = s_nm;
     const int k = min((p.D + p.S - 1) / p.S, nm);
     int rank = 0;
     for (int j = 0; j < p.D; ++j) {
         const float cj = __shfl(cf, j, 64);
-        const int mj = __shfl((int)mk, j, 64);
+        const bool mj = (s_mask >> j) & 1ull;
         if (mj && j != lane && (cj > cf || (cj == cf && j < lane))) ++rank;
     }
     const bool take = mk && (rank < k || cf > p.tau);
@@ -225,7 +223,7 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     }
     if (lane == 0) {
         if (p.n_committed) p.n_committed[r] = __popcll(tb);
-        p.req_cnt[r] = 0;
+        bd_coherent_store(p.req_cnt + r, 0);
     }
 }
 
@@ -245,10 +243,7 @@ RowParams make_params(const RowPlan &pl, const RowArgs &a) {
     p.part_m = (float *)(ws + pl.part_off);
     p.part_s = p.part_m + np;
     p.part_i = (int *)(p.part_s + np);
-    p.row_conf = (float *)(ws + pl.rowres_off);
-    p.row_arg = (int *)(p.row_conf + pl.rows);
-    p.row_cnt = (int *)(ws + pl.cnt_off);
-    p.req_cnt = p.row_cnt + pl.rows;
+    p.req_cnt = (int *)(ws + pl.cnt_off);
     p.n_req = a.n_req;
     p.D = a.D;
     p.V = a.V;
@@ -264,9 +259,14 @@ RowParams make_params(const RowPlan &pl, const RowArgs &a) {
 RowPlan plan_rows(int n_req, int D, int V) {
     RowPlan pl{};
     pl.rows = n_req * D;
+    // Chunks of about 16 strides of 1024 floats (64 KB): enough bytes per
+    // workgroup to keep its loads streaming, few enough workgroups per request
+    // that its ticket counter is not a point of contention.  Rows that are
+    // short or few get smaller chunks so that at least ~256 workgroups run.
     const int strides = (V + 1023) / 1024;  // 1024-float strides per row
-    const int want = std::max(1, (2048 + pl.rows - 1) / pl.rows);
-    int chunks = std::min(strides, want);
+    int chunks = std::max(1, (strides + 15) / 16);
+    const int want = std::max(1, (256 + pl.rows - 1) / pl.rows);
+    chunks = std::min(strides, std::max(chunks, want));
     const int per = (strides + chunks - 1) / chunks;
     pl.chunk_elems = per * 1024;
     pl.chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
@@ -277,8 +277,7 @@ RowPlan plan_rows(int n_req, int D, int V) {
         return o;
     };
     pl.part_off = take((size_t)pl.rows * pl.chunks * 12);
-    pl.rowres_off = take((size_t)pl.rows * 8);
-    pl.cnt_off = take((size_t)(pl.rows + n_req) * 4);
+    pl.cnt_off = take((size_t)n_req * 4);
     pl.ws_bytes = off;
     return pl;
 }
