@@ -91,6 +91,19 @@ def cpu_baseline(step, budget_s):
                        "%.1f s wall" % (done, el))
 
 
+def copy_calibration(n_bytes=256 << 20, reps=5):
+    """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
+    WRITE_SIZE for this copy kernel give the scale between counter readings and
+    bytes moved (each copy reads and writes n_bytes)."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n_bytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,7 +111,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain 256 MiB device copies (to scale HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)

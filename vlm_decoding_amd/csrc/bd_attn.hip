@@ -117,13 +117,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     const int ntail_all = (P - P64 + p.D + TK - 1) / TK;
     const int nsplit = unit_splits(P, p.tiles_per_split, p.max_splits);
     if (split >= nsplit) return;
-    const int total_tiles = nbulk + ntail_all;
+    // Tail tiles count double: they are gathered, not streamed.
+    const int total_tiles = nbulk + 2 * ntail_all;
     const int t0 = min(nbulk, (int)(((long)split * total_tiles) / nsplit));
     const bool last = split == nsplit - 1;
     const int t1 = last ? nbulk : min(nbulk, (int)(((long)(split + 1) * total_tiles) / nsplit));
     const int nb_split = t1 - t0;
     const int tail_len = last ? (P - P64) + p.D : 0;
-    const int ntiles = nb_split + (last ? ntail_all : 0);
+    // The last split takes its tail tiles first: their gathers overlap the
+    // copy of its first bulk tile instead of extending the end of the split.
+    const int ntail = last ? ntail_all : 0;
 
     const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD;   // [cap][HD]
     const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap;   // [HD][cap]
@@ -185,10 +188,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         }
     };
     // Tail tiles: the last P % 64 cache positions followed by the D block slots,
-    // zero past the end (at most two tiles, always in the unit's last split).
-    // Every 16-byte unit is gathered into registers first (all loads in flight
-    // together), then written to LDS with the same swizzle as the bulk tiles.
+    // zero past the end (at most two tiles, in the unit's last split).  K rows
+    // and cache V^T rows are gathered as 16-byte units.  Block V rows arrive
+    // d-contiguous ([slot][Hkv][d]); they are loaded as 16-byte units and
+    // scattered transposed into the V^T tile after the other units are written.
+    constexpr int BU = HD / 8;  // 16-byte units per block V row
     auto load_tail = [&](int st, int tt) __attribute__((always_inline)) {
+        const int pc = P - P64;  // cache positions in the tail
         u32x4 kr[LK], vr[LV];
 #pragma unroll
         for (int i = 0; i < LK; ++i) {
@@ -209,19 +215,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
             const int u = tid + i * NT;
             const int dd = u >> 3, lu = u & 7;
             const int j0 = tt * TK + lu * 8;
-            const int pos0 = P64 + j0;
-            u32x4 v;
-            if (j0 + 8 <= tail_len && pos0 + 8 <= P) {
-                v = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + pos0);
-            } else {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (j0 + 8 <= pc) {
+                v = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + P64 + j0);
+            } else if (j0 < pc) {  // unit straddles the end of the cache part
                 uint16_t e8[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = j0 + e, pos = pos0 + e;
-                    e8[e] = j >= tail_len ? (uint16_t)0
-                            : pos < P    ? p.vc[vc_base + (size_t)dd * p.cap + pos]
-                                         : p.vb[(((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + dd];
-                }
+                for (int e = 0; e < 8; ++e)
+                    e8[e] = j0 + e < pc ? p.vc[vc_base + (size_t)dd * p.cap + P64 + j0 + e] : (uint16_t)0;
                 v = u32x4{e8[0] | ((uint32_t)e8[1] << 16), e8[2] | ((uint32_t)e8[3] << 16),
                           e8[4] | ((uint32_t)e8[5] << 16), e8[6] | ((uint32_t)e8[7] << 16)};
             }
@@ -238,6 +239,34 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
             const int u = tid + i * NT;
             const int dd = u >> 3, lu = u & 7;
             *reinterpret_cast<u32x4 *>(vbuf(st) + dd * TK + ((lu ^ v_swz(dd)) << 3)) = vr[i];
+        }
+        bd_barrier_lds();  // the scatter below overwrites zeros written above
+        // Block V units that land in this tile: slot b covers tail position pc + b.
+        constexpr int VB_MAX = (64 * BU + NT - 1) / NT;  // D <= 64
+        u32x4 br[VB_MAX];
+        int bkey[VB_MAX];
+#pragma unroll
+        for (int i = 0; i < VB_MAX; ++i) {
+            const int u = tid + i * NT;
+            const int b = u / BU, du = u % BU;
+            const int j = pc + b - tt * TK;  // key index inside this tile
+            bkey[i] = (b < p.D && j >= 0 && j < TK) ? j : -1;
+            if (bkey[i] >= 0)
+                br[i] = *reinterpret_cast<const u32x4 *>(p.vb + (((size_t)it * p.D + b) * p.Hkv + g) * HD + du * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < VB_MAX; ++i) {
+            if (bkey[i] < 0) continue;
+            const int u = tid + i * NT;
+            const int du = u % BU;
+            const int key = bkey[i];
+            const uint32_t w4[4] = {br[i].x, br[i].y, br[i].z, br[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int dd = du * 8 + e;
+                const uint16_t val = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+                vbuf(st)[dd * TK + (((key >> 3) ^ v_swz(dd)) << 3) + (key & 7)] = val;
+            }
         }
     };
 
@@ -288,15 +317,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
             m_run = m_new;
         }
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-        float lsum = 0.f;
         bf16x8 pb[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = bd_exp2(fmaf(s[kb][i], p.c, -msub));
-                lsum += pv;
-                pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
+            for (int i = 0; i < 16; ++i) pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)bd_exp2(fmaf(s[kb][i], p.c, -msub));
+        // Row sum of the rounded weights (exactly what the P.V product uses),
+        // two at a time with v_dot2_f32_bf16.
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float lsum = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2 pr = {pb[c4][2 * e], pb[c4][2 * e + 1]};
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
             }
         l_run += lsum;
 #pragma unroll
@@ -312,31 +347,31 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         }
     };
 
-    // Two LDS stages: tile tl+1 is in flight while tile tl is computed.
-    if (nb_split > 0)
-        issue_bulk(t0, 0);
-    else
-        load_tail(0, 0);
+    // Tail tiles first (last split only): the first bulk tile is copied into
+    // stage 0 while the tail is gathered into stage 1 and computed.
+    if (nb_split > 0) issue_bulk(t0, 0);
+    for (int tt = 0; tt < ntail; ++tt) {
+        if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
+        load_tail(1, tt);
+        bd_barrier_lds();
+        if (wave_active) compute(1, tt);
+    }
+    // Bulk tiles, two LDS stages: tile tl+1 is in flight while tile tl is computed.
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        if (tl + 1 < ntiles) {
-            bd_barrier_lds();  // every wave is done with stage 1-ST (tile tl-1)
-            if (tl + 1 < nb_split) {
-                issue_bulk(t0 + tl + 1, 1 - ST);
-                bd_wait_vmcnt<LK + LV>();  // tile tl's copies have landed
-            } else {
-                load_tail(1 - ST, tl + 1 - nb_split);
-                bd_wait_vmcnt<0>();
-            }
+        if (tl + 1 < nb_split) {
+            bd_barrier_lds();  // every wave is done with stage 1-ST
+            issue_bulk(t0 + tl + 1, 1 - ST);
+            bd_wait_vmcnt<LK + LV>();  // tile tl's copies have landed
         } else {
             bd_wait_vmcnt<0>();
         }
         bd_barrier_lds();  // tile tl is visible to every wave
-        if (wave_active) compute(ST, tl < nb_split ? -1 : tl - nb_split);
+        if (wave_active) compute(ST, -1);
     };
-    for (int tl = 0; tl < ntiles; tl += 2) {
+    for (int tl = 0; tl < nb_split; tl += 2) {
         step(std::integral_constant<int, 0>{}, tl);
-        if (tl + 1 < ntiles) step(std::integral_constant<int, 1>{}, tl + 1);
+        if (tl + 1 < nb_split) step(std::integral_constant<int, 1>{}, tl + 1);
     }
 
     const float l_tot = l_run + bd_swap_halves(l_run);
@@ -360,38 +395,46 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         return;
     }
 
-    // Split-K partials: unnormalised o plus (m, l), stored lane-major so that
-    // every store of a wave covers one contiguous 1 KB span: quad q (4 floats)
-    // of thread t of split s of unit u lives at [(u * max_splits + s) * QUADS + q][t].
-    // The merge kernel reads them back with the same thread -> (row, d) mapping.
+    // Split-K partials: the split's normalised output o / l as bf16 plus its
+    // (m, l) in fp32, stored lane-major so that every store of a wave covers
+    // one contiguous span: quad q (4 outputs) of thread t of split s of unit u
+    // lives at [(u * max_splits + s) * QUADS + q][t].  The merge kernel reads
+    // them back with the same thread -> (row, d) mapping.
     constexpr int QUADS = MB * 4;
     if (wave_active) {
         const size_t base = ((size_t)unit * p.max_splits + split);
-        float4 *wo = reinterpret_cast<float4 *>(p.ws_o) + base * QUADS * NT + tid;
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        uint2 *wo = reinterpret_cast<uint2 *>(p.ws_o) + base * QUADS * NT + tid;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4)
-                wo[(size_t)(mb * 4 + i4) * NT] =
-                    make_float4(o[mb][4 * i4], o[mb][4 * i4 + 1], o[mb][4 * i4 + 2], o[mb][4 * i4 + 3]);
+            for (int i4 = 0; i4 < 4; ++i4) {
+                uint2 v;
+                v.x = bd_f32_to_bf16(o[mb][4 * i4 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 1] * inv) << 16);
+                v.y = bd_f32_to_bf16(o[mb][4 * i4 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 3] * inv) << 16);
+                wo[(size_t)(mb * 4 + i4) * NT] = v;
+            }
         p.ws_ml[base * NT + tid] = make_float2(m_run, l_tot);
     }
 }
 
 // Merge of the split-K partials (second launch; the kernel boundary orders
-// the partial stores before these loads).  Thread t of block (unit, q)
-// finishes output quad q of the row that thread t of the tile kernel owned:
-//   M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s o_s / sum_s w_s l_s,
+// the partial stores before these loads).  Thread t of block (unit, q0)
+// finishes output quads q0 and q0 + QUADS/2 of the row that thread t of the
+// tile kernel owned:
+//   M = max_s m_s,  c_s = 2^(m_s - M) l_s,  o = sum_s c_s (o_s / l_s) / sum_s c_s,
 // summed in split order.  All loads of a thread are issued before use.
 template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(MfmaParams p) {
     constexpr int NT = NW * 64;
     constexpr int MB = HD / 32;
     constexpr int QUADS = MB * 4;
+    constexpr int QPT = 2;                 // output quads per thread
+    constexpr int QB = QUADS / QPT;        // blocks per unit
     constexpr int RPG = NW * 32;
     constexpr int MAXS = kMaxSplits;
-    const int unit = blockIdx.x / QUADS;
-    const int q = blockIdx.x - unit * QUADS;
+    const int unit = blockIdx.x / QB;
+    const int q0 = blockIdx.x - unit * QB;
     const int rb = unit % p.row_blocks;
     const int pair = unit / p.row_blocks;
     const int g = pair % p.Hkv;
@@ -406,37 +449,47 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(MfmaParams p) {
     const int slot = r / p.G;
     const int head = g * p.G + (r - slot * p.G);
     const size_t base = (size_t)unit * p.max_splits;
+    const uint2 *wo = reinterpret_cast<const uint2 *>(p.ws_o);
     float2 ml[MAXS];
-    float4 v[MAXS];
+    uint2 v[QPT][MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (s < nsplit) {
             ml[s] = p.ws_ml[(base + s) * NT + tid];
-            v[s] = reinterpret_cast<const float4 *>(p.ws_o)[((base + s) * QUADS + q) * NT + tid];
+#pragma unroll
+            for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QUADS + q0 + j * QB) * NT + tid];
         }
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (s < nsplit) M = fmaxf(M, ml[s].x);
     float L = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float acc[QPT][4] = {};
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (s < nsplit) {
-            const float wgt = (ml[s].x == -INFINITY) ? 0.f : bd_exp2(ml[s].x - M);
-            L += wgt * ml[s].y;
-            acc.x += wgt * v[s].x;
-            acc.y += wgt * v[s].y;
-            acc.z += wgt * v[s].z;
-            acc.w += wgt * v[s].w;
+            const float c = (ml[s].x == -INFINITY) ? 0.f : bd_exp2(ml[s].x - M) * ml[s].y;
+            L += c;
+#pragma unroll
+            for (int j = 0; j < QPT; ++j) {
+                acc[j][0] += c * bd_bf16_to_f32((uint16_t)(v[j][s].x & 0xffff));
+                acc[j][1] += c * bd_bf16_to_f32((uint16_t)(v[j][s].x >> 16));
+                acc[j][2] += c * bd_bf16_to_f32((uint16_t)(v[j][s].y & 0xffff));
+                acc[j][3] += c * bd_bf16_to_f32((uint16_t)(v[j][s].y >> 16));
+            }
         }
     const float inv = 1.0f / L;
-    const int mb = q >> 2, i4 = q & 3;
-    const int dd = mb * 32 + 8 * i4 + 4 * half;
-    uint2 o;
-    o.x = bd_f32_to_bf16(acc.x * inv) | ((uint32_t)bd_f32_to_bf16(acc.y * inv) << 16);
-    o.y = bd_f32_to_bf16(acc.z * inv) | ((uint32_t)bd_f32_to_bf16(acc.w * inv) << 16);
-    *reinterpret_cast<uint2 *>(p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD + dd) = o;
+    uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int q = q0 + j * QB;
+        const int mb = q >> 2, i4 = q & 3;
+        const int dd = mb * 32 + 8 * i4 + 4 * half;
+        uint2 o;
+        o.x = bd_f32_to_bf16(acc[j][0] * inv) | ((uint32_t)bd_f32_to_bf16(acc[j][1] * inv) << 16);
+        o.y = bd_f32_to_bf16(acc[j][2] * inv) | ((uint32_t)bd_f32_to_bf16(acc[j][3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(op + dd) = o;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -550,11 +603,11 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
             off += (bytes + 255) / 256 * 256;
             return o;
         };
-        // Per (unit, split): every thread of the workgroup stores d/2 floats of
-        // unnormalised output plus one (m, l) pair.
+        // Per (unit, split): every thread of the workgroup stores d/2 bf16
+        // outputs of the split (normalised) plus one fp32 (m, l) pair.
         const size_t lanes = (size_t)pl.units * pl.max_splits * pl.nw * 64;
         pl.ws_ml_off = take(sizeof(float) * 2 * lanes);
-        pl.ws_o_off = take(sizeof(float) * (size_t)(d / 2) * lanes);
+        pl.ws_o_off = take(sizeof(uint16_t) * (size_t)(d / 2) * lanes);
         pl.ws_bytes = off;
     }
     return pl;
@@ -597,7 +650,7 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
     if (e != hipSuccess || pl.max_splits == 1) return e;
-    return hipLaunchKernel(merge, dim3(pl.units * (a.d / 8)), block, args, 0, s);
+    return hipLaunchKernel(merge, dim3(pl.units * (a.d / 16)), block, args, 0, s);
 }
 
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -40,8 +41,10 @@ __device__ __forceinline__ void bd_wait_vmcnt() {
 // its outstanding global loads (unlike __syncthreads, whose fence drains
 // vmcnt).  Callers order global->LDS copies with bd_wait_vmcnt first.
 __device__ __forceinline__ void bd_barrier_lds() {
+    asm volatile("" ::: "memory");  // compiler-only fence: no access moves across
     __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ bool bd_wave_any(bool p) {

@@ -84,6 +84,7 @@ struct RowParams {
 
 template <bool VERIFY>
 __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
+    extern __shared__ float s_dyn[];  // merge staging: D * chunks partials (m, s, i)
     __shared__ Part s_part[NT / 64];
     __shared__ float s_conf[64];
     __shared__ int s_arg[64];
@@ -98,9 +99,26 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     const int slot = row - r * p.D;
     const size_t ob = (size_t)r * p.D;
 
+    // The masked flags are requested first and the chunk's first logits loads
+    // right behind them, so deciding whether this row takes part costs no
+    // extra round trip (rows that do not take part drop their loads).
+    bool mk = false;
+    if (!VERIFY && w == 0) mk = lane < p.D && p.masked[ob + lane] != 0;
+    const float *x = p.logits + (size_t)row * p.V;
+    const int beg = chunk * p.chunk_elems;
+    const int end = min(p.V, beg + p.chunk_elems);
+    const bool vec = (p.V & 3) == 0;
+    constexpr int U = 4;
+    float4 v[U];
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = beg + tid * 4 + u * NT * 4;
+            if (e < end) v[u] = *reinterpret_cast<const float4 *>(x + e);
+        }
+    }
     if (!VERIFY) {
         if (w == 0) {
-            const bool mk = lane < p.D && p.masked[ob + lane] != 0;
             const unsigned long long b = __builtin_amdgcn_ballot_w64(mk);
             if (lane == 0) {
                 s_mask = b;
@@ -120,20 +138,10 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         }
     }
 
-    // Stream this chunk of the row.
-    const float *x = p.logits + (size_t)row * p.V;
-    const int beg = chunk * p.chunk_elems;
-    const int end = min(p.V, beg + p.chunk_elems);
+    // Stream this chunk of the row (the first batch is already in flight).
     Part acc{-INFINITY, 0.f, 0x7fffffff};
-    if ((p.V & 3) == 0) {
-        constexpr int U = 4;
-        for (int e0 = beg + tid * 4; e0 < end; e0 += U * NT * 4) {
-            float4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = e0 + u * NT * 4;
-                if (e < end) v[u] = *reinterpret_cast<const float4 *>(x + e);
-            }
+    if (vec) {
+        for (int e0 = beg + tid * 4;; e0 += U * NT * 4) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = e0 + u * NT * 4;
@@ -143,6 +151,13 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
                     push<!VERIFY>(acc, v[u].z, e + 2);
                     push<!VERIFY>(acc, v[u].w, e + 3);
                 }
+            }
+            const int n0 = e0 + U * NT * 4;
+            if (n0 >= end) break;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = n0 + u * NT * 4;
+                if (e < end) v[u] = *reinterpret_cast<const float4 *>(x + e);
             }
         }
     } else {
@@ -167,16 +182,27 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     __syncthreads();
     if (!s_done) return;
 
-    // Merge every participating row of request r, each in chunk order (fixed tree),
-    // one wave per row.
+    // Last workgroup of request r: fetch every partial of the request in one
+    // parallel round trip, then merge each row in chunk order (fixed tree).
+    const int nparts = p.D * p.chunks;
+    float *lm = s_dyn, *ls = s_dyn + nparts;
+    int *li = reinterpret_cast<int *>(s_dyn + 2 * nparts);
+    for (int t = tid; t < nparts; t += NT) {
+        const int i = t / p.chunks;
+        if (VERIFY || ((s_mask >> i) & 1ull)) {
+            const size_t o = ob * p.chunks + t;
+            lm[t] = bd_coherent_load(p.part_m + o);
+            ls[t] = bd_coherent_load(p.part_s + o);
+            li[t] = bd_coherent_load(p.part_i + o);
+        }
+    }
+    __syncthreads();
     for (int i = w; i < p.D; i += NT / 64) {
-        const bool part = VERIFY || ((s_mask >> i) & 1ull);
-        if (!part) continue;
-        const size_t rw = ob + i;
+        if (!(VERIFY || ((s_mask >> i) & 1ull))) continue;
         Part t{-INFINITY, 0.f, 0x7fffffff};
         for (int c = lane; c < p.chunks; c += 64) {
-            const size_t o = rw * p.chunks + c;
-            Part q{bd_coherent_load(p.part_m + o), bd_coherent_load(p.part_s + o), bd_coherent_load(p.part_i + o)};
+            const int o = i * p.chunks + c;
+            Part q{lm[o], ls[o], li[o]};
             t = (c == lane) ? q : combine(t, q);
         }
         t = wave_reduce(t);
@@ -199,9 +225,9 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         return;
     }
     // Commit (one wave, one lane per slot).
-    const bool mk = lane < p.D && ((s_mask >> lane) & 1ull);
-    const float cf = mk ? s_conf[lane] : __int_as_float(0x7fc00000);
-    const int am = mk ? s_arg[lane] : -1;
+    const bool m_l = lane < p.D && ((s_mask >> lane) & 1ull);
+    const float cf = m_l ? s_conf[lane] : __int_as_float(0x7fc00000);
+    const int am = m_l ? s_arg[lane] : -1;
     const int nm = s_nm;
     const int k = min((p.D + p.S - 1) / p.S, nm);
     int rank = 0;
@@ -210,7 +236,7 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         const bool mj = (s_mask >> j) & 1ull;
         if (mj && j != lane && (cj > cf || (cj == cf && j < lane))) ++rank;
     }
-    const bool take = mk && (rank < k || cf > p.tau);
+    const bool take = m_l && (rank < k || cf > p.tau);
     const unsigned long long tb = __builtin_amdgcn_ballot_w64(take);
     if (lane < p.D) {
         if (take) {
@@ -267,9 +293,13 @@ RowPlan plan_rows(int n_req, int D, int V) {
     int chunks = std::max(1, (strides + 15) / 16);
     const int want = std::max(1, (256 + pl.rows - 1) / pl.rows);
     chunks = std::min(strides, std::max(chunks, want));
-    const int per = (strides + chunks - 1) / chunks;
+    int per = (strides + chunks - 1) / chunks;
+    // The finishing workgroup stages D * chunks partials (12 bytes each) in LDS:
+    // keep that within 48 KB by growing the chunks if needed.
+    while ((size_t)D * ((strides + per - 1) / per) * 12 > 48 * 1024) ++per;
     pl.chunk_elems = per * 1024;
     pl.chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
+    pl.merge_lds = (size_t)D * pl.chunks * 12;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -284,13 +314,13 @@ RowPlan plan_rows(int n_req, int D, int V) {
 
 hipError_t launch_confidence_commit(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
     RowParams p = make_params(pl, a);
-    hipLaunchKernelGGL((row_kernel<false>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((row_kernel<false>), dim3(pl.rows * pl.chunks), dim3(NT), pl.merge_lds, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_spec_verify(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
     RowParams p = make_params(pl, a);
-    hipLaunchKernelGGL((row_kernel<true>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((row_kernel<true>), dim3(pl.rows * pl.chunks), dim3(NT), pl.merge_lds, s, p);
     return hipGetLastError();
 }
 
