@@ -99,7 +99,8 @@ bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_bl
 
 size_t bd_commit_workspace_bytes(const bd_commit_desc *desc) {
     if (check_commit_desc(desc) != BD_OK) return SIZE_MAX;
-    return bd::plan_rows(desc->n_req, desc->D, desc->V).ws_bytes;
+    const bd::RowPlan pl = bd::plan_rows(desc->n_req, desc->D, desc->V);
+    return pl.ok ? pl.ws_bytes : SIZE_MAX;
 }
 
 bd_status bd_confidence_commit(const bd_commit_desc *desc, const float *logits, uint8_t *masked,
@@ -110,6 +111,7 @@ bd_status bd_confidence_commit(const bd_commit_desc *desc, const float *logits, 
     if (!logits || !masked || !tokens) return BD_E_NULL;
     if (!aligned16(logits)) return BD_E_PARAM;
     const bd::RowPlan pl = bd::plan_rows(desc->n_req, desc->D, desc->V);
+    if (!pl.ok) return BD_E_SHAPE;
     if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) return BD_E_WORKSPACE;
     bd::RowArgs a{};
     a.logits = logits;
@@ -130,7 +132,8 @@ bd_status bd_confidence_commit(const bd_commit_desc *desc, const float *logits, 
 
 size_t bd_verify_workspace_bytes(int32_t n_req, int32_t D, int32_t V) {
     if (check_rows(n_req, D, V) != BD_OK) return SIZE_MAX;
-    return bd::plan_rows(n_req, D, V).ws_bytes;
+    const bd::RowPlan pl = bd::plan_rows(n_req, D, V);
+    return pl.ok ? pl.ws_bytes : SIZE_MAX;
 }
 
 bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logits, const int32_t *draft,
@@ -141,6 +144,7 @@ bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logit
     if (!logits || !draft || !accepted_len) return BD_E_NULL;
     if (!aligned16(logits)) return BD_E_PARAM;
     const bd::RowPlan pl = bd::plan_rows(n_req, D, V);
+    if (!pl.ok) return BD_E_SHAPE;
     if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) return BD_E_WORKSPACE;
     bd::RowArgs a{};
     a.logits = logits;

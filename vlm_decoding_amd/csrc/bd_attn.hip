@@ -54,9 +54,17 @@ __device__ __forceinline__ int key_perm(int rho) {
 
 // Splits of a unit with prefix P: about tiles_per_split bulk (64-key) tiles
 // each, at least one, at most max_splits.  Shared by the tile and merge kernels.
-__device__ __forceinline__ int unit_splits(int P, int tiles_per_split, int max_splits) {
+// Bulk splits of a unit with prefix P: about tiles_per_split 64-key tiles each,
+// none if P < 64, at most max_splits - 1.  A unit has these plus one tail split
+// (index = number of bulk splits) for the last P % 64 cache positions and the
+// block.  Shared by the tile and merge kernels.
+__device__ __forceinline__ int unit_bulk_splits(int P, int tiles_per_split, int max_splits) {
     const int nbulk = P / kTileKeys;
-    return min(max_splits, max(1, (nbulk + tiles_per_split - 1) / tiles_per_split));
+    if (nbulk == 0) return 0;
+    return min(max_splits - 1, (nbulk + tiles_per_split - 1) / tiles_per_split);
+}
+__device__ __forceinline__ int unit_splits(int P, int tiles_per_split, int max_splits) {
+    return unit_bulk_splits(P, tiles_per_split, max_splits) + 1;
 }
 
 // 16-byte-unit XOR swizzles of the LDS tiles.
@@ -110,23 +118,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     const int P = min(max(p.prefix[it], 0), p.cap);
     const int P64 = P & ~(TK - 1);
     const int nbulk = P64 / TK;
-    // Splits per unit grow with the prefix (about tiles_per_split bulk tiles
-    // each) up to max_splits, so a prefix above the host's max_prefix widens the
-    // splits instead of overrunning the workspace.  Tiles are dealt out evenly,
-    // counting the tail tiles, which always belong to the last split.
-    const int ntail_all = (P - P64 + p.D + TK - 1) / TK;
-    const int nsplit = unit_splits(P, p.tiles_per_split, p.max_splits);
+    // Bulk splits stream an even share of the 64-key cache tiles; the tail
+    // split (the last one) gathers the remaining P % 64 cache positions and the
+    // D block slots.  A prefix above the host's max_prefix widens the bulk
+    // splits instead of overrunning the workspace.
+    const int nbs = unit_bulk_splits(P, p.tiles_per_split, p.max_splits);
+    const int nsplit = nbs + 1;
     if (split >= nsplit) return;
-    // Tail tiles count double: they are gathered, not streamed.
-    const int total_tiles = nbulk + 2 * ntail_all;
-    const int t0 = min(nbulk, (int)(((long)split * total_tiles) / nsplit));
-    const bool last = split == nsplit - 1;
-    const int t1 = last ? nbulk : min(nbulk, (int)(((long)(split + 1) * total_tiles) / nsplit));
-    const int nb_split = t1 - t0;
-    const int tail_len = last ? (P - P64) + p.D : 0;
-    // The last split takes its tail tiles first: their gathers overlap the
-    // copy of its first bulk tile instead of extending the end of the split.
-    const int ntail = last ? ntail_all : 0;
+    const bool is_tail = split == nbs;
+    const int t0 = is_tail ? 0 : (int)(((long)split * nbulk) / nbs);
+    const int nb_split = is_tail ? 0 : (int)(((long)(split + 1) * nbulk) / nbs) - t0;
+    const int tail_len = is_tail ? (P - P64) + p.D : 0;
+    const int ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
 
     const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD;   // [cap][HD]
     const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap;   // [HD][cap]
@@ -305,7 +308,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = fmaxf(mx, bd_swap_halves(mx));
+        mx = bd_max_halves(mx);
         const float mx2 = mx * p.c;
         const bool need = mx2 > m_run + 8.0f;
         if (bd_wave_any(need)) {
@@ -347,15 +350,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         }
     };
 
-    // Tail tiles first (last split only): the first bulk tile is copied into
-    // stage 0 while the tail is gathered into stage 1 and computed.
-    if (nb_split > 0) issue_bulk(t0, 0);
+    // Tail split: gather and compute its (one or two) tiles.
     for (int tt = 0; tt < ntail; ++tt) {
         if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
-        load_tail(1, tt);
+        load_tail(0, tt);
         bd_barrier_lds();
-        if (wave_active) compute(1, tt);
+        if (wave_active) compute(0, tt);
     }
+    if (nb_split > 0) issue_bulk(t0, 0);
     // Bulk tiles, two LDS stages: tile tl+1 is in flight while tile tl is computed.
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         if (tl + 1 < nb_split) step(std::integral_constant<int, 1>{}, tl + 1);
     }
 
-    const float l_tot = l_run + bd_swap_halves(l_run);
+    const float l_tot = bd_sum_halves(l_run);
     // Output element mapping of the O^T accumulators: block mb, register i of
     // half h holds d = mb*32 + 8*(i/4) + 4*h + (i%4) of this lane's row.
     if (nsplit == 1) {
@@ -592,8 +594,9 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     const int slots = pl.nw == 4 ? 2 * kCUs : kCUs;
     const int ntiles_max = max_prefix / kTileKeys;
     const int want = std::max(1, slots / pl.units);
-    pl.max_splits = std::max(1, std::min(std::min(want, ntiles_max), kMaxSplits));
-    pl.tiles_per_split = std::max(1, (ntiles_max + pl.max_splits - 1) / pl.max_splits);
+    // Splits per unit: up to max_splits - 1 bulk splits plus the tail split.
+    pl.max_splits = ntiles_max == 0 ? 1 : std::max(2, std::min(std::min(want, ntiles_max + 1), kMaxSplits));
+    pl.tiles_per_split = pl.max_splits == 1 ? 1 : std::max(1, (ntiles_max + pl.max_splits - 2) / (pl.max_splits - 1));
     const long total = (long)pl.units * pl.max_splits;
     pl.grid = (int)((total + 7) / 8 * 8);
     if (pl.max_splits > 1) {

@@ -24,8 +24,17 @@ __device__ __forceinline__ uint16_t bd_f32_to_bf16(float f) {
 
 __device__ __forceinline__ float bd_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of lane (lane ^ 32): exchanges the two 32-lane halves of a wave.
-__device__ __forceinline__ float bd_swap_halves(float v) { return __shfl_xor(v, 32, 64); }
+// Combine each lane's value with that of lane (lane ^ 32) using
+// v_permlane32_swap (a VALU lane exchange, no LDS round trip).  Both lanes of
+// a pair see the same two operands, so they get bitwise-identical results.
+__device__ __forceinline__ float bd_max_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float bd_sum_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -77,6 +86,15 @@ __device__ __forceinline__ float bd_coherent_load(const float *p) {
 }
 __device__ __forceinline__ int bd_coherent_load(const int *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void bd_coherent_store_u2(uint2 *p, uint2 v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 bd_coherent_load_u2(const uint2 *p) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
 }
 // Wait until every memory operation this thread issued has completed.
 __device__ __forceinline__ void bd_wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }

@@ -42,6 +42,7 @@ hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s);
 struct RowPlan {
     int rows, chunks, chunk_elems;
     size_t part_off, cnt_off, ws_bytes, merge_lds;
+    bool ok;  // the finishing workgroup's LDS staging fits
 };
 RowPlan plan_rows(int n_req, int D, int V);
 

@@ -23,6 +23,7 @@ namespace bd {
 namespace {
 
 constexpr int NT = 256;
+constexpr int kRowLoads = 16;  // float4 loads per thread per chunk (chunk <= 16 x 1024 floats)
 
 struct Part {
     float m;  // running maximum
@@ -99,20 +100,20 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     const int slot = row - r * p.D;
     const size_t ob = (size_t)r * p.D;
 
-    // The masked flags are requested first and the chunk's first logits loads
-    // right behind them, so deciding whether this row takes part costs no
-    // extra round trip (rows that do not take part drop their loads).
+    // The masked flags are requested first and the chunk's logits right behind
+    // them (all of a thread's loads in flight together), so deciding whether this
+    // row takes part costs no extra round trip; rows that do not take part drop
+    // their loads.
     bool mk = false;
     if (!VERIFY && w == 0) mk = lane < p.D && p.masked[ob + lane] != 0;
     const float *x = p.logits + (size_t)row * p.V;
     const int beg = chunk * p.chunk_elems;
     const int end = min(p.V, beg + p.chunk_elems);
     const bool vec = (p.V & 3) == 0;
-    constexpr int U = 4;
-    float4 v[U];
+    float4 v[kRowLoads];
     if (vec) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < kRowLoads; ++u) {
             const int e = beg + tid * 4 + u * NT * 4;
             if (e < end) v[u] = *reinterpret_cast<const float4 *>(x + e);
         }
@@ -138,26 +139,17 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         }
     }
 
-    // Stream this chunk of the row (the first batch is already in flight).
+    // Reduce this chunk of the row.
     Part acc{-INFINITY, 0.f, 0x7fffffff};
     if (vec) {
-        for (int e0 = beg + tid * 4;; e0 += U * NT * 4) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = e0 + u * NT * 4;
-                if (e < end) {
-                    push<!VERIFY>(acc, v[u].x, e);
-                    push<!VERIFY>(acc, v[u].y, e + 1);
-                    push<!VERIFY>(acc, v[u].z, e + 2);
-                    push<!VERIFY>(acc, v[u].w, e + 3);
-                }
-            }
-            const int n0 = e0 + U * NT * 4;
-            if (n0 >= end) break;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = n0 + u * NT * 4;
-                if (e < end) v[u] = *reinterpret_cast<const float4 *>(x + e);
+        for (int u = 0; u < kRowLoads; ++u) {
+            const int e = beg + tid * 4 + u * NT * 4;
+            if (e < end) {
+                push<!VERIFY>(acc, v[u].x, e);
+                push<!VERIFY>(acc, v[u].y, e + 1);
+                push<!VERIFY>(acc, v[u].z, e + 2);
+                push<!VERIFY>(acc, v[u].w, e + 3);
             }
         }
     } else {
@@ -183,7 +175,9 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     if (!s_done) return;
 
     // Last workgroup of request r: fetch every partial of the request in one
-    // parallel round trip, then merge each row in chunk order (fixed tree).
+    // parallel round trip, then one lane per row merges that row's chunks in
+    // chunk order.  (Short loops on purpose: this path runs once per request,
+    // on one workgroup, with its instructions not yet cached.)
     const int nparts = p.D * p.chunks;
     float *lm = s_dyn, *ls = s_dyn + nparts;
     int *li = reinterpret_cast<int *>(s_dyn + 2 * nparts);
@@ -197,22 +191,17 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         }
     }
     __syncthreads();
-    for (int i = w; i < p.D; i += NT / 64) {
-        if (!(VERIFY || ((s_mask >> i) & 1ull))) continue;
-        Part t{-INFINITY, 0.f, 0x7fffffff};
-        for (int c = lane; c < p.chunks; c += 64) {
-            const int o = i * p.chunks + c;
-            Part q{lm[o], ls[o], li[o]};
-            t = (c == lane) ? q : combine(t, q);
-        }
-        t = wave_reduce(t);
-        if (lane == 0) {
-            s_conf[i] = 1.0f / t.s;
-            s_arg[i] = t.i;
-        }
-    }
-    __syncthreads();
     if (w != 0) return;
+    const bool part_i = lane < p.D && (VERIFY || ((s_mask >> lane) & 1ull));
+    if (part_i) {
+        Part t{lm[lane * p.chunks], ls[lane * p.chunks], li[lane * p.chunks]};
+        for (int c = 1; c < p.chunks; ++c) {
+            const int o = lane * p.chunks + c;
+            t = combine(t, Part{lm[o], ls[o], li[o]});
+        }
+        s_conf[lane] = 1.0f / t.s;
+        s_arg[lane] = t.i;
+    }
     if (VERIFY) {
         const int a = lane < p.D ? s_arg[lane] : 0;
         const bool bad = lane < p.D && a != p.draft[ob + lane];
@@ -224,19 +213,19 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         }
         return;
     }
-    // Commit (one wave, one lane per slot).
-    const bool m_l = lane < p.D && ((s_mask >> lane) & 1ull);
-    const float cf = m_l ? s_conf[lane] : __int_as_float(0x7fc00000);
-    const int am = m_l ? s_arg[lane] : -1;
+    // Commit (one lane per slot; confidences read back from LDS).
+    const float cf = part_i ? s_conf[lane] : __int_as_float(0x7fc00000);
+    const int am = part_i ? s_arg[lane] : -1;
     const int nm = s_nm;
     const int k = min((p.D + p.S - 1) / p.S, nm);
     int rank = 0;
-    for (int j = 0; j < p.D; ++j) {
-        const float cj = __shfl(cf, j, 64);
-        const bool mj = (s_mask >> j) & 1ull;
-        if (mj && j != lane && (cj > cf || (cj == cf && j < lane))) ++rank;
-    }
-    const bool take = m_l && (rank < k || cf > p.tau);
+    if (part_i)
+        for (int j = 0; j < p.D; ++j) {
+            if (j == lane || !((s_mask >> j) & 1ull)) continue;
+            const float cj = s_conf[j];
+            if (cj > cf || (cj == cf && j < lane)) ++rank;
+        }
+    const bool take = part_i && (rank < k || cf > p.tau);
     const unsigned long long tb = __builtin_amdgcn_ballot_w64(take);
     if (lane < p.D) {
         if (take) {
@@ -295,11 +284,13 @@ RowPlan plan_rows(int n_req, int D, int V) {
     chunks = std::min(strides, std::max(chunks, want));
     int per = (strides + chunks - 1) / chunks;
     // The finishing workgroup stages D * chunks partials (12 bytes each) in LDS:
-    // keep that within 48 KB by growing the chunks if needed.
-    while ((size_t)D * ((strides + per - 1) / per) * 12 > 48 * 1024) ++per;
+    // keep that within 48 KB by growing the chunks if needed (a chunk holds at
+    // most kRowLoads strides; the grid grows instead beyond that).
+    while (per < 16 && (size_t)D * ((strides + per - 1) / per) * 12 > 48 * 1024) ++per;
     pl.chunk_elems = per * 1024;
     pl.chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
     pl.merge_lds = (size_t)D * pl.chunks * 12;
+    pl.ok = pl.merge_lds <= 48 * 1024;  // vocabularies up to ~1M tokens at D = 64
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
