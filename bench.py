@@ -91,6 +91,50 @@ def cpu_baseline(step, budget_s):
                        "%.1f s wall" % (done, el))
 
 
+def _pmc_values(db_path, counter):
+    """(kernel name, value) per dispatch of ``counter`` from a rocprofv3 database."""
+    import sqlite3
+    db = sqlite3.connect(db_path)
+    rows = db.execute("select kernel_name, value, dispatch_id from counters_collection "
+                      "where counter_name = ? order by dispatch_id", (counter,)).fetchall()
+    db.close()
+    return [(k, float(v)) for k, v, _ in rows]
+
+
+def write_traffic(pmc_dir, copy_bytes=256 << 20):
+    """HBM bytes per bd_attn_step launch from four rocprofv3 --pmc runs in ``pmc_dir``:
+    copyfetch/copywrite (FETCH_SIZE / WRITE_SIZE over --copy-calibration) give the
+    counter-to-bytes scale; fetch/write (the same counters over a short bench run)
+    give the attention kernels' readings, averaged over their dispatches."""
+    def scale(db, counter):
+        vals = [v for k, v in _pmc_values(os.path.join(pmc_dir, db), counter) if "copyBuffer" in k]
+        return copy_bytes / (sum(vals) / len(vals) * 1024.0)
+    f_scale = scale("copyfetch_results.db", "FETCH_SIZE")
+    w_scale = scale("copywrite_results.db", "WRITE_SIZE")
+    per_kernel = {}
+    for db, counter, sc in (("fetch_results.db", "FETCH_SIZE", f_scale), ("write_results.db", "WRITE_SIZE", w_scale)):
+        acc = {}
+        for k, v in _pmc_values(os.path.join(pmc_dir, db), counter):
+            if "attn_" not in k:
+                continue
+            name = k.replace("void bd::(anonymous namespace)::", "").split("(")[0]
+            acc.setdefault(name, []).append(v * 1024.0 * sc)
+        for name, vals in acc.items():
+            per_kernel.setdefault(name, {})[counter.lower() + "_bytes"] = sum(vals) / len(vals)
+    total = sum(v.get("fetch_size_bytes", 0.0) + v.get("write_size_bytes", 0.0) for v in per_kernel.values())
+    out = {
+        "bytes_per_launch": round(total),
+        "per_kernel": {k: {kk: round(vv) for kk, vv in v.items()} for k, v in per_kernel.items()},
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "calibration": "FETCH_SIZE/WRITE_SIZE over plain %d-byte device copies (bench.py --copy-calibration)" % copy_bytes,
+        "kernel_source_sha256": attn_source_hash(),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def copy_calibration(n_bytes=256 << 20, reps=5):
     """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
     WRITE_SIZE for this copy kernel give the scale between counter readings and
@@ -113,7 +157,12 @@ def main():
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain 256 MiB device copies (to scale HBM byte counters)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="summarise rocprofv3 --pmc databases in DIR into the committed traffic file")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
