@@ -13,9 +13,12 @@ rotated so that no step finds its K/V in the 256 MB last-level cache: every
 step streams its bytes from HBM.
 
 Prints one JSON line (see the keys below).  ``roofline`` describes the
-attention kernel (the dominant one): algorithmic bytes per launch divided by
-its average duration from HIP events recorded on the launch stream during
-the timed steps.  ``cpu_baseline`` times the fp64 CPU oracle on the host.
+attention call (the dominant one): algorithmic bytes per launch divided by
+its average duration from HIP events recorded on the launch stream around
+the calls of every 10th timed step (--event-stride; an event record costs the
+GPU a few microseconds, so instrumenting every step would slow the steps it
+measures).  ``value`` is steps over the wall time of all timed steps.
+``cpu_baseline`` times the fp64 CPU oracle on the host.
 """
 
 import argparse
@@ -153,6 +156,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--event-stride", type=int, default=10,
+                    help="record the per-call HIP events on every N-th timed step (0: none)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -200,30 +205,65 @@ def main():
     step_bytes = attn_bytes + logit_bytes + state_bytes
     stream = torch.cuda.current_stream()
 
-    def one_step(i, ev=None):
+    # The timed loop calls the C ABI directly with argument tuples prepared
+    # here (raw device pointers, the stream handle), so that enqueueing a step
+    # costs the host far less than the step costs the GPU and the GPU never
+    # waits for the host.  Step i uses its own state row (masked at +0, tokens
+    # at +64).
+    import ctypes
+    from vlm_decoding_amd import bd
+    lib = bd.lib
+    sh = stream.cuda_stream
+    attn_args = [(ctypes.byref(ds.adesc), ds.q.data_ptr(), ds.k_blk.data_ptr(), ds.v_blk.data_ptr(),
+                  ds.k_cache.data_ptr(), ds.v_cache.data_ptr(), ds.prefix.data_ptr(), ds.out.data_ptr(),
+                  ds.attn_ws.data_ptr(), ds.attn_ws.numel(), sh) for ds in sets]
+    base = state.data_ptr()
+    commit_args = []
+    for i in range(total):
         ds = sets[i % N_SETS]
-        ds.masked = state[i, :16].view(1, 16)
-        ds.tokens = state[i, 64:128].view(torch.int32).view(1, 16)
-        if ev is not None:
-            ev[0].record(stream)
-        ds.attn()
-        if ev is not None:
-            ev[1].record(stream)
-        ds.confidence_commit()
+        commit_args.append((ctypes.byref(ds.cdesc), ds.logits.data_ptr(), base + 128 * i, base + 128 * i + 64,
+                            ds.conf.data_ptr(), ds.argmax.data_ptr(), ds.committed.data_ptr(),
+                            ds.n_committed.data_ptr(), ds.commit_ws.data_ptr(), ds.commit_ws.numel(), sh))
+    attn_call, commit_call = lib.bd_attn_step, lib.bd_confidence_commit
 
+    status = 0
     for i in range(args.warmup):
-        one_step(i)
+        status |= attn_call(*attn_args[i % N_SETS])
+        status |= commit_call(*commit_args[i])
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    if status:
+        raise RuntimeError("a library call failed during warm-up (status %d)" % status)
+    stride = args.event_stride
+    timed = [i for i in range(args.steps) if stride > 0 and i % stride == 0]
+    evs = {i: tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for i in timed}
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    t_begin.record(stream)
     for i in range(args.steps):
-        one_step(args.warmup + i, evs[i])
+        j = args.warmup + i
+        ev = evs.get(i)
+        if ev is None:
+            status |= attn_call(*attn_args[j % N_SETS])
+            status |= commit_call(*commit_args[j])
+            continue
+        ev[0].record(stream)
+        status |= attn_call(*attn_args[j % N_SETS])
+        ev[1].record(stream)
+        status |= commit_call(*commit_args[j])
+        ev[2].record(stream)
+    t_end.record(stream)
+    t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if status:
+        raise RuntimeError("a library call failed in the timed loop (status %d)" % status)
     ms_per_step = elapsed * 1e3 / args.steps
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    gpu_ms_per_step = t_begin.elapsed_time(t_end) / args.steps
+    if not evs:
+        raise SystemExit("--event-stride 0 leaves no per-call timing; use a stride >= 1")
+    attn_ms = np.array([a.elapsed_time(b) for a, b, _ in evs.values()])
+    conf_ms = np.array([b.elapsed_time(c) for _, b, c in evs.values()])
     attn_avg_s = float(attn_ms.mean()) * 1e-3
     achieved = attn_bytes / attn_avg_s / 1e9
 
@@ -265,6 +305,10 @@ def main():
         "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes_per_step": step_bytes,
+        "confidence_commit_avg_us": round(float(conf_ms.mean()) * 1e3, 2),
+        "host_enqueue_us_per_step": round(t_enq * 1e6 / args.steps, 2),
+        "gpu_event_us_per_step": round(gpu_ms_per_step * 1e3, 2),
+        "event_stride": stride,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

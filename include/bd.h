@@ -124,9 +124,6 @@ size_t bd_commit_workspace_bytes(const bd_commit_desc *desc);
  *   conf f32[n_req][D] (NaN at unmasked slots), argmax i32[n_req][D] (-1 at unmasked),
  *   committed u8[n_req][D] (1 where committed now), n_committed i32[n_req].
  * NaN logits are not supported (results unspecified).
- * Per-chunk partial results of all D rows are merged in one workgroup's LDS:
- * D * ceil(V / 16384) must not exceed 4096 (V up to about 1M tokens at
- * D = 64); larger shapes return BD_E_SHAPE (also for bd_spec_verify).
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH. */
 bd_status bd_confidence_commit(const bd_commit_desc *desc, const float *logits, uint8_t *masked,
                                int32_t *tokens, float *conf, int32_t *argmax, uint8_t *committed,

@@ -21,8 +21,8 @@
 // for softmax", 2018) only rescales when the running maximum grows by more
 // than 2^8, which keeps every exponent <= 2^8 and is exact after the final
 // normalisation.  The cached prefix is split across workgroups (split-K);
-// the last workgroup of a unit to finish merges the (m, l, o) partials in
-// split order, so results do not depend on scheduling.
+// a second kernel merges each unit's (m, l, o) partials in split order, so
+// results do not depend on scheduling.
 #include <type_traits>
 
 #include "bd_common.h"
@@ -52,19 +52,43 @@ __device__ __forceinline__ int key_perm(int rho) {
     return ((q >> 1) << 4) + (h << 3) + ((q & 1) << 2) + e;
 }
 
-// Splits of a unit with prefix P: about tiles_per_split bulk (64-key) tiles
-// each, at least one, at most max_splits.  Shared by the tile and merge kernels.
-// Bulk splits of a unit with prefix P: about tiles_per_split 64-key tiles each,
-// none if P < 64, at most max_splits - 1.  A unit has these plus one tail split
-// (index = number of bulk splits) for the last P % 64 cache positions and the
-// block.  Shared by the tile and merge kernels.
-__device__ __forceinline__ int unit_bulk_splits(int P, int tiles_per_split, int max_splits) {
+// Work split of a unit with prefix P.  The unit streams nbulk = P / 64 whole
+// cache tiles plus ntail tail tiles (the last P % 64 cache positions and the
+// D block slots, gathered by a slower path that costs about kTailCost bulk
+// tiles).  nsplit = ceil(work / tiles_per_split) splits, at most max_splits
+// and at most nbulk + 1; the last split runs the tail and takes whatever bulk
+// tiles are left once the others have ceil(work / nsplit) each, so that no
+// split carries much more than the average.  Shared by the tile and merge
+// kernels.
+constexpr int kTailCost = 3;
+struct UnitSplit {
+    int nsplit;  // splits of this unit (the last one holds the tail)
+    int t0, nb;  // bulk tile range of the queried split
+};
+__device__ __forceinline__ int unit_nsplit(int P, int D, int tiles_per_split, int max_splits) {
     const int nbulk = P / kTileKeys;
-    if (nbulk == 0) return 0;
-    return min(max_splits - 1, (nbulk + tiles_per_split - 1) / tiles_per_split);
+    const int ntail = ((P - nbulk * kTileKeys) + D + kTileKeys - 1) / kTileKeys;
+    const int work = nbulk + kTailCost * ntail;
+    return max(1, min(min(max_splits, nbulk + 1), (work + tiles_per_split - 1) / tiles_per_split));
 }
-__device__ __forceinline__ int unit_splits(int P, int tiles_per_split, int max_splits) {
-    return unit_bulk_splits(P, tiles_per_split, max_splits) + 1;
+__device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_split, int max_splits, int split) {
+    UnitSplit u;
+    const int nbulk = P / kTileKeys;
+    const int ntail = ((P - nbulk * kTileKeys) + D + kTileKeys - 1) / kTileKeys;
+    const int work = nbulk + kTailCost * ntail;
+    u.nsplit = unit_nsplit(P, D, tiles_per_split, max_splits);
+    const int nbs = u.nsplit - 1;                                      // bulk-only splits
+    const int w = (work + u.nsplit - 1) / u.nsplit;                    // target work per split
+    const int tail_bulk = nbs == 0 ? nbulk : max(0, nbulk - nbs * w);  // bulk tiles of the tail split
+    const int shared = nbulk - tail_bulk;                              // >= nbs: every bulk split gets one
+    if (split < nbs) {
+        u.t0 = (int)(((long)split * shared) / nbs);
+        u.nb = (int)(((long)(split + 1) * shared) / nbs) - u.t0;
+    } else {
+        u.t0 = shared;
+        u.nb = tail_bulk;
+    }
+    return u;
 }
 
 // 16-byte-unit XOR swizzles of the LDS tiles.
@@ -118,16 +142,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     const int P = min(max(p.prefix[it], 0), p.cap);
     const int P64 = P & ~(TK - 1);
     const int nbulk = P64 / TK;
-    // Bulk splits stream an even share of the 64-key cache tiles; the tail
-    // split (the last one) gathers the remaining P % 64 cache positions and the
-    // D block slots.  A prefix above the host's max_prefix widens the bulk
-    // splits instead of overrunning the workspace.
-    const int nbs = unit_bulk_splits(P, p.tiles_per_split, p.max_splits);
-    const int nsplit = nbs + 1;
+    // A prefix above the host's max_prefix widens the splits instead of
+    // overrunning the workspace (at most max_splits per unit).
+    const UnitSplit us = unit_split(P, p.D, p.tiles_per_split, p.max_splits, split);
+    const int nsplit = us.nsplit;
     if (split >= nsplit) return;
-    const bool is_tail = split == nbs;
-    const int t0 = is_tail ? 0 : (int)(((long)split * nbulk) / nbs);
-    const int nb_split = is_tail ? 0 : (int)(((long)(split + 1) * nbulk) / nbs) - t0;
+    const bool is_tail = split == nsplit - 1;
+    const int t0 = us.t0;
+    const int nb_split = us.nb;
     const int tail_len = is_tail ? (P - P64) + p.D : 0;
     const int ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
 
@@ -357,7 +379,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         bd_barrier_lds();
         if (wave_active) compute(0, tt);
     }
-    if (nb_split > 0) issue_bulk(t0, 0);
+    if (nb_split > 0) {
+        if (ntail > 0) bd_barrier_lds();  // every wave is done with the tail tile in stage 0
+        issue_bulk(t0, 0);
+    }
     // Bulk tiles, two LDS stages: tile tl+1 is in flight while tile tl is computed.
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
@@ -391,7 +416,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
                     uint2 v;
                     v.x = bd_f32_to_bf16(o[mb][4 * i4 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 1] * inv) << 16);
                     v.y = bd_f32_to_bf16(o[mb][4 * i4 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 3] * inv) << 16);
-                    *reinterpret_cast<uint2 *>(op + dd) = v;
+                    bd_store_nt(op + dd, v);
                 }
         }
         return;
@@ -399,74 +424,75 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
 
     // Split-K partials: the split's normalised output o / l as bf16 plus its
     // (m, l) in fp32, stored lane-major so that every store of a wave covers
-    // one contiguous span: quad q (4 outputs) of thread t of split s of unit u
-    // lives at [(u * max_splits + s) * QUADS + q][t].  The merge kernel reads
-    // them back with the same thread -> (row, d) mapping.
+    // one contiguous span.  16-byte unit qq (output quads 2qq and 2qq+1, i.e.
+    // block mb = qq/2, quads i4 = 2(qq%2) and 2(qq%2)+1) of thread t of split
+    // s of unit u lives at [(u * max_splits + s) * (QUADS/2) + qq][t].
     constexpr int QUADS = MB * 4;
     if (wave_active) {
         const size_t base = ((size_t)unit * p.max_splits + split);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        uint2 *wo = reinterpret_cast<uint2 *>(p.ws_o) + base * QUADS * NT + tid;
+        uint4 *wo = reinterpret_cast<uint4 *>(p.ws_o) + base * (QUADS / 2) * NT + tid;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                uint2 v;
-                v.x = bd_f32_to_bf16(o[mb][4 * i4 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 1] * inv) << 16);
-                v.y = bd_f32_to_bf16(o[mb][4 * i4 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][4 * i4 + 3] * inv) << 16);
-                wo[(size_t)(mb * 4 + i4) * NT] = v;
-            }
-        p.ws_ml[base * NT + tid] = make_float2(m_run, l_tot);
+        for (int qq = 0; qq < QUADS / 2; ++qq) {
+            const int mb = qq >> 1, i0 = 8 * (qq & 1);
+            uint4 v;
+            v.x = bd_f32_to_bf16(o[mb][i0 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][i0 + 1] * inv) << 16);
+            v.y = bd_f32_to_bf16(o[mb][i0 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][i0 + 3] * inv) << 16);
+            v.z = bd_f32_to_bf16(o[mb][i0 + 4] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][i0 + 5] * inv) << 16);
+            v.w = bd_f32_to_bf16(o[mb][i0 + 6] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][i0 + 7] * inv) << 16);
+            bd_store_nt(&wo[(size_t)qq * NT], v);
+        }
+        bd_store_nt(&p.ws_ml[base * NT + tid], make_float2(m_run, l_tot));
     }
 }
 
 // Merge of the split-K partials (second launch; the kernel boundary orders
-// the partial stores before these loads).  Thread t of block (unit, q0)
-// finishes output quads q0 and q0 + QUADS/2 of the row that thread t of the
-// tile kernel owned:
+// the partial stores before these loads).  One 256-thread block per (unit,
+// 32-row group): the group's rows are the rows one wave of the tile kernel
+// owned.  Thread (j, lane) merges 16-byte partial units qq = j * QPT .. of
+// lane `lane` of that wave:
 //   M = max_s m_s,  c_s = 2^(m_s - M) l_s,  o = sum_s c_s (o_s / l_s) / sum_s c_s,
-// summed in split order.  All loads of a thread are issued before use.
+// summed in split order.  The merged 32 rows are staged in LDS and written
+// out as whole rows (HD * 2 contiguous bytes each).
 template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_merge_kernel(MfmaParams p) {
-    constexpr int NT = NW * 64;
+__global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
+    constexpr int NT_TILE = NW * 64;    // threads of the tile kernel's block
     constexpr int MB = HD / 32;
-    constexpr int QUADS = MB * 4;
-    constexpr int QPT = 2;                 // output quads per thread
-    constexpr int QB = QUADS / QPT;        // blocks per unit
-    constexpr int RPG = NW * 32;
+    constexpr int QQ = MB * 2;          // 16-byte partial units per lane
+    constexpr int QPT = QQ / 4;         // units per thread here
     constexpr int MAXS = kMaxSplits;
-    const int unit = blockIdx.x / QB;
-    const int q0 = blockIdx.x - unit * QB;
+    constexpr int RS = HD + 8;          // LDS row stride (elements), staggers banks
+    __shared__ __attribute__((aligned(16))) uint16_t rows_lds[32 * RS];
+    const int unit = blockIdx.x / NW;
+    const int wv = blockIdx.x - unit * NW;
     const int rb = unit % p.row_blocks;
     const int pair = unit / p.row_blocks;
     const int g = pair % p.Hkv;
     const int it = pair / p.Hkv;
     const int P = min(max(p.prefix[it], 0), p.cap);
-    const int nsplit = unit_splits(P, p.tiles_per_split, p.max_splits);
-    if (nsplit == 1) return;  // written directly by the tile kernel
+    const int nsplit = unit_nsplit(P, p.D, p.tiles_per_split, p.max_splits);
+    const int row0 = rb * (NW * 32) + wv * 32;
+    if (nsplit == 1 || row0 >= p.R) return;  // single split: written by the tile kernel
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, half = lane >> 5, col = lane & 31;
-    const int r = rb * RPG + w * 32 + col;
-    if (r >= p.R) return;
-    const int slot = r / p.G;
-    const int head = g * p.G + (r - slot * p.G);
+    const int lane = tid & 63, jq = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int src_t = wv * 64 + lane;      // thread of the tile kernel's block
     const size_t base = (size_t)unit * p.max_splits;
-    const uint2 *wo = reinterpret_cast<const uint2 *>(p.ws_o);
+    const uint4 *wo = reinterpret_cast<const uint4 *>(p.ws_o);
     float2 ml[MAXS];
-    uint2 v[QPT][MAXS];
+    uint4 v[QPT][MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (s < nsplit) {
-            ml[s] = p.ws_ml[(base + s) * NT + tid];
+            ml[s] = p.ws_ml[(base + s) * NT_TILE + src_t];
 #pragma unroll
-            for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QUADS + q0 + j * QB) * NT + tid];
+            for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t];
         }
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (s < nsplit) M = fmaxf(M, ml[s].x);
     float L = 0.f;
-    float acc[QPT][4] = {};
+    float acc[QPT][8] = {};
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (s < nsplit) {
@@ -474,23 +500,40 @@ __global__ __launch_bounds__(NW * 64) void attn_merge_kernel(MfmaParams p) {
             L += c;
 #pragma unroll
             for (int j = 0; j < QPT; ++j) {
-                acc[j][0] += c * bd_bf16_to_f32((uint16_t)(v[j][s].x & 0xffff));
-                acc[j][1] += c * bd_bf16_to_f32((uint16_t)(v[j][s].x >> 16));
-                acc[j][2] += c * bd_bf16_to_f32((uint16_t)(v[j][s].y & 0xffff));
-                acc[j][3] += c * bd_bf16_to_f32((uint16_t)(v[j][s].y >> 16));
+                const uint32_t w4[4] = {v[j][s].x, v[j][s].y, v[j][s].z, v[j][s].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[j][e] += c * bd_bf16_to_f32((uint16_t)(w4[e >> 1] >> (16 * (e & 1))));
             }
         }
-    const float inv = 1.0f / L;
-    uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    // Unit qq holds d = mb*32 + 16*(qq%2) + 4*half + {0..3} and the same + 8.
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
-        const int q = q0 + j * QB;
-        const int mb = q >> 2, i4 = q & 3;
-        const int dd = mb * 32 + 8 * i4 + 4 * half;
-        uint2 o;
-        o.x = bd_f32_to_bf16(acc[j][0] * inv) | ((uint32_t)bd_f32_to_bf16(acc[j][1] * inv) << 16);
-        o.y = bd_f32_to_bf16(acc[j][2] * inv) | ((uint32_t)bd_f32_to_bf16(acc[j][3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(op + dd) = o;
+        const int qq = jq * QPT + j;
+        const int d0 = (qq >> 1) * 32 + 16 * (qq & 1) + 4 * half;
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+            uint2 o;
+            o.x = bd_f32_to_bf16(acc[j][4 * h8 + 0] * inv) | ((uint32_t)bd_f32_to_bf16(acc[j][4 * h8 + 1] * inv) << 16);
+            o.y = bd_f32_to_bf16(acc[j][4 * h8 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(acc[j][4 * h8 + 3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(&rows_lds[col * RS + d0 + 8 * h8]) = o;
+        }
+    }
+    __syncthreads();
+    // Whole rows out: HD/8 threads per row, 16 bytes each.
+    constexpr int TPR = HD / 8;
+    constexpr int RPP = 256 / TPR;  // rows per pass
+#pragma unroll
+    for (int r0 = 0; r0 < 32; r0 += RPP) {
+        const int rr = r0 + tid / TPR, u = tid % TPR;
+        const int r = row0 + rr;
+        if (r < p.R) {
+            const int slot = r / p.G;
+            const int head = g * p.G + (r - slot * p.G);
+            uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD + u * 8;
+            bd_store_nt(op, *reinterpret_cast<const uint4 *>(&rows_lds[rr * RS + u * 8]));
+        }
     }
 }
 
@@ -594,9 +637,10 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     const int slots = pl.nw == 4 ? 2 * kCUs : kCUs;
     const int ntiles_max = max_prefix / kTileKeys;
     const int want = std::max(1, slots / pl.units);
-    // Splits per unit: up to max_splits - 1 bulk splits plus the tail split.
+    // Splits per unit (the device side derives each unit's count from its own
+    // prefix): sized so that a unit at max_prefix gets about `want` splits.
     pl.max_splits = ntiles_max == 0 ? 1 : std::max(2, std::min(std::min(want, ntiles_max + 1), kMaxSplits));
-    pl.tiles_per_split = pl.max_splits == 1 ? 1 : std::max(1, (ntiles_max + pl.max_splits - 2) / (pl.max_splits - 1));
+    pl.tiles_per_split = std::max(1, (ntiles_max + 3 + pl.max_splits - 1) / pl.max_splits);
     const long total = (long)pl.units * pl.max_splits;
     pl.grid = (int)((total + 7) / 8 * 8);
     if (pl.max_splits > 1) {
@@ -653,7 +697,7 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
     if (e != hipSuccess || pl.max_splits == 1) return e;
-    return hipLaunchKernel(merge, dim3(pl.units * (a.d / 16)), block, args, 0, s);
+    return hipLaunchKernel(merge, dim3(pl.units * pl.nw), dim3(256), args, 0, s);
 }
 
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -96,6 +96,20 @@ __device__ __forceinline__ uint2 bd_coherent_load_u2(const uint2 *p) {
                                          __HIP_MEMORY_SCOPE_AGENT);
     return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
 }
+// Non-temporal stores for data the next kernel consumes: the lines are not
+// kept dirty in L2, so the write-back that ends a kernel has little left to
+// do and the next kernel on the stream starts sooner.
+typedef float floatx2_nt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void bd_store_nt(void *p, uint4 v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void bd_store_nt(void *p, float2 v) {
+    __builtin_nontemporal_store(floatx2_nt{v.x, v.y}, reinterpret_cast<floatx2_nt *>(p));
+}
+__device__ __forceinline__ void bd_store_nt(void *p, uint2 v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2 *>(p));
+}
 // Wait until every memory operation this thread issued has completed.
 __device__ __forceinline__ void bd_wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 // Relaxed agent-scope ticket: returns the previous count.

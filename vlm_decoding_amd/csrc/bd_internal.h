@@ -41,8 +41,8 @@ hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s);
 // ---- confidence / verify ----------------------------------------------------
 struct RowPlan {
     int rows, chunks, chunk_elems;
-    size_t part_off, cnt_off, ws_bytes, merge_lds;
-    bool ok;  // the finishing workgroup's LDS staging fits
+    size_t part_off, cnt_off, ws_bytes;
+    bool ok;  // the grid fits one launch
 };
 RowPlan plan_rows(int n_req, int D, int V);
 

@@ -53,17 +53,42 @@ __device__ __forceinline__ void push(Part &p, float x, int idx) {
     }
 }
 
+// Lane exchanges without an LDS round trip.  combine() is commutative, so both
+// lanes of every exchanged pair compute the same value and, after a full tree,
+// every lane of the group holds the group's result.  The tree is fixed, so
+// the result does not depend on timing.
+template <int CTRL>  // gfx9 DPP control inside 16-lane rows
+__device__ __forceinline__ Part dpp_part(Part p) {
+    Part o;
+    o.m = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p.m), CTRL, 0xf, 0xf, false));
+    o.s = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p.s), CTRL, 0xf, 0xf, false));
+    o.i = __builtin_amdgcn_update_dpp(0, p.i, CTRL, 0xf, 0xf, false);
+    return combine(p, o);
+}
+// Reduce over the 16 lanes of each DPP row: lane ^ 1, lane ^ 2 (quad
+// permutes), then the 8-lane and 16-lane mirrors.
+__device__ __forceinline__ Part reduce16(Part p) {
+    p = dpp_part<0xB1>(p);   // quad_perm [1,0,3,2]
+    p = dpp_part<0x4E>(p);   // quad_perm [2,3,0,1]
+    p = dpp_part<0x141>(p);  // row_half_mirror
+    return dpp_part<0x140>(p);  // row_mirror
+}
+// Exchange with the lane 16 (row pair) or 32 (half) lanes away: the swap hands
+// both lanes the same ordered pair (lower group's value, upper group's value).
+template <bool HALVES>
+__device__ __forceinline__ Part swap_part(Part p) {
+    const unsigned m = __float_as_uint(p.m), s = __float_as_uint(p.s), i = (unsigned)p.i;
+    const auto rm = HALVES ? __builtin_amdgcn_permlane32_swap(m, m, false, false)
+                           : __builtin_amdgcn_permlane16_swap(m, m, false, false);
+    const auto rs = HALVES ? __builtin_amdgcn_permlane32_swap(s, s, false, false)
+                           : __builtin_amdgcn_permlane16_swap(s, s, false, false);
+    const auto ri = HALVES ? __builtin_amdgcn_permlane32_swap(i, i, false, false)
+                           : __builtin_amdgcn_permlane16_swap(i, i, false, false);
+    return combine(Part{__uint_as_float(rm[0]), __uint_as_float(rs[0]), (int)ri[0]},
+                   Part{__uint_as_float(rm[1]), __uint_as_float(rs[1]), (int)ri[1]});
+}
 __device__ __forceinline__ Part wave_reduce(Part p) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        Part o;
-        o.m = __shfl_xor(p.m, off, 64);
-        o.s = __shfl_xor(p.s, off, 64);
-        o.i = __shfl_xor(p.i, off, 64);
-        // Fixed operand order (lower lane first) keeps the tree deterministic.
-        p = ((threadIdx.x & off) == 0) ? combine(p, o) : combine(o, p);
-    }
-    return p;
+    return swap_part<true>(swap_part<false>(reduce16(p)));
 }
 
 struct RowParams {
@@ -85,9 +110,8 @@ struct RowParams {
 
 template <bool VERIFY>
 __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
-    extern __shared__ float s_dyn[];  // merge staging: D * chunks partials (m, s, i)
     __shared__ Part s_part[NT / 64];
-    __shared__ float s_conf[64];
+    __shared__ __attribute__((aligned(16))) float s_conf[64];
     __shared__ int s_arg[64];
     __shared__ int s_done, s_nm;
     __shared__ unsigned long long s_mask;
@@ -174,34 +198,28 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     __syncthreads();
     if (!s_done) return;
 
-    // Last workgroup of request r: fetch every partial of the request in one
-    // parallel round trip, then one lane per row merges that row's chunks in
-    // chunk order.  (Short loops on purpose: this path runs once per request,
-    // on one workgroup, with its instructions not yet cached.)
-    const int nparts = p.D * p.chunks;
-    float *lm = s_dyn, *ls = s_dyn + nparts;
-    int *li = reinterpret_cast<int *>(s_dyn + 2 * nparts);
-    for (int t = tid; t < nparts; t += NT) {
-        const int i = t / p.chunks;
-        if (VERIFY || ((s_mask >> i) & 1ull)) {
-            const size_t o = ob * p.chunks + t;
-            lm[t] = bd_coherent_load(p.part_m + o);
-            ls[t] = bd_coherent_load(p.part_s + o);
-            li[t] = bd_coherent_load(p.part_i + o);
+    // Last workgroup of request r.  Sixteen lanes per row merge that row's chunk
+    // partials (lane c takes chunks c, c + 16, ... in order, then a fixed
+    // 16-lane tree), four rows per wave, sixteen rows per pass.
+    for (int r0 = 0; r0 < p.D; r0 += 16) {
+        const int i = r0 + w * 4 + (lane >> 4);
+        const bool act = i < p.D && (VERIFY || ((s_mask >> i) & 1ull));
+        Part t{-INFINITY, 0.f, 0x7fffffff};
+        if (act) {
+            const size_t o = (ob + i) * p.chunks;
+            for (int c = lane & 15; c < p.chunks; c += 16)
+                t = combine(t, Part{bd_coherent_load(p.part_m + o + c), bd_coherent_load(p.part_s + o + c),
+                                    bd_coherent_load(p.part_i + o + c)});
+        }
+        t = reduce16(t);
+        if (act && (lane & 15) == 0) {
+            s_conf[i] = 1.0f / t.s;
+            s_arg[i] = t.i;
         }
     }
     __syncthreads();
     if (w != 0) return;
     const bool part_i = lane < p.D && (VERIFY || ((s_mask >> lane) & 1ull));
-    if (part_i) {
-        Part t{lm[lane * p.chunks], ls[lane * p.chunks], li[lane * p.chunks]};
-        for (int c = 1; c < p.chunks; ++c) {
-            const int o = lane * p.chunks + c;
-            t = combine(t, Part{lm[o], ls[o], li[o]});
-        }
-        s_conf[lane] = 1.0f / t.s;
-        s_arg[lane] = t.i;
-    }
     if (VERIFY) {
         const int a = lane < p.D ? s_arg[lane] : 0;
         const bool bad = lane < p.D && a != p.draft[ob + lane];
@@ -213,18 +231,32 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         }
         return;
     }
-    // Commit (one lane per slot; confidences read back from LDS).
+    // Commit, one lane per slot: rank = number of masked slots ahead in
+    // (confidence desc, index asc); the confidences are read as 16-byte LDS
+    // broadcasts, sixteen slots per round.
     const float cf = part_i ? s_conf[lane] : __int_as_float(0x7fc00000);
     const int am = part_i ? s_arg[lane] : -1;
-    const int nm = s_nm;
-    const int k = min((p.D + p.S - 1) / p.S, nm);
+    const unsigned long long mask = s_mask;
+    const int k = min((p.D + p.S - 1) / p.S, s_nm);
     int rank = 0;
-    if (part_i)
-        for (int j = 0; j < p.D; ++j) {
-            if (j == lane || !((s_mask >> j) & 1ull)) continue;
-            const float cj = s_conf[j];
-            if (cj > cf || (cj == cf && j < lane)) ++rank;
+    for (int j0 = 0; j0 < p.D; j0 += 16) {
+        float cj[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 c4 = *reinterpret_cast<const float4 *>(&s_conf[j0 + 4 * q]);
+            cj[4 * q] = c4.x;
+            cj[4 * q + 1] = c4.y;
+            cj[4 * q + 2] = c4.z;
+            cj[4 * q + 3] = c4.w;
         }
+        const unsigned mj = (unsigned)(mask >> j0) & 0xffffu;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = j0 + e;
+            const bool ahead = ((mj >> e) & 1u) && (cj[e] > cf || (cj[e] == cf && j < lane));
+            rank += ahead ? 1 : 0;
+        }
+    }
     const bool take = part_i && (rank < k || cf > p.tau);
     const unsigned long long tb = __builtin_amdgcn_ballot_w64(take);
     if (lane < p.D) {
@@ -282,15 +314,10 @@ RowPlan plan_rows(int n_req, int D, int V) {
     int chunks = std::max(1, (strides + 15) / 16);
     const int want = std::max(1, (256 + pl.rows - 1) / pl.rows);
     chunks = std::min(strides, std::max(chunks, want));
-    int per = (strides + chunks - 1) / chunks;
-    // The finishing workgroup stages D * chunks partials (12 bytes each) in LDS:
-    // keep that within 48 KB by growing the chunks if needed (a chunk holds at
-    // most kRowLoads strides; the grid grows instead beyond that).
-    while (per < 16 && (size_t)D * ((strides + per - 1) / per) * 12 > 48 * 1024) ++per;
+    const int per = (strides + chunks - 1) / chunks;
     pl.chunk_elems = per * 1024;
     pl.chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
-    pl.merge_lds = (size_t)D * pl.chunks * 12;
-    pl.ok = pl.merge_lds <= 48 * 1024;  // vocabularies up to ~1M tokens at D = 64
+    pl.ok = (size_t)pl.rows * pl.chunks * NT < (1ull << 32);  // HIP grid limit
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
@@ -305,13 +332,13 @@ RowPlan plan_rows(int n_req, int D, int V) {
 
 hipError_t launch_confidence_commit(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
     RowParams p = make_params(pl, a);
-    hipLaunchKernelGGL((row_kernel<false>), dim3(pl.rows * pl.chunks), dim3(NT), pl.merge_lds, s, p);
+    hipLaunchKernelGGL((row_kernel<false>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_spec_verify(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
     RowParams p = make_params(pl, a);
-    hipLaunchKernelGGL((row_kernel<true>), dim3(pl.rows * pl.chunks), dim3(NT), pl.merge_lds, s, p);
+    hipLaunchKernelGGL((row_kernel<true>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
