@@ -76,8 +76,10 @@ def test_attn_null_and_workspace_errors(bd):
 
 
 def test_single_split_needs_no_workspace(bd):
-    desc = _attn(bd, n_items=1, max_prefix=63, cap=128)
-    assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == 0
+    # A prefix shorter than one 32-key tile never splits.
+    for mp in (0, 16, 31):
+        desc = _attn(bd, n_items=1, max_prefix=mp, cap=128)
+        assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == 0
     desc32 = _attn(bd, dtype=0)
     assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc32)) == 0
 

@@ -88,6 +88,8 @@ ATTN_CASES = [
     ("P_lt_tile", dict(prefix=("fixed", 37))),
     ("P_exact_tiles", dict(prefix=("fixed", 256))),
     ("P_ragged", dict(prefix=("list", [1, 63, 64, 65, 200, 511, 640, 1000]), n_items=8)),
+    ("P_ragged32", dict(prefix=("list", [31, 32, 33, 95, 96, 97, 1023, 1024]), n_items=8)),
+    ("D64_three_tail_tiles", dict(D=64, prefix=("list", [31, 94]), n_items=2)),
     ("D1_decode", dict(D=1, prefix=("fixed", 300))),
     ("D3_rows_pad", dict(D=3, prefix=("fixed", 129))),
     ("D64_two_row_blocks", dict(D=64, prefix=("fixed", 130))),

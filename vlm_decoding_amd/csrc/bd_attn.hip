@@ -52,8 +52,8 @@ __device__ __forceinline__ int key_perm(int rho) {
     return ((q >> 1) << 4) + (h << 3) + ((q & 1) << 2) + e;
 }
 
-// Work split of a unit with prefix P.  The unit streams nbulk = P / 64 whole
-// cache tiles plus ntail tail tiles (the last P % 64 cache positions and the
+// Work split of a unit with prefix P.  The unit streams nbulk = P / TK whole
+// cache tiles plus ntail tail tiles (the last P % TK cache positions and the
 // D block slots, gathered by a slower path that costs about kTailCost bulk
 // tiles).  nsplit = ceil(work / tiles_per_split) splits, at most max_splits
 // and at most nbulk + 1; the last split runs the tail and takes whatever bulk
@@ -97,10 +97,21 @@ __device__ __forceinline__ int k_swz(int key) {
     // K tile rows are HD*2 bytes = HD/8 units; 16 units span all LDS banks.
     return (HD == 128) ? (key & 15) : ((key >> 1) & 7);
 }
-__device__ __forceinline__ int v_swz(int dd) { return (dd >> 1) & 7; }  // V^T rows: 8 units
+// V^T rows hold TK/8 units and 128/TK of them share one 256-byte bank span.
+__device__ __forceinline__ int v_swz(int dd) { return (dd / (128 / kTileKeys)) & (kTileKeys / 8 - 1); }
+
+// Tile pipeline depth: NS LDS stages per workgroup, so NS - 1 tiles stay in
+// flight while one is computed.  Four stages of 32-key tiles take 64 KB of
+// LDS with d = 128: two workgroups (two waves per SIMD) share a CU, and each
+// keeps three tiles (48 KB) in flight.  Two per CU is also the cap for d = 64,
+// where registers rather than LDS are the limit.
+constexpr int kStages = 4;
+constexpr int occupancy_for(int hd) {
+    return (160 * 1024) / (kStages * 2 * kTileKeys * hd * 2) < 2 ? (160 * 1024) / (kStages * 2 * kTileKeys * hd * 2) : 2;
+}
 
 template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
+__global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(MfmaParams p) {
     constexpr int NT = NW * 64;
     constexpr int KU = HD / 8;          // 16-byte units per K row
     constexpr int K_UNITS = TK * KU;
@@ -110,16 +121,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     constexpr int KC = HD / 16;         // d-chunks of the first MFMA
     constexpr int MB = HD / 32;         // d-blocks of the second MFMA
     constexpr int RPG = NW * 32;        // rows per workgroup
+    constexpr int KB = TK / 32;         // 32-key blocks of the first MFMA per tile
+    constexpr int C4 = TK / 16;         // 16-key chunks of the second MFMA per tile
+    constexpr int VU = TK / 8;          // 16-byte units per V^T row
+    constexpr int NS = kStages;
+    static_assert(NS == 4, "the stage arrays below are written out for four stages");
+    static_assert((NS - 1) * (LK + LV) < 64, "outstanding copies must fit the vmcnt counter");
 
-    // One array per stage: the tile loop below is unrolled by two so that every
+    // One array per stage: the tile loop below is unrolled by NS so that every
     // LDS access names a fixed array, which lets the compiler see that reads of
-    // one stage never alias the global->LDS copies in flight into the other.
+    // one stage never alias the global->LDS copies in flight into the others.
     __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * HD];
     __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * HD];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k2[TK * HD];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_k3[TK * HD];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v0[HD * TK];
     __shared__ __attribute__((aligned(16))) uint16_t lds_v1[HD * TK];
-    auto kbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * { return st ? lds_k1 : lds_k0; };
-    auto vbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * { return st ? lds_v1 : lds_v0; };
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v2[HD * TK];
+    __shared__ __attribute__((aligned(16))) uint16_t lds_v3[HD * TK];
+    auto kbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * {
+        return st == 0 ? lds_k0 : st == 1 ? lds_k1 : st == 2 ? lds_k2 : lds_k3;
+    };
+    auto vbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * {
+        return st == 0 ? lds_v0 : st == 1 ? lds_v1 : st == 2 ? lds_v2 : lds_v3;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -140,8 +165,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
 
     // Prefix lengths are clamped into [0, cap] so that no access leaves the cache.
     const int P = min(max(p.prefix[it], 0), p.cap);
-    const int P64 = P & ~(TK - 1);
-    const int nbulk = P64 / TK;
+    const int Pb = P & ~(TK - 1);  // cache positions in whole tiles
+    const int nbulk = Pb / TK;
     // A prefix above the host's max_prefix widens the splits instead of
     // overrunning the workspace (at most max_splits per unit).
     const UnitSplit us = unit_split(P, p.D, p.tiles_per_split, p.max_splits, split);
@@ -150,7 +175,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     const bool is_tail = split == nsplit - 1;
     const int t0 = us.t0;
     const int nb_split = us.nb;
-    const int tail_len = is_tail ? (P - P64) + p.D : 0;
+    const int tail_len = is_tail ? (P - Pb) + p.D : 0;
     const int ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
 
     const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD;   // [cap][HD]
@@ -206,27 +231,27 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         for (int j = 0; j < LV; ++j) {
             const int base = (j * NW + w) * 64;
             const int slot = base + lane;
-            const int dd = slot >> 3, pu = slot & 7;
+            const int dd = slot / VU, pu = slot % VU;
             const int lu = pu ^ v_swz(dd);
             const uint16_t *src = p.vc + vc_base + (size_t)dd * p.cap + key0 + lu * 8;
             __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 8], 16, 0, 0);
         }
     };
-    // Tail tiles: the last P % 64 cache positions followed by the D block slots,
-    // zero past the end (at most two tiles, in the unit's last split).  K rows
+    // Tail tiles: the last P % TK cache positions followed by the D block slots,
+    // zero past the end (at most three tiles, in the unit's last split).  K rows
     // and cache V^T rows are gathered as 16-byte units.  Block V rows arrive
     // d-contiguous ([slot][Hkv][d]); they are loaded as 16-byte units and
     // scattered transposed into the V^T tile after the other units are written.
     constexpr int BU = HD / 8;  // 16-byte units per block V row
     auto load_tail = [&](int st, int tt) __attribute__((always_inline)) {
-        const int pc = P - P64;  // cache positions in the tail
+        const int pc = P - Pb;  // cache positions in the tail
         u32x4 kr[LK], vr[LV];
 #pragma unroll
         for (int i = 0; i < LK; ++i) {
             const int u = tid + i * NT;
             const int key = u / KU, lu = u % KU;
             const int j = tt * TK + key;
-            const int pos = P64 + j;
+            const int pos = Pb + j;
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
             if (j < tail_len) {
                 const uint16_t *src = pos < P ? p.kc + kc_base + (size_t)pos * HD + lu * 8
@@ -238,16 +263,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
 #pragma unroll
         for (int i = 0; i < LV; ++i) {
             const int u = tid + i * NT;
-            const int dd = u >> 3, lu = u & 7;
+            const int dd = u / VU, lu = u % VU;
             const int j0 = tt * TK + lu * 8;
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
             if (j0 + 8 <= pc) {
-                v = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + P64 + j0);
+                v = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + Pb + j0);
             } else if (j0 < pc) {  // unit straddles the end of the cache part
                 uint16_t e8[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    e8[e] = j0 + e < pc ? p.vc[vc_base + (size_t)dd * p.cap + P64 + j0 + e] : (uint16_t)0;
+                    e8[e] = j0 + e < pc ? p.vc[vc_base + (size_t)dd * p.cap + Pb + j0 + e] : (uint16_t)0;
                 v = u32x4{e8[0] | ((uint32_t)e8[1] << 16), e8[2] | ((uint32_t)e8[3] << 16),
                           e8[4] | ((uint32_t)e8[5] << 16), e8[6] | ((uint32_t)e8[7] << 16)};
             }
@@ -262,7 +287,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
 #pragma unroll
         for (int i = 0; i < LV; ++i) {
             const int u = tid + i * NT;
-            const int dd = u >> 3, lu = u & 7;
+            const int dd = u / VU, lu = u % VU;
             *reinterpret_cast<u32x4 *>(vbuf(st) + dd * TK + ((lu ^ v_swz(dd)) << 3)) = vr[i];
         }
         bd_barrier_lds();  // the scatter below overwrites zeros written above
@@ -298,9 +323,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
     auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */) __attribute__((always_inline)) {
         const uint16_t *Kt = kbuf(st);
         const uint16_t *Vt = vbuf(st);
-        floatx16 s[2];
+        floatx16 s[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             s[kb] = floatx16{};
             const int key = kb * 32 + key_perm(col);
             const int sw = k_swz<HD>(key);
@@ -313,13 +338,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         }
         if (tt >= 0) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int j = tt * TK + kb * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
                     bool ok = j < tail_len;
                     if (p.mode == 1) {
-                        const int pos = P64 + j;
+                        const int pos = Pb + j;
                         ok = ok && (pos < P || pos - P <= slot);
                     }
                     if (!ok) s[kb][i] = -INFINITY;
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         }
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
         mx = bd_max_halves(mx);
@@ -342,9 +367,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
             m_run = m_new;
         }
         const float msub = (m_run == -INFINITY) ? 0.f : m_run;
-        bf16x8 pb[4];
+        bf16x8 pb[C4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)bd_exp2(fmaf(s[kb][i], p.c, -msub));
         // Row sum of the rounded weights (exactly what the P.V product uses),
@@ -352,7 +377,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         float lsum = 0.f;
 #pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4)
+        for (int c4 = 0; c4 < C4; ++c4)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bf16x2 pr = {pb[c4][2 * e], pb[c4][2 * e + 1]};
@@ -364,7 +389,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
             const int dd = mb * 32 + col;
             const int sw = v_swz(dd);
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
+            for (int c4 = 0; c4 < C4; ++c4) {
                 const int lu = c4 * 2 + half;
                 const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&Vt[dd * TK + ((lu ^ sw) << 3)]);
                 o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c4], o[mb], 0, 0, 0);
@@ -379,26 +404,40 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_mfma_kernel(MfmaParams p) {
         bd_barrier_lds();
         if (wave_active) compute(0, tt);
     }
+    // Bulk tiles through NS stages: tiles tl+1 .. tl+NS-1 are in flight while
+    // tile tl is computed.
     if (nb_split > 0) {
         if (ntail > 0) bd_barrier_lds();  // every wave is done with the tail tile in stage 0
-        issue_bulk(t0, 0);
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (i < nb_split) issue_bulk(t0 + i, i);
     }
-    // Bulk tiles, two LDS stages: tile tl+1 is in flight while tile tl is computed.
+    auto wait_tile = [&](int ahead) __attribute__((always_inline)) {
+        // ahead = tiles issued after the one needed now (each LK + LV copies per thread)
+        if (ahead >= 3)
+            bd_wait_vmcnt<3 * (LK + LV)>();
+        else if (ahead == 2)
+            bd_wait_vmcnt<2 * (LK + LV)>();
+        else if (ahead == 1)
+            bd_wait_vmcnt<LK + LV>();
+        else
+            bd_wait_vmcnt<0>();
+    };
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        if (tl + 1 < nb_split) {
-            bd_barrier_lds();  // every wave is done with stage 1-ST
-            issue_bulk(t0 + tl + 1, 1 - ST);
-            bd_wait_vmcnt<LK + LV>();  // tile tl's copies have landed
-        } else {
-            bd_wait_vmcnt<0>();
+        if (tl + NS - 1 < nb_split) {
+            bd_barrier_lds();  // every wave is done with tile tl-1, whose stage is refilled now
+            issue_bulk(t0 + tl + NS - 1, (ST + NS - 1) % NS);
         }
-        bd_barrier_lds();  // tile tl is visible to every wave
+        wait_tile(min(NS - 1, nb_split - 1 - tl));  // tile tl's copies have landed
+        bd_barrier_lds();                           // ... and are visible to every wave
         if (wave_active) compute(ST, -1);
     };
-    for (int tl = 0; tl < nb_split; tl += 2) {
+    for (int tl = 0; tl < nb_split; tl += NS) {
         step(std::integral_constant<int, 0>{}, tl);
         if (tl + 1 < nb_split) step(std::integral_constant<int, 1>{}, tl + 1);
+        if (tl + 2 < nb_split) step(std::integral_constant<int, 2>{}, tl + 2);
+        if (tl + 3 < nb_split) step(std::integral_constant<int, 3>{}, tl + 3);
     }
 
     const float l_tot = bd_sum_halves(l_run);
@@ -629,12 +668,14 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
         pl.ws_bytes = 0;
         return pl;
     }
-    pl.nw = pl.rows <= 128 ? 4 : 8;
+    // 8-wave workgroups (256 rows) only for d = 128: with d = 64 a 32-key tile
+    // has fewer 16-byte units than 8 waves have lanes.
+    pl.nw = (pl.rows <= 128 || d == 64) ? 4 : 8;
     pl.rows_per_group = pl.nw * 32;
     pl.row_blocks = (pl.rows + pl.rows_per_group - 1) / pl.rows_per_group;
     pl.units = n * Hkv * pl.row_blocks;
-    // Resident workgroups: two 4-wave or one 8-wave workgroup per CU (256 CUs).
-    const int slots = pl.nw == 4 ? 2 * kCUs : kCUs;
+    // Resident workgroups: LDS (kStages tile stages) bounds them per CU.
+    const int slots = kCUs * occupancy_for(d);
     const int ntiles_max = max_prefix / kTileKeys;
     const int want = std::max(1, slots / pl.units);
     // Splits per unit (the device side derives each unit's count from its own
@@ -691,8 +732,8 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
         tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4> : (const void *)attn_mfma_kernel<128, 8>;
         merge = pl.nw == 4 ? (const void *)attn_merge_kernel<128, 4> : (const void *)attn_merge_kernel<128, 8>;
     } else {
-        tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<64, 4> : (const void *)attn_mfma_kernel<64, 8>;
-        merge = pl.nw == 4 ? (const void *)attn_merge_kernel<64, 4> : (const void *)attn_merge_kernel<64, 8>;
+        tile = (const void *)attn_mfma_kernel<64, 4>;
+        merge = (const void *)attn_merge_kernel<64, 4>;
     }
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);

@@ -8,7 +8,7 @@
 namespace bd {
 
 // ---- block attention -------------------------------------------------------
-constexpr int kTileKeys = 64;       // keys per LDS tile
+constexpr int kTileKeys = 32;       // keys per LDS tile
 constexpr int kCUs = 256;           // compute units of an MI355X
 constexpr int kMaxSplits = 16;      // split-K pieces per unit (merge registers)
 
