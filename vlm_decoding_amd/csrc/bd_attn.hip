@@ -163,10 +163,29 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const int g = pair % p.Hkv;
     const int it = pair / p.Hkv;
 
+    // This lane's query row.  Its loads are issued before the prefix length
+    // is known (they do not depend on it), so the two round trips overlap.
+    const int r_local = w * 32 + col;
+    const int r = rb * RPG + r_local;
+    const bool row_valid = r < p.R;
+    const bool wave_active = rb * RPG + w * 32 < p.R;
+    const int slot = r / p.G;
+    const int head = g * p.G + (r - slot * p.G);
+    bf16x8 qf[KC];
+    {
+        const uint16_t *qp = p.q + (((size_t)it * p.D + slot) * p.Hq + head) * HD + half * 8;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            if (row_valid)
+                qf[kc] = *reinterpret_cast<const bf16x8 *>(qp + kc * 16);
+            else
+                qf[kc] = bf16x8{};
+        }
+    }
+
     // Prefix lengths are clamped into [0, cap] so that no access leaves the cache.
     const int P = min(max(p.prefix[it], 0), p.cap);
     const int Pb = P & ~(TK - 1);  // cache positions in whole tiles
-    const int nbulk = Pb / TK;
     // A prefix above the host's max_prefix widens the splits instead of
     // overrunning the workspace (at most max_splits per unit).
     const UnitSplit us = unit_split(P, p.D, p.tiles_per_split, p.max_splits, split);
@@ -181,30 +200,6 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD;   // [cap][HD]
     const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap;   // [HD][cap]
 
-    // This lane's query row.
-    const int r_local = w * 32 + col;
-    const int r = rb * RPG + r_local;
-    const bool row_valid = r < p.R;
-    const bool wave_active = rb * RPG + w * 32 < p.R;
-    const int slot = r / p.G;
-    const int head = g * p.G + (r - slot * p.G);
-
-    bf16x8 qf[KC];
-    {
-        const uint16_t *qp = p.q + (((size_t)it * p.D + slot) * p.Hq + head) * HD + half * 8;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            if (row_valid)
-                qf[kc] = *reinterpret_cast<const bf16x8 *>(qp + kc * 16);
-            else
-                qf[kc] = bf16x8{};
-        }
-        // Retire the Q loads here, before any tile copy is issued: otherwise the
-        // compiler re-waits for them (vmcnt(0)) inside the loop and so drains the
-        // tile prefetch every iteration.
-        bd_wait_vmcnt<0>();
-    }
-
     floatx16 o[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) o[mb] = floatx16{};
@@ -216,7 +211,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // LDS slots, one per lane, so the XOR swizzle is applied by choosing every
     // lane's source address.  No VGPRs hold tile data.
     static_assert(K_UNITS % NT == 0 && V_UNITS % NT == 0, "tile units must split evenly over lanes");
-    auto issue_bulk = [&](int t, int st) __attribute__((always_inline)) {
+    auto issue_bulk = [&](int t, int st, bool real) __attribute__((always_inline)) {
         const int key0 = t * TK;
 #pragma unroll
         for (int j = 0; j < LK; ++j) {
@@ -224,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             const int slot = base + lane;
             const int key = slot / KU, pu = slot % KU;
             const int lu = pu ^ k_swz<HD>(key);
-            const uint16_t *src = p.kc + kc_base + (size_t)(key0 + key) * HD + lu * 8;
+            const uint16_t *src = real ? p.kc + kc_base + (size_t)(key0 + key) * HD + lu * 8 : p.kc + kc_base;
             __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&kbuf(st)[base * 8], 16, 0, 0);
         }
 #pragma unroll
@@ -233,7 +228,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             const int slot = base + lane;
             const int dd = slot / VU, pu = slot % VU;
             const int lu = pu ^ v_swz(dd);
-            const uint16_t *src = p.vc + vc_base + (size_t)dd * p.cap + key0 + lu * 8;
+            const uint16_t *src = real ? p.vc + vc_base + (size_t)dd * p.cap + key0 + lu * 8 : p.kc + kc_base;
             __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 8], 16, 0, 0);
         }
     };
@@ -404,41 +399,38 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         bd_barrier_lds();
         if (wave_active) compute(0, tt);
     }
-    // Bulk tiles through NS stages: tiles tl+1 .. tl+NS-1 are in flight while
-    // tile tl is computed.
+    // Bulk tiles through NS stages, all NS filled up front: tiles tl+1 ..
+    // tl+NS-1 are in flight while tile tl is computed.  Every step has the same
+    // shape - wait for all but the last NS-1 copy groups, compute, refill the
+    // stage just freed with tile tl+NS - and the
+    // step count is rounded up to a multiple of NS, with dummy copy groups
+    // (each lane reading one fixed, cached 16-byte unit into a stage nobody
+    // reads) past the split's last tile.  The compiler can then prove that a
+    // stage's reads never wait for copies into the other stages; with a
+    // varying count it falls back to draining every copy before each tile.
+    // The Q loads, issued before the first copies, are retired by the first
+    // fixed-count wait.
+    const int nb_round = (nb_split + NS - 1) / NS * NS;
     if (nb_split > 0) {
         if (ntail > 0) bd_barrier_lds();  // every wave is done with the tail tile in stage 0
 #pragma unroll
-        for (int i = 0; i < NS - 1; ++i)
-            if (i < nb_split) issue_bulk(t0 + i, i);
+        for (int i = 0; i < NS; ++i) issue_bulk(t0 + i, i, i < nb_split);
     }
-    auto wait_tile = [&](int ahead) __attribute__((always_inline)) {
-        // ahead = tiles issued after the one needed now (each LK + LV copies per thread)
-        if (ahead >= 3)
-            bd_wait_vmcnt<3 * (LK + LV)>();
-        else if (ahead == 2)
-            bd_wait_vmcnt<2 * (LK + LV)>();
-        else if (ahead == 1)
-            bd_wait_vmcnt<LK + LV>();
-        else
-            bd_wait_vmcnt<0>();
-    };
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        if (tl + NS - 1 < nb_split) {
-            bd_barrier_lds();  // every wave is done with tile tl-1, whose stage is refilled now
-            issue_bulk(t0 + tl + NS - 1, (ST + NS - 1) % NS);
-        }
-        wait_tile(min(NS - 1, nb_split - 1 - tl));  // tile tl's copies have landed
-        bd_barrier_lds();                           // ... and are visible to every wave
-        if (wave_active) compute(ST, -1);
+        bd_wait_vmcnt<(NS - 1) * (LK + LV)>();  // tile tl's copies have landed
+        bd_barrier_lds();                        // ... and are visible to every wave
+        if (wave_active && tl < nb_split) compute(ST, -1);
+        bd_barrier_lds();  // every wave is done with stage ST, which is refilled now
+        issue_bulk(t0 + tl + NS, ST, tl + NS < nb_split);
     };
-    for (int tl = 0; tl < nb_split; tl += NS) {
+    for (int tl = 0; tl < nb_round; tl += NS) {
         step(std::integral_constant<int, 0>{}, tl);
-        if (tl + 1 < nb_split) step(std::integral_constant<int, 1>{}, tl + 1);
-        if (tl + 2 < nb_split) step(std::integral_constant<int, 2>{}, tl + 2);
-        if (tl + 3 < nb_split) step(std::integral_constant<int, 3>{}, tl + 3);
+        step(std::integral_constant<int, 1>{}, tl + 1);
+        step(std::integral_constant<int, 2>{}, tl + 2);
+        step(std::integral_constant<int, 3>{}, tl + 3);
     }
+    if (nb_split > 0) bd_wait_vmcnt<0>();  // no copy may still target LDS when the workgroup ends
 
     const float l_tot = bd_sum_halves(l_run);
     // Output element mapping of the O^T accumulators: block mb, register i of
@@ -508,24 +500,28 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
     const int pair = unit / p.row_blocks;
     const int g = pair % p.Hkv;
     const int it = pair / p.Hkv;
-    const int P = min(max(p.prefix[it], 0), p.cap);
-    const int nsplit = unit_nsplit(P, p.D, p.tiles_per_split, p.max_splits);
     const int row0 = rb * (NW * 32) + wv * 32;
-    if (nsplit == 1 || row0 >= p.R) return;  // single split: written by the tile kernel
+    if (row0 >= p.R) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, jq = tid >> 6, half = lane >> 5, col = lane & 31;
     const int src_t = wv * 64 + lane;      // thread of the tile kernel's block
     const size_t base = (size_t)unit * p.max_splits;
     const uint4 *wo = reinterpret_cast<const uint4 *>(p.ws_o);
+    // Every workspace slot of the unit is requested before the prefix length
+    // (which decides how many of them hold this call's partials) arrives;
+    // slots past the unit's split count are read but not used.
     float2 ml[MAXS];
     uint4 v[QPT][MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
-        if (s < nsplit) {
+        if (s < p.max_splits) {
             ml[s] = p.ws_ml[(base + s) * NT_TILE + src_t];
 #pragma unroll
             for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t];
         }
+    const int P = min(max(p.prefix[it], 0), p.cap);
+    const int nsplit = unit_nsplit(P, p.D, p.tiles_per_split, p.max_splits);
+    if (nsplit == 1) return;  // single split: written by the tile kernel
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
