@@ -37,7 +37,8 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        # Build on first use, and again whenever the source is newer than the library.
+        if not os.path.exists(_LIB) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB):
             build()
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
@@ -51,6 +52,8 @@ def _load():
         lib.bdo_spec_verify.argtypes = [i32, i32, i32, P, P, P, P]
         lib.bdo_kv_append.argtypes = [i32] * 6 + [P] * 7
         lib.bdo_num_threads.restype = i32
+        lib.bdo_softmax_partial.argtypes = [i32, i32, P, P, P, P, P]
+        lib.bdo_merge_partials.argtypes = [i32, i32, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -159,3 +162,30 @@ def kv_append(k_cache, v_cache, prefix, k_blk, v_blk, n_accept=None):
     lib.bdo_kv_append(n, D, Hkv, d, cap, dtype, _ptr(k_cache), _ptr(v_cache), _ptr(prefix),
                       _ptr(kb), _ptr(vb), _ptr(na), _ptr(err))
     return k_cache, v_cache, prefix, int(err[0])
+
+
+def softmax_partial(s, v):
+    """Split-K partial of one key range (online softmax normaliser, Milakov and
+    Gimelshein 2018): returns (m, l, o) with m = max s, l = sum exp(s - m) and o
+    the range's normalised weighted value sum.  s: [nk], v: [nk][d]."""
+    lib = _load()
+    s = _c(s, np.float64)
+    v = _c(v, np.float64)
+    nk, d = v.shape
+    m = ctypes.c_double()
+    l = ctypes.c_double()
+    o = np.zeros(d, np.float64)
+    lib.bdo_softmax_partial(nk, d, _ptr(s), _ptr(v), ctypes.byref(m), ctypes.byref(l), _ptr(o))
+    return m.value, l.value, o
+
+
+def merge_partials(parts):
+    """Merge split-K partials in the given order: M = max m_p, c_p = exp(m_p - M) l_p,
+    out = sum c_p o_p / sum c_p (the same source).  parts: list of (m, l, o)."""
+    lib = _load()
+    m = np.array([p[0] for p in parts], np.float64)
+    l = np.array([p[1] for p in parts], np.float64)
+    o = np.ascontiguousarray(np.stack([p[2] for p in parts]).astype(np.float64))
+    out = np.zeros(o.shape[1], np.float64)
+    lib.bdo_merge_partials(len(parts), o.shape[1], _ptr(m), _ptr(l), _ptr(o), _ptr(out))
+    return out

@@ -285,3 +285,48 @@ void bdo_kv_append(int n, int D, int Hkv, int d, int cap, int dtype, void *k_cac
         prefix_len[it] = P + L;
     }
 }
+
+/*
+ * Split-K softmax partial over one key range (online normaliser: Milakov and
+ * Gimelshein, "Online normalizer calculation for softmax", 2018):
+ *   m = max_j s_j,  l = sum_j exp(s_j - m),  o = sum_j exp(s_j - m) v_j / l.
+ * s[nk] are the range's scores, v[nk][d] its values.  An empty range gives
+ * m = -inf, l = 0 and o = 0.
+ */
+void bdo_softmax_partial(int nk, int d, const double *s, const double *v, double *m, double *l,
+                         double *o) {
+    double mx = -INFINITY;
+    for (int j = 0; j < nk; ++j)
+        if (s[j] > mx) mx = s[j];
+    double sum = 0.0;
+    for (int e = 0; e < d; ++e) o[e] = 0.0;
+    for (int j = 0; j < nk; ++j) {
+        double w = exp(s[j] - mx);
+        sum += w;
+        for (int e = 0; e < d; ++e) o[e] += w * v[(size_t)j * d + e];
+    }
+    if (sum > 0.0)
+        for (int e = 0; e < d; ++e) o[e] /= sum;
+    *m = mx;
+    *l = sum;
+}
+
+/*
+ * Merge of np partials in the given order (the same source):
+ *   M = max_p m_p,  c_p = exp(m_p - M) l_p,  out = sum_p c_p o_p / sum_p c_p.
+ * Partials of empty ranges (l = 0) contribute nothing.
+ */
+void bdo_merge_partials(int np, int d, const double *m, const double *l, const double *o,
+                        double *out) {
+    double M = -INFINITY;
+    for (int p = 0; p < np; ++p)
+        if (m[p] > M) M = m[p];
+    double L = 0.0;
+    for (int e = 0; e < d; ++e) out[e] = 0.0;
+    for (int p = 0; p < np; ++p) {
+        double c = l[p] > 0.0 ? exp(m[p] - M) * l[p] : 0.0;
+        L += c;
+        for (int e = 0; e < d; ++e) out[e] += c * o[(size_t)p * d + e];
+    }
+    for (int e = 0; e < d; ++e) out[e] /= L;
+}

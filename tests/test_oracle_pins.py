@@ -426,3 +426,60 @@ def test_kv_append_is_bitwise_and_bounded(dtype):
     kc3, vc3, p3, err = oracle.kv_append(kc, vc, np.array([12, 0, 0], np.int32), kb, vb, None)
     assert err == 1 and p3.tolist() == [12, 6, 6]
     assert kc3[0].view(np.uint8).tobytes() == kc[0].view(np.uint8).tobytes()
+
+
+# ---------------------------------------------------------------------------
+# Split-K merge rule (online softmax normaliser, Milakov and Gimelshein 2018):
+# any partition of the keys, merged in order, equals the unsplit softmax.
+# ---------------------------------------------------------------------------
+
+def _direct_softmax_sum(s, v):
+    w = np.exp(s - s.max())
+    return (w[:, None] * v).sum(axis=0) / w.sum()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_merge_of_any_partition_equals_unsplit(seed):
+    rng = np.random.default_rng(seed)
+    n, d = int(rng.integers(5, 400)), 32
+    s = rng.standard_normal(n) * float(rng.choice([0.5, 4.0, 40.0]))
+    v = rng.standard_normal((n, d))
+    want = _direct_softmax_sum(s, v)
+    # random contiguous ranges, one of them empty
+    cuts = np.sort(rng.choice(np.arange(1, n), size=min(6, n - 1), replace=False))
+    bounds = [0] + cuts.tolist() + [n]
+    ranges = [(a, b) for a, b in zip(bounds[:-1], bounds[1:])] + [(n, n)]
+    parts = [oracle.softmax_partial(s[a:b], v[a:b].reshape(b - a, d)) for a, b in ranges]
+    got = oracle.merge_partials(parts)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # the order of merging changes only the rounding
+    np.testing.assert_allclose(oracle.merge_partials(parts[::-1]), want, rtol=0, atol=1e-12)
+
+
+def test_single_partial_is_the_softmax_and_empty_is_neutral():
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal(50) * 3
+    v = rng.standard_normal((50, 8))
+    m, l, o = oracle.softmax_partial(s, v)
+    assert m == s.max()
+    np.testing.assert_allclose(l, np.exp(s - s.max()).sum(), rtol=1e-15)
+    np.testing.assert_allclose(o, _direct_softmax_sum(s, v), atol=1e-13)
+    me, le, oe = oracle.softmax_partial(np.zeros(0), np.zeros((0, 8)))
+    assert me == -np.inf and le == 0.0 and not oe.any()
+    np.testing.assert_array_equal(oracle.merge_partials([(m, l, o), (me, le, oe)]),
+                                  oracle.merge_partials([(m, l, o)]))
+
+
+def test_merge_matches_split_attention_rows():
+    """A block-attention row computed by the oracle equals the merge of partials
+    over a split of its keys (cache part, block part)."""
+    p = synth.params_for(1, n_items=1, D=4, prefix=("fixed", 40), Hq=2, Hkv=1, d=64)
+    st = synth.make_step(p, 11)
+    out = oracle.attention(st["q"], st["k_blk"], st["v_blk"], st["k_cache"], st["v_cache"],
+                           st["prefix"], oracle.BIDIR)
+    q = st["q"][0, 2, 1].astype(np.float64)
+    K = np.concatenate([st["k_cache"][0, 0, :40], st["k_blk"][0, :, 0]]).astype(np.float64)
+    Vv = np.concatenate([st["v_cache"][0, 0, :, :40].T, st["v_blk"][0, :, 0]]).astype(np.float64)
+    sc = K @ q / np.sqrt(64)
+    parts = [oracle.softmax_partial(sc[a:b], Vv[a:b]) for a, b in ((0, 17), (17, 40), (40, 44))]
+    np.testing.assert_allclose(oracle.merge_partials(parts), out[0, 2, 1], atol=1e-12)
