@@ -138,6 +138,51 @@ def write_traffic(pmc_dir, copy_bytes=256 << 20):
     print(json.dumps(out))
 
 
+def bench_lmhead(torch, stream, calls=50, warmup=5):
+    """The next step of the path, measured beside the headline: the 3B LM head
+    (16 slots x 2048 hidden x 151936 vocabulary, bf16 weight of 622 MB) fused with
+    the confidence + commit of the 8 masked slots.  Each call starts from the same
+    block state (restored by a small device copy outside the timed events)."""
+    import ctypes
+    import synth
+    from vlm_decoding_amd import bd
+    st = synth.lmhead_step(1)
+    p = st["params"]
+    c = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    hidden, weight = c(st["hidden"].view(np.int16)), c(st["weight"].view(np.int16))
+    masked0, tokens0 = c(st["masked"]), c(st["tokens"])
+    masked, tokens = masked0.clone(), tokens0.clone()
+    nr, D = p["n_req"], p["D"]
+    conf = torch.empty((nr, D), dtype=torch.float32, device="cuda")
+    amax = torch.empty((nr, D), dtype=torch.int32, device="cuda")
+    com = torch.empty((nr, D), dtype=torch.uint8, device="cuda")
+    ncom = torch.empty((nr,), dtype=torch.int32, device="cuda")
+    desc = bd.lmhead_desc(nr, D, p["V"], p["H"], p["S"], p["tau"])
+    ws = torch.zeros(bd.bd_lmhead_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    args = (ctypes.byref(desc), hidden.data_ptr(), weight.data_ptr(), masked.data_ptr(), tokens.data_ptr(),
+            conf.data_ptr(), amax.data_ptr(), com.data_ptr(), ncom.data_ptr(), ws.data_ptr(), ws.numel(),
+            stream.cuda_stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    status = 0
+    for i in range(warmup + calls):
+        masked.copy_(masked0)
+        tokens.copy_(tokens0)
+        if i >= warmup:
+            evs[i - warmup][0].record(stream)
+        status |= bd.lib.bd_lmhead_confidence_commit(*args)
+        if i >= warmup:
+            evs[i - warmup][1].record(stream)
+    torch.cuda.synchronize()
+    if status:
+        raise RuntimeError("bd_lmhead_confidence_commit failed (status %d)" % status)
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    nbytes = p["V"] * p["H"] * 2 + nr * D * p["H"] * 2
+    return dict(workload="3B LM head: 16 slots x H 2048 x V 151936 bf16 (8 masked, S=16, tau=0.9)",
+                us_per_call=round(us, 2), algorithmic_bytes=nbytes,
+                achieved_gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), calls=calls)
+
+
 def copy_calibration(n_bytes=256 << 20, reps=5):
     """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
     WRITE_SIZE for this copy kernel give the scale between counter readings and
@@ -158,6 +203,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--event-stride", type=int, default=10,
                     help="record the per-call HIP events on every N-th timed step (0: none)")
+    ap.add_argument("--lmhead-calls", type=int, default=50,
+                    help="timed calls of the fused LM head + confidence + commit (0 to skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -276,6 +323,8 @@ def main():
                                        round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
                     algorithmic_bytes_per_launch=attn_bytes)
 
+    lmhead = bench_lmhead(torch, stream, calls=args.lmhead_calls) if args.lmhead_calls > 0 else None
+
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(host0, args.cpu_budget)
@@ -311,6 +360,7 @@ def main():
         "event_stride": stride,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "lm_head_confidence_commit": lmhead,
     }
     print(json.dumps(out), flush=True)
 

@@ -156,6 +156,33 @@ bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache,
                        int32_t *prefix_len, const void *k_blk, const void *v_blk,
                        const int32_t *n_accept, int32_t *dev_err, void *stream);
 
+/* Shape of one LM-head + confidence + commit call.
+ *  R = n_req * D block slots (1..16 in total, D 1..64), vocabulary V >= 2,
+ *  hidden size H (a multiple of 256, at most 4096), S >= 1, tau not NaN. */
+typedef struct {
+    int32_t n_req, D, V, H, S;
+    float tau;
+} bd_lmhead_desc;
+
+/* Workspace bytes bd_lmhead_confidence_commit needs; SIZE_MAX if desc is invalid. */
+size_t bd_lmhead_workspace_bytes(const bd_lmhead_desc *desc);
+
+/* The vocabulary projection that produces a denoising step's logits, fused with
+ * that step's confidence + commit ([DV] cached block decoding: the confidence is
+ * the model's probability of the chosen token, then Algorithm 1's commit rule).
+ *   logits[r][i][v] = sum_h hidden[r][i][h] * weight[v][h]  (bf16 inputs, fp32 sums),
+ * followed by exactly the confidence + commit of bd_confidence_commit on those
+ * logits (same outputs, same rules).  The logits themselves never reach memory.
+ *   hidden  bf16 [n_req][D][H]   final hidden state of every block slot
+ *   weight  bf16 [V][H]          the vocabulary projection (a linear layer's weight)
+ * Every slot's logits are formed (the weight is read once for all of them);
+ * only masked slots take part in the confidence and the commit.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH. */
+bd_status bd_lmhead_confidence_commit(const bd_lmhead_desc *desc, const void *hidden, const void *weight,
+                                      uint8_t *masked, int32_t *tokens, float *conf, int32_t *argmax,
+                                      uint8_t *committed, int32_t *n_committed, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *bd_status_string(bd_status status);
 

@@ -54,6 +54,7 @@ def _load():
         lib.bdo_num_threads.restype = i32
         lib.bdo_softmax_partial.argtypes = [i32, i32, P, P, P, P, P]
         lib.bdo_merge_partials.argtypes = [i32, i32, P, P, P, P]
+        lib.bdo_lm_head_logits.argtypes = [i32, i32, i32, P, P, P]
         _lib = lib
     return _lib
 
@@ -188,4 +189,20 @@ def merge_partials(parts):
     o = np.ascontiguousarray(np.stack([p[2] for p in parts]).astype(np.float64))
     out = np.zeros(o.shape[1], np.float64)
     lib.bdo_merge_partials(len(parts), o.shape[1], _ptr(m), _ptr(l), _ptr(o), _ptr(out))
+    return out
+
+
+def lm_head_logits(hidden, weight):
+    """Logits of every block slot: the vocabulary projection of its final hidden
+    state, logits[r][i][v] = sum_h hidden[r][i][h] * weight[v][h], in fp64.
+    hidden: raw bf16 [n_req][D][H]; weight: raw bf16 [V][H].  Their softmax is the
+    distribution whose top probability is the confidence (DiffusionVL notes,
+    cached block decoding)."""
+    lib = _load()
+    n_req, D, H = hidden.shape
+    V = weight.shape[0]
+    h = _c(hidden, np.uint16)
+    w = _c(weight, np.uint16)
+    out = np.zeros((n_req, D, V), np.float64)
+    lib.bdo_lm_head_logits(n_req * D, V, H, _ptr(h), _ptr(w), _ptr(out))
     return out

@@ -330,3 +330,22 @@ void bdo_merge_partials(int np, int d, const double *m, const double *l, const d
     }
     for (int e = 0; e < d; ++e) out[e] /= L;
 }
+
+/*
+ * Logits of the block's masked-token predictions: the language model's
+ * vocabulary projection applied to the final hidden state of every block
+ * slot, logits[r][v] = sum_h hidden[r][h] * weight[v][h] (hidden bf16
+ * [R][H], weight bf16 [V][H], out fp64 [R][V]).  These are the logits whose
+ * softmax gives the confidence of [DV]'s cached block decoding.
+ */
+void bdo_lm_head_logits(int R, int V, int H, const uint16_t *hidden, const uint16_t *weight,
+                        double *out) {
+#pragma omp parallel for schedule(static)
+    for (long v = 0; v < V; ++v)
+        for (int r = 0; r < R; ++r) {
+            double acc = 0.0;
+            for (int h = 0; h < H; ++h)
+                acc += widen(hidden, BDO_BF16, (size_t)r * H + h) * widen(weight, BDO_BF16, (size_t)v * H + h);
+            out[(size_t)r * V + v] = acc;
+        }
+}

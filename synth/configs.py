@@ -58,3 +58,22 @@ CONFIGS = {
 
 def seed_of(cfg_id: int) -> int:
     return 1000 + int(cfg_id)
+
+
+# LM head with a fused confidence epilogue (a step after the attention layers:
+# the block's final hidden states times the vocabulary projection give the
+# logits that the confidence / commit rule reads).  Shapes of the Qwen2.5-VL-3B
+# language model (hidden 2048, vocabulary 151936) at block D = 16.  Hidden
+# states ~ N(0, 1); weights ~ N(0, 4 / H), so a logit has variance 4 like the
+# logits configs above; ``plants`` masked rows get one token whose weight row
+# is a scaled copy of that row's hidden state (a logit near ``gain``).
+LMHEAD_CONFIGS = {
+    1: dict(name="3B LM head: H=2048, V=151936, D=16 with 8 masked, S=16, tau=0.9",
+            n_req=1, D=16, n_masked=8, V=151936, H=2048, S=16, tau=0.9, plants=3, gain=17.0),
+    2: dict(name="small LM head: H=256, V=5003, 2 requests x D=8 (5 masked), S=4, tau=0.5",
+            n_req=2, D=8, n_masked=5, V=5003, H=256, S=4, tau=0.5, plants=2, gain=17.0),
+}
+
+
+def lmhead_seed_of(cfg_id: int) -> int:
+    return 2000 + int(cfg_id)

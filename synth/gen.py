@@ -29,7 +29,7 @@ token ids, logits, then plants.
 
 import numpy as np
 
-from .configs import BF16, CONFIGS, F32, seed_of
+from .configs import BF16, CONFIGS, F32, LMHEAD_CONFIGS, lmhead_seed_of, seed_of
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -150,3 +150,44 @@ def fresh_logits(p: dict, rng: np.random.Generator) -> np.ndarray:
 def config_step(cfg_id: int, **overrides) -> dict:
     """The canonical seeded step of a config (seed 1000 + config number)."""
     return make_step(params_for(cfg_id, **overrides), seed_of(cfg_id))
+
+
+def make_lmhead(p: dict, seed: int) -> dict:
+    """Draw the inputs of one LM-head + confidence step.
+
+    Layouts: hidden bf16 [n_req][D][H], weight bf16 [V][H] (a linear layer's
+    row-major weight), masked u8 [n_req][D], tokens i32 [n_req][D].
+    Draw order: hidden, weight, masked set, committed ids, planted tokens.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_req, D, V, H = p["n_req"], p["D"], p["V"], p["H"]
+    hidden = f32_to_bf16_bits(rng.standard_normal(size=(n_req, D, H), dtype=np.float32))
+    w_std = np.float32(2.0 / np.sqrt(H))
+    weight = np.empty((V, H), dtype=np.uint16)
+    step = 1 << 14
+    for v0 in range(0, V, step):  # in slices, to bound the float32 temporary
+        v1 = min(V, v0 + step)
+        weight[v0:v1] = f32_to_bf16_bits(rng.standard_normal(size=(v1 - v0, H), dtype=np.float32) * w_std)
+    masked = np.zeros((n_req, D), dtype=np.uint8)
+    tokens = np.full((n_req, D), -1, dtype=np.int32)
+    for r in range(n_req):
+        masked[r, rng.permutation(D)[: p["n_masked"]]] = 1
+    for r in range(n_req):
+        ids = rng.integers(0, V, size=D, dtype=np.int64).astype(np.int32)
+        tokens[r] = np.where(masked[r] == 1, -1, ids)
+    planted = []
+    scale = np.float32(p["gain"] / H)
+    for r in range(n_req):
+        rows = np.flatnonzero(masked[r])[: p["plants"]]
+        for i in rows:
+            v_star = int(rng.integers(0, V))
+            weight[v_star] = f32_to_bf16_bits(bf16_bits_to_f32(hidden[r, i]) * scale)
+            planted.append((r, int(i), v_star))
+    return dict(params=p, seed=seed, hidden=hidden, weight=weight, masked=masked, tokens=tokens,
+                planted=planted)
+
+
+def lmhead_step(cfg_id: int, **overrides) -> dict:
+    p = dict(LMHEAD_CONFIGS[cfg_id])
+    p.update(overrides)
+    return make_lmhead(p, lmhead_seed_of(cfg_id))

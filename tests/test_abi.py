@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for must in ["bd_attn_step", "bd_confidence_commit", "bd_spec_verify", "bd_kv_append"]:
+    for must in ["bd_attn_step", "bd_confidence_commit", "bd_spec_verify", "bd_kv_append",
+                 "bd_lmhead_confidence_commit"]:
         assert must in names
     assert len(names) >= 9
 
@@ -126,6 +127,43 @@ def test_verify_and_append_validation(bd):
     assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_SHAPE
     desc = _attn(bd)
     assert bd.lib.bd_kv_append(ctypes.byref(desc), None, fake, fake, fake, fake, None, None, None) == bd.BD_E_NULL
+
+
+BAD_LMHEAD = [
+    (dict(n_req=0), "BD_E_SHAPE"), (dict(D=0), "BD_E_SHAPE"), (dict(D=17), "BD_E_SHAPE"),
+    (dict(n_req=2, D=16), "BD_E_SHAPE"), (dict(V=1), "BD_E_SHAPE"), (dict(H=128), "BD_E_SHAPE"),
+    (dict(H=2050), "BD_E_SHAPE"), (dict(H=4352), "BD_E_SHAPE"), (dict(S=0), "BD_E_PARAM"),
+    (dict(tau=float("nan")), "BD_E_PARAM"),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_LMHEAD)
+def test_lmhead_validation(bd, kw, code):
+    base = dict(n_req=1, D=16, V=151936, H=2048, S=16, tau=0.9)
+    base.update(kw)
+    desc = bd.BdLmheadDesc(*[base[f] for f, _ in bd.BdLmheadDesc._fields_])
+    fake = 1 << 20
+    st = bd.lib.bd_lmhead_confidence_commit(ctypes.byref(desc), fake, fake, fake, fake, None, None, None, None,
+                                            fake, 1 << 30, None)
+    assert st == getattr(bd, code)
+    assert bd.lib.bd_lmhead_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
+
+
+def test_lmhead_null_alignment_and_workspace(bd):
+    desc = bd.BdLmheadDesc(1, 16, 151936, 2048, 16, 0.9)
+    fake = 1 << 20
+    need = bd.lib.bd_lmhead_workspace_bytes(ctypes.byref(desc))
+    assert 0 < need < bd.SIZE_MAX
+    call = bd.lib.bd_lmhead_confidence_commit
+    assert call(ctypes.byref(desc), None, fake, fake, fake, None, None, None, None, fake, need, None) == bd.BD_E_NULL
+    assert call(ctypes.byref(desc), fake, fake, None, fake, None, None, None, None, fake, need, None) == bd.BD_E_NULL
+    assert call(ctypes.byref(desc), fake + 8, fake, fake, fake, None, None, None, None, fake, need, None) == bd.BD_E_PARAM
+    assert call(ctypes.byref(desc), fake, fake, fake, fake, None, None, None, None, fake, need - 1, None) == bd.BD_E_WORKSPACE
+    assert call(ctypes.byref(desc), fake, fake, fake, fake, None, None, None, None, None, need, None) == bd.BD_E_WORKSPACE
+    # 7B hidden size (3584) and the largest supported (4096) are accepted
+    for H in (3584, 4096):
+        ok = bd.BdLmheadDesc(1, 16, 152064, H, 8, 0.8)
+        assert bd.lib.bd_lmhead_workspace_bytes(ctypes.byref(ok)) < bd.SIZE_MAX
 
 
 def test_status_strings(bd):

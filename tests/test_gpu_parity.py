@@ -345,3 +345,134 @@ def test_append_overflow_and_partial(dev, dtype):
     el = np.uint16 if dtype == BF16 else np.float32
     assert ds.k_cache.cpu().numpy().view(el).tobytes() == kc.tobytes()
     assert ds.v_cache.cpu().numpy().view(el).tobytes() == vc.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# LM head fused with confidence + commit (the logits never reach memory).
+# The oracle forms fp64 logits, rounds them to fp32 and applies its confidence /
+# commit; the GPU sums bf16 products in fp32 (MFMA).  Its logits therefore
+# differ from the exact ones by ~1e-5, so a slot whose two largest exact logits
+# are within LOGIT_GAP has a fragile greedy token: it is excluded from the
+# token comparison (and counted) like a fragile commit decision.
+# ---------------------------------------------------------------------------
+
+LOGIT_GAP = 1e-3
+
+
+class _LmDev:
+    def __init__(self, dev, st):
+        torch = dev["torch"]
+        bd = dev["bd"]
+        p = st["params"]
+        self.p = p
+        c = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.hidden = c(st["hidden"].view(np.int16))
+        self.weight = c(st["weight"].view(np.int16))
+        self.masked = c(st["masked"])
+        self.tokens = c(st["tokens"])
+        nr, D = p["n_req"], p["D"]
+        self.conf = torch.empty((nr, D), dtype=torch.float32, device="cuda")
+        self.argmax = torch.empty((nr, D), dtype=torch.int32, device="cuda")
+        self.committed = torch.empty((nr, D), dtype=torch.uint8, device="cuda")
+        self.n_committed = torch.empty((nr,), dtype=torch.int32, device="cuda")
+        self.desc = bd.lmhead_desc(nr, D, p["V"], p["H"], p["S"], p["tau"])
+        need = bd.bd_lmhead_workspace_bytes(self.desc)
+        assert need < bd.SIZE_MAX
+        self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+        self.bd = bd
+
+    def run(self):
+        self.bd.bd_lmhead_confidence_commit(self.desc, self.hidden, self.weight, self.masked, self.tokens,
+                                            self.conf, self.argmax, self.committed, self.n_committed, self.ws)
+
+
+def _compare_lmhead(dev, g, st, label):
+    torch = dev["torch"]
+    torch.cuda.synchronize()
+    p = st["params"]
+    logits64 = oracle.lm_head_logits(st["hidden"], st["weight"])
+    ref = oracle.confidence_commit(logits64.astype(np.float32), st["masked"], st["tokens"], p["S"], p["tau"])
+    g_conf, g_arg = g.conf.cpu().numpy(), g.argmax.cpu().numpy()
+    g_com, g_ncom = g.committed.cpu().numpy(), g.n_committed.cpu().numpy()
+    g_mask, g_tok = g.masked.cpu().numpy(), g.tokens.cpu().numpy()
+    excluded = 0
+    for r in range(p["n_req"]):
+        m = st["masked"][r].astype(bool)
+        nm = int(m.sum())
+        k = min(-(-p["D"] // p["S"]), nm)
+        assert np.all(np.isnan(g_conf[r][~m])) and np.all(g_arg[r][~m] == -1)
+        frag = _fragile(ref["conf"][r], m, k, p["tau"])
+        for i in np.flatnonzero(m):
+            top2 = np.partition(logits64[r, i], -2)[-2:]
+            if top2[1] - top2[0] < LOGIT_GAP:
+                frag.add(int(i))
+            else:
+                assert g_arg[r, i] == ref["argmax"][r, i], (label, r, i)
+            assert abs(float(g_conf[r, i]) - ref["conf"][r, i]) <= CONF_ABS, (label, r, i)
+        own = _rule_commit(g_conf[r], m, k, p["tau"])
+        assert set(np.nonzero(g_com[r])[0].tolist()) == own, (label, r)
+        excluded += len(frag)
+        for i in range(p["D"]):
+            if i in frag:
+                continue
+            assert g_com[r, i] == ref["committed"][r, i], (label, r, i)
+            assert g_mask[r, i] == ref["masked"][r, i]
+            assert g_tok[r, i] == ref["tokens"][r, i]
+        assert g_ncom[r] == int(g_com[r].sum())
+        np.testing.assert_array_equal(g_tok[r][~m], st["tokens"][r][~m])
+    return excluded, ref
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_lmhead_configs(dev, cfg):
+    st = synth.lmhead_step(cfg)
+    p = st["params"]
+    _say("lmhead cfg%d n_req=%d D=%d V=%d H=%d" % (cfg, p["n_req"], p["D"], p["V"], p["H"]))
+    g = _LmDev(dev, st)
+    g.run()
+    excl, ref = _compare_lmhead(dev, g, st, "lmhead cfg%d" % cfg)
+    # the planted slots are confident and committed
+    for r, i, v_star in st["planted"]:
+        assert ref["argmax"][r, i] == v_star and ref["committed"][r, i] == 1
+    _say("lmhead cfg%d excluded fragile decisions: %d" % (cfg, excl))
+
+
+LMHEAD_CASES = [
+    ("V2", dict(V=2)),
+    ("V17_one_tile_plus_one", dict(V=17)),
+    ("D1", dict(n_req=1, D=1, n_masked=1, plants=0)),
+    ("sixteen_requests", dict(n_req=16, D=1, n_masked=1, plants=1)),
+    ("H4096_lds_over_64k", dict(H=4096, V=3001)),
+    ("H3584_7B_hidden", dict(H=3584, V=4099, n_req=1, D=16, n_masked=16, S=8, tau=0.8)),
+    ("none_masked", dict(n_masked=0, plants=0)),
+    ("tau_ge_1", dict(tau=1.0)),
+    ("many_tiles", dict(V=65537, n_req=1, D=16, n_masked=12, S=3)),
+]
+
+
+@pytest.mark.parametrize("label,ov", LMHEAD_CASES, ids=[c[0] for c in LMHEAD_CASES])
+def test_lmhead_edge_cases(dev, label, ov):
+    p = dict(synth.LMHEAD_CONFIGS[2])
+    p.update(ov)
+    st = synth.make_lmhead(p, seed=len(label) * 17 + 5)
+    _say("lmhead %s n_req=%d D=%d V=%d H=%d" % (label, p["n_req"], p["D"], p["V"], p["H"]))
+    g = _LmDev(dev, st)
+    g.run()
+    _compare_lmhead(dev, g, st, label)
+
+
+def test_lmhead_deterministic_and_reusable_workspace(dev):
+    torch = dev["torch"]
+    st = synth.lmhead_step(2)
+    g = _LmDev(dev, st)
+    outs = []
+    for _ in range(3):
+        g.masked.copy_(torch.from_numpy(st["masked"]))
+        g.tokens.copy_(torch.from_numpy(st["tokens"]))
+        g.run()
+        torch.cuda.synchronize()
+        outs.append((g.conf.cpu().numpy().copy(), g.argmax.cpu().numpy().copy(), g.committed.cpu().numpy().copy()))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(np.nan_to_num(o[0], nan=-1), np.nan_to_num(outs[0][0], nan=-1))
+        np.testing.assert_array_equal(o[1], outs[0][1])
+        np.testing.assert_array_equal(o[2], outs[0][2])

@@ -483,3 +483,37 @@ def test_merge_matches_split_attention_rows():
     sc = K @ q / np.sqrt(64)
     parts = [oracle.softmax_partial(sc[a:b], Vv[a:b]) for a, b in ((0, 17), (17, 40), (40, 44))]
     np.testing.assert_allclose(oracle.merge_partials(parts), out[0, 2, 1], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# LM-head logits (vocabulary projection of the block's final hidden states).
+# ---------------------------------------------------------------------------
+
+def test_lm_head_logits_brute_force_and_unit_weights():
+    rng = np.random.default_rng(3)
+    n_req, D, H, V = 2, 3, 64, 37
+    hidden = synth.f32_to_bf16_bits(rng.standard_normal((n_req, D, H), dtype=np.float32))
+    weight = synth.f32_to_bf16_bits(rng.standard_normal((V, H), dtype=np.float32))
+    got = oracle.lm_head_logits(hidden, weight)
+    hf = synth.bf16_bits_to_f32(hidden).astype(np.float64)
+    wf = synth.bf16_bits_to_f32(weight).astype(np.float64)
+    for r in range(n_req):
+        for i in range(D):
+            for v in range(V):
+                want = math.fsum(float(hf[r, i, h]) * float(wf[v, h]) for h in range(H))
+                assert abs(got[r, i, v] - want) <= 1e-12 * (1 + abs(want))
+    # unit weight rows pick single hidden components exactly
+    unit = np.zeros((H, H), np.float32)
+    unit[np.arange(H), (np.arange(H) * 7) % H] = 1.0
+    picked = oracle.lm_head_logits(hidden, synth.f32_to_bf16_bits(unit))
+    np.testing.assert_array_equal(picked, hf[:, :, (np.arange(H) * 7) % H])
+
+
+def test_lm_head_planted_tokens_win():
+    """The generator's planted weight rows (a scaled copy of a masked row's hidden
+    state) give that row a logit near the gain, far above the rest."""
+    st = synth.lmhead_step(2)
+    logits = oracle.lm_head_logits(st["hidden"], st["weight"])
+    for r, i, v_star in st["planted"]:
+        assert int(np.argmax(logits[r, i])) == v_star
+        assert logits[r, i, v_star] > 12.0

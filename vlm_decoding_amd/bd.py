@@ -30,6 +30,11 @@ class BdCommitDesc(ctypes.Structure):
                 ("S", ctypes.c_int32), ("tau", ctypes.c_float)]
 
 
+class BdLmheadDesc(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("D", ctypes.c_int32), ("V", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("S", ctypes.c_int32), ("tau", ctypes.c_float)]
+
+
 class BdError(RuntimeError):
     def __init__(self, fn, status, lib):
         msg = lib.bd_status_string(status).decode()
@@ -53,6 +58,7 @@ def _load():
     i32 = ctypes.c_int32
     AD = ctypes.POINTER(BdAttnDesc)
     CD = ctypes.POINTER(BdCommitDesc)
+    LD = ctypes.POINTER(BdLmheadDesc)
     sig = {
         "bd_attn_workspace_bytes": (sz, [AD]),
         "bd_attn_step": (i32, [AD, P, P, P, P, P, P, P, P, sz, P]),
@@ -61,6 +67,8 @@ def _load():
         "bd_verify_workspace_bytes": (sz, [i32, i32, i32]),
         "bd_spec_verify": (i32, [i32, i32, i32, P, P, P, P, P, sz, P]),
         "bd_kv_append": (i32, [AD, P, P, P, P, P, P, P, P]),
+        "bd_lmhead_workspace_bytes": (sz, [LD]),
+        "bd_lmhead_confidence_commit": (i32, [LD, P, P, P, P, P, P, P, P, P, sz, P]),
         "bd_status_string": (ctypes.c_char_p, [i32]),
         "bd_last_hip_error": (i32, []),
     }
@@ -148,3 +156,20 @@ def bd_kv_append(desc, k_cache, v_cache, prefix_len, k_blk, v_blk, n_accept=None
     _check("bd_kv_append", lib.bd_kv_append(
         ctypes.byref(desc), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len), _ptr(k_blk), _ptr(v_blk),
         _ptr(n_accept), _ptr(dev_err), _stream(stream)))
+
+
+def lmhead_desc(n_req, D, V, H, S, tau):
+    return BdLmheadDesc(n_req, D, V, H, S, tau)
+
+
+def bd_lmhead_workspace_bytes(desc):
+    return lib.bd_lmhead_workspace_bytes(ctypes.byref(desc))
+
+
+def bd_lmhead_confidence_commit(desc, hidden, weight, masked, tokens, conf=None, argmax=None, committed=None,
+                                n_committed=None, workspace=None, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bd_lmhead_confidence_commit", lib.bd_lmhead_confidence_commit(
+        ctypes.byref(desc), _ptr(hidden), _ptr(weight), _ptr(masked), _ptr(tokens), _ptr(conf), _ptr(argmax),
+        _ptr(committed), _ptr(n_committed), _ptr(workspace), workspace_bytes, _stream(stream)))

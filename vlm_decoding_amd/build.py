@@ -7,7 +7,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbd.so")
-SOURCES = ["bd_api.hip", "bd_attn.hip", "bd_rows.hip"]
+SOURCES = ["bd_api.hip", "bd_attn.hip", "bd_rows.hip", "bd_lmhead.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -44,6 +44,14 @@ bd_status check_rows(int32_t n_req, int32_t D, int32_t V) {
     return BD_OK;
 }
 
+bd_status check_lmhead_desc(const bd_lmhead_desc *d) {
+    if (!d) return BD_E_NULL;
+    if (d->n_req < 1 || d->D < 1 || d->D > 64 || (int64_t)d->n_req * d->D > 16) return BD_E_SHAPE;
+    if (d->V < 2 || d->H < 256 || d->H % 256 != 0 || d->H > 4096) return BD_E_SHAPE;
+    if (d->S < 1 || isnan(d->tau)) return BD_E_PARAM;
+    return BD_OK;
+}
+
 bd_status launched(hipError_t e) {
     if (e != hipSuccess) {
         g_last_hip_error = (int32_t)e;
@@ -171,6 +179,42 @@ bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache, i
     return launched(bd::launch_kv_append(desc->n_items, desc->D, desc->Hkv, desc->d, desc->cap,
                                          desc->dtype == BD_F32 ? 4 : 2, k_cache, v_cache, prefix_len, k_blk,
                                          v_blk, n_accept, dev_err, (hipStream_t)stream));
+}
+
+size_t bd_lmhead_workspace_bytes(const bd_lmhead_desc *desc) {
+    if (check_lmhead_desc(desc) != BD_OK) return SIZE_MAX;
+    const bd::LhPlan pl = bd::plan_lmhead(desc->n_req, desc->D, desc->V, desc->H);
+    return pl.ok ? pl.ws_bytes : SIZE_MAX;
+}
+
+bd_status bd_lmhead_confidence_commit(const bd_lmhead_desc *desc, const void *hidden, const void *weight,
+                                      uint8_t *masked, int32_t *tokens, float *conf, int32_t *argmax,
+                                      uint8_t *committed, int32_t *n_committed, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
+    bd_status st = check_lmhead_desc(desc);
+    if (st != BD_OK) return st;
+    if (!hidden || !weight || !masked || !tokens) return BD_E_NULL;
+    if (!aligned16(hidden) || !aligned16(weight)) return BD_E_PARAM;
+    const bd::LhPlan pl = bd::plan_lmhead(desc->n_req, desc->D, desc->V, desc->H);
+    if (!pl.ok) return BD_E_SHAPE;
+    if (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)) return BD_E_WORKSPACE;
+    bd::LhArgs a{};
+    a.hidden = hidden;
+    a.weight = weight;
+    a.masked = masked;
+    a.tokens = tokens;
+    a.conf = conf;
+    a.argmax = argmax;
+    a.committed = committed;
+    a.n_committed = n_committed;
+    a.ws = workspace;
+    a.n_req = desc->n_req;
+    a.D = desc->D;
+    a.V = desc->V;
+    a.H = desc->H;
+    a.S = desc->S;
+    a.tau = desc->tau;
+    return launched(bd::launch_lmhead(pl, a, (hipStream_t)stream));
 }
 
 const char *bd_status_string(bd_status s) {

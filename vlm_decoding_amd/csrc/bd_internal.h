@@ -63,6 +63,32 @@ struct RowArgs {
 hipError_t launch_confidence_commit(const RowPlan &plan, const RowArgs &a, hipStream_t s);
 hipError_t launch_spec_verify(const RowPlan &plan, const RowArgs &a, hipStream_t s);
 
+// ---- LM head + confidence + commit ------------------------------------------
+struct LhPlan {
+    int R;               // block slots = n_req * D (<= 16)
+    int tiles;           // 16-row vocabulary tiles
+    int tiles_per_wave;
+    int G;               // workgroups
+    size_t lds;          // dynamic LDS: the hidden states, 16 rows of H + 8
+    size_t ms_off, i_off, cnt_off, ws_bytes;
+    bool ok;             // G within the finisher's reach
+};
+LhPlan plan_lmhead(int n_req, int D, int V, int H);
+
+struct LhArgs {
+    const void *hidden, *weight;
+    uint8_t *masked;
+    int32_t *tokens;
+    float *conf;
+    int32_t *argmax;
+    uint8_t *committed;
+    int32_t *n_committed;
+    void *ws;
+    int n_req, D, V, H, S;
+    float tau;
+};
+hipError_t launch_lmhead(const LhPlan &plan, const LhArgs &a, hipStream_t s);
+
 // ---- KV append --------------------------------------------------------------
 hipError_t launch_kv_append(int n, int D, int Hkv, int d, int cap, int elem_bytes, void *k_cache,
                             void *v_cache, int32_t *prefix, const void *k_blk, const void *v_blk,

@@ -18,78 +18,13 @@
 // results are identical run to run.
 #include "bd_common.h"
 #include "bd_internal.h"
+#include "bd_rowreduce.h"
 
 namespace bd {
 namespace {
 
 constexpr int NT = 256;
 constexpr int kRowLoads = 16;  // float4 loads per thread per chunk (chunk <= 16 x 1024 floats)
-
-struct Part {
-    float m;  // running maximum
-    float s;  // sum of exp(x - m)
-    int i;    // index of the first maximum
-};
-
-__device__ __forceinline__ Part combine(Part a, Part b) {
-    Part r;
-    const bool take_b = b.m > a.m || (b.m == a.m && b.i < a.i);
-    r.m = take_b ? b.m : a.m;
-    r.i = take_b ? b.i : a.i;
-    const float sa = a.m == -INFINITY ? 0.f : a.s * bd_exp2((a.m - r.m) * BD_LOG2E);
-    const float sb = b.m == -INFINITY ? 0.f : b.s * bd_exp2((b.m - r.m) * BD_LOG2E);
-    r.s = sa + sb;
-    return r;
-}
-
-template <bool WITH_SUM>
-__device__ __forceinline__ void push(Part &p, float x, int idx) {
-    if (x > p.m) {
-        if (WITH_SUM) p.s = p.s * bd_exp2((p.m - x) * BD_LOG2E) + 1.0f;
-        p.m = x;
-        p.i = idx;
-    } else if (WITH_SUM) {
-        p.s += bd_exp2((x - p.m) * BD_LOG2E);
-    }
-}
-
-// Lane exchanges without an LDS round trip.  combine() is commutative, so both
-// lanes of every exchanged pair compute the same value and, after a full tree,
-// every lane of the group holds the group's result.  The tree is fixed, so
-// the result does not depend on timing.
-template <int CTRL>  // gfx9 DPP control inside 16-lane rows
-__device__ __forceinline__ Part dpp_part(Part p) {
-    Part o;
-    o.m = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p.m), CTRL, 0xf, 0xf, false));
-    o.s = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(p.s), CTRL, 0xf, 0xf, false));
-    o.i = __builtin_amdgcn_update_dpp(0, p.i, CTRL, 0xf, 0xf, false);
-    return combine(p, o);
-}
-// Reduce over the 16 lanes of each DPP row: lane ^ 1, lane ^ 2 (quad
-// permutes), then the 8-lane and 16-lane mirrors.
-__device__ __forceinline__ Part reduce16(Part p) {
-    p = dpp_part<0xB1>(p);   // quad_perm [1,0,3,2]
-    p = dpp_part<0x4E>(p);   // quad_perm [2,3,0,1]
-    p = dpp_part<0x141>(p);  // row_half_mirror
-    return dpp_part<0x140>(p);  // row_mirror
-}
-// Exchange with the lane 16 (row pair) or 32 (half) lanes away: the swap hands
-// both lanes the same ordered pair (lower group's value, upper group's value).
-template <bool HALVES>
-__device__ __forceinline__ Part swap_part(Part p) {
-    const unsigned m = __float_as_uint(p.m), s = __float_as_uint(p.s), i = (unsigned)p.i;
-    const auto rm = HALVES ? __builtin_amdgcn_permlane32_swap(m, m, false, false)
-                           : __builtin_amdgcn_permlane16_swap(m, m, false, false);
-    const auto rs = HALVES ? __builtin_amdgcn_permlane32_swap(s, s, false, false)
-                           : __builtin_amdgcn_permlane16_swap(s, s, false, false);
-    const auto ri = HALVES ? __builtin_amdgcn_permlane32_swap(i, i, false, false)
-                           : __builtin_amdgcn_permlane16_swap(i, i, false, false);
-    return combine(Part{__uint_as_float(rm[0]), __uint_as_float(rs[0]), (int)ri[0]},
-                   Part{__uint_as_float(rm[1]), __uint_as_float(rs[1]), (int)ri[1]});
-}
-__device__ __forceinline__ Part wave_reduce(Part p) {
-    return swap_part<true>(swap_part<false>(reduce16(p)));
-}
 
 struct RowParams {
     const float *logits;
@@ -219,7 +154,6 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     }
     __syncthreads();
     if (w != 0) return;
-    const bool part_i = lane < p.D && (VERIFY || ((s_mask >> lane) & 1ull));
     if (VERIFY) {
         const int a = lane < p.D ? s_arg[lane] : 0;
         const bool bad = lane < p.D && a != p.draft[ob + lane];
@@ -231,43 +165,10 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         }
         return;
     }
-    // Commit, one lane per slot: rank = number of masked slots ahead in
-    // (confidence desc, index asc); the confidences are read as 16-byte LDS
-    // broadcasts, sixteen slots per round.
-    const float cf = part_i ? s_conf[lane] : __int_as_float(0x7fc00000);
-    const int am = part_i ? s_arg[lane] : -1;
-    const unsigned long long mask = s_mask;
-    const int k = min((p.D + p.S - 1) / p.S, s_nm);
-    int rank = 0;
-    for (int j0 = 0; j0 < p.D; j0 += 16) {
-        float cj[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 c4 = *reinterpret_cast<const float4 *>(&s_conf[j0 + 4 * q]);
-            cj[4 * q] = c4.x;
-            cj[4 * q + 1] = c4.y;
-            cj[4 * q + 2] = c4.z;
-            cj[4 * q + 3] = c4.w;
-        }
-        const unsigned mj = (unsigned)(mask >> j0) & 0xffffu;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int j = j0 + e;
-            const bool ahead = ((mj >> e) & 1u) && (cj[e] > cf || (cj[e] == cf && j < lane));
-            rank += ahead ? 1 : 0;
-        }
-    }
-    const bool take = part_i && (rank < k || cf > p.tau);
-    const unsigned long long tb = __builtin_amdgcn_ballot_w64(take);
-    if (lane < p.D) {
-        if (take) {
-            p.tokens[ob + lane] = am;
-            p.masked[ob + lane] = 0;
-        }
-        if (p.conf) p.conf[ob + lane] = cf;
-        if (p.argmax) p.argmax[ob + lane] = am;
-        if (p.committed) p.committed[ob + lane] = take ? 1 : 0;
-    }
+    const unsigned long long tb = commit_request(s_conf, s_arg, s_mask, s_nm, p.D, p.S, p.tau, lane, p.masked + ob,
+                                                 p.tokens + ob, p.conf ? p.conf + ob : nullptr,
+                                                 p.argmax ? p.argmax + ob : nullptr,
+                                                 p.committed ? p.committed + ob : nullptr);
     if (lane == 0) {
         if (p.n_committed) p.n_committed[r] = __popcll(tb);
         bd_coherent_store(p.req_cnt + r, 0);
