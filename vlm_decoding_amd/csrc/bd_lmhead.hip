@@ -13,10 +13,12 @@
 // Layout of the work.  The R <= 16 slots are the N dimension of
 // v_mfma_f32_16x16x32_bf16; vocabulary rows are its M dimension.  Every wave
 // owns a contiguous range of 16-row vocabulary tiles and runs through them
-// with the weight loads three 64-column blocks ahead (register ring), so its
-// loads never wait on its MFMAs.  Each lane loads 32 contiguous bytes of one
-// weight row per block; the hidden states sit in LDS (rows padded by 16
-// bytes, so the 16 rows of one MFMA operand fall in distinct banks).  The
+// with the weight loads three 256-column blocks ahead (register ring), so its
+// loads never wait on its MFMAs.  Load j of a step covers columns 32j..32j+31
+// of the block for all 16 rows (each row's 64 bytes contiguous; a step reads
+// 512 contiguous bytes of every row, which measured faster than narrower
+// steps); the hidden states sit in LDS (rows padded by 16 bytes, so the 16
+// rows of one MFMA operand fall in distinct banks).  The
 // workgroup's per-slot partials go out with write-through stores; the last
 // workgroup (one ticket) merges them in workgroup order and commits.  No float
 // atomics: results are identical run to run.
@@ -29,8 +31,9 @@ namespace {
 
 constexpr int LH_NT = 256;      // four waves
 constexpr int LH_SLOTS = 16;    // MFMA N dimension (slots, zero-padded)
-constexpr int LH_BLK = 64;      // hidden columns per pipeline step (two MFMAs)
+constexpr int LH_BLK = 256;     // hidden columns per pipeline step (eight MFMAs)
 constexpr int LH_RING = 4;      // register ring: loads run LH_RING - 1 steps ahead
+constexpr int LH_LPS = LH_BLK / 32;  // 16-byte loads (and MFMAs) per lane and step
 
 struct LhParams {
     const uint16_t *hidden, *weight;
@@ -71,26 +74,26 @@ __global__ __launch_bounds__(LH_NT, 2) void lmhead_kernel(LhParams p) {
     }
     __syncthreads();
 
-    // This wave's tiles and pipeline steps (tile-major, 64 hidden columns a step).
+    // This wave's tiles and pipeline steps (tile-major, LH_BLK hidden columns a step).
     const int gw = blockIdx.x * (LH_NT / 64) + w;
     const int t_beg = min(p.tiles, gw * p.tiles_per_wave);
     const int t_end = min(p.tiles, t_beg + p.tiles_per_wave);
     const int nsteps = (t_end - t_beg) * NHB;
     const int n = lane & 15;    // slot column of the MFMA operands and results
-    const int kq = lane >> 4;   // which 16 columns of the 64-column block
-    const uint16_t *xrow = xs + n * XS + 16 * kq;
+    const int kq = lane >> 4;   // which 8 columns of each 32-column MFMA chunk
+    const uint16_t *xrow = xs + n * XS + 8 * kq;
 
     // Every step has the same shape - issue the loads of step q + 3, then two
     // MFMAs on the block loaded three steps earlier - so the compiler can wait
     // for exactly the loads it needs.  The step count is rounded up to the
     // ring size; loads past the wave's last step read one fixed, cached row.
-    uint4 ring[LH_RING][2];
+    uint4 ring[LH_RING][LH_LPS];
     int lt = t_beg, lb = 0;  // load cursor: tile, column block
-    auto load = [&](uint4 (&dst)[2], bool real) __attribute__((always_inline)) {
+    auto load = [&](uint4 (&dst)[LH_LPS], bool real) __attribute__((always_inline)) {
         const int vrow = min(lt * 16 + n, p.V - 1);  // rows past V are formed but never used
-        const uint16_t *src = real ? p.weight + (size_t)vrow * p.H + lb * LH_BLK + 16 * kq : p.weight;
-        dst[0] = *reinterpret_cast<const uint4 *>(src);
-        dst[1] = *reinterpret_cast<const uint4 *>(src + 8);
+        const uint16_t *src = real ? p.weight + (size_t)vrow * p.H + lb * LH_BLK + 8 * kq : p.weight;
+#pragma unroll
+        for (int j = 0; j < LH_LPS; ++j) dst[j] = *reinterpret_cast<const uint4 *>(src + 32 * j);
         if (++lb == NHB) {
             lb = 0;
             ++lt;
@@ -106,10 +109,14 @@ __global__ __launch_bounds__(LH_NT, 2) void lmhead_kernel(LhParams p) {
         constexpr int J = decltype(slot)::value;
         load(ring[(J + LH_RING - 1) % LH_RING], q + LH_RING - 1 < nsteps);
         if (q < nsteps) {
-            const bf16x8 x0 = *reinterpret_cast<const bf16x8 *>(xrow + cb * LH_BLK);
-            const bf16x8 x1 = *reinterpret_cast<const bf16x8 *>(xrow + cb * LH_BLK + 8);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(&ring[J][0]), x0, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(&ring[J][1]), x1, acc, 0, 0, 0);
+            // MFMA j: lane (n, kq) supplies weight row n and slot n's hidden state at
+            // the same eight columns, 32j + 8kq .. +7 of the block.
+#pragma unroll
+            for (int j = 0; j < LH_LPS; ++j) {
+                const bf16x8 xj = *reinterpret_cast<const bf16x8 *>(xrow + cb * LH_BLK + 32 * j);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(&ring[J][j]), xj, acc,
+                                                              0, 0, 0);
+            }
             if (++cb == NHB) {
                 // Tile done: this lane holds vocabulary rows 16*ct + 4*kq + i of slot n.
 #pragma unroll
