@@ -10,6 +10,7 @@ Each wrapper names the passage its C function follows.
 """
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -20,7 +21,7 @@ _SRC = os.path.join(_HERE, "bd_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, FP8 = 0, 1, 2
 BIDIR, CAUSAL = 0, 1
 
 
@@ -55,6 +56,8 @@ def _load():
         lib.bdo_softmax_partial.argtypes = [i32, i32, P, P, P, P, P]
         lib.bdo_merge_partials.argtypes = [i32, i32, P, P, P, P]
         lib.bdo_lm_head_logits.argtypes = [i32, i32, i32, P, P, P]
+        lib.bdo_attention_fp8kv.argtypes = [i32] * 7 + [ctypes.c_double] + [P] * 9
+        lib.bdo_fp8_e4m3_decode.argtypes = [i32, P, P]
         _lib = lib
     return _lib
 
@@ -205,4 +208,34 @@ def lm_head_logits(hidden, weight):
     w = _c(weight, np.uint16)
     out = np.zeros((n_req, D, V), np.float64)
     lib.bdo_lm_head_logits(n_req * D, V, H, _ptr(h), _ptr(w), _ptr(out))
+    return out
+
+
+def attention_fp8kv(q, k_blk, v_blk, k_cache, v_cache, k_scale, v_scale, prefix, mode, scale=None):
+    """Block attention with an FP8 KV cache (the same mask rules as attention()):
+    q raw bf16; k_blk, v_blk, k_cache, v_cache raw OCP E4M3 bytes in the same
+    layouts; every key / value is its byte's E4M3 value times the fp32 scale of its
+    (item, KV head), k_scale / v_scale [n][Hkv].  Returns fp64 [n][D][Hq][d]."""
+    lib = _load()
+    n, D, Hq, d = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q = _c(q, np.uint16)
+    kb, vb = _c(k_blk, np.uint8), _c(v_blk, np.uint8)
+    kc, vc = _c(k_cache, np.uint8), _c(v_cache, np.uint8)
+    ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    pre = _c(prefix, np.int32)
+    out = np.zeros((n, D, Hq, d), np.float64)
+    lib.bdo_attention_fp8kv(n, D, Hq, Hkv, d, cap, int(mode), float(scale), _ptr(q), _ptr(kb), _ptr(vb),
+                            _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(pre), _ptr(out))
+    return out
+
+
+def fp8_e4m3_decode(b):
+    """OCP FP8 E4M3 bytes -> fp64 (the decode the FP8-KV attention applies)."""
+    lib = _load()
+    b = _c(b, np.uint8)
+    out = np.zeros(b.shape, np.float64)
+    lib.bdo_fp8_e4m3_decode(b.size, _ptr(b), _ptr(out))
     return out

@@ -50,8 +50,20 @@
 #define BDO_BIDIR 0
 #define BDO_CAUSAL 1
 
+#define BDO_FP8 2  /* OCP FP8 E4M3 ("e4m3fn") */
+
+/* OCP FP8 E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0
+ * holds the subnormals m/8 * 2^-6; S.1111.111 is NaN; no infinities. */
+static double fp8_e4m3(uint8_t b) {
+    const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
 static double widen(const void *base, int dtype, size_t idx) {
     if (dtype == BDO_F32) return (double)((const float *)base)[idx];
+    if (dtype == BDO_FP8) return fp8_e4m3(((const uint8_t *)base)[idx]);
     uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
     float f;
     memcpy(&f, &bits, sizeof f);
@@ -81,10 +93,37 @@ int bdo_num_threads(void) {
  * k_cache [n][Hkv][cap][d], v_cache [n][Hkv][d][cap] (transposed),
  * out [n][D][Hq][d] double.
  */
+static void attention_impl(int n, int D, int Hq, int Hkv, int d, int cap, int q_dtype, int kv_dtype,
+                           int mode, double scale, const void *q, const void *k_blk, const void *v_blk,
+                           const void *k_cache, const void *v_cache, const float *k_scale,
+                           const float *v_scale, const int32_t *prefix_len, double *out);
+
 void bdo_attention(int n, int D, int Hq, int Hkv, int d, int cap, int dtype, int mode,
                    double scale, const void *q, const void *k_blk, const void *v_blk,
                    const void *k_cache, const void *v_cache, const int32_t *prefix_len,
                    double *out) {
+    attention_impl(n, D, Hq, Hkv, d, cap, dtype, dtype, mode, scale, q, k_blk, v_blk, k_cache, v_cache,
+                   NULL, NULL, prefix_len, out);
+}
+
+/*
+ * The same block attention with an FP8 KV cache: queries bf16, every key and
+ * value (cache and block) an OCP E4M3 byte times the fp32 scale of its
+ * (item, KV head), k_scale / v_scale [n][Hkv]:
+ *   k_j = e4m3(K_j) * k_scale[n][g],  v_j = e4m3(V_j) * v_scale[n][g].
+ */
+void bdo_attention_fp8kv(int n, int D, int Hq, int Hkv, int d, int cap, int mode, double scale,
+                         const void *q, const void *k_blk, const void *v_blk, const void *k_cache,
+                         const void *v_cache, const float *k_scale, const float *v_scale,
+                         const int32_t *prefix_len, double *out) {
+    attention_impl(n, D, Hq, Hkv, d, cap, BDO_BF16, BDO_FP8, mode, scale, q, k_blk, v_blk, k_cache, v_cache,
+                   k_scale, v_scale, prefix_len, out);
+}
+
+static void attention_impl(int n, int D, int Hq, int Hkv, int d, int cap, int q_dtype, int kv_dtype,
+                           int mode, double scale, const void *q, const void *k_blk, const void *v_blk,
+                           const void *k_cache, const void *v_cache, const float *k_scale,
+                           const float *v_scale, const int32_t *prefix_len, double *out) {
     const int group = Hq / Hkv;
     long total = (long)n * D * Hq;
 #ifdef _OPENMP
@@ -107,10 +146,11 @@ void bdo_attention(int n, int D, int Hq, int Hkv, int d, int cap, int dtype, int
             for (int t = 0; t < d; ++t) {
                 double kv;
                 if (j < P)
-                    kv = widen(k_cache, dtype, (((size_t)it * Hkv + g) * cap + j) * (size_t)d + t);
+                    kv = widen(k_cache, kv_dtype, (((size_t)it * Hkv + g) * cap + j) * (size_t)d + t);
                 else
-                    kv = widen(k_blk, dtype, (((size_t)it * D + (j - P)) * Hkv + g) * (size_t)d + t);
-                acc += widen(q, dtype, qoff + t) * kv;
+                    kv = widen(k_blk, kv_dtype, (((size_t)it * D + (j - P)) * Hkv + g) * (size_t)d + t);
+                if (k_scale) kv *= (double)k_scale[(size_t)it * Hkv + g];
+                acc += widen(q, q_dtype, qoff + t) * kv;
             }
             s[j] = scale * acc;
             if (s[j] > m) m = s[j];
@@ -126,9 +166,10 @@ void bdo_attention(int n, int D, int Hq, int Hkv, int d, int cap, int dtype, int
                 if (s[j] == 0.0) continue;
                 double vv;
                 if (j < P)
-                    vv = widen(v_cache, dtype, (((size_t)it * Hkv + g) * d + t) * (size_t)cap + j);
+                    vv = widen(v_cache, kv_dtype, (((size_t)it * Hkv + g) * d + t) * (size_t)cap + j);
                 else
-                    vv = widen(v_blk, dtype, (((size_t)it * D + (j - P)) * Hkv + g) * (size_t)d + t);
+                    vv = widen(v_blk, kv_dtype, (((size_t)it * D + (j - P)) * Hkv + g) * (size_t)d + t);
+                if (v_scale) vv *= (double)v_scale[(size_t)it * Hkv + g];
                 acc += s[j] * vv;
             }
             out[qoff + t] = acc / denom;
@@ -348,4 +389,9 @@ void bdo_lm_head_logits(int R, int V, int H, const uint16_t *hidden, const uint1
                 acc += widen(hidden, BDO_BF16, (size_t)r * H + h) * widen(weight, BDO_BF16, (size_t)v * H + h);
             out[(size_t)r * V + v] = acc;
         }
+}
+
+/* Decode OCP FP8 E4M3 bytes (the definition used by the FP8-KV attention). */
+void bdo_fp8_e4m3_decode(int n, const uint8_t *b, double *out) {
+    for (int i = 0; i < n; ++i) out[i] = fp8_e4m3(b[i]);
 }

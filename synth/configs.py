@@ -14,6 +14,7 @@ deviation 2.  Nothing here computes any part of the method.
 
 F32 = 0
 BF16 = 1
+FP8KV = 2   # bf16 queries, OCP E4M3 keys and values with one fp32 scale per (item, KV head)
 
 BIDIR = 0   # denoise step: the whole current block is visible to each slot
 CAUSAL = 1  # verify step: slot i sees the block only up to itself

@@ -29,7 +29,7 @@ token ids, logits, then plants.
 
 import numpy as np
 
-from .configs import BF16, CONFIGS, F32, LMHEAD_CONFIGS, lmhead_seed_of, seed_of
+from .configs import BF16, CONFIGS, F32, FP8KV, LMHEAD_CONFIGS, lmhead_seed_of, seed_of
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -44,6 +44,27 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen raw bf16 patterns to float32 exactly."""
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# The non-negative finite OCP FP8 E4M3 values (exponent bias 7, 3 mantissa bits,
+# subnormals below 2^-6, 448 the largest; S.1111.111 is NaN), as a sorted table of
+# (value, code) used to round float32 data to the nearest E4M3 code.
+_E4M3_CODES = np.array([c for c in range(0x7F)], dtype=np.uint8)
+_E4M3_VALUES = np.array([((c & 7) / 8.0) * 2.0 ** -6 if (c >> 3) == 0 else (1 + (c & 7) / 8.0) * 2.0 ** ((c >> 3) - 7)
+                         for c in range(0x7F)], dtype=np.float64)
+E4M3_NAN = np.uint8(0x7F)
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest OCP E4M3 code (ties to an even code), saturating at +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_VALUES, a), 1, len(_E4M3_VALUES) - 1)
+    lo = hi - 1
+    dlo, dhi = a - _E4M3_VALUES[lo], _E4M3_VALUES[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(_E4M3_CODES[lo] % 2 == 0, lo, hi)))
+    code = _E4M3_CODES[pick]
+    return np.where(x < 0, code | np.uint8(0x80), code).astype(np.uint8)
 
 
 def _normal(rng, shape, dtype):
@@ -84,6 +105,8 @@ def make_step(p: dict, seed: int, plant_L=None) -> dict:
         raise ValueError(kind)
     max_prefix = int(prefix.max()) if n else 0
     cap = p.get("cap") or cache_capacity(max_prefix, D)
+    if dtype == FP8KV:
+        return _make_step_fp8kv(p, rng, prefix, cap, plant_L, seed)
     elem = np.uint16 if dtype == BF16 else np.float32
     nan = BF16_NAN if dtype == BF16 else np.float32(np.nan)
 
@@ -191,3 +214,39 @@ def lmhead_step(cfg_id: int, **overrides) -> dict:
     p = dict(LMHEAD_CONFIGS[cfg_id])
     p.update(overrides)
     return make_lmhead(p, lmhead_seed_of(cfg_id))
+
+
+def _make_step_fp8kv(p, rng, prefix, cap, plant_L, seed):
+    """The FP8-KV variant of make_step: queries bf16; the cache and block keys and
+    values drawn as float32 N(0, 1) in make_step's order, then stored as OCP E4M3
+    codes of value / scale, one fp32 scale per (item, KV head): the largest
+    magnitude over that head's valid cache entries and block entries, over 448.
+    Cache slots past the prefix hold the E4M3 NaN code.  Logits, masked set and
+    plants follow make_step (a bf16-dtype draw of the same parameters)."""
+    n, D, Hq, Hkv, d = p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"]
+    q = _normal(rng, (n, D, Hq, d), BF16)
+    kf = [rng.standard_normal(size=(Hkv, int(prefix[it]), d), dtype=np.float32) for it in range(n)]
+    vf = [rng.standard_normal(size=(Hkv, int(prefix[it]), d), dtype=np.float32) for it in range(n)]
+    kbf = rng.standard_normal(size=(n, D, Hkv, d), dtype=np.float32)
+    vbf = rng.standard_normal(size=(n, D, Hkv, d), dtype=np.float32)
+    k_scale = np.zeros((n, Hkv), np.float32)
+    v_scale = np.zeros((n, Hkv), np.float32)
+    for it in range(n):
+        for g in range(Hkv):
+            k_scale[it, g] = max(float(np.abs(kf[it][g]).max(initial=0.0)), float(np.abs(kbf[it, :, g]).max())) / 448.0
+            v_scale[it, g] = max(float(np.abs(vf[it][g]).max(initial=0.0)), float(np.abs(vbf[it, :, g]).max())) / 448.0
+    k_cache = np.full((n, Hkv, cap, d), E4M3_NAN, dtype=np.uint8)
+    v_cache = np.full((n, Hkv, d, cap), E4M3_NAN, dtype=np.uint8)
+    k_blk = np.zeros((n, D, Hkv, d), np.uint8)
+    v_blk = np.zeros((n, D, Hkv, d), np.uint8)
+    for it in range(n):
+        P = int(prefix[it])
+        for g in range(Hkv):
+            k_cache[it, g, :P, :] = f32_to_e4m3_bits(kf[it][g] / k_scale[it, g])
+            v_cache[it, g, :, :P] = f32_to_e4m3_bits(vf[it][g] / v_scale[it, g]).T
+            k_blk[it, :, g, :] = f32_to_e4m3_bits(kbf[it, :, g] / k_scale[it, g])
+            v_blk[it, :, g, :] = f32_to_e4m3_bits(vbf[it, :, g] / v_scale[it, g])
+    rest = make_step(dict(p, dtype=BF16, n_items=1, prefix=("fixed", 0), Hq=1, Hkv=1, d=8), seed + 7919)
+    return dict(params=p, seed=seed, cap=cap, prefix=prefix, q=q, k_cache=k_cache, v_cache=v_cache,
+                k_blk=k_blk, v_blk=v_blk, k_scale=k_scale, v_scale=v_scale, masked=rest["masked"],
+                tokens=rest["tokens"], logits=rest["logits"], **{k: rest[k] for k in ("draft", "planted_L") if k in rest})

@@ -517,3 +517,39 @@ def test_lm_head_planted_tokens_win():
     for r, i, v_star in st["planted"]:
         assert int(np.argmax(logits[r, i])) == v_star
         assert logits[r, i, v_star] > 12.0
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) KV cache variant of the block attention.
+# ---------------------------------------------------------------------------
+
+def test_fp8_e4m3_decode_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.fp8_e4m3_decode(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2  # 0x7F and 0xFF
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+@pytest.mark.parametrize("mode", [oracle.BIDIR, oracle.CAUSAL])
+def test_attention_fp8kv_equals_attention_on_dequantized_values(mode):
+    """With power-of-two scales every dequantized key / value is exact in fp32, so the
+    FP8-KV oracle must agree with the plain oracle fed those fp32 values."""
+    p = synth.params_for(1, n_items=2, D=5, prefix=("list", [37, 70]), Hq=4, Hkv=2, d=64, dtype=synth.FP8KV)
+    st = synth.make_step(p, 21)
+    ks = np.exp2(np.round(np.log2(st["k_scale"]))).astype(np.float32)
+    vs = np.exp2(np.round(np.log2(st["v_scale"]))).astype(np.float32)
+    got = oracle.attention_fp8kv(st["q"], st["k_blk"], st["v_blk"], st["k_cache"], st["v_cache"], ks, vs,
+                                 st["prefix"], mode)
+    dec = lambda a, sc, axis_g: (oracle.fp8_e4m3_decode(a) * np.expand_dims(sc, axis=tuple(
+        i for i in range(a.ndim) if i not in (0, axis_g)))).astype(np.float32)
+    qf = synth.bf16_bits_to_f32(st["q"])
+    kc = dec(st["k_cache"], ks, 1)
+    vc = dec(st["v_cache"], vs, 1)
+    kb = dec(st["k_blk"], ks, 2)
+    vb = dec(st["v_blk"], vs, 2)
+    # NaN canaries past the prefix stay NaN in the dequantized cache and must not be read
+    want = oracle.attention(qf, kb, vb, kc, vc, st["prefix"], mode)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
