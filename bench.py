@@ -18,7 +18,10 @@ its average duration from HIP events recorded on the launch stream around
 the calls of every 10th timed step (--event-stride; an event record costs the
 GPU a few microseconds, so instrumenting every step would slow the steps it
 measures).  ``value`` is steps over the wall time of all timed steps.
-``cpu_baseline`` times the fp64 CPU oracle on the host.
+``cpu_baseline`` times the fp64 CPU oracle on the host.  Two further legs
+measure the next rows of the path beside the headline: the LM head fused with
+the confidence + commit (``lm_head_confidence_commit``) and the same attention
+call over an E4M3 KV cache (``fp8kv_attention``).
 """
 
 import argparse
@@ -61,7 +64,7 @@ def attn_source_hash():
     return h.hexdigest()
 
 
-def traffic_per_launch():
+def traffic_per_launch(key="bytes_per_launch"):
     """HBM bytes per attention launch from committed counter runs, if they still
     describe the current kernel source; else None."""
     try:
@@ -71,7 +74,7 @@ def traffic_per_launch():
         return None
     if t.get("kernel_source_sha256") != attn_source_hash():
         return None
-    return t.get("bytes_per_launch")
+    return t.get(key)
 
 
 def cpu_baseline(step, budget_s):
@@ -124,9 +127,14 @@ def write_traffic(pmc_dir, copy_bytes=256 << 20):
             acc.setdefault(name, []).append(v * 1024.0 * sc)
         for name, vals in acc.items():
             per_kernel.setdefault(name, {})[counter.lower() + "_bytes"] = sum(vals) / len(vals)
-    total = sum(v.get("fetch_size_bytes", 0.0) + v.get("write_size_bytes", 0.0) for v in per_kernel.values())
+    # The headline call is the bf16 instance pair (tile kernel <.., false>, merge
+    # <.., 32>); the E4M3 pair (<.., true>, <.., 64>) is summed on its own.
+    def launch_bytes(tags):
+        return sum(v.get("fetch_size_bytes", 0.0) + v.get("write_size_bytes", 0.0)
+                   for k, v in per_kernel.items() if k.endswith(tags))
     out = {
-        "bytes_per_launch": round(total),
+        "bytes_per_launch": round(launch_bytes((", false>", ", 32>"))),
+        "fp8kv_bytes_per_launch": round(launch_bytes((", true>", ", 64>"))),
         "per_kernel": {k: {kk: round(vv) for kk, vv in v.items()} for k, v in per_kernel.items()},
         "fetch_scale": f_scale, "write_scale": w_scale,
         "calibration": "FETCH_SIZE/WRITE_SIZE over plain %d-byte device copies (bench.py --copy-calibration)" % copy_bytes,
@@ -183,6 +191,48 @@ def bench_lmhead(torch, stream, calls=50, warmup=5):
                 frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), calls=calls)
 
 
+def bench_fp8kv_attention(torch, stream, calls=200, warmup=20):
+    """The E4M3 KV-cache variant of the headline attention call, measured beside it:
+    the same 36-layer 3B-shape step (prefix 4096, D = 16) with keys and values stored
+    as one byte each plus one fp32 scale per (layer, KV head).  Four input sets are
+    rotated as in the main loop; the timed calls run back to back between two
+    events, so the figure is the average launch-to-launch time of one call (tile
+    kernel + merge)."""
+    import ctypes
+    import synth
+    from vlm_decoding_amd import bd
+    from vlm_decoding_amd.step import DeviceStep
+    p = synth.params_for(CFG, dtype=synth.FP8KV)
+    sets = [DeviceStep(synth.make_step(p, synth.seed_of(CFG) + 1000 * k)) for k in range(N_SETS)]
+    sh = stream.cuda_stream
+    args = [(ctypes.byref(ds.adesc), ds.q.data_ptr(), ds.k_blk.data_ptr(), ds.v_blk.data_ptr(), ds.k_cache.data_ptr(),
+             ds.v_cache.data_ptr(), ds.k_scale.data_ptr(), ds.v_scale.data_ptr(), ds.prefix.data_ptr(),
+             ds.out.data_ptr(), ds.attn_ws.data_ptr(), ds.attn_ws.numel(), sh) for ds in sets]
+    call = bd.lib.bd_attn_step_fp8kv
+    status = 0
+    for i in range(warmup):
+        status |= call(*args[i % N_SETS])
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(calls):
+        status |= call(*args[i % N_SETS])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    if status:
+        raise RuntimeError("bd_attn_step_fp8kv failed (status %d)" % status)
+    us = t0.elapsed_time(t1) * 1e3 / calls
+    prefix = sets[0].prefix.cpu().numpy()
+    n, D, Hq, Hkv, d = p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"]
+    nbytes = int(np.sum(prefix.astype(np.int64) + D)) * Hkv * d * 2 + n * D * Hq * d * 2 * 2 + n * Hkv * 2 * 4
+    return dict(workload="36 layers x block attention, 16q/2kv heads, d128, prefix 4096, D=16, "
+                         "bf16 queries, E4M3 K/V cache with per-(layer, KV head) scales",
+                us_per_call=round(us, 2), algorithmic_bytes=nbytes,
+                achieved_gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                frac=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), calls=calls,
+                traffic=traffic_per_launch("fp8kv_bytes_per_launch"))
+
+
 def copy_calibration(n_bytes=256 << 20, reps=5):
     """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
     WRITE_SIZE for this copy kernel give the scale between counter readings and
@@ -205,6 +255,8 @@ def main():
                     help="record the per-call HIP events on every N-th timed step (0: none)")
     ap.add_argument("--lmhead-calls", type=int, default=50,
                     help="timed calls of the fused LM head + confidence + commit (0 to skip)")
+    ap.add_argument("--fp8kv-calls", type=int, default=200,
+                    help="timed calls of the E4M3 KV-cache attention variant (0 to skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -317,13 +369,14 @@ def main():
     tr = traffic_per_launch()
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=tr,
-                    kernel="bd_attn_step (attn_mfma_kernel<128,4> + attn_merge_kernel<128,4>)",
+                    kernel="bd_attn_step (attn_mfma_kernel<128, 4, false> + attn_merge_kernel<128, 4, 32>)",
                     kernel_avg_us=round(attn_avg_s * 1e6, 2),
                     kernel_p10_p90_us=[round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
                                        round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
                     algorithmic_bytes_per_launch=attn_bytes)
 
     lmhead = bench_lmhead(torch, stream, calls=args.lmhead_calls) if args.lmhead_calls > 0 else None
+    fp8kv = bench_fp8kv_attention(torch, stream, calls=args.fp8kv_calls) if args.fp8kv_calls > 0 else None
 
     cpu = None
     if args.cpu_budget > 0:
@@ -361,6 +414,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "lm_head_confidence_commit": lmhead,
+        "fp8kv_attention": fp8kv,
     }
     print(json.dumps(out), flush=True)
 

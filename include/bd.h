@@ -68,7 +68,7 @@ typedef int32_t bd_status;
 #define BD_E_WORKSPACE 5 /* workspace missing or too small */
 #define BD_E_LAUNCH 6    /* the HIP runtime rejected a launch */
 
-enum { BD_F32 = 0, BD_BF16 = 1 };
+enum { BD_F32 = 0, BD_BF16 = 1, BD_FP8KV = 2 };
 enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1 };
 
 /* Shape of one block-attention call.
@@ -76,8 +76,9 @@ enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1 };
  *  D          block length, 1..64
  *  Hq, Hkv    query / KV heads, Hq % Hkv == 0; head h uses KV head h / (Hq/Hkv)
  *  d          head dim, 64 or 128
- *  cap        cache capacity in tokens, a multiple of 8
- *  dtype      BD_BF16 (MFMA path) or BD_F32 (vector path)
+ *  cap        cache capacity in tokens, a multiple of 8 (of 16 for BD_FP8KV)
+ *  dtype      BD_BF16 (MFMA path), BD_F32 (vector path) or BD_FP8KV (bf16
+ *             queries and outputs, E4M3 keys and values: bd_attn_step_fp8kv)
  *  mode       BD_BLOCK_BIDIR or BD_BLOCK_CAUSAL
  *  max_prefix host-side upper bound of every prefix_len[i], 0..cap; sizes the grid
  *  scale      softmax scale (normally 1/sqrt(d)); finite and > 0 */
@@ -110,6 +111,26 @@ bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_bl
                        const void *v_blk, const void *k_cache, const void *v_cache,
                        const int32_t *prefix_len, void *out, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* Block attention over an FP8 KV cache (desc->dtype == BD_FP8KV).  The same
+ * operation, masks and layouts as bd_attn_step (for BD_FP8KV,
+ * bd_attn_workspace_bytes sizes its workspace), with keys and values stored
+ * as one byte each in OCP FP8 E4M3 (bias 7, no infinities, 0x7F / 0xFF NaN;
+ * the FP8 rung of [FD] 5.4 and Table 4, applied here to the cache):
+ *   key   = e4m3(k_cache or k_blk byte) * k_scale[i][g]
+ *   value = e4m3(v_cache or v_blk byte) * v_scale[i][g]
+ * for item i and KV head g.  q and out are bf16 [n][D][Hq][d].
+ *   k_blk, v_blk   u8 [n][D][Hkv][d]      k_cache u8 [n][Hkv][cap][d]
+ *   v_cache        u8 [n][Hkv][d][cap]    k_scale, v_scale f32 [n][Hkv] (device)
+ * E4M3 values are widened to bf16 exactly; products and sums are fp32, the
+ * attention weights bf16, as in bd_attn_step.  Every k_scale and v_scale
+ * entry must be finite and > 0 (device values, not checked).
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE (dtype != BD_FP8KV), BD_E_PARAM,
+ * BD_E_WORKSPACE, BD_E_LAUNCH.  bd_attn_step rejects BD_FP8KV with BD_E_DTYPE. */
+bd_status bd_attn_step_fp8kv(const bd_attn_desc *desc, const void *q, const void *k_blk,
+                             const void *v_blk, const void *k_cache, const void *v_cache,
+                             const float *k_scale, const float *v_scale, const int32_t *prefix_len,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes bd_confidence_commit needs; SIZE_MAX if desc is invalid. */
 size_t bd_commit_workspace_bytes(const bd_commit_desc *desc);
@@ -148,7 +169,8 @@ bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logit
  * prefix; [DV] a finished block joins the history cache).  Uses n_items, D, Hkv, d,
  * cap and dtype of `desc`.  For item i with P = prefix_len[i] and
  * L = n_accept ? n_accept[i] : D (device values): cache slots P..P+L-1 receive block
- * slots 0..L-1 bit for bit (keys row-wise, values into the d-major layout) and
+ * slots 0..L-1 bit for bit (keys row-wise, values into the d-major layout; for
+ * BD_FP8KV the E4M3 bytes, which share the cache's per-(item, KV head) scales) and
  * prefix_len[i] becomes P + L.  Nothing else is written.  If L is outside 0..D or
  * P + L > cap, item i is left untouched and *dev_err (optional device int32) is set to 1.
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_LAUNCH. */

@@ -151,11 +151,12 @@ def spec_verify(logits, draft):
 def kv_append(k_cache, v_cache, prefix, k_blk, v_blk, n_accept=None):
     """Append accepted block K/V to the cache (Fast-dVLM write-up, section 5.3: crop
     the cache to the accepted prefix; DiffusionVL notes: a finished block joins the
-    history cache).  Returns new (k_cache, v_cache, prefix, err)."""
+    history cache).  Element type from k_cache: float32, bf16 bits (uint16) or E4M3
+    bytes (uint8).  Returns new (k_cache, v_cache, prefix, err)."""
     lib = _load()
     n, Hkv, cap, d = k_cache.shape
     D = k_blk.shape[1]
-    dtype = F32 if k_cache.dtype == np.float32 else BF16
+    dtype = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): FP8}[k_cache.dtype]
     k_cache = np.array(k_cache, copy=True, order="C")
     v_cache = np.array(v_cache, copy=True, order="C")
     prefix = np.array(prefix, dtype=np.int32, copy=True)

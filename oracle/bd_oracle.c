@@ -306,7 +306,7 @@ void bdo_spec_verify(int n_req, int D, int V, const float *logits, const int32_t
 void bdo_kv_append(int n, int D, int Hkv, int d, int cap, int dtype, void *k_cache, void *v_cache,
                    int32_t *prefix_len, const void *k_blk, const void *v_blk,
                    const int32_t *n_accept, int32_t *err) {
-    size_t es = dtype == BDO_F32 ? 4 : 2;
+    size_t es = dtype == BDO_F32 ? 4 : dtype == BDO_FP8 ? 1 : 2;
     for (int it = 0; it < n; ++it) {
         int P = prefix_len[it];
         int L = n_accept ? n_accept[it] : D;

@@ -22,16 +22,16 @@ def bd():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(bd_[a-z_]+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(bd_[a-z0-9_]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for must in ["bd_attn_step", "bd_confidence_commit", "bd_spec_verify", "bd_kv_append",
+    for must in ["bd_attn_step", "bd_attn_step_fp8kv", "bd_confidence_commit", "bd_spec_verify", "bd_kv_append",
                  "bd_lmhead_confidence_commit"]:
         assert must in names
-    assert len(names) >= 9
+    assert len(names) >= 10
 
 
 def test_library_exports_every_declared_symbol(bd):
@@ -83,6 +83,45 @@ def test_single_split_needs_no_workspace(bd):
         assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == 0
     desc32 = _attn(bd, dtype=0)
     assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc32)) == 0
+
+
+def _fp8_call(bd, desc, k_scale=1 << 20, v_scale=1 << 20, ws_bytes=1 << 30, q=1 << 20, ws=1 << 20):
+    fake = 1 << 20
+    return bd.lib.bd_attn_step_fp8kv(ctypes.byref(desc) if desc is not None else None, q, fake, fake, fake, fake,
+                                     k_scale, v_scale, fake, fake, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", BAD_ATTN + [(dict(cap=4168), "BD_E_SHAPE")])
+def test_fp8kv_attn_validation(bd, kw, code):
+    # The shape rules of bd_attn_step, plus a cache capacity that is a multiple of 16
+    # (each d-major E4M3 value row starts on a 16-byte boundary).
+    desc = _attn(bd, **dict(dict(dtype=bd.BD_FP8KV), **kw))
+    assert _fp8_call(bd, desc) == getattr(bd, code)
+    assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
+
+
+def test_fp8kv_dtype_routing_and_errors(bd):
+    fake = 1 << 20
+    fp8 = _attn(bd, dtype=bd.BD_FP8KV)
+    bf16 = _attn(bd, dtype=bd.BD_BF16)
+    # Each entry point takes only its own dtype.
+    assert _fp8_call(bd, bf16) == bd.BD_E_DTYPE
+    assert bd.lib.bd_attn_step(ctypes.byref(fp8), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 30, None) == bd.BD_E_DTYPE
+    assert _fp8_call(bd, None) == bd.BD_E_NULL
+    assert _fp8_call(bd, fp8, k_scale=None) == bd.BD_E_NULL
+    assert _fp8_call(bd, fp8, v_scale=None) == bd.BD_E_NULL
+    need = bd.lib.bd_attn_workspace_bytes(ctypes.byref(fp8))
+    assert 0 < need < bd.SIZE_MAX
+    assert _fp8_call(bd, fp8, ws_bytes=need - 1) == bd.BD_E_WORKSPACE
+    assert _fp8_call(bd, fp8, ws=None, ws_bytes=need) == bd.BD_E_WORKSPACE
+    assert _fp8_call(bd, fp8, q=fake + 2, ws_bytes=need) == bd.BD_E_PARAM
+    # 64-key E4M3 tiles: a prefix below 64 never splits.
+    for mp in (0, 32, 63):
+        desc = _attn(bd, n_items=1, max_prefix=mp, cap=128, dtype=bd.BD_FP8KV)
+        assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == 0
+    # kv_append copies E4M3 bytes; its capacity rule follows the dtype.
+    assert bd.lib.bd_kv_append(ctypes.byref(_attn(bd, dtype=bd.BD_FP8KV, cap=4168)), fake, fake, fake, fake, fake,
+                               None, None, None) == bd.BD_E_SHAPE
 
 
 BAD_COMMIT = [

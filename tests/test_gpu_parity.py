@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import synth
-from synth import BF16, BIDIR, CAUSAL, F32
+from synth import BF16, BIDIR, CAUSAL, F32, FP8KV
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def _say(msg):
 def _out_host(dev, ds):
     dev["torch"].cuda.synchronize()
     a = ds.out.cpu().numpy()
-    if ds.dtype == BF16:
+    if ds.dtype in (BF16, FP8KV):  # E4M3 K/V attention writes bf16 outputs
         return synth.bf16_bits_to_f32(a.view(np.uint16)).astype(np.float64)
     return a.astype(np.float64)
 
@@ -70,8 +70,13 @@ def _run_attention(dev, step_np, mode=None, label=""):
         np.unique(step_np["prefix"])[:8].tolist()))
     ds.attn(mode=mode)
     got = _out_host(dev, ds)
-    ref = oracle.attention(step_np["q"], step_np["k_blk"], step_np["v_blk"], step_np["k_cache"],
-                           step_np["v_cache"], step_np["prefix"], mode)
+    if p["dtype"] == FP8KV:
+        ref = oracle.attention_fp8kv(step_np["q"], step_np["k_blk"], step_np["v_blk"], step_np["k_cache"],
+                                     step_np["v_cache"], step_np["k_scale"], step_np["v_scale"],
+                                     step_np["prefix"], mode)
+    else:
+        ref = oracle.attention(step_np["q"], step_np["k_blk"], step_np["v_blk"], step_np["k_cache"],
+                               step_np["v_cache"], step_np["prefix"], mode)
     _check_attention(got, ref, label)
     return ds, got
 
@@ -138,6 +143,80 @@ def test_attention_rejects_bad_arguments_before_launch(dev):
     with pytest.raises(bd.BdError) as e:
         bd.bd_attn_step(bad, ds.q, ds.k_blk, ds.v_blk, ds.k_cache, ds.v_cache, ds.prefix, ds.out, ds.attn_ws)
     assert e.value.status == bd.BD_E_SHAPE
+
+
+# ---------------------------------------------------------------------------
+# Attention over an FP8 (E4M3) KV cache.  The bar is the bf16 one: E4M3 codes
+# widen to bf16 exactly, so the GPU's arithmetic differs from the oracle's
+# fp64 (on the same decoded values) only as the bf16 path's does.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,mode", [(3, BIDIR), (4, CAUSAL), (5, BIDIR)])
+def test_fp8kv_attention_configs(dev, cfg, mode):
+    """The 3B long-context step, the 3B verify shape and the 7B batch at full size with
+    an E4M3 cache, every output element against the oracle."""
+    _run_attention(dev, synth.config_step(cfg, dtype=FP8KV), mode=mode, label="fp8kv_cfg%d" % cfg)
+
+
+FP8_CASES = [
+    # 64-key E4M3 tiles: prefixes around tile edges, tails of one and two tiles
+    ("tail_only_P0", dict(prefix=("fixed", 0))),
+    ("P_lt_tile", dict(prefix=("fixed", 37))),
+    ("P_exact_tiles", dict(prefix=("fixed", 256))),
+    ("P_ragged64", dict(prefix=("list", [1, 63, 64, 65, 127, 128, 129, 1000]), n_items=8)),
+    ("P_ragged16", dict(prefix=("list", [15, 16, 17, 31, 33, 47, 49, 1023]), n_items=8)),
+    ("D64_two_tail_tiles", dict(D=64, prefix=("list", [63, 126]), n_items=2)),
+    ("D1_decode", dict(D=1, prefix=("fixed", 300))),
+    ("D3_rows_pad", dict(D=3, prefix=("fixed", 129))),
+    ("D64_two_row_blocks", dict(D=64, prefix=("fixed", 130))),
+    ("G7_rows224", dict(Hq=28, Hkv=4, D=32, prefix=("list", [70, 500]), n_items=2)),
+    ("d64", dict(d=64, prefix=("fixed", 333))),
+    ("d64_ragged", dict(d=64, D=32, prefix=("list", [0, 64, 65, 700]), n_items=4)),
+    ("many_items", dict(n_items=40, prefix=("fixed", 150))),
+]
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("label,ov", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8kv_attention_edge_cases(dev, label, ov, mode):
+    base = dict(n_items=2, Hq=16, Hkv=2, d=128, dtype=FP8KV, D=16, n_masked=8, V=1000, plant=None)
+    base.update(ov)
+    p = synth.params_for(3, **base)
+    _run_attention(dev, synth.make_step(p, seed=zlib.crc32(("fp8" + label).encode()) % 10000), mode=mode,
+                   label="fp8kv_" + label)
+
+
+def test_fp8kv_deterministic_append_and_reattend(dev):
+    """Repeated calls are bitwise identical; the E4M3 block appended to the cache is
+    its bytes exactly, and attention over the grown cache matches the oracle."""
+    torch = dev["torch"]
+    p = synth.params_for(3, n_items=3, dtype=FP8KV, D=16, prefix=("list", [100, 64, 1500]), V=1000,
+                         n_masked=8, plant=None)
+    s = synth.make_step(p, seed=4242)
+    ds = dev["step"].DeviceStep(s)
+    ds.attn()
+    torch.cuda.synchronize()
+    first = ds.out.clone()
+    for _ in range(2):
+        ds.out.zero_()
+        ds.attn()
+    torch.cuda.synchronize()
+    assert torch.equal(first, ds.out)
+    acc = np.array([16, 5, 0], np.int32)
+    ds.append(n_accept=torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+    kc, vc, pref, err = oracle.kv_append(s["k_cache"], s["v_cache"], s["prefix"], s["k_blk"], s["v_blk"], acc)
+    assert err == 0 and int(ds.dev_err.cpu()[0]) == 0
+    np.testing.assert_array_equal(ds.prefix.cpu().numpy(), pref)
+    assert ds.k_cache.cpu().numpy().tobytes() == kc.tobytes()
+    assert ds.v_cache.cpu().numpy().tobytes() == vc.tobytes()
+    # The same block queried again over the grown cache (the desc keeps max_prefix
+    # as the bound of the split plan; the grown prefixes stay within the capacity).
+    s2 = dict(s, k_cache=kc, v_cache=vc, prefix=pref)
+    ds.attn()
+    got = _out_host(dev, ds)
+    ref = oracle.attention_fp8kv(s2["q"], s2["k_blk"], s2["v_blk"], kc, vc, s["k_scale"], s["v_scale"], pref, BIDIR)
+    _check_attention(got, ref, "fp8kv_after_append")
 
 
 # ---------------------------------------------------------------------------

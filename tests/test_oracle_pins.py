@@ -428,6 +428,27 @@ def test_kv_append_is_bitwise_and_bounded(dtype):
     assert kc3[0].view(np.uint8).tobytes() == kc[0].view(np.uint8).tobytes()
 
 
+def test_kv_append_fp8_bytes():
+    """E4M3 caches are appended byte for byte (any code, NaN codes included)."""
+    rng = np.random.Generator(np.random.PCG64(52))
+    n, D, Hkv, d, cap = 2, 5, 2, 16, 32
+    kc = rng.integers(0, 256, size=(n, Hkv, cap, d), dtype=np.uint8)
+    vc = rng.integers(0, 256, size=(n, Hkv, d, cap), dtype=np.uint8)
+    kb = rng.integers(0, 256, size=(n, D, Hkv, d), dtype=np.uint8)
+    vb = rng.integers(0, 256, size=(n, D, Hkv, d), dtype=np.uint8)
+    prefix = np.array([3, 27], np.int32)
+    kc2, vc2, p2, err = oracle.kv_append(kc, vc, prefix, kb, vb, np.array([5, 5], np.int32))
+    assert err == 0 and p2.tolist() == [8, 32]
+    for it in range(n):
+        P = int(prefix[it])
+        np.testing.assert_array_equal(kc2[it, :, P:P + D], np.swapaxes(kb[it], 0, 1))
+        np.testing.assert_array_equal(vc2[it, :, :, P:P + D], np.transpose(vb[it], (1, 2, 0)))
+        keep = np.ones(cap, bool)
+        keep[P:P + D] = False
+        np.testing.assert_array_equal(kc2[it][:, keep], kc[it][:, keep])
+        np.testing.assert_array_equal(vc2[it][:, :, keep], vc[it][:, :, keep])
+
+
 # ---------------------------------------------------------------------------
 # Split-K merge rule (online softmax normaliser, Milakov and Gimelshein 2018):
 # any partition of the keys, merged in order, equals the unsplit softmax.

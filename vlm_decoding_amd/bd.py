@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbd.so")
 
 BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH = range(7)
-BD_F32, BD_BF16 = 0, 1
+BD_F32, BD_BF16, BD_FP8KV = 0, 1, 2
 BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL = 0, 1
 SIZE_MAX = (1 << 64) - 1
 
@@ -62,6 +62,7 @@ def _load():
     sig = {
         "bd_attn_workspace_bytes": (sz, [AD]),
         "bd_attn_step": (i32, [AD, P, P, P, P, P, P, P, P, sz, P]),
+        "bd_attn_step_fp8kv": (i32, [AD, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "bd_commit_workspace_bytes": (sz, [CD]),
         "bd_confidence_commit": (i32, [CD, P, P, P, P, P, P, P, P, sz, P]),
         "bd_verify_workspace_bytes": (sz, [i32, i32, i32]),
@@ -123,6 +124,15 @@ def bd_attn_step(desc, q, k_blk, v_blk, k_cache, v_cache, prefix_len, out, works
     _check("bd_attn_step", lib.bd_attn_step(
         ctypes.byref(desc), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
         _ptr(prefix_len), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def bd_attn_step_fp8kv(desc, q, k_blk, v_blk, k_cache, v_cache, k_scale, v_scale, prefix_len, out,
+                       workspace, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bd_attn_step_fp8kv", lib.bd_attn_step_fp8kv(
+        ctypes.byref(desc), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(prefix_len), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def bd_commit_workspace_bytes(desc):

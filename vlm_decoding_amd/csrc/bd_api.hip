@@ -17,13 +17,13 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bd_status check_attn_desc(const bd_attn_desc *d) {
     if (!d) return BD_E_NULL;
-    if (d->dtype != BD_F32 && d->dtype != BD_BF16) return BD_E_DTYPE;
+    if (d->dtype != BD_F32 && d->dtype != BD_BF16 && d->dtype != BD_FP8KV) return BD_E_DTYPE;
     if (d->mode != BD_BLOCK_BIDIR && d->mode != BD_BLOCK_CAUSAL) return BD_E_PARAM;
     if (!(d->scale > 0.f) || !isfinite(d->scale)) return BD_E_PARAM;
     if (d->n_items < 1 || d->D < 1 || d->D > 64) return BD_E_SHAPE;
     if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return BD_E_SHAPE;
     if (d->d != 64 && d->d != 128) return BD_E_SHAPE;
-    if (d->cap < 1 || d->cap % 8 != 0) return BD_E_SHAPE;
+    if (d->cap < 1 || d->cap % (d->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
     if (d->max_prefix < 0 || d->max_prefix > d->cap) return BD_E_SHAPE;
     // Index arithmetic in the kernels uses 32-bit ints for per-item quantities.
     if ((int64_t)d->D * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
@@ -71,15 +71,11 @@ size_t bd_attn_workspace_bytes(const bd_attn_desc *desc) {
     return pl.ws_bytes;
 }
 
-bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_blk, const void *v_blk,
-                       const void *k_cache, const void *v_cache, const int32_t *prefix_len, void *out,
-                       void *workspace, size_t workspace_bytes, void *stream) {
-    bd_status st = check_attn_desc(desc);
-    if (st != BD_OK) return st;
-    if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !prefix_len || !out) return BD_E_NULL;
-    if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
-        !aligned16(v_cache) || !aligned16(out))
-        return BD_E_PARAM;
+namespace {
+bd_status attn_common(const bd_attn_desc *desc, const void *q, const void *k_blk, const void *v_blk,
+                      const void *k_cache, const void *v_cache, const float *k_scale, const float *v_scale,
+                      const int32_t *prefix_len, void *out, void *workspace, size_t workspace_bytes,
+                      void *stream) {
     const bd::AttnPlan pl = bd::plan_attention(desc->n_items, desc->D, desc->Hq, desc->Hkv, desc->d,
                                                desc->dtype, desc->max_prefix);
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
@@ -91,6 +87,8 @@ bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_bl
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.prefix = prefix_len;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
     a.out = out;
     a.ws = workspace;
     a.n = desc->n_items;
@@ -103,6 +101,37 @@ bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_bl
     a.scale = desc->scale;
     hipStream_t s = (hipStream_t)stream;
     return launched(pl.mfma ? bd::launch_attention_mfma(pl, a, s) : bd::launch_attention_vec(a, desc->dtype, s));
+}
+}  // namespace
+
+bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_blk, const void *v_blk,
+                       const void *k_cache, const void *v_cache, const int32_t *prefix_len, void *out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+    bd_status st = check_attn_desc(desc);
+    if (st != BD_OK) return st;
+    if (desc->dtype == BD_FP8KV) return BD_E_DTYPE;  // needs the scales: bd_attn_step_fp8kv
+    if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !prefix_len || !out) return BD_E_NULL;
+    if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return BD_E_PARAM;
+    return attn_common(desc, q, k_blk, v_blk, k_cache, v_cache, nullptr, nullptr, prefix_len, out, workspace,
+                       workspace_bytes, stream);
+}
+
+bd_status bd_attn_step_fp8kv(const bd_attn_desc *desc, const void *q, const void *k_blk, const void *v_blk,
+                             const void *k_cache, const void *v_cache, const float *k_scale,
+                             const float *v_scale, const int32_t *prefix_len, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    bd_status st = check_attn_desc(desc);
+    if (st != BD_OK) return st;
+    if (desc->dtype != BD_FP8KV) return BD_E_DTYPE;
+    if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !k_scale || !v_scale || !prefix_len || !out)
+        return BD_E_NULL;
+    if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return BD_E_PARAM;
+    return attn_common(desc, q, k_blk, v_blk, k_cache, v_cache, k_scale, v_scale, prefix_len, out, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t bd_commit_workspace_bytes(const bd_commit_desc *desc) {
@@ -171,13 +200,13 @@ bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache, i
                        const void *k_blk, const void *v_blk, const int32_t *n_accept, int32_t *dev_err,
                        void *stream) {
     if (!desc) return BD_E_NULL;
-    if (desc->dtype != BD_F32 && desc->dtype != BD_BF16) return BD_E_DTYPE;
+    if (desc->dtype != BD_F32 && desc->dtype != BD_BF16 && desc->dtype != BD_FP8KV) return BD_E_DTYPE;
     if (desc->n_items < 1 || desc->D < 1 || desc->D > 64 || desc->Hkv < 1) return BD_E_SHAPE;
     if (desc->d != 64 && desc->d != 128) return BD_E_SHAPE;
-    if (desc->cap < 1 || desc->cap % 8 != 0) return BD_E_SHAPE;
+    if (desc->cap < 1 || desc->cap % (desc->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
     if (!k_cache || !v_cache || !prefix_len || !k_blk || !v_blk) return BD_E_NULL;
     return launched(bd::launch_kv_append(desc->n_items, desc->D, desc->Hkv, desc->d, desc->cap,
-                                         desc->dtype == BD_F32 ? 4 : 2, k_cache, v_cache, prefix_len, k_blk,
+                                         desc->dtype == BD_F32 ? 4 : desc->dtype == BD_BF16 ? 2 : 1, k_cache, v_cache, prefix_len, k_blk,
                                          v_blk, n_accept, dev_err, (hipStream_t)stream));
 }
 

@@ -6,17 +6,21 @@
 // (verify / AR step).  GQA: the Hq/Hkv query heads sharing one KV head are
 // processed together as D * Hq/Hkv "grouped rows" against one K/V stream.
 //
-// MFMA path (bf16, d = 64 or 128).  One workgroup owns one (item, KV head,
-// row block, key split).  Each wave owns 32 grouped rows and computes
+// MFMA path (bf16 queries, bf16 or E4M3 K/V, d = 64 or 128).  One workgroup
+// owns one (item, KV head, row block, key split).  Each wave owns 32 grouped
+// rows and computes
 //     S^T = K . Q^T        (v_mfma_f32_32x32x16_bf16, keys x rows)
 //     O^T += V^T . P^T     (same instruction, d x rows)
 // so that each lane holds one query row: the softmax max is an in-lane
 // reduction plus one exchange between the two 32-lane halves.  K rows are
-// fed to the first MFMA in a permuted order so that the eight scores a lane
-// holds for each 16-key chunk are eight consecutive keys; the second MFMA
-// then reads its V^T operand as one 16-byte LDS load per lane from the
-// d-major value tile.  K and V^T tiles (64 keys) are staged through LDS in
-// two buffers with XOR swizzles that keep 16-lane groups conflict-free.
+// fed to the first MFMA in a permuted order so that the scores a lane holds
+// for each 16-key chunk are consecutive keys; the second MFMA then reads its
+// V^T operand as one 16-byte LDS load per lane from the d-major value tile.
+// K and V^T tiles (32 bf16 or 64 E4M3 keys, 8 KB each at d = 128) stream
+// through four LDS stages with XOR swizzles that keep 16-lane read phases
+// conflict-free.  E4M3 K/V (the FP8 rung of the Fast-dVLM write-up, section
+// 5.4 and Table 4, applied to the cache) are widened to bf16 exactly, right
+// after each LDS read, with one fp32 scale per (item, KV head) for K and V.
 // The online softmax (Milakov & Gimelshein, "Online normalizer calculation
 // for softmax", 2018) only rescales when the running maximum grows by more
 // than 2^8, which keeps every exponent <= 2^8 and is exact after the final
@@ -31,11 +35,11 @@
 namespace bd {
 namespace {
 
-constexpr int TK = kTileKeys;
-
 struct MfmaParams {
-    const uint16_t *q, *kb, *vb, *kc, *vc;
+    const uint16_t *q;
+    const uint8_t *kb, *vb, *kc, *vc;  // K / V storage (bf16 or E4M3), byte addressed
     const int32_t *prefix;
+    const float *k_scale, *v_scale;    // [n][Hkv], E4M3 K / V only
     uint16_t *out;
     float *ws_o;
     float2 *ws_ml;
@@ -44,46 +48,58 @@ struct MfmaParams {
     float c;  // scale * log2(e)
 };
 
-// Row permutation of the K operand: A-row rho (= lane % 32) of a 32-key block
-// loads key pi(rho), which makes output register i of half h hold key
-// 16 * (i / 8) + 8 * h + (i % 8).
+// Row permutations of the K operand.  A-row rho (= lane % 32) of a 32-key
+// block loads key pi(rho).
+//  bf16: output register i of half h then holds key 16 (i / 8) + 8 h + (i % 8),
+//        so 16-key chunk c of the second product is registers 8 (c % 2) .. of
+//        block c / 2 and its V^T operand is one 16-byte unit (8 keys) per lane.
+//  E4M3: register i of half h holds key 16 h + i.  Chunk c = 2m + j then
+//        covers keys 32m + 16h + 8j .. +7 for half h, which are bytes
+//        8j .. 8j+7 of the 16-byte unit 2m + h of a V^T row: one LDS read
+//        feeds the operands of two chunks.
 __device__ __forceinline__ int key_perm(int rho) {
     int q = rho >> 3, h = (rho >> 2) & 1, e = rho & 3;
     return ((q >> 1) << 4) + (h << 3) + ((q & 1) << 2) + e;
 }
+__device__ __forceinline__ int key_perm8(int rho) {
+    return (((rho >> 2) & 1) << 4) + ((rho >> 3) << 2) + (rho & 3);
+}
 
-// Work split of a unit with prefix P.  The unit streams nbulk = P / TK whole
-// cache tiles plus ntail tail tiles (the last P % TK cache positions and the
-// D block slots, gathered by a slower path that costs about kTailCost bulk
-// tiles).  nsplit = ceil(work / tiles_per_split) splits, at most max_splits
-// and at most nbulk + 1; the last split runs the tail and takes whatever bulk
-// tiles are left once the others have ceil(work / nsplit) each, so that no
-// split carries much more than the average.  Shared by the tile and merge
-// kernels.
+// Work split of a unit with prefix P and TK-key tiles.  The unit streams
+// nbulk = P / TK whole cache tiles plus ntail tail tiles (the last P % TK
+// cache positions and the D block slots, gathered by a slower path that costs
+// about kTailCost bulk tiles).  nsplit = ceil(work / tiles_per_split) splits,
+// at most max_splits and at most nbulk + 1; the last split runs the tail and
+// takes whatever bulk tiles are left once the others have ceil(work / nsplit)
+// each, so that no split carries much more than the average.  Shared by the
+// tile and merge kernels.
 constexpr int kTailCost = 3;
 struct UnitSplit {
     int nsplit;  // splits of this unit (the last one holds the tail)
     int t0, nb;  // bulk tile range of the queried split
 };
+template <int TK>
 __device__ __forceinline__ int unit_nsplit(int P, int D, int tiles_per_split, int max_splits) {
-    const int nbulk = P / kTileKeys;
-    const int ntail = ((P - nbulk * kTileKeys) + D + kTileKeys - 1) / kTileKeys;
+    const int nbulk = P / TK;
+    const int ntail = ((P - nbulk * TK) + D + TK - 1) / TK;
     const int work = nbulk + kTailCost * ntail;
     return max(1, min(min(max_splits, nbulk + 1), (work + tiles_per_split - 1) / tiles_per_split));
 }
+template <int TK>
 __device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_split, int max_splits, int split) {
     UnitSplit u;
-    const int nbulk = P / kTileKeys;
-    const int ntail = ((P - nbulk * kTileKeys) + D + kTileKeys - 1) / kTileKeys;
+    const int nbulk = P / TK;
+    const int ntail = ((P - nbulk * TK) + D + TK - 1) / TK;
     const int work = nbulk + kTailCost * ntail;
-    u.nsplit = unit_nsplit(P, D, tiles_per_split, max_splits);
+    u.nsplit = unit_nsplit<TK>(P, D, tiles_per_split, max_splits);
     const int nbs = u.nsplit - 1;                                      // bulk-only splits
     const int w = (work + u.nsplit - 1) / u.nsplit;                    // target work per split
     const int tail_bulk = nbs == 0 ? nbulk : max(0, nbulk - nbs * w);  // bulk tiles of the tail split
     const int shared = nbulk - tail_bulk;                              // >= nbs: every bulk split gets one
+    // 32-bit arithmetic is enough: split < 16 and shared <= cap / TK < 2^19.
     if (split < nbs) {
-        u.t0 = (int)(((long)split * shared) / nbs);
-        u.nb = (int)(((long)(split + 1) * shared) / nbs) - u.t0;
+        u.t0 = (int)((unsigned)(split * shared) / (unsigned)nbs);
+        u.nb = (int)((unsigned)((split + 1) * shared) / (unsigned)nbs) - u.t0;
     } else {
         u.t0 = shared;
         u.nb = tail_bulk;
@@ -91,31 +107,63 @@ __device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_spli
     return u;
 }
 
-// 16-byte-unit XOR swizzles of the LDS tiles.
-template <int HD>
+// 16-byte-unit XOR swizzles of the LDS tiles.  A tile row of U units shares
+// one 256-byte bank span (16 units) with 16/U - 1 other rows.  One ds_read_b128
+// phase serves 16 lanes that read the same logical unit of 16 different rows;
+// the swizzle sends those 16 reads to 16 different unit slots of the span.
+// V^T rows (and bf16 K rows) are read 16 consecutive rows at a time.
+template <int U>
+__device__ __forceinline__ int row_swz(int row) { return (row / (16 / U)) & (U - 1); }
+// E4M3 K rows are read in key_perm8 order: the 16 keys of a phase differ in
+// bits 0-2 and 4 (bit 3 fixed), so the swizzle is taken from those bits.
+template <int HD, bool KV8>
 __device__ __forceinline__ int k_swz(int key) {
-    // K tile rows are HD*2 bytes = HD/8 units; 16 units span all LDS banks.
-    return (HD == 128) ? (key & 15) : ((key >> 1) & 7);
+    if constexpr (!KV8) return row_swz<HD / 8>(key);
+    else if constexpr (HD == 128) return ((key >> 1) & 3) | ((key >> 2) & 4);  // 2 rows per span
+    else return ((key >> 2) & 1) | ((key >> 3) & 2);                             // 4 rows per span
 }
-// V^T rows hold TK/8 units and 128/TK of them share one 256-byte bank span.
-__device__ __forceinline__ int v_swz(int dd) { return (dd / (128 / kTileKeys)) & (kTileKeys / 8 - 1); }
 
 // Tile pipeline depth: NS LDS stages per workgroup, so NS - 1 tiles stay in
-// flight while one is computed.  Four stages of 32-key tiles take 64 KB of
-// LDS with d = 128: two workgroups (two waves per SIMD) share a CU, and each
-// keeps three tiles (48 KB) in flight.  Two per CU is also the cap for d = 64,
-// where registers rather than LDS are the limit.
+// flight while one is computed.  A stage holds 32 bf16 keys or 64 E4M3 keys:
+// with d = 128, four stages take 64 KB of LDS and two workgroups (two waves
+// per SIMD) share a CU, each keeping three tiles (48 KB) in flight.  Two per
+// CU is also the cap for d = 64, where registers rather than LDS are the limit.
 constexpr int kStages = 4;
+constexpr int kStageBytesPerD = kTileKeys * 2;  // LDS bytes of one K (or V) stage per head-dim element
 constexpr int occupancy_for(int hd) {
-    return (160 * 1024) / (kStages * 2 * kTileKeys * hd * 2) < 2 ? (160 * 1024) / (kStages * 2 * kTileKeys * hd * 2) : 2;
+    return (160 * 1024) / (kStages * 2 * kStageBytesPerD * hd) < 2 ? (160 * 1024) / (kStages * 2 * kStageBytesPerD * hd)
+                                                                   : 2;
 }
 
-template <int HD, int NW>
+// Two E4M3 values (bytes 2 SEL, 2 SEL + 1 of w) -> two bf16, exact (every
+// E4M3 value is a bf16 value), with v_cvt_scalef32_pk_bf16_fp8 at scale 1.
+template <bool SEL>
+__device__ __forceinline__ bf16x2 bd_e4m3x2_to_bf16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL);
+}
+// Eight E4M3 bytes (lo, hi) -> one bf16x8 MFMA operand, byte order kept.
+__device__ __forceinline__ bf16x8 bd_e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2 a = bd_e4m3x2_to_bf16<false>(lo), b = bd_e4m3x2_to_bf16<true>(lo);
+    const bf16x2 c = bd_e4m3x2_to_bf16<false>(hi), d = bd_e4m3x2_to_bf16<true>(hi);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// KV8 = false: bf16 K / V, 32-key tiles.  KV8 = true: E4M3 K / V with one
+// fp32 scale per (item, KV head) for K and for V, 64-key tiles (the same
+// bytes per stage), converted to bf16 right after each LDS read; the K scale
+// is folded into the softmax constant and the V scale into the final
+// normalisation.
+template <int HD, int NW, bool KV8>
 __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(MfmaParams p) {
     constexpr int NT = NW * 64;
-    constexpr int KU = HD / 8;          // 16-byte units per K row
+    constexpr int EB = KV8 ? 1 : 2;     // bytes per K / V element
+    constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;  // keys per tile
+    constexpr int EPU = 16 / EB;        // elements per 16-byte unit
+    constexpr int KU = HD * EB / 16;    // 16-byte units per K row
+    constexpr int VU = TK * EB / 16;    // 16-byte units per V^T row
+    constexpr int SB = TK * HD * EB;    // bytes per K (or V) stage
     constexpr int K_UNITS = TK * KU;
-    constexpr int V_UNITS = HD * (TK / 8);
+    constexpr int V_UNITS = HD * VU;
     constexpr int LK = (K_UNITS + NT - 1) / NT;
     constexpr int LV = (V_UNITS + NT - 1) / NT;
     constexpr int KC = HD / 16;         // d-chunks of the first MFMA
@@ -123,28 +171,31 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     constexpr int RPG = NW * 32;        // rows per workgroup
     constexpr int KB = TK / 32;         // 32-key blocks of the first MFMA per tile
     constexpr int C4 = TK / 16;         // 16-key chunks of the second MFMA per tile
-    constexpr int VU = TK / 8;          // 16-byte units per V^T row
     constexpr int NS = kStages;
+    static_assert(SB == kStageBytesPerD * HD, "stage size must match occupancy_for");
     static_assert(NS == 4, "the stage arrays below are written out for four stages");
     static_assert((NS - 1) * (LK + LV) < 64, "outstanding copies must fit the vmcnt counter");
 
     // One array per stage: the tile loop below is unrolled by NS so that every
     // LDS access names a fixed array, which lets the compiler see that reads of
     // one stage never alias the global->LDS copies in flight into the others.
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k0[TK * HD];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k1[TK * HD];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k2[TK * HD];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k3[TK * HD];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v0[HD * TK];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v1[HD * TK];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v2[HD * TK];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v3[HD * TK];
-    auto kbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k0[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k1[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k2[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k3[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v0[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v1[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v2[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v3[SB];
+    auto kbuf = [&](int st) __attribute__((always_inline)) -> uint8_t * {
         return st == 0 ? lds_k0 : st == 1 ? lds_k1 : st == 2 ? lds_k2 : lds_k3;
     };
-    auto vbuf = [&](int st) __attribute__((always_inline)) -> uint16_t * {
+    auto vbuf = [&](int st) __attribute__((always_inline)) -> uint8_t * {
         return st == 0 ? lds_v0 : st == 1 ? lds_v1 : st == 2 ? lds_v2 : lds_v3;
     };
+    // Byte offsets of 16-byte unit lu of K row `key` / V^T row `dd` in a stage.
+    auto k_at = [](int key, int lu) __attribute__((always_inline)) { return (key * KU + (lu ^ k_swz<HD, KV8>(key))) * 16; };
+    auto v_at = [](int dd, int lu) __attribute__((always_inline)) { return (dd * VU + (lu ^ row_swz<VU>(dd))) * 16; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -165,6 +216,8 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 
     // This lane's query row.  Its loads are issued before the prefix length
     // is known (they do not depend on it), so the two round trips overlap.
+    // MFMA kc reads d = 16 kc + 8 half .. +7 (bf16) or, in the order an
+    // E4M3 K unit is split into two operands, d = 32 (kc/2) + 16 half + 8 (kc%2) .. +7.
     const int r_local = w * 32 + col;
     const int r = rb * RPG + r_local;
     const bool row_valid = r < p.R;
@@ -173,14 +226,20 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const int head = g * p.G + (r - slot * p.G);
     bf16x8 qf[KC];
     {
-        const uint16_t *qp = p.q + (((size_t)it * p.D + slot) * p.Hq + head) * HD + half * 8;
+        const uint16_t *qp = p.q + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
+            const int d0 = KV8 ? (kc >> 1) * 32 + half * 16 + (kc & 1) * 8 : kc * 16 + half * 8;
             if (row_valid)
-                qf[kc] = *reinterpret_cast<const bf16x8 *>(qp + kc * 16);
+                qf[kc] = *reinterpret_cast<const bf16x8 *>(qp + d0);
             else
                 qf[kc] = bf16x8{};
         }
+    }
+    float cs = p.c, vs = 1.0f;
+    if constexpr (KV8) {
+        cs *= p.k_scale[it * p.Hkv + g];
+        vs = p.v_scale[it * p.Hkv + g];
     }
 
     // Prefix lengths are clamped into [0, cap] so that no access leaves the cache.
@@ -188,7 +247,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const int Pb = P & ~(TK - 1);  // cache positions in whole tiles
     // A prefix above the host's max_prefix widens the splits instead of
     // overrunning the workspace (at most max_splits per unit).
-    const UnitSplit us = unit_split(P, p.D, p.tiles_per_split, p.max_splits, split);
+    const UnitSplit us = unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
     const int nsplit = us.nsplit;
     if (split >= nsplit) return;
     const bool is_tail = split == nsplit - 1;
@@ -197,8 +256,10 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const int tail_len = is_tail ? (P - Pb) + p.D : 0;
     const int ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
 
-    const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD;   // [cap][HD]
-    const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap;   // [HD][cap]
+    // Byte offsets of this (item, KV head)'s cache rows.
+    const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD * EB;   // [cap][HD]
+    const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap * EB;   // [HD][cap]
+    const size_t row_v = (size_t)p.cap * EB;                              // bytes per V^T cache row
 
     floatx16 o[MB];
 #pragma unroll
@@ -216,20 +277,20 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 #pragma unroll
         for (int j = 0; j < LK; ++j) {
             const int base = (j * NW + w) * 64;
-            const int slot = base + lane;
-            const int key = slot / KU, pu = slot % KU;
-            const int lu = pu ^ k_swz<HD>(key);
-            const uint16_t *src = real ? p.kc + kc_base + (size_t)(key0 + key) * HD + lu * 8 : p.kc + kc_base;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&kbuf(st)[base * 8], 16, 0, 0);
+            const int u = base + lane;
+            const int key = u / KU, pu = u % KU;
+            const int lu = pu ^ k_swz<HD, KV8>(key);
+            const uint8_t *src = real ? p.kc + kc_base + (size_t)(key0 + key) * HD * EB + lu * 16 : p.kc + kc_base;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&kbuf(st)[base * 16], 16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < LV; ++j) {
             const int base = (j * NW + w) * 64;
-            const int slot = base + lane;
-            const int dd = slot / VU, pu = slot % VU;
-            const int lu = pu ^ v_swz(dd);
-            const uint16_t *src = real ? p.vc + vc_base + (size_t)dd * p.cap + key0 + lu * 8 : p.kc + kc_base;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 8], 16, 0, 0);
+            const int u = base + lane;
+            const int dd = u / VU, pu = u % VU;
+            const int lu = pu ^ row_swz<VU>(dd);
+            const uint8_t *src = real ? p.vc + vc_base + (size_t)dd * row_v + (size_t)key0 * EB + lu * 16 : p.kc + kc_base;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 16], 16, 0, 0);
         }
     };
     // Tail tiles: the last P % TK cache positions followed by the D block slots,
@@ -237,7 +298,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // and cache V^T rows are gathered as 16-byte units.  Block V rows arrive
     // d-contiguous ([slot][Hkv][d]); they are loaded as 16-byte units and
     // scattered transposed into the V^T tile after the other units are written.
-    constexpr int BU = HD / 8;  // 16-byte units per block V row
+    constexpr int BU = HD * EB / 16;  // 16-byte units per block V row
     auto load_tail = [&](int st, int tt) __attribute__((always_inline)) {
         const int pc = P - Pb;  // cache positions in the tail
         u32x4 kr[LK], vr[LV];
@@ -249,8 +310,8 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             const int pos = Pb + j;
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
             if (j < tail_len) {
-                const uint16_t *src = pos < P ? p.kc + kc_base + (size_t)pos * HD + lu * 8
-                                              : p.kb + (((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD + lu * 8;
+                const uint8_t *src = pos < P ? p.kc + kc_base + (size_t)pos * HD * EB + lu * 16
+                                             : p.kb + (((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD * EB + lu * 16;
                 v = *reinterpret_cast<const u32x4 *>(src);
             }
             kr[i] = v;
@@ -259,17 +320,28 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         for (int i = 0; i < LV; ++i) {
             const int u = tid + i * NT;
             const int dd = u / VU, lu = u % VU;
-            const int j0 = tt * TK + lu * 8;
+            const int j0 = tt * TK + lu * EPU;
+            const uint8_t *row = p.vc + vc_base + (size_t)dd * row_v + (size_t)(Pb + j0) * EB;
             u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (j0 + 8 <= pc) {
-                v = *reinterpret_cast<const u32x4 *>(p.vc + vc_base + (size_t)dd * p.cap + Pb + j0);
+            if (j0 + EPU <= pc) {
+                v = *reinterpret_cast<const u32x4 *>(row);
             } else if (j0 < pc) {  // unit straddles the end of the cache part
-                uint16_t e8[8];
+                // Every lane loads all EPU elements (positions past the cache
+                // part re-read its last one) and zeroes the extra ones after,
+                // so the loads issue back to back with one wait.
+                uint32_t x[EPU];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    e8[e] = j0 + e < pc ? p.vc[vc_base + (size_t)dd * p.cap + Pb + j0 + e] : (uint16_t)0;
-                v = u32x4{e8[0] | ((uint32_t)e8[1] << 16), e8[2] | ((uint32_t)e8[3] << 16),
-                          e8[4] | ((uint32_t)e8[5] << 16), e8[6] | ((uint32_t)e8[7] << 16)};
+                for (int e = 0; e < EPU; ++e) {
+                    const int ee = min(e, pc - 1 - j0);
+                    x[e] = KV8 ? (uint32_t)row[ee] : (uint32_t)reinterpret_cast<const uint16_t *>(row)[ee];
+                }
+#pragma unroll
+                for (int e = 0; e < EPU; ++e)
+                    if (j0 + e >= pc) x[e] = 0u;
+                uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < EPU; ++e) w4[(e * EB) >> 2] |= x[e] << (8 * ((e * EB) & 3));
+                v = u32x4{w4[0], w4[1], w4[2], w4[3]};
             }
             vr[i] = v;
         }
@@ -277,13 +349,13 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         for (int i = 0; i < LK; ++i) {
             const int u = tid + i * NT;
             const int key = u / KU, lu = u % KU;
-            *reinterpret_cast<u32x4 *>(kbuf(st) + key * HD + ((lu ^ k_swz<HD>(key)) << 3)) = kr[i];
+            *reinterpret_cast<u32x4 *>(kbuf(st) + k_at(key, lu)) = kr[i];
         }
 #pragma unroll
         for (int i = 0; i < LV; ++i) {
             const int u = tid + i * NT;
             const int dd = u / VU, lu = u % VU;
-            *reinterpret_cast<u32x4 *>(vbuf(st) + dd * TK + ((lu ^ v_swz(dd)) << 3)) = vr[i];
+            *reinterpret_cast<u32x4 *>(vbuf(st) + v_at(dd, lu)) = vr[i];
         }
         bd_barrier_lds();  // the scatter below overwrites zeros written above
         // Block V units that land in this tile: slot b covers tail position pc + b.
@@ -297,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             const int j = pc + b - tt * TK;  // key index inside this tile
             bkey[i] = (b < p.D && j >= 0 && j < TK) ? j : -1;
             if (bkey[i] >= 0)
-                br[i] = *reinterpret_cast<const u32x4 *>(p.vb + (((size_t)it * p.D + b) * p.Hkv + g) * HD + du * 8);
+                br[i] = *reinterpret_cast<const u32x4 *>(p.vb + (((size_t)it * p.D + b) * p.Hkv + g) * HD * EB + du * 16);
         }
 #pragma unroll
         for (int i = 0; i < VB_MAX; ++i) {
@@ -307,28 +379,38 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             const int key = bkey[i];
             const uint32_t w4[4] = {br[i].x, br[i].y, br[i].z, br[i].w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int dd = du * 8 + e;
-                const uint16_t val = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-                vbuf(st)[dd * TK + (((key >> 3) ^ v_swz(dd)) << 3) + (key & 7)] = val;
+            for (int e = 0; e < EPU; ++e) {
+                const int dd = du * EPU + e;
+                uint8_t *dst = vbuf(st) + v_at(dd, key / EPU) + (key % EPU) * EB;
+                if constexpr (KV8)
+                    *dst = (uint8_t)(w4[e >> 2] >> (8 * (e & 3)));
+                else
+                    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
             }
         }
     };
 
     auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */) __attribute__((always_inline)) {
-        const uint16_t *Kt = kbuf(st);
-        const uint16_t *Vt = vbuf(st);
+        const uint8_t *Kt = kbuf(st);
+        const uint8_t *Vt = vbuf(st);
         floatx16 s[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             s[kb] = floatx16{};
-            const int key = kb * 32 + key_perm(col);
-            const int sw = k_swz<HD>(key);
+            const int key = kb * 32 + (KV8 ? key_perm8(col) : key_perm(col));
+            if constexpr (!KV8) {
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-                const int lu = kc * 2 + half;
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&Kt[key * HD + ((lu ^ sw) << 3)]);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+                for (int kc = 0; kc < KC; ++kc) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Kt + k_at(key, kc * 2 + half));
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kc], s[kb], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < KC / 2; ++m) {
+                    const u32x4 raw = *reinterpret_cast<const u32x4 *>(Kt + k_at(key, m * 2 + half));
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd_e4m3x8_to_bf16(raw.x, raw.y), qf[2 * m], s[kb], 0, 0, 0);
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd_e4m3x8_to_bf16(raw.z, raw.w), qf[2 * m + 1], s[kb], 0, 0, 0);
+                }
             }
         }
         if (tt >= 0) {
@@ -336,7 +418,8 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int j = tt * TK + kb * 32 + 16 * (i >> 3) + 8 * half + (i & 7);
+                    const int kin = KV8 ? 16 * half + i : 16 * (i >> 3) + 8 * half + (i & 7);
+                    const int j = tt * TK + kb * 32 + kin;
                     bool ok = j < tail_len;
                     if (p.mode == 1) {
                         const int pos = Pb + j;
@@ -351,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
         mx = bd_max_halves(mx);
-        const float mx2 = mx * p.c;
+        const float mx2 = mx * cs;
         const bool need = mx2 > m_run + 8.0f;
         if (bd_wave_any(need)) {
             const float m_new = need ? mx2 : m_run;
@@ -366,7 +449,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)bd_exp2(fmaf(s[kb][i], p.c, -msub));
+            for (int i = 0; i < 16; ++i) pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)bd_exp2(fmaf(s[kb][i], cs, -msub));
         // Row sum of the rounded weights (exactly what the P.V product uses),
         // two at a time with v_dot2_f32_bf16.
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -382,17 +465,24 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int dd = mb * 32 + col;
-            const int sw = v_swz(dd);
+            if constexpr (!KV8) {
 #pragma unroll
-            for (int c4 = 0; c4 < C4; ++c4) {
-                const int lu = c4 * 2 + half;
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&Vt[dd * TK + ((lu ^ sw) << 3)]);
-                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c4], o[mb], 0, 0, 0);
+                for (int c4 = 0; c4 < C4; ++c4) {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vt + v_at(dd, c4 * 2 + half));
+                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c4], o[mb], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < C4 / 2; ++m) {
+                    const u32x4 raw = *reinterpret_cast<const u32x4 *>(Vt + v_at(dd, m * 2 + half));
+                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd_e4m3x8_to_bf16(raw.x, raw.y), pb[2 * m], o[mb], 0, 0, 0);
+                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd_e4m3x8_to_bf16(raw.z, raw.w), pb[2 * m + 1], o[mb], 0, 0, 0);
+                }
             }
         }
     };
 
-    // Tail split: gather and compute its (one or two) tiles.
+    // Tail split: gather and compute its (one to three) tiles.
     for (int tt = 0; tt < ntail; ++tt) {
         if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
         load_tail(0, tt);
@@ -437,7 +527,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // half h holds d = mb*32 + 8*(i/4) + 4*h + (i%4) of this lane's row.
     if (nsplit == 1) {
         if (row_valid) {
-            const float inv = 1.0f / l_tot;
+            const float inv = vs / l_tot;
             uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -453,15 +543,15 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         return;
     }
 
-    // Split-K partials: the split's normalised output o / l as bf16 plus its
-    // (m, l) in fp32, stored lane-major so that every store of a wave covers
-    // one contiguous span.  16-byte unit qq (output quads 2qq and 2qq+1, i.e.
-    // block mb = qq/2, quads i4 = 2(qq%2) and 2(qq%2)+1) of thread t of split
-    // s of unit u lives at [(u * max_splits + s) * (QUADS/2) + qq][t].
+    // Split-K partials: the split's normalised output o / l (times the V scale)
+    // as bf16 plus its (m, l) in fp32, stored lane-major so that every store of
+    // a wave covers one contiguous span.  16-byte unit qq (output quads 2qq and
+    // 2qq+1, i.e. block mb = qq/2, quads i4 = 2(qq%2) and 2(qq%2)+1) of thread t
+    // of split s of unit u lives at [(u * max_splits + s) * (QUADS/2) + qq][t].
     constexpr int QUADS = MB * 4;
     if (wave_active) {
         const size_t base = ((size_t)unit * p.max_splits + split);
-        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        const float inv = l_tot > 0.f ? vs / l_tot : 0.f;
         uint4 *wo = reinterpret_cast<uint4 *>(p.ws_o) + base * (QUADS / 2) * NT + tid;
 #pragma unroll
         for (int qq = 0; qq < QUADS / 2; ++qq) {
@@ -485,7 +575,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 //   M = max_s m_s,  c_s = 2^(m_s - M) l_s,  o = sum_s c_s (o_s / l_s) / sum_s c_s,
 // summed in split order.  The merged 32 rows are staged in LDS and written
 // out as whole rows (HD * 2 contiguous bytes each).
-template <int HD, int NW>
+template <int HD, int NW, int TK>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
     constexpr int NT_TILE = NW * 64;    // threads of the tile kernel's block
     constexpr int MB = HD / 32;
@@ -520,7 +610,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
             for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t];
         }
     const int P = min(max(p.prefix[it], 0), p.cap);
-    const int nsplit = unit_nsplit(P, p.D, p.tiles_per_split, p.max_splits);
+    const int nsplit = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
     if (nsplit == 1) return;  // single split: written by the tile kernel
     float M = -INFINITY;
 #pragma unroll
@@ -657,22 +747,24 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
 
 AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix) {
     AttnPlan pl{};
-    pl.mfma = (dtype == 1);
+    pl.mfma = (dtype == 1 || dtype == 2);
+    pl.fp8 = (dtype == 2);
+    pl.tk = pl.fp8 ? 2 * kTileKeys : kTileKeys;
     pl.rows = D * (Hq / Hkv);
     if (!pl.mfma) {
         pl.grid = (int)(((long)n * D * Hq + 3) / 4);
         pl.ws_bytes = 0;
         return pl;
     }
-    // 8-wave workgroups (256 rows) only for d = 128: with d = 64 a 32-key tile
-    // has fewer 16-byte units than 8 waves have lanes.
+    // 8-wave workgroups (256 rows) only for d = 128: with d = 64 a tile has
+    // fewer 16-byte units than 8 waves have lanes.
     pl.nw = (pl.rows <= 128 || d == 64) ? 4 : 8;
     pl.rows_per_group = pl.nw * 32;
     pl.row_blocks = (pl.rows + pl.rows_per_group - 1) / pl.rows_per_group;
     pl.units = n * Hkv * pl.row_blocks;
     // Resident workgroups: LDS (kStages tile stages) bounds them per CU.
     const int slots = kCUs * occupancy_for(d);
-    const int ntiles_max = max_prefix / kTileKeys;
+    const int ntiles_max = max_prefix / pl.tk;
     const int want = std::max(1, slots / pl.units);
     // Splits per unit (the device side derives each unit's count from its own
     // prefix): sized so that a unit at max_prefix gets about `want` splits.
@@ -697,14 +789,30 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     return pl;
 }
 
+namespace {
+template <bool KV8>
+void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge) {
+    constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;
+    if (d == 128) {
+        *tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4, KV8> : (const void *)attn_mfma_kernel<128, 8, KV8>;
+        *merge = pl.nw == 4 ? (const void *)attn_merge_kernel<128, 4, TK> : (const void *)attn_merge_kernel<128, 8, TK>;
+    } else {
+        *tile = (const void *)attn_mfma_kernel<64, 4, KV8>;
+        *merge = (const void *)attn_merge_kernel<64, 4, TK>;
+    }
+}
+}  // namespace
+
 hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStream_t s) {
     MfmaParams p{};
     p.q = (const uint16_t *)a.q;
-    p.kb = (const uint16_t *)a.k_blk;
-    p.vb = (const uint16_t *)a.v_blk;
-    p.kc = (const uint16_t *)a.k_cache;
-    p.vc = (const uint16_t *)a.v_cache;
+    p.kb = (const uint8_t *)a.k_blk;
+    p.vb = (const uint8_t *)a.v_blk;
+    p.kc = (const uint8_t *)a.k_cache;
+    p.vc = (const uint8_t *)a.v_cache;
     p.prefix = a.prefix;
+    p.k_scale = a.k_scale;
+    p.v_scale = a.v_scale;
     p.out = (uint16_t *)a.out;
     char *ws = (char *)a.ws;
     p.ws_ml = pl.max_splits > 1 ? (float2 *)(ws + pl.ws_ml_off) : nullptr;
@@ -724,13 +832,10 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.c = a.scale * BD_LOG2E;
     dim3 block(pl.nw * 64);
     const void *tile, *merge;
-    if (a.d == 128) {
-        tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4> : (const void *)attn_mfma_kernel<128, 8>;
-        merge = pl.nw == 4 ? (const void *)attn_merge_kernel<128, 4> : (const void *)attn_merge_kernel<128, 8>;
-    } else {
-        tile = (const void *)attn_mfma_kernel<64, 4>;
-        merge = (const void *)attn_merge_kernel<64, 4>;
-    }
+    if (pl.fp8)
+        pick_kernels<true>(pl, a.d, &tile, &merge);
+    else
+        pick_kernels<false>(pl, a.d, &tile, &merge);
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
     if (e != hipSuccess || pl.max_splits == 1) return e;

@@ -8,12 +8,14 @@
 namespace bd {
 
 // ---- block attention -------------------------------------------------------
-constexpr int kTileKeys = 32;       // keys per LDS tile
+constexpr int kTileKeys = 32;       // keys per LDS tile (bf16; E4M3 tiles hold twice as many)
 constexpr int kCUs = 256;           // compute units of an MI355X
 constexpr int kMaxSplits = 16;      // split-K pieces per unit (merge registers)
 
 struct AttnPlan {
-    bool mfma;            // bf16 MFMA path (else the fp32/any vector path)
+    bool mfma;            // MFMA path: bf16, or bf16 queries with E4M3 K/V (else the fp32 vector path)
+    bool fp8;             // E4M3 K/V (64-key tiles)
+    int tk;               // keys per tile
     int nw;               // waves per workgroup (MFMA path)
     int rows;             // grouped query rows per (item, KV head) = D * Hq/Hkv
     int rows_per_group;   // rows one workgroup covers (32 * nw)
@@ -28,6 +30,7 @@ struct AttnPlan {
 struct AttnArgs {
     const void *q, *k_blk, *v_blk, *k_cache, *v_cache;
     const int32_t *prefix;
+    const float *k_scale, *v_scale;  // E4M3 K/V only
     void *out;
     void *ws;
     int n, D, Hq, Hkv, d, cap, mode;

@@ -280,10 +280,14 @@ hipError_t launch_kv_append(int n, int D, int Hkv, int d, int cap, int elem_byte
         hipLaunchKernelGGL((kv_append_kernel<uint32_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
                            (uint32_t *)k_cache, (uint32_t *)v_cache, prefix, (const uint32_t *)k_blk,
                            (const uint32_t *)v_blk, n_accept, dev_err);
-    else
+    else if (elem_bytes == 2)
         hipLaunchKernelGGL((kv_append_kernel<uint16_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
                            (uint16_t *)k_cache, (uint16_t *)v_cache, prefix, (const uint16_t *)k_blk,
                            (const uint16_t *)v_blk, n_accept, dev_err);
+    else
+        hipLaunchKernelGGL((kv_append_kernel<uint8_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
+                           (uint8_t *)k_cache, (uint8_t *)v_cache, prefix, (const uint8_t *)k_blk,
+                           (const uint8_t *)v_blk, n_accept, dev_err);
     return hipGetLastError();
 }
 

@@ -46,6 +46,10 @@ class DeviceStep:
         self.k_cache = to_device(step["k_cache"], device)
         self.v_cache = to_device(step["v_cache"], device)
         self.prefix = to_device(step["prefix"], device)
+        # E4M3 K/V carry one fp32 scale per (item, KV head) for keys and for values.
+        self.fp8kv = self.dtype == bd.BD_FP8KV
+        self.k_scale = to_device(step["k_scale"], device) if self.fp8kv else None
+        self.v_scale = to_device(step["v_scale"], device) if self.fp8kv else None
         self.logits = to_device(step["logits"], device)
         self.masked0 = to_device(step["masked"], device)
         self.tokens0 = to_device(step["tokens"], device)
@@ -78,8 +82,12 @@ class DeviceStep:
         if mode is not None and mode != desc.mode:
             desc = bd.attn_desc(desc.n_items, desc.D, desc.Hq, desc.Hkv, desc.d, desc.cap, desc.dtype,
                                 mode, desc.max_prefix, desc.scale)
-        bd.bd_attn_step(desc, self.q, self.k_blk, self.v_blk, self.k_cache, self.v_cache, self.prefix,
-                        self.out, self.attn_ws, stream=stream)
+        if self.fp8kv:
+            bd.bd_attn_step_fp8kv(desc, self.q, self.k_blk, self.v_blk, self.k_cache, self.v_cache, self.k_scale,
+                                  self.v_scale, self.prefix, self.out, self.attn_ws, stream=stream)
+        else:
+            bd.bd_attn_step(desc, self.q, self.k_blk, self.v_blk, self.k_cache, self.v_cache, self.prefix,
+                            self.out, self.attn_ws, stream=stream)
         return self.out
 
     def confidence_commit(self, logits=None, stream=None):
