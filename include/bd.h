@@ -69,17 +69,17 @@ typedef int32_t bd_status;
 #define BD_E_LAUNCH 6    /* the HIP runtime rejected a launch */
 
 enum { BD_F32 = 0, BD_BF16 = 1, BD_FP8KV = 2 };
-enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1 };
+enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1, BD_BLOCK_QUAD = 2 };
 
 /* Shape of one block-attention call.
  *  n_items    independent (request, layer) items, >= 1
- *  D          block length, 1..64
+ *  D          block length, 1..64 (BD_BLOCK_QUAD: the draft block size B, 1..32)
  *  Hq, Hkv    query / KV heads, Hq % Hkv == 0; head h uses KV head h / (Hq/Hkv)
  *  d          head dim, 64 or 128
  *  cap        cache capacity in tokens, a multiple of 8 (of 16 for BD_FP8KV)
  *  dtype      BD_BF16 (MFMA path), BD_F32 (vector path) or BD_FP8KV (bf16
  *             queries and outputs, E4M3 keys and values: bd_attn_step_fp8kv)
- *  mode       BD_BLOCK_BIDIR or BD_BLOCK_CAUSAL
+ *  mode       BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL or BD_BLOCK_QUAD
  *  max_prefix host-side upper bound of every prefix_len[i], 0..cap; sizes the grid
  *  scale      softmax scale (normally 1/sqrt(d)); finite and > 0 */
 typedef struct {
@@ -103,6 +103,16 @@ size_t bd_attn_workspace_bytes(const bd_attn_desc *desc);
  *   keys/values are cache positions 0..P-1 followed by block slots 0..D-1;
  *   BD_BLOCK_BIDIR  : slot s sees all P + D of them (denoise step);
  *   BD_BLOCK_CAUSAL : slot s sees cache 0..P-1 and block slots 0..s (verify / AR step);
+ *   BD_BLOCK_QUAD   : quadratic self-speculative step ([FD] 5.3, the quadratic variant:
+ *                     verify fused with the next block's draft).  With B = desc->D the
+ *                     block holds S = B (B + 3) / 2 slots: slots 0..B-1 are the B draft
+ *                     tokens, then for g = 0..B-1 the B - g mask tokens of group g (the
+ *                     next-block proposal under the hypothesis that drafts 0..g-1 are
+ *                     accepted).  Every slot sees cache 0..P-1; draft t sees drafts
+ *                     0..t; a mask token of group g sees drafts 0..g-1 and every mask
+ *                     token of group g.  (The B x B expansion of the pages, with each
+ *                     draft token's K/V held once since it is the same in every group.)
+ *                     q, out, k_blk, v_blk then have S slots per item instead of D.
  *   out = softmax(scale * q k^T) v over the visible keys.
  * Cache positions >= P are never read.  `out` has the input dtype.
  * Preconditions (device): 0 <= prefix_len[i] <= max_prefix.
@@ -167,13 +177,17 @@ bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logit
 
 /* Append accepted block K/V to the cache ([FD] 5.3: crop the cache to the accepted
  * prefix; [DV] a finished block joins the history cache).  Uses n_items, D, Hkv, d,
- * cap and dtype of `desc`.  For item i with P = prefix_len[i] and
+ * cap, dtype and mode of `desc`.  For item i with P = prefix_len[i] and
  * L = n_accept ? n_accept[i] : D (device values): cache slots P..P+L-1 receive block
- * slots 0..L-1 bit for bit (keys row-wise, values into the d-major layout; for
- * BD_FP8KV the E4M3 bytes, which share the cache's per-(item, KV head) scales) and
- * prefix_len[i] becomes P + L.  Nothing else is written.  If L is outside 0..D or
- * P + L > cap, item i is left untouched and *dev_err (optional device int32) is set to 1.
- * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_LAUNCH. */
+ * slots 0..L-1 bit for bit (keys row-wise, values into the d-major layout) and
+ * prefix_len[i] becomes P + L.  Nothing else is written.
+ *  - BD_FP8KV: the E4M3 bytes are copied; they share the cache's per-(item, KV head)
+ *    scales.
+ *  - BD_BLOCK_QUAD: k_blk / v_blk hold B (B + 3) / 2 slots per item (the layout of
+ *    that mode) and L <= B accepted drafts, slots 0..L-1, are appended.
+ * If L is outside 0..D or P + L > cap, item i is left untouched and *dev_err
+ * (optional device int32) is set to 1.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_LAUNCH. */
 bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache,
                        int32_t *prefix_len, const void *k_blk, const void *v_blk,
                        const int32_t *n_accept, int32_t *dev_err, void *stream);

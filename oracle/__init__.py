@@ -22,7 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 F32, BF16, FP8 = 0, 1, 2
-BIDIR, CAUSAL = 0, 1
+BIDIR, CAUSAL, QUAD = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -58,6 +58,8 @@ def _load():
         lib.bdo_lm_head_logits.argtypes = [i32, i32, i32, P, P, P]
         lib.bdo_attention_fp8kv.argtypes = [i32] * 7 + [ctypes.c_double] + [P] * 9
         lib.bdo_fp8_e4m3_decode.argtypes = [i32, P, P]
+        lib.bdo_attention_quad.argtypes = [i32] * 7 + [ctypes.c_double] + [P] * 7
+        lib.bdo_attention_quad_fp8kv.argtypes = [i32] * 6 + [ctypes.c_double] + [P] * 9
         _lib = lib
     return _lib
 
@@ -212,11 +214,12 @@ def lm_head_logits(hidden, weight):
     return out
 
 
-def attention_fp8kv(q, k_blk, v_blk, k_cache, v_cache, k_scale, v_scale, prefix, mode, scale=None):
-    """Block attention with an FP8 KV cache (the same mask rules as attention()):
+def attention_fp8kv(q, k_blk, v_blk, k_cache, v_cache, k_scale, v_scale, prefix, mode, scale=None, B=None):
+    """Block attention with an FP8 KV cache (the same mask rules as attention(), or
+    attention_quad()'s when mode is QUAD with draft block size B):
     q raw bf16; k_blk, v_blk, k_cache, v_cache raw OCP E4M3 bytes in the same
     layouts; every key / value is its byte's E4M3 value times the fp32 scale of its
-    (item, KV head), k_scale / v_scale [n][Hkv].  Returns fp64 [n][D][Hq][d]."""
+    (item, KV head), k_scale / v_scale [n][Hkv].  Returns fp64 [n][slots][Hq][d]."""
     lib = _load()
     n, D, Hq, d = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
@@ -228,8 +231,41 @@ def attention_fp8kv(q, k_blk, v_blk, k_cache, v_cache, k_scale, v_scale, prefix,
     ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
     pre = _c(prefix, np.int32)
     out = np.zeros((n, D, Hq, d), np.float64)
+    if mode == QUAD:
+        assert D == quad_slots(B), (D, B)
+        lib.bdo_attention_quad_fp8kv(n, int(B), Hq, Hkv, d, cap, float(scale), _ptr(q), _ptr(kb), _ptr(vb),
+                                     _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(pre), _ptr(out))
+        return out
     lib.bdo_attention_fp8kv(n, D, Hq, Hkv, d, cap, int(mode), float(scale), _ptr(q), _ptr(kb), _ptr(vb),
                             _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(pre), _ptr(out))
+    return out
+
+
+def quad_slots(B):
+    """Block slots of a quadratic self-speculative step: B drafts, then B - g mask
+    tokens for each group g = 0..B-1."""
+    return B * (B + 3) // 2
+
+
+def attention_quad(q, k_blk, v_blk, k_cache, v_cache, prefix, B, scale=None):
+    """Quadratic self-speculative attention (Fast-dVLM write-up, section 5.3, the
+    quadratic variant): block slots 0..B-1 are the draft tokens (causal among
+    themselves), then group g's mask tokens (B - g slots) see the drafts before g
+    and their own group.  Every slot sees the cache.  Layouts as attention() with
+    quad_slots(B) block slots.  Returns float64 [n][quad_slots(B)][Hq][d]."""
+    lib = _load()
+    n, S, Hq, d = q.shape
+    assert S == quad_slots(B), (S, B)
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    dtype = F32 if q.dtype == np.float32 else BF16
+    el = np.float32 if dtype == F32 else np.uint16
+    arrs = [_c(a, el) for a in (q, k_blk, v_blk, k_cache, v_cache)]
+    prefix = _c(prefix, np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n, S, Hq, d), dtype=np.float64)
+    lib.bdo_attention_quad(n, int(B), Hq, Hkv, d, cap, dtype, float(scale), *[_ptr(a) for a in arrs],
+                           _ptr(prefix), _ptr(out))
     return out
 
 

@@ -49,6 +49,7 @@
 #define BDO_BF16 1
 #define BDO_BIDIR 0
 #define BDO_CAUSAL 1
+#define BDO_QUAD 2  /* quadratic self-speculative block: B draft slots + B groups of mask slots */
 
 #define BDO_FP8 2  /* OCP FP8 E4M3 ("e4m3fn") */
 
@@ -94,7 +95,7 @@ int bdo_num_threads(void) {
  * out [n][D][Hq][d] double.
  */
 static void attention_impl(int n, int D, int Hq, int Hkv, int d, int cap, int q_dtype, int kv_dtype,
-                           int mode, double scale, const void *q, const void *k_blk, const void *v_blk,
+                           int mode, int B, double scale, const void *q, const void *k_blk, const void *v_blk,
                            const void *k_cache, const void *v_cache, const float *k_scale,
                            const float *v_scale, const int32_t *prefix_len, double *out);
 
@@ -102,7 +103,7 @@ void bdo_attention(int n, int D, int Hq, int Hkv, int d, int cap, int dtype, int
                    double scale, const void *q, const void *k_blk, const void *v_blk,
                    const void *k_cache, const void *v_cache, const int32_t *prefix_len,
                    double *out) {
-    attention_impl(n, D, Hq, Hkv, d, cap, dtype, dtype, mode, scale, q, k_blk, v_blk, k_cache, v_cache,
+    attention_impl(n, D, Hq, Hkv, d, cap, dtype, dtype, mode, 0, scale, q, k_blk, v_blk, k_cache, v_cache,
                    NULL, NULL, prefix_len, out);
 }
 
@@ -116,12 +117,73 @@ void bdo_attention_fp8kv(int n, int D, int Hq, int Hkv, int d, int cap, int mode
                          const void *q, const void *k_blk, const void *v_blk, const void *k_cache,
                          const void *v_cache, const float *k_scale, const float *v_scale,
                          const int32_t *prefix_len, double *out) {
-    attention_impl(n, D, Hq, Hkv, d, cap, BDO_BF16, BDO_FP8, mode, scale, q, k_blk, v_blk, k_cache, v_cache,
+    attention_impl(n, D, Hq, Hkv, d, cap, BDO_BF16, BDO_FP8, mode, 0, scale, q, k_blk, v_blk, k_cache, v_cache,
                    k_scale, v_scale, prefix_len, out);
 }
 
+static int quad_slots(int B);
+
+/* The quadratic self-speculative mask (bdo_attention_quad) over an FP8 KV cache. */
+void bdo_attention_quad_fp8kv(int n, int B, int Hq, int Hkv, int d, int cap, double scale, const void *q,
+                              const void *k_blk, const void *v_blk, const void *k_cache, const void *v_cache,
+                              const float *k_scale, const float *v_scale, const int32_t *prefix_len,
+                              double *out) {
+    attention_impl(n, quad_slots(B), Hq, Hkv, d, cap, BDO_BF16, BDO_FP8, BDO_QUAD, B, scale, q, k_blk, v_blk,
+                   k_cache, v_cache, k_scale, v_scale, prefix_len, out);
+}
+
+/*
+ * Quadratic self-speculative attention ([FD] 5.3, the quadratic variant;
+ * [FD] Fig. 6 and section 9.3 on its kernel).  One forward pass both
+ * verifies a block of B draft tokens and proposes the next block for every
+ * possible acceptance length: the B drafts are expanded into B groups of B
+ * tokens, group g holding draft tokens 0..g-1 (the hypothesis that they are
+ * accepted) followed by B - g mask tokens that draft what comes next.
+ * Within a group the drafts attend causally and the mask tokens attend to
+ * the whole group; groups do not see each other; everything sees the
+ * cache.  (The pages state the B x B expansion and a non-standard mask;
+ * this mask is the reading of that expansion: causal verify plus
+ * bidirectional draft, per hypothesis.)
+ *
+ * A draft token's keys and values are the same in every group that holds
+ * it (its context, the cache and the drafts before it, is the same), so
+ * the slots here hold each draft once: slot t < B is draft token t, then
+ * group g's mask tokens t = g..B-1 follow in group order (B - g slots per
+ * group, B (B + 3) / 2 slots in all).  Visibility of block slot b from
+ * query slot i:
+ *   draft t     : draft slots t' <= t;
+ *   mask of g   : draft slots t' < g, and every mask slot of group g.
+ * Cache positions 0..P-1 are visible to every slot.
+ */
+static int quad_slots(int B) { return B * (B + 3) / 2; }
+
+/* Group of block slot i: -1 for a draft slot, else g with its mask tokens. */
+static int quad_group(int B, int i) {
+    if (i < B) return -1;
+    int rest = i - B;
+    for (int g = 0; g < B; ++g) {
+        if (rest < B - g) return g;
+        rest -= B - g;
+    }
+    return B; /* not reached for i < quad_slots(B) */
+}
+
+static int quad_visible(int B, int i, int b) {
+    const int gi = quad_group(B, i), gb = quad_group(B, b);
+    if (gi < 0) return gb < 0 && b <= i; /* draft query: causal over the drafts */
+    if (gb < 0) return b < gi;           /* mask query: the drafts its group assumes */
+    return gb == gi;                     /* ... and its own group's mask tokens */
+}
+
+void bdo_attention_quad(int n, int B, int Hq, int Hkv, int d, int cap, int dtype, double scale,
+                        const void *q, const void *k_blk, const void *v_blk, const void *k_cache,
+                        const void *v_cache, const int32_t *prefix_len, double *out) {
+    attention_impl(n, quad_slots(B), Hq, Hkv, d, cap, dtype, dtype, BDO_QUAD, B, scale, q, k_blk, v_blk,
+                   k_cache, v_cache, NULL, NULL, prefix_len, out);
+}
+
 static void attention_impl(int n, int D, int Hq, int Hkv, int d, int cap, int q_dtype, int kv_dtype,
-                           int mode, double scale, const void *q, const void *k_blk, const void *v_blk,
+                           int mode, int B, double scale, const void *q, const void *k_blk, const void *v_blk,
                            const void *k_cache, const void *v_cache, const float *k_scale,
                            const float *v_scale, const int32_t *prefix_len, double *out) {
     const int group = Hq / Hkv;
@@ -140,7 +202,8 @@ static void attention_impl(int n, int D, int Hq, int Hkv, int d, int cap, int q_
         const size_t qoff = (((size_t)it * D + i) * Hq + h) * (size_t)d;
         double m = -INFINITY;
         for (int j = 0; j < nkeys; ++j) {
-            int allowed = (j < P) || (mode == BDO_BIDIR) || (j - P <= i);
+            int allowed = (j < P) || (mode == BDO_BIDIR) || (mode == BDO_CAUSAL && j - P <= i) ||
+                          (mode == BDO_QUAD && quad_visible(B, i, j - P));
             if (!allowed) { s[j] = -INFINITY; continue; }
             double acc = 0.0;
             for (int t = 0; t < d; ++t) {

@@ -18,6 +18,7 @@ FP8KV = 2   # bf16 queries, OCP E4M3 keys and values with one fp32 scale per (it
 
 BIDIR = 0   # denoise step: the whole current block is visible to each slot
 CAUSAL = 1  # verify step: slot i sees the block only up to itself
+QUAD = 2    # quadratic self-speculative step: B drafts (causal) + B groups of mask tokens
 
 CONFIGS = {
     1: dict(
@@ -78,3 +79,19 @@ LMHEAD_CONFIGS = {
 
 def lmhead_seed_of(cfg_id: int) -> int:
     return 2000 + int(cfg_id)
+
+
+# Quadratic self-speculative step (Fast-dVLM write-up, section 5.3, the quadratic
+# variant; Fig. 6 sweeps block sizes 4..32): the 3B long-reasoning shape of config 3
+# with a draft block of B = 16, i.e. B (B + 3) / 2 = 152 block slots per layer
+# (16 drafts, then 16 + 15 + ... + 1 mask tokens of the 16 acceptance hypotheses).
+QUAD_CONFIGS = {
+    1: dict(name="3B quadratic speculative step: 36 layers x (16q/2kv, d128, bf16, prefix 4096), B=16 (152 slots)",
+            n_items=36, Hq=16, Hkv=2, d=128, dtype=BF16, prefix=("fixed", 4096), B=16),
+    2: dict(name="small quadratic step: 3 items, 8q/2kv, d128, bf16, prefixes 0/77/300, B=5 (20 slots)",
+            n_items=3, Hq=8, Hkv=2, d=128, dtype=BF16, prefix=("list", [0, 77, 300]), B=5),
+}
+
+
+def quad_seed_of(cfg_id: int) -> int:
+    return 3000 + int(cfg_id)

@@ -29,7 +29,8 @@ token ids, logits, then plants.
 
 import numpy as np
 
-from .configs import BF16, CONFIGS, F32, FP8KV, LMHEAD_CONFIGS, lmhead_seed_of, seed_of
+from .configs import (BF16, CONFIGS, F32, FP8KV, LMHEAD_CONFIGS, QUAD, QUAD_CONFIGS, lmhead_seed_of, quad_seed_of,
+                      seed_of)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -250,3 +251,29 @@ def _make_step_fp8kv(p, rng, prefix, cap, plant_L, seed):
     return dict(params=p, seed=seed, cap=cap, prefix=prefix, q=q, k_cache=k_cache, v_cache=v_cache,
                 k_blk=k_blk, v_blk=v_blk, k_scale=k_scale, v_scale=v_scale, masked=rest["masked"],
                 tokens=rest["tokens"], logits=rest["logits"], **{k: rest[k] for k in ("draft", "planted_L") if k in rest})
+
+
+def quad_slot_count(B: int) -> int:
+    """Block slots of a quadratic self-speculative step (layout only): B drafts,
+    then B - g mask tokens for each group g = 0..B-1."""
+    return B * (B + 3) // 2
+
+
+def make_quad_step(p: dict, seed: int) -> dict:
+    """Inputs of one quadratic self-speculative attention step: make_step's draws
+    (prefix, Q, cache K/V, block K/V) with quad_slot_count(B) block slots.  The
+    commit-side fields are drawn for one request over 2 tokens and are unused.
+    ``params`` keeps D = slot count, B and mode = QUAD."""
+    B = int(p["B"])
+    S = quad_slot_count(B)
+    q = dict(p, D=S, mode=QUAD, n_req=1, n_masked=0, V=2, plant=None, S=1, tau=1.0, logit_sigma2=1.0)
+    st = make_step(q, seed)
+    st["params"] = q
+    return st
+
+
+def quad_step(cfg_id: int, **overrides) -> dict:
+    """The canonical seeded quadratic step (seed 3000 + config number)."""
+    p = dict(QUAD_CONFIGS[cfg_id])
+    p.update(overrides)
+    return make_quad_step(p, quad_seed_of(cfg_id))

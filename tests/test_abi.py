@@ -50,7 +50,7 @@ BAD_ATTN = [
     (dict(d=96), "BD_E_SHAPE"), (dict(D=0), "BD_E_SHAPE"), (dict(D=65), "BD_E_SHAPE"),
     (dict(Hq=15), "BD_E_SHAPE"), (dict(Hkv=0), "BD_E_SHAPE"), (dict(cap=4161), "BD_E_SHAPE"),
     (dict(max_prefix=5000), "BD_E_SHAPE"), (dict(max_prefix=-1), "BD_E_SHAPE"), (dict(n_items=0), "BD_E_SHAPE"),
-    (dict(dtype=7), "BD_E_DTYPE"), (dict(mode=2), "BD_E_PARAM"), (dict(scale=float("nan")), "BD_E_PARAM"),
+    (dict(dtype=7), "BD_E_DTYPE"), (dict(mode=3), "BD_E_PARAM"), (dict(scale=float("nan")), "BD_E_PARAM"),
     (dict(scale=0.0), "BD_E_PARAM"), (dict(scale=float("inf")), "BD_E_PARAM"),
 ]
 
@@ -121,6 +121,27 @@ def test_fp8kv_dtype_routing_and_errors(bd):
         assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == 0
     # kv_append copies E4M3 bytes; its capacity rule follows the dtype.
     assert bd.lib.bd_kv_append(ctypes.byref(_attn(bd, dtype=bd.BD_FP8KV, cap=4168)), fake, fake, fake, fake, fake,
+                               None, None, None) == bd.BD_E_SHAPE
+
+
+def test_quad_mode_validation(bd):
+    """Quadratic mode: D is the draft block size B (1..32); its block holds B (B + 3) / 2 slots."""
+    fake = 1 << 20
+    for B, code in ((0, "BD_E_SHAPE"), (33, "BD_E_SHAPE")):
+        desc = _attn(bd, mode=bd.BD_BLOCK_QUAD, D=B)
+        assert bd.lib.bd_attn_step(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 30,
+                                   None) == getattr(bd, code)
+        assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
+    for B in (1, 16, 32):
+        desc = _attn(bd, mode=bd.BD_BLOCK_QUAD, D=B)
+        assert 0 < bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) < bd.SIZE_MAX
+    # More slots mean more rows, hence more workspace, than the same B as a plain block.
+    quad = bd.lib.bd_attn_workspace_bytes(ctypes.byref(_attn(bd, mode=bd.BD_BLOCK_QUAD, D=16)))
+    plain = bd.lib.bd_attn_workspace_bytes(ctypes.byref(_attn(bd, mode=bd.BD_BLOCK_BIDIR, D=16)))
+    assert quad > plain
+    assert bd.lib.bd_kv_append(ctypes.byref(_attn(bd, mode=3)), fake, fake, fake, fake, fake, None, None,
+                               None) == bd.BD_E_PARAM
+    assert bd.lib.bd_kv_append(ctypes.byref(_attn(bd, mode=bd.BD_BLOCK_QUAD, D=33)), fake, fake, fake, fake, fake,
                                None, None, None) == bd.BD_E_SHAPE
 
 

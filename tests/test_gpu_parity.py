@@ -19,7 +19,7 @@ import pytest
 
 import oracle
 import synth
-from synth import BF16, BIDIR, CAUSAL, F32, FP8KV
+from synth import BF16, BIDIR, CAUSAL, F32, FP8KV, QUAD
 
 pytestmark = pytest.mark.gpu
 
@@ -70,15 +70,22 @@ def _run_attention(dev, step_np, mode=None, label=""):
         np.unique(step_np["prefix"])[:8].tolist()))
     ds.attn(mode=mode)
     got = _out_host(dev, ds)
-    if p["dtype"] == FP8KV:
-        ref = oracle.attention_fp8kv(step_np["q"], step_np["k_blk"], step_np["v_blk"], step_np["k_cache"],
-                                     step_np["v_cache"], step_np["k_scale"], step_np["v_scale"],
-                                     step_np["prefix"], mode)
-    else:
-        ref = oracle.attention(step_np["q"], step_np["k_blk"], step_np["v_blk"], step_np["k_cache"],
-                               step_np["v_cache"], step_np["prefix"], mode)
+    ref = _reference(step_np, mode)
     _check_attention(got, ref, label)
     return ds, got
+
+
+def _reference(step_np, mode, items=None):
+    """The oracle's attention for the step (all items, or the listed ones)."""
+    p = step_np["params"]
+    sl = (lambda a: a) if items is None else (lambda a: np.ascontiguousarray(a[items]))
+    args = [sl(step_np[k]) for k in ("q", "k_blk", "v_blk", "k_cache", "v_cache")]
+    if p["dtype"] == FP8KV:
+        return oracle.attention_fp8kv(*args, sl(step_np["k_scale"]), sl(step_np["v_scale"]), sl(step_np["prefix"]),
+                                      mode, B=p.get("B"))
+    if mode == QUAD:
+        return oracle.attention_quad(*args, sl(step_np["prefix"]), p["B"])
+    return oracle.attention(*args, sl(step_np["prefix"]), mode)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -217,6 +224,78 @@ def test_fp8kv_deterministic_append_and_reattend(dev):
     got = _out_host(dev, ds)
     ref = oracle.attention_fp8kv(s2["q"], s2["k_blk"], s2["v_blk"], kc, vc, s["k_scale"], s["v_scale"], pref, BIDIR)
     _check_attention(got, ref, "fp8kv_after_append")
+
+
+# ---------------------------------------------------------------------------
+# Quadratic self-speculative attention (BD_BLOCK_QUAD): B drafts, causal among
+# themselves, then B groups of mask tokens, group g seeing drafts 0..g-1 and
+# itself.  Same bar as the bf16 attention.
+# ---------------------------------------------------------------------------
+
+def test_quad_small_config(dev):
+    _run_attention(dev, synth.quad_step(2), label="quad_small")
+
+
+def test_quad_3b_sampled_items(dev):
+    """The 3B quadratic step at its full size (36 layers, prefix 4096, B = 16, 152
+    slots): the GPU computes every layer in the launch that bench.py times; the
+    oracle checks three whole layers of it."""
+    st = synth.quad_step(1)
+    ds = dev["step"].DeviceStep(st)
+    p = st["params"]
+    _say("quad 3b: n=%d slots=%d B=%d" % (p["n_items"], p["D"], p["B"]))
+    ds.attn()
+    got = _out_host(dev, ds)
+    items = [0, 17, 35]
+    ref = _reference(st, QUAD, items=items)
+    _check_attention(got[items], ref, "quad_3b_items")
+
+
+QUAD_CASES = [
+    ("B1", dict(B=1, prefix=("list", [0, 50, 64]))),
+    ("B2_ragged", dict(B=2, prefix=("list", [31, 32, 33]))),
+    ("B8_G7", dict(B=8, Hq=28, Hkv=4, prefix=("list", [70, 500, 1]))),
+    ("B16_ragged", dict(B=16, n_items=4, prefix=("list", [0, 95, 96, 1200]))),
+    ("B32_560_slots", dict(B=32, n_items=1, prefix=("fixed", 100))),
+    ("d64", dict(B=6, d=64, prefix=("list", [333, 64, 0]))),
+]
+
+
+@pytest.mark.parametrize("label,ov", QUAD_CASES, ids=[c[0] for c in QUAD_CASES])
+def test_quad_edge_cases(dev, label, ov):
+    p = dict(synth.QUAD_CONFIGS[2])
+    p.update(ov)
+    _run_attention(dev, synth.make_quad_step(p, zlib.crc32(("quad" + label).encode()) % 10000), label="quad_" + label)
+
+
+@pytest.mark.parametrize("dtype", [F32, FP8KV])
+def test_quad_fp32_and_fp8kv(dev, dtype):
+    """The quadratic mask on the fp32 vector path and on the E4M3 KV-cache path."""
+    p = dict(synth.QUAD_CONFIGS[2], dtype=dtype, B=6, prefix=("list", [0, 129, 700]))
+    if dtype == F32:
+        p.update(Hq=6, Hkv=2, d=64)
+    _run_attention(dev, synth.make_quad_step(p, 99 + dtype), label="quad_dtype%d" % dtype)
+
+
+def test_quad_append_accepted_drafts(dev):
+    """After a quadratic step the accepted drafts (slots 0..L-1 of the B (B + 3) / 2)
+    join the cache; L > B is refused on the device."""
+    torch = dev["torch"]
+    B = 5
+    st = synth.make_quad_step(dict(synth.QUAD_CONFIGS[2], B=B), 123)
+    ds = dev["step"].DeviceStep(st)
+    acc = np.array([B, 0, 3], np.int32)
+    ds.append(n_accept=torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+    kc, vc, pref, err = oracle.kv_append(st["k_cache"], st["v_cache"], st["prefix"], st["k_blk"], st["v_blk"], acc)
+    assert err == 0 and int(ds.dev_err.cpu()[0]) == 0
+    np.testing.assert_array_equal(ds.prefix.cpu().numpy(), pref)
+    assert ds.k_cache.cpu().numpy().view(np.uint16).tobytes() == kc.tobytes()
+    assert ds.v_cache.cpu().numpy().view(np.uint16).tobytes() == vc.tobytes()
+    ds.append(n_accept=torch.tensor([B + 1, 0, 0], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(ds.dev_err.cpu()[0]) == 1
+    np.testing.assert_array_equal(ds.prefix.cpu().numpy(), pref)  # item 0 refused, the others add 0
 
 
 # ---------------------------------------------------------------------------

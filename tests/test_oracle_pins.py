@@ -114,6 +114,90 @@ def test_attention_matches_two_stream_dense_mask(dtype, Hq, Hkv, d):
         np.testing.assert_allclose(out[0], np.swapaxes(ref[:, cl], 0, 1), rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------------------
+# Quadratic self-speculative attention (Fast-dVLM write-up, section 5.3, the
+# quadratic variant): the oracle's compact slot form against (a) the causal
+# verify pass over the drafts, (b) a denoise pass per acceptance hypothesis,
+# and (c) the literal B x B expansion evaluated with a dense mask by SDPA.
+# ---------------------------------------------------------------------------
+
+def _quad_layout(B):
+    """[(group, token)] of the compact slots: drafts (-1, t), then (g, t) for t = g..B-1."""
+    return [(-1, t) for t in range(B)] + [(g, t) for g in range(B) for t in range(g, B)]
+
+
+def _quad_inputs(rng, B, Hq, Hkv, d, P, dtype):
+    S = oracle.quad_slots(B)
+    q = _rand(rng, (1, S, Hq, d), dtype)
+    kb = _rand(rng, (1, S, Hkv, d), dtype)
+    vb = _rand(rng, (1, S, Hkv, d), dtype)
+    kseq = _rand(rng, (Hkv, P, d), dtype)
+    vseq = _rand(rng, (Hkv, P, d), dtype)
+    return q, kb, vb, kseq, vseq
+
+
+@pytest.mark.parametrize("B", [1, 2, 5])
+def test_quad_draft_rows_are_the_causal_verify_pass(B):
+    rng = np.random.Generator(np.random.PCG64(60 + B))
+    Hq, Hkv, d, P = 4, 2, 8, 9
+    q, kb, vb, kseq, vseq = _quad_inputs(rng, B, Hq, Hkv, d, P, F32)
+    kc, vc = _pack_cache(kseq, vseq, P + oracle.quad_slots(B) + 2, F32)
+    pre = np.array([P], np.int32)
+    out = oracle.attention_quad(q, kb, vb, kc, vc, pre, B)
+    ref = oracle.attention(q[:, :B], kb[:, :B], vb[:, :B], kc, vc, pre, CAUSAL)
+    np.testing.assert_allclose(out[:, :B], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B", [1, 3, 6])
+def test_quad_group_rows_are_a_denoise_pass_over_the_accepted_drafts(B):
+    """Group g's mask tokens see the cache plus drafts 0..g-1 as context and their
+    own group bidirectionally: a denoise step whose cache holds those drafts."""
+    rng = np.random.Generator(np.random.PCG64(70 + B))
+    Hq, Hkv, d, P = 6, 3, 8, 7
+    q, kb, vb, kseq, vseq = _quad_inputs(rng, B, Hq, Hkv, d, P, BF16)
+    cap = P + oracle.quad_slots(B) + 4
+    kc, vc = _pack_cache(kseq, vseq, cap, BF16)
+    out = oracle.attention_quad(q, kb, vb, kc, vc, np.array([P], np.int32), B)
+    slots = _quad_layout(B)
+    for g in range(B):
+        rows = [i for i, (gg, _) in enumerate(slots) if gg == g]
+        ctx_k = np.concatenate([kseq, np.swapaxes(kb[0, :g], 0, 1)], axis=1)
+        ctx_v = np.concatenate([vseq, np.swapaxes(vb[0, :g], 0, 1)], axis=1)
+        kc_g, vc_g = _pack_cache(ctx_k, ctx_v, cap, BF16)
+        ref = oracle.attention(q[:, rows], kb[:, rows], vb[:, rows], kc_g, vc_g, np.array([P + g], np.int32), BIDIR)
+        np.testing.assert_allclose(out[:, rows], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B", [2, 4])
+def test_quad_matches_the_b_by_b_expansion_with_a_dense_mask(B):
+    """The literal form: B groups of B tokens, group g = drafts 0..g-1 then B - g mask
+    tokens; inside a group drafts are causal and mask tokens see the whole group; no
+    group sees another; all see the cache.  Evaluated densely by SDPA over
+    [cache ; B*B expanded tokens]; every expanded row equals its compact slot's row."""
+    rng = np.random.Generator(np.random.PCG64(80 + B))
+    Hq, Hkv, d, P = 4, 1, 16, 11
+    q, kb, vb, kseq, vseq = _quad_inputs(rng, B, Hq, Hkv, d, P, F32)
+    kc, vc = _pack_cache(kseq, vseq, P + oracle.quad_slots(B), F32)
+    out = oracle.attention_quad(q, kb, vb, kc, vc, np.array([P], np.int32), B)
+    slots = _quad_layout(B)
+    index = {gt: i for i, gt in enumerate(slots)}
+    src = []                                   # compact slot of every expanded token
+    for g in range(B):
+        src += [index[(-1, t)] for t in range(g)] + [index[(g, t)] for t in range(g, B)]
+    L = B * B
+    mask = np.zeros((L, P + L), bool)
+    mask[:, :P] = True
+    for g in range(B):
+        for t in range(B):
+            for t2 in range(B):
+                mask[g * B + t, P + g * B + t2] = (t >= g) or (t2 <= t)
+    Q = np.swapaxes(q[0, src], 0, 1)
+    K = np.concatenate([kseq, np.swapaxes(kb[0, src], 0, 1)], axis=1)
+    V = np.concatenate([vseq, np.swapaxes(vb[0, src], 0, 1)], axis=1)
+    ref = _sdpa(_widen(Q), _widen(K), _widen(V), mask, Hq // Hkv)
+    np.testing.assert_allclose(out[0, src], np.swapaxes(ref, 0, 1), rtol=0, atol=1e-12)
+
+
 def _random_step(rng, n, D, Hq, Hkv, d, P, dtype, cap=None):
     prefix = np.asarray(P, np.int32)
     cap = cap or int(prefix.max()) + D + 5
@@ -573,4 +657,21 @@ def test_attention_fp8kv_equals_attention_on_dequantized_values(mode):
     vb = dec(st["v_blk"], vs, 2)
     # NaN canaries past the prefix stay NaN in the dequantized cache and must not be read
     want = oracle.attention(qf, kb, vb, kc, vc, st["prefix"], mode)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_quad_fp8kv_equals_quad_on_dequantized_values():
+    """The quadratic mask over an E4M3 cache (power-of-two scales, so every
+    dequantized value is exact in fp32) equals the plain quadratic oracle."""
+    B = 4
+    p = dict(synth.QUAD_CONFIGS[2], n_items=2, Hq=4, Hkv=2, d=64, B=B, prefix=("list", [21, 66]), dtype=synth.FP8KV)
+    st = synth.make_quad_step(p, 31)
+    ks = np.exp2(np.round(np.log2(st["k_scale"]))).astype(np.float32)
+    vs = np.exp2(np.round(np.log2(st["v_scale"]))).astype(np.float32)
+    got = oracle.attention_fp8kv(st["q"], st["k_blk"], st["v_blk"], st["k_cache"], st["v_cache"], ks, vs,
+                                 st["prefix"], oracle.QUAD, B=B)
+    dec = lambda a, sc, axis_g: (oracle.fp8_e4m3_decode(a) * np.expand_dims(sc, axis=tuple(
+        i for i in range(a.ndim) if i not in (0, axis_g)))).astype(np.float32)
+    want = oracle.attention_quad(synth.bf16_bits_to_f32(st["q"]), dec(st["k_blk"], ks, 2), dec(st["v_blk"], vs, 2),
+                                 dec(st["k_cache"], ks, 1), dec(st["v_cache"], vs, 1), st["prefix"], B)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libbd.so")
 
 BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH = range(7)
 BD_F32, BD_BF16, BD_FP8KV = 0, 1, 2
-BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL = 0, 1
+BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL, BD_BLOCK_QUAD = 0, 1, 2
 SIZE_MAX = (1 << 64) - 1
 
 

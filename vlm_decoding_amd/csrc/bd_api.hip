@@ -15,18 +15,21 @@ thread_local int32_t g_last_hip_error = 0;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Block slots per item: D, or B (B + 3) / 2 for the quadratic mode (D = B).
+int block_slots(const bd_attn_desc *d) { return d->mode == BD_BLOCK_QUAD ? d->D * (d->D + 3) / 2 : d->D; }
+
 bd_status check_attn_desc(const bd_attn_desc *d) {
     if (!d) return BD_E_NULL;
     if (d->dtype != BD_F32 && d->dtype != BD_BF16 && d->dtype != BD_FP8KV) return BD_E_DTYPE;
-    if (d->mode != BD_BLOCK_BIDIR && d->mode != BD_BLOCK_CAUSAL) return BD_E_PARAM;
+    if (d->mode != BD_BLOCK_BIDIR && d->mode != BD_BLOCK_CAUSAL && d->mode != BD_BLOCK_QUAD) return BD_E_PARAM;
     if (!(d->scale > 0.f) || !isfinite(d->scale)) return BD_E_PARAM;
-    if (d->n_items < 1 || d->D < 1 || d->D > 64) return BD_E_SHAPE;
+    if (d->n_items < 1 || d->D < 1 || d->D > (d->mode == BD_BLOCK_QUAD ? 32 : 64)) return BD_E_SHAPE;
     if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return BD_E_SHAPE;
     if (d->d != 64 && d->d != 128) return BD_E_SHAPE;
     if (d->cap < 1 || d->cap % (d->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
     if (d->max_prefix < 0 || d->max_prefix > d->cap) return BD_E_SHAPE;
     // Index arithmetic in the kernels uses 32-bit ints for per-item quantities.
-    if ((int64_t)d->D * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
+    if ((int64_t)block_slots(d) * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
     return BD_OK;
 }
 
@@ -66,7 +69,7 @@ extern "C" {
 
 size_t bd_attn_workspace_bytes(const bd_attn_desc *desc) {
     if (check_attn_desc(desc) != BD_OK) return SIZE_MAX;
-    const bd::AttnPlan pl = bd::plan_attention(desc->n_items, desc->D, desc->Hq, desc->Hkv, desc->d,
+    const bd::AttnPlan pl = bd::plan_attention(desc->n_items, block_slots(desc), desc->Hq, desc->Hkv, desc->d,
                                                desc->dtype, desc->max_prefix);
     return pl.ws_bytes;
 }
@@ -76,7 +79,7 @@ bd_status attn_common(const bd_attn_desc *desc, const void *q, const void *k_blk
                       const void *k_cache, const void *v_cache, const float *k_scale, const float *v_scale,
                       const int32_t *prefix_len, void *out, void *workspace, size_t workspace_bytes,
                       void *stream) {
-    const bd::AttnPlan pl = bd::plan_attention(desc->n_items, desc->D, desc->Hq, desc->Hkv, desc->d,
+    const bd::AttnPlan pl = bd::plan_attention(desc->n_items, block_slots(desc), desc->Hq, desc->Hkv, desc->d,
                                                desc->dtype, desc->max_prefix);
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
         return BD_E_WORKSPACE;
@@ -92,7 +95,8 @@ bd_status attn_common(const bd_attn_desc *desc, const void *q, const void *k_blk
     a.out = out;
     a.ws = workspace;
     a.n = desc->n_items;
-    a.D = desc->D;
+    a.D = block_slots(desc);
+    a.B = desc->mode == BD_BLOCK_QUAD ? desc->D : 0;
     a.Hq = desc->Hq;
     a.Hkv = desc->Hkv;
     a.d = desc->d;
@@ -201,13 +205,17 @@ bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache, i
                        void *stream) {
     if (!desc) return BD_E_NULL;
     if (desc->dtype != BD_F32 && desc->dtype != BD_BF16 && desc->dtype != BD_FP8KV) return BD_E_DTYPE;
-    if (desc->n_items < 1 || desc->D < 1 || desc->D > 64 || desc->Hkv < 1) return BD_E_SHAPE;
+    if (desc->mode != BD_BLOCK_BIDIR && desc->mode != BD_BLOCK_CAUSAL && desc->mode != BD_BLOCK_QUAD) return BD_E_PARAM;
+    if (desc->n_items < 1 || desc->D < 1 || desc->D > (desc->mode == BD_BLOCK_QUAD ? 32 : 64) || desc->Hkv < 1)
+        return BD_E_SHAPE;
     if (desc->d != 64 && desc->d != 128) return BD_E_SHAPE;
     if (desc->cap < 1 || desc->cap % (desc->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
     if (!k_cache || !v_cache || !prefix_len || !k_blk || !v_blk) return BD_E_NULL;
-    return launched(bd::launch_kv_append(desc->n_items, desc->D, desc->Hkv, desc->d, desc->cap,
-                                         desc->dtype == BD_F32 ? 4 : desc->dtype == BD_BF16 ? 2 : 1, k_cache, v_cache, prefix_len, k_blk,
-                                         v_blk, n_accept, dev_err, (hipStream_t)stream));
+    // Quadratic mode: the block holds B (B + 3) / 2 slots, of which the first B
+    // (the drafts) can be accepted.
+    return launched(bd::launch_kv_append(desc->n_items, desc->D, block_slots(desc), desc->Hkv, desc->d, desc->cap,
+                                         desc->dtype == BD_F32 ? 4 : desc->dtype == BD_BF16 ? 2 : 1, k_cache,
+                                         v_cache, prefix_len, k_blk, v_blk, n_accept, dev_err, (hipStream_t)stream));
 }
 
 size_t bd_lmhead_workspace_bytes(const bd_lmhead_desc *desc) {

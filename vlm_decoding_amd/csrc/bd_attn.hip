@@ -44,9 +44,37 @@ struct MfmaParams {
     float *ws_o;
     float2 *ws_ml;
     int n, D, Hq, Hkv, G, cap, mode;
+    int B;  // quadratic mode: draft block size (D = B (B + 3) / 2 slots)
     int R, row_blocks, max_splits, tiles_per_split, total_logical;
     float c;  // scale * log2(e)
 };
+
+// Block slots a query slot may attend to, as two half-open slot ranges
+// [0, hi1) and [lo2, hi2).  Cache positions, given as negative slot numbers,
+// are visible to every slot (hi1 >= 0).
+//  BIDIR (mode 0): the whole block.  CAUSAL (mode 1): slots 0..slot.
+//  QUAD (mode 2), the quadratic self-speculative block (Fast-dVLM write-up,
+//  section 5.3): slots 0..B-1 are the drafts, causal among themselves; then
+//  group g = 0..B-1 holds B - g mask tokens, which see drafts 0..g-1 and
+//  every mask token of their own group.
+struct SlotRanges {
+    int hi1, lo2, hi2;
+};
+__device__ __forceinline__ SlotRanges block_ranges(int mode, int slot, int D, int B) {
+    if (mode == 0) return {D, 0, 0};
+    if (mode == 1 || slot < B) return {slot + 1, 0, 0};
+    int m = slot - B, g = 0, start = B;
+    while (g < B && m >= B - g) {
+        m -= B - g;
+        start += B - g;
+        ++g;
+    }
+    return {g, start, start + (B - g)};
+}
+// Bitwise, not short-circuit: the result feeds a select, with no branches.
+__device__ __forceinline__ bool in_ranges(const SlotRanges &r, int b) {
+    return (b < r.hi1) | ((b >= r.lo2) & (b < r.hi2));
+}
 
 // Row permutations of the K operand.  A-row rho (= lane % 32) of a 32-key
 // block loads key pi(rho).
@@ -224,6 +252,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const bool wave_active = rb * RPG + w * 32 < p.R;
     const int slot = r / p.G;
     const int head = g * p.G + (r - slot * p.G);
+    const SlotRanges vis = row_valid ? block_ranges(p.mode, slot, p.D, p.B) : SlotRanges{0, 0, 0};
     bf16x8 qf[KC];
     {
         const uint16_t *qp = p.q + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
@@ -358,21 +387,23 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             *reinterpret_cast<u32x4 *>(vbuf(st) + v_at(dd, lu)) = vr[i];
         }
         bd_barrier_lds();  // the scatter below overwrites zeros written above
-        // Block V units that land in this tile: slot b covers tail position pc + b.
-        constexpr int VB_MAX = (64 * BU + NT - 1) / NT;  // D <= 64
-        u32x4 br[VB_MAX];
-        int bkey[VB_MAX];
+        // Block V units that land in this tile: slot b covers tail position pc + b,
+        // so this tile holds slots b0 .. b0 + TK - 1 (those in 0..D-1).
+        constexpr int VB_N = (TK * BU + NT - 1) / NT;
+        const int b0 = tt * TK - pc;
+        u32x4 br[VB_N];
+        int bkey[VB_N];
 #pragma unroll
-        for (int i = 0; i < VB_MAX; ++i) {
+        for (int i = 0; i < VB_N; ++i) {
             const int u = tid + i * NT;
-            const int b = u / BU, du = u % BU;
-            const int j = pc + b - tt * TK;  // key index inside this tile
-            bkey[i] = (b < p.D && j >= 0 && j < TK) ? j : -1;
+            const int key = u / BU, du = u % BU;  // key index inside this tile
+            const int b = b0 + key;
+            bkey[i] = (u < TK * BU && b >= 0 && b < p.D) ? key : -1;
             if (bkey[i] >= 0)
                 br[i] = *reinterpret_cast<const u32x4 *>(p.vb + (((size_t)it * p.D + b) * p.Hkv + g) * HD * EB + du * 16);
         }
 #pragma unroll
-        for (int i = 0; i < VB_MAX; ++i) {
+        for (int i = 0; i < VB_N; ++i) {
             if (bkey[i] < 0) continue;
             const int u = tid + i * NT;
             const int du = u % BU;
@@ -420,12 +451,9 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
                 for (int i = 0; i < 16; ++i) {
                     const int kin = KV8 ? 16 * half + i : 16 * (i >> 3) + 8 * half + (i & 7);
                     const int j = tt * TK + kb * 32 + kin;
-                    bool ok = j < tail_len;
-                    if (p.mode == 1) {
-                        const int pos = Pb + j;
-                        ok = ok && (pos < P || pos - P <= slot);
-                    }
-                    if (!ok) s[kb][i] = -INFINITY;
+                    const int b = Pb + j - P;  // block slot (a cache position if < 0)
+                    const bool ok = (j < tail_len) & in_ranges(vis, b);
+                    s[kb][i] = ok ? s[kb][i] : -INFINITY;
                 }
         }
         float mx = -INFINITY;
@@ -678,7 +706,7 @@ __device__ __forceinline__ void st(uint16_t *p, size_t i, float v) { p[i] = bd_f
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, const T *vb, const T *kc,
                                                        const T *vc, const int32_t *prefix, T *out, int n,
-                                                       int D, int Hq, int Hkv, int cap, int mode, float scale) {
+                                                       int D, int Hq, int Hkv, int cap, int mode, int B, float scale) {
     constexpr int PER = HD / 64;
     __shared__ float qs[4][HD];
     const int lane = threadIdx.x & 63;
@@ -695,6 +723,7 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
     if (!active) return;
     const int P = min(max(prefix[it], 0), cap);
     const int nk = P + D;
+    const SlotRanges vis = block_ranges(mode, slot, D, B);
     const size_t kc_base = ((size_t)it * Hkv + g) * cap * HD;
     const size_t vc_base = ((size_t)it * Hkv + g) * HD * cap;
     float m = -INFINITY, l = 0.f, o[PER];
@@ -702,7 +731,7 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
     for (int base = 0; base < nk; base += 64) {
         const int key = base + lane;
-        const bool valid = key < nk && (mode == 0 || key < P || key - P <= slot);
+        const bool valid = (key < nk) & in_ranges(vis, key - P);
         float s = -INFINITY;
         if (valid) {
             float acc = 0.f;
@@ -769,7 +798,11 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     // Splits per unit (the device side derives each unit's count from its own
     // prefix): sized so that a unit at max_prefix gets about `want` splits.
     pl.max_splits = ntiles_max == 0 ? 1 : std::max(2, std::min(std::min(want, ntiles_max + 1), kMaxSplits));
-    pl.tiles_per_split = std::max(1, (ntiles_max + 3 + pl.max_splits - 1) / pl.max_splits);
+    // Work of a unit at max_prefix in bulk-tile units: its bulk tiles plus
+    // kTailCost per tail tile (up to tk - 1 cache positions and the D slots).
+    const int ntail_max = (pl.tk - 1 + D + pl.tk - 1) / pl.tk;
+    const int work_max = ntiles_max + kTailCost * ntail_max;
+    pl.tiles_per_split = std::max(1, (work_max + pl.max_splits - 1) / pl.max_splits);
     const long total = (long)pl.units * pl.max_splits;
     pl.grid = (int)((total + 7) / 8 * 8);
     if (pl.max_splits > 1) {
@@ -824,6 +857,7 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.G = a.Hq / a.Hkv;
     p.cap = a.cap;
     p.mode = a.mode;
+    p.B = a.B;
     p.R = pl.rows;
     p.row_blocks = pl.row_blocks;
     p.max_splits = pl.max_splits;
@@ -850,23 +884,23 @@ hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {
         if (a.d == 128)
             hipLaunchKernelGGL((attn_vec_kernel<float, 128>), grid, block, 0, s, q, (const float *)a.k_blk,
                                (const float *)a.v_blk, (const float *)a.k_cache, (const float *)a.v_cache,
-                               a.prefix, (float *)a.out, a.n, a.D, a.Hq, a.Hkv, a.cap, a.mode, a.scale);
+                               a.prefix, (float *)a.out, a.n, a.D, a.Hq, a.Hkv, a.cap, a.mode, a.B, a.scale);
         else
             hipLaunchKernelGGL((attn_vec_kernel<float, 64>), grid, block, 0, s, q, (const float *)a.k_blk,
                                (const float *)a.v_blk, (const float *)a.k_cache, (const float *)a.v_cache,
-                               a.prefix, (float *)a.out, a.n, a.D, a.Hq, a.Hkv, a.cap, a.mode, a.scale);
+                               a.prefix, (float *)a.out, a.n, a.D, a.Hq, a.Hkv, a.cap, a.mode, a.B, a.scale);
     } else {
         auto *q = (const uint16_t *)a.q;
         if (a.d == 128)
             hipLaunchKernelGGL((attn_vec_kernel<uint16_t, 128>), grid, block, 0, s, q, (const uint16_t *)a.k_blk,
                                (const uint16_t *)a.v_blk, (const uint16_t *)a.k_cache,
                                (const uint16_t *)a.v_cache, a.prefix, (uint16_t *)a.out, a.n, a.D, a.Hq,
-                               a.Hkv, a.cap, a.mode, a.scale);
+                               a.Hkv, a.cap, a.mode, a.B, a.scale);
         else
             hipLaunchKernelGGL((attn_vec_kernel<uint16_t, 64>), grid, block, 0, s, q, (const uint16_t *)a.k_blk,
                                (const uint16_t *)a.v_blk, (const uint16_t *)a.k_cache,
                                (const uint16_t *)a.v_cache, a.prefix, (uint16_t *)a.out, a.n, a.D, a.Hq,
-                               a.Hkv, a.cap, a.mode, a.scale);
+                               a.Hkv, a.cap, a.mode, a.B, a.scale);
     }
     return hipGetLastError();
 }

@@ -34,6 +34,7 @@ struct AttnArgs {
     void *out;
     void *ws;
     int n, D, Hq, Hkv, d, cap, mode;
+    int B;  // quadratic mode: draft block size (D is then the slot count B (B + 3) / 2)
     float scale;
 };
 
@@ -93,7 +94,8 @@ struct LhArgs {
 hipError_t launch_lmhead(const LhPlan &plan, const LhArgs &a, hipStream_t s);
 
 // ---- KV append --------------------------------------------------------------
-hipError_t launch_kv_append(int n, int D, int Hkv, int d, int cap, int elem_bytes, void *k_cache,
+// D: most slots an item may append; S: block slots per item (the row stride of k_blk / v_blk).
+hipError_t launch_kv_append(int n, int D, int S, int Hkv, int d, int cap, int elem_bytes, void *k_cache,
                             void *v_cache, int32_t *prefix, const void *k_blk, const void *v_blk,
                             const int32_t *n_accept, int32_t *dev_err, hipStream_t s);
 

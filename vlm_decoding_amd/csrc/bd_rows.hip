@@ -250,7 +250,7 @@ hipError_t launch_spec_verify(const RowPlan &pl, const RowArgs &a, hipStream_t s
 // host round trip is needed between verify and append.
 // ---------------------------------------------------------------------------
 template <typename E>
-__global__ __launch_bounds__(256) void kv_append_kernel(int D, int Hkv, int d, int cap, E *k_cache, E *v_cache,
+__global__ __launch_bounds__(256) void kv_append_kernel(int D, int S, int Hkv, int d, int cap, E *k_cache, E *v_cache,
                                                         int32_t *prefix, const E *k_blk, const E *v_blk,
                                                         const int32_t *n_accept, int32_t *dev_err) {
     const int it = blockIdx.x;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(int D, int Hkv, int d, i
         const int t = e / per_t;
         const int g = (e / d) % Hkv;
         const int dd = e % d;
-        const size_t src = (((size_t)it * D + t) * Hkv + g) * d + dd;
+        const size_t src = (((size_t)it * S + t) * Hkv + g) * d + dd;
         k_cache[(((size_t)it * Hkv + g) * cap + (P + t)) * d + dd] = k_blk[src];
         v_cache[(((size_t)it * Hkv + g) * d + dd) * cap + (P + t)] = v_blk[src];
     }
@@ -273,19 +273,19 @@ __global__ __launch_bounds__(256) void kv_append_kernel(int D, int Hkv, int d, i
     if (threadIdx.x == 0) prefix[it] = P + L;
 }
 
-hipError_t launch_kv_append(int n, int D, int Hkv, int d, int cap, int elem_bytes, void *k_cache, void *v_cache,
+hipError_t launch_kv_append(int n, int D, int S, int Hkv, int d, int cap, int elem_bytes, void *k_cache, void *v_cache,
                             int32_t *prefix, const void *k_blk, const void *v_blk, const int32_t *n_accept,
                             int32_t *dev_err, hipStream_t s) {
     if (elem_bytes == 4)
-        hipLaunchKernelGGL((kv_append_kernel<uint32_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
+        hipLaunchKernelGGL((kv_append_kernel<uint32_t>), dim3(n), dim3(256), 0, s, D, S, Hkv, d, cap,
                            (uint32_t *)k_cache, (uint32_t *)v_cache, prefix, (const uint32_t *)k_blk,
                            (const uint32_t *)v_blk, n_accept, dev_err);
     else if (elem_bytes == 2)
-        hipLaunchKernelGGL((kv_append_kernel<uint16_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
+        hipLaunchKernelGGL((kv_append_kernel<uint16_t>), dim3(n), dim3(256), 0, s, D, S, Hkv, d, cap,
                            (uint16_t *)k_cache, (uint16_t *)v_cache, prefix, (const uint16_t *)k_blk,
                            (const uint16_t *)v_blk, n_accept, dev_err);
     else
-        hipLaunchKernelGGL((kv_append_kernel<uint8_t>), dim3(n), dim3(256), 0, s, D, Hkv, d, cap,
+        hipLaunchKernelGGL((kv_append_kernel<uint8_t>), dim3(n), dim3(256), 0, s, D, S, Hkv, d, cap,
                            (uint8_t *)k_cache, (uint8_t *)v_cache, prefix, (const uint8_t *)k_blk,
                            (const uint8_t *)v_blk, n_accept, dev_err);
     return hipGetLastError();

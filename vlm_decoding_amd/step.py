@@ -57,11 +57,17 @@ class DeviceStep:
         self.tokens = self.tokens0.clone()
         self.draft = to_device(step["draft"], device) if "draft" in step else None
         self.out = torch.empty_like(self.q)
-        self.adesc = bd.attn_desc(n, D, Hq, Hkv, d, self.cap, self.dtype, p["mode"], self.max_prefix)
+        # The quadratic mode's descriptor takes the draft block size B; its tensors hold D = B (B + 3) / 2 slots.
+        d_desc = p["B"] if p["mode"] == bd.BD_BLOCK_QUAD else D
+        self.adesc = bd.attn_desc(n, d_desc, Hq, Hkv, d, self.cap, self.dtype, p["mode"], self.max_prefix)
         self.cdesc = bd.commit_desc(p["n_req"], D, p["V"], p["S"], p["tau"])
         ab = bd.bd_attn_workspace_bytes(self.adesc)
         cb = bd.bd_commit_workspace_bytes(self.cdesc)
         vb = bd.bd_verify_workspace_bytes(p["n_req"], D, p["V"])
+        # A block shape the commit / verify calls do not take (the quadratic mode's
+        # slot count) leaves their workspaces minimal; those calls then report it.
+        cb = 16 if cb == bd.SIZE_MAX else cb
+        vb = 16 if vb == bd.SIZE_MAX else vb
         self.attn_ws = torch.zeros(max(ab, 16), dtype=torch.uint8, device=device)
         self.commit_ws = torch.zeros(max(cb, 16), dtype=torch.uint8, device=device)
         self.verify_ws = torch.zeros(max(vb, 16), dtype=torch.uint8, device=device)
