@@ -21,7 +21,8 @@ measures).  ``value`` is steps over the wall time of all timed steps.
 ``cpu_baseline`` times the fp64 CPU oracle on the host.  Two further legs
 measure the next rows of the path beside the headline: the LM head fused with
 the confidence + commit (``lm_head_confidence_commit``) and the same attention
-call over an E4M3 KV cache (``fp8kv_attention``).
+call over an E4M3 KV cache (``fp8kv_attention``), and the quadratic
+self-speculative step (``quad_spec_attention``).
 """
 
 import argparse
@@ -39,6 +40,7 @@ sys.path.insert(0, ROOT)
 CFG = 3
 N_SETS = 4
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 METRIC = "denoise steps/sec + achieved HBM GB/s (%peak), 3B-shape block-16, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_cfg3_traffic.json")
 ATTN_SOURCES = ["vlm_decoding_amd/csrc/bd_attn.hip", "vlm_decoding_amd/csrc/bd_common.h",
@@ -233,6 +235,72 @@ def bench_fp8kv_attention(torch, stream, calls=200, warmup=20):
                 traffic=traffic_per_launch("fp8kv_bytes_per_launch"))
 
 
+def bench_quad_attention(torch, stream, calls=50, warmup=5):
+    """The quadratic self-speculative step beside the headline: 36 layers of the
+    3B shape (prefix 4096) with a draft block of B = 16, i.e. 152 block slots per
+    layer (16 drafts + the mask tokens of 16 acceptance hypotheses), in one
+    bd_attn_step call (mode BD_BLOCK_QUAD).  The linear variant needs two block
+    passes for the same block, a bidirectional draft and a causal verify, each of
+    the headline call's shape; both are timed here the same way for comparison.
+    Work is MFMA-bound: the figure of merit is bf16 TFLOP/s over the algorithmic
+    flops (4 d per visible (row, key) pair: the two products)."""
+    import ctypes
+    import synth
+    from vlm_decoding_amd import bd
+    from vlm_decoding_amd.step import DeviceStep
+    sh = stream.cuda_stream
+
+    def timed(args_list, n_calls):
+        status = 0
+        for i in range(warmup):
+            for a in args_list[i % len(args_list)]:
+                status |= bd.lib.bd_attn_step(*a)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(n_calls):
+            for a in args_list[i % len(args_list)]:
+                status |= bd.lib.bd_attn_step(*a)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        if status:
+            raise RuntimeError("bd_attn_step failed (status %d)" % status)
+        return t0.elapsed_time(t1) * 1e3 / n_calls
+
+    def args_of(ds, desc):
+        return (ctypes.byref(desc), ds.q.data_ptr(), ds.k_blk.data_ptr(), ds.v_blk.data_ptr(), ds.k_cache.data_ptr(),
+                ds.v_cache.data_ptr(), ds.prefix.data_ptr(), ds.out.data_ptr(), ds.attn_ws.data_ptr(),
+                ds.attn_ws.numel(), sh)
+
+    qsets = [DeviceStep(synth.make_quad_step(dict(synth.QUAD_CONFIGS[1]), synth.quad_seed_of(1) + 1000 * k))
+             for k in range(N_SETS)]
+    quad_us = timed([[args_of(ds, ds.adesc)] for ds in qsets], calls)
+    p = qsets[0].p
+    B, S, n, Hq, d = p["B"], p["D"], p["n_items"], p["Hq"], p["d"]
+    P = int(qsets[0].prefix.cpu().numpy()[0])
+    del qsets
+    # Visible keys summed over the slots of one (item, head): every slot sees the
+    # prefix; draft t sees t + 1 drafts; a mask token of group g sees g drafts
+    # and the B - g mask tokens of its group.
+    vis = S * P + sum(t + 1 for t in range(B)) + sum((B - g) * B for g in range(B))
+    flops = 4.0 * d * vis * n * Hq
+    lsets = [DeviceStep(synth.make_step(synth.params_for(CFG), synth.seed_of(CFG) + 1000 * k)) for k in range(N_SETS)]
+    pairs = []
+    for ds in lsets:
+        verify = bd.attn_desc(ds.adesc.n_items, ds.adesc.D, ds.adesc.Hq, ds.adesc.Hkv, ds.adesc.d, ds.adesc.cap,
+                              ds.adesc.dtype, bd.BD_BLOCK_CAUSAL, ds.adesc.max_prefix)
+        ds._verify_desc = verify
+        pairs.append([args_of(ds, ds.adesc), args_of(ds, verify)])
+    linear_us = timed(pairs, calls)
+    tflops = flops / (quad_us * 1e-6) / 1e12
+    return dict(workload="36 layers x quadratic speculative block attention, 16q/2kv heads, d128, bf16, prefix 4096, "
+                         "B=16 (152 slots: 16 drafts + 136 mask tokens)",
+                us_per_call=round(quad_us, 2), algorithmic_tflop=round(flops / 1e12, 4),
+                achieved_tflops=round(tflops, 1), peak_tflops=MFMA_BF16_PEAK_TFLOPS,
+                frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                linear_draft_plus_verify_us=round(linear_us, 2), calls=calls)
+
+
 def copy_calibration(n_bytes=256 << 20, reps=5):
     """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
     WRITE_SIZE for this copy kernel give the scale between counter readings and
@@ -257,6 +325,8 @@ def main():
                     help="timed calls of the fused LM head + confidence + commit (0 to skip)")
     ap.add_argument("--fp8kv-calls", type=int, default=200,
                     help="timed calls of the E4M3 KV-cache attention variant (0 to skip)")
+    ap.add_argument("--quad-calls", type=int, default=50,
+                    help="timed calls of the quadratic self-speculative attention step (0 to skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -377,6 +447,7 @@ def main():
 
     lmhead = bench_lmhead(torch, stream, calls=args.lmhead_calls) if args.lmhead_calls > 0 else None
     fp8kv = bench_fp8kv_attention(torch, stream, calls=args.fp8kv_calls) if args.fp8kv_calls > 0 else None
+    quad = bench_quad_attention(torch, stream, calls=args.quad_calls) if args.quad_calls > 0 else None
 
     cpu = None
     if args.cpu_budget > 0:
@@ -415,6 +486,7 @@ def main():
         "cpu_baseline": cpu,
         "lm_head_confidence_commit": lmhead,
         "fp8kv_attention": fp8kv,
+        "quad_spec_attention": quad,
     }
     print(json.dumps(out), flush=True)
 
