@@ -60,6 +60,7 @@ def _load():
         lib.bdo_fp8_e4m3_decode.argtypes = [i32, P, P]
         lib.bdo_attention_quad.argtypes = [i32] * 7 + [ctypes.c_double] + [P] * 7
         lib.bdo_attention_quad_fp8kv.argtypes = [i32] * 6 + [ctypes.c_double] + [P] * 9
+        lib.bdo_two_stream_attention.argtypes = [i32] * 9 + [ctypes.c_double, i32] + [P] * 6
         _lib = lib
     return _lib
 
@@ -266,6 +267,32 @@ def attention_quad(q, k_blk, v_blk, k_cache, v_cache, prefix, B, scale=None):
     out = np.zeros((n, S, Hq, d), dtype=np.float64)
     lib.bdo_attention_quad(n, int(B), Hq, Hkv, d, cap, dtype, float(scale), *[_ptr(a) for a in arrs],
                            _ptr(prefix), _ptr(out))
+    return out
+
+
+def two_stream_attention(q, k, v, spans, n_spans, Lc, D, scale=None):
+    """Two-stream training attention (Fast-dVLM write-up, sections 4.1, 4.3, 4.4;
+    summary page Fig. 3) over [clean stream ; noisy stream]: clean queries are
+    causal over the clean stream; a noisy query sees the clean positions before its
+    block and its own block of the noisy stream (bidirectional), blocks of D tokens
+    cut from each response's start and truncated at its end.
+    q [n][L][Hq][d] (L = Lc + Ln), k [n][Hkv][cap][d], v [n][Hkv][d][cap] (bf16 bits
+    or fp32), spans int32 [n][max_spans][2] = (clean start, length) of each response,
+    n_spans int32 [n].  Returns float64 [n][L][Hq][d]."""
+    lib = _load()
+    n, L, Hq, d = q.shape
+    Hkv, cap = k.shape[1], k.shape[2]
+    Ln = L - Lc
+    dtype = F32 if q.dtype == np.float32 else BF16
+    el = np.float32 if dtype == F32 else np.uint16
+    q, k, v = _c(q, el), _c(k, el), _c(v, el)
+    spans = _c(spans, np.int32)
+    n_spans = _c(n_spans, np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((n, L, Hq, d), np.float64)
+    lib.bdo_two_stream_attention(n, Lc, Ln, cap, D, Hq, Hkv, d, dtype, float(scale), spans.shape[1], _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(spans), _ptr(n_spans), _ptr(out))
     return out
 
 

@@ -458,3 +458,95 @@ void bdo_lm_head_logits(int R, int V, int H, const uint16_t *hidden, const uint1
 void bdo_fp8_e4m3_decode(int n, const uint8_t *b, double *out) {
     for (int i = 0; i < n; ++i) out[i] = fp8_e4m3(b[i]);
 }
+
+/*
+ * Two-stream training attention ([FD] section 4.1, causal-context attention;
+ * section 4.3, auto-truncation; section 4.4, vision-efficient concatenation;
+ * [FD2] Fig. 3).
+ *
+ * Sequence s is the clean stream x (Lc tokens: vision, prompts and responses
+ * in order) followed by the noisy stream w (Ln tokens).  Only response text is
+ * corrupted, so w holds the response tokens alone, in order: response r is the
+ * span (start c_r, length len_r) of x and occupies w[o_r .. o_r + len_r),
+ * o_r = len_0 + ... + len_{r-1}.  Vision tokens appear only in x.  Each
+ * response is cut into blocks of D tokens from its start; its last block ends
+ * at the response boundary (auto-truncation), so no block reaches into the
+ * next prompt.  Keys are the positions of [x ; w]:
+ *   clean query at position p           : clean keys 0..p            (M_C2C, token causal)
+ *   noisy query in the block of response r covering x[b0, b1):
+ *                                          clean keys 0..b0-1        (M_N2C: every earlier clean
+ *                                                                      position, vision included)
+ *                                          the noisy keys of its own  (M_N2N: bidirectional in the
+ *                                          block, w[o_r + b0 - c_r .. o_r + b1 - c_r)   block)
+ *   clean queries never see noisy keys; noisy positions past the last
+ *   response see nothing and their output is 0.
+ *
+ * Layouts: q, out [n][L][Hq][d] with L = Lc + Ln (clean positions first);
+ * k [n][Hkv][cap][d], v [n][Hkv][d][cap] over the same L positions;
+ * spans int32 [n][max_spans][2] = (c_r, len_r), n_spans int32 [n].
+ */
+static int ts_noisy_block(const int32_t *sp, int ns, int D, int i, int *b0, int *b1, int *w0) {
+    int o = 0;
+    for (int r = 0; r < ns; ++r) {
+        const int c = sp[2 * r], len = sp[2 * r + 1];
+        if (i < o + len) {
+            const int k = (i - o) / D;
+            *b0 = c + k * D;
+            *b1 = c + (k + 1) * D < c + len ? c + (k + 1) * D : c + len;
+            *w0 = o + k * D;
+            return 1;
+        }
+        o += len;
+    }
+    return 0;
+}
+
+static int ts_visible(int Lc, const int32_t *sp, int ns, int D, int i, int j) {
+    if (i < Lc) return j <= i; /* clean query: causal over the clean stream */
+    int b0, b1, w0;
+    if (!ts_noisy_block(sp, ns, D, i - Lc, &b0, &b1, &w0)) return 0;
+    if (j < Lc) return j < b0;                     /* earlier clean positions */
+    return j - Lc >= w0 && j - Lc < w0 + (b1 - b0); /* its own noisy block */
+}
+
+void bdo_two_stream_attention(int n, int Lc, int Ln, int cap, int D, int Hq, int Hkv, int d, int dtype,
+                              double scale, int max_spans, const void *q, const void *k, const void *v,
+                              const int32_t *spans, const int32_t *n_spans, double *out) {
+    const int L = Lc + Ln, group = Hq / Hkv;
+    const long total = (long)n * L * Hq;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (long u = 0; u < total; ++u) {
+        const int it = (int)(u / ((long)L * Hq));
+        const int i = (int)((u / Hq) % L);
+        const int h = (int)(u % Hq);
+        const int g = h / group;
+        const int32_t *sp = spans + (size_t)it * max_spans * 2;
+        const int ns = n_spans[it];
+        const size_t qoff = (((size_t)it * L + i) * Hq + h) * (size_t)d;
+        double *s = (double *)malloc(sizeof(double) * (size_t)L);
+        double m = -INFINITY;
+        for (int j = 0; j < L; ++j) {
+            s[j] = -INFINITY;
+            if (!ts_visible(Lc, sp, ns, D, i, j)) continue;
+            double acc = 0.0;
+            for (int t = 0; t < d; ++t)
+                acc += widen(q, dtype, qoff + t) * widen(k, dtype, (((size_t)it * Hkv + g) * cap + j) * (size_t)d + t);
+            s[j] = scale * acc;
+            if (s[j] > m) m = s[j];
+        }
+        double denom = 0.0;
+        for (int j = 0; j < L; ++j) {
+            s[j] = (s[j] == -INFINITY) ? 0.0 : exp(s[j] - m);
+            denom += s[j];
+        }
+        for (int t = 0; t < d; ++t) {
+            double acc = 0.0;
+            for (int j = 0; j < L; ++j)
+                if (s[j] != 0.0) acc += s[j] * widen(v, dtype, (((size_t)it * Hkv + g) * d + t) * (size_t)cap + j);
+            out[qoff + t] = denom > 0.0 ? acc / denom : 0.0;
+        }
+        free(s);
+    }
+}

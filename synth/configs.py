@@ -95,3 +95,25 @@ QUAD_CONFIGS = {
 
 def quad_seed_of(cfg_id: int) -> int:
     return 3000 + int(cfg_id)
+
+
+# Two-stream training attention (Fast-dVLM write-up, sections 4.1-4.4; summary
+# page Fig. 3): [clean stream ; noisy stream].  The clean stream is vision tokens
+# followed by (prompt, response) turns; the noisy stream holds the responses'
+# tokens only.  ``turns`` lists (prompt length, response length) pairs, either one
+# list for every sequence or one list per sequence.  Config 1 is the 3B training
+# shape at the 2048-token context the write-up's memory figure uses (section 4.4)
+# with the target block size 32 (section 4.2); responses are not multiples of 32,
+# so the last block of each is truncated.
+TWO_STREAM_CONFIGS = {
+    1: dict(name="3B two-stream training attention: 8 sequences, 16q/2kv, d128, bf16, clean 2048 "
+                 "(1024 vision + 2 turns), noisy 832, D=32",
+            n_seq=8, vision=1024, turns=[(128, 638), (64, 194)], D=32, Hq=16, Hkv=2, d=128, dtype=BF16),
+    2: dict(name="small two-stream: 2 sequences, 4q/2kv, d64, bf16, ragged turns, D=8",
+            n_seq=2, vision=40, turns=[[(8, 37), (5, 20)], [(3, 16), (9, 9), (2, 1)]], D=8, Hq=4, Hkv=2, d=64,
+            dtype=BF16),
+}
+
+
+def two_stream_seed_of(cfg_id: int) -> int:
+    return 4000 + int(cfg_id)

@@ -29,8 +29,8 @@ token ids, logits, then plants.
 
 import numpy as np
 
-from .configs import (BF16, CONFIGS, F32, FP8KV, LMHEAD_CONFIGS, QUAD, QUAD_CONFIGS, lmhead_seed_of, quad_seed_of,
-                      seed_of)
+from .configs import (BF16, CONFIGS, F32, FP8KV, LMHEAD_CONFIGS, QUAD, QUAD_CONFIGS, TWO_STREAM_CONFIGS,
+                      lmhead_seed_of, quad_seed_of, seed_of, two_stream_seed_of)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -277,3 +277,56 @@ def quad_step(cfg_id: int, **overrides) -> dict:
     p = dict(QUAD_CONFIGS[cfg_id])
     p.update(overrides)
     return make_quad_step(p, quad_seed_of(cfg_id))
+
+
+def make_two_stream(p: dict, seed: int) -> dict:
+    """Inputs of one two-stream training attention call.
+
+    Sequence layout: clean stream = vision, then each turn's prompt and response;
+    noisy stream = the responses' tokens in order (padding after them when a
+    sequence has fewer response tokens than the longest).  Lc and Ln are the
+    maxima over sequences; a shorter clean stream ends in plain clean tokens.
+    Arrays: q [n][L][Hq][d] with L = Lc + Ln; k [n][Hkv][cap][d] and v
+    [n][Hkv][d][cap] (cap = L rounded up to 64, zeros past L); spans int32
+    [n][max_spans][2] = (clean start, length) of each response; n_spans [n].
+    Draw order: q, then k, then v, as N(0, 1) rounded to bf16.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n, Hq, Hkv, d, dtype = p["n_seq"], p["Hq"], p["Hkv"], p["d"], p["dtype"]
+    turns = p["turns"]
+    per_seq = turns if isinstance(turns[0], list) else [turns] * n
+    assert len(per_seq) == n
+    spans_l, lc_l, ln_l = [], [], []
+    for t in per_seq:
+        pos, sp = p["vision"], []
+        for prompt, resp in t:
+            pos += prompt
+            sp.append((pos, resp))
+            pos += resp
+        spans_l.append(sp)
+        lc_l.append(pos)
+        ln_l.append(sum(r for _, r in sp))
+    Lc, Ln = max(lc_l), max(ln_l)
+    L = Lc + Ln
+    cap = (L + 63) // 64 * 64
+    max_spans = max(len(sp) for sp in spans_l)
+    spans = np.zeros((n, max_spans, 2), np.int32)
+    n_spans = np.zeros(n, np.int32)
+    for i, sp in enumerate(spans_l):
+        n_spans[i] = len(sp)
+        for r, (c, ln) in enumerate(sp):
+            spans[i, r] = (c, ln)
+    elem = np.uint16 if dtype == BF16 else np.float32
+    q = _normal(rng, (n, L, Hq, d), dtype)
+    k = np.zeros((n, Hkv, cap, d), elem)
+    v = np.zeros((n, Hkv, d, cap), elem)
+    k[:, :, :L, :] = _normal(rng, (n, Hkv, L, d), dtype)
+    v[:, :, :, :L] = np.swapaxes(_normal(rng, (n, Hkv, L, d), dtype), 2, 3)
+    return dict(params=dict(p, Lc=Lc, Ln=Ln, L=L), seed=seed, q=q, k=k, v=v, spans=spans, n_spans=n_spans,
+                cap=cap, Lc=Lc, Ln=Ln)
+
+
+def two_stream_step(cfg_id: int, **overrides) -> dict:
+    p = dict(TWO_STREAM_CONFIGS[cfg_id])
+    p.update(overrides)
+    return make_two_stream(p, two_stream_seed_of(cfg_id))

@@ -675,3 +675,78 @@ def test_quad_fp8kv_equals_quad_on_dequantized_values():
     want = oracle.attention_quad(synth.bf16_bits_to_f32(st["q"]), dec(st["k_blk"], ks, 2), dec(st["v_blk"], vs, 2),
                                  dec(st["k_cache"], ks, 1), dec(st["v_cache"], vs, 1), st["prefix"], B)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Two-stream training attention (Fast-dVLM write-up, sections 4.1, 4.3, 4.4;
+# summary page Fig. 3): the oracle against (a) a dense mask built turn by turn
+# from the three mask rules plus auto-truncation, evaluated by SDPA, and (b)
+# the decode-time forms: causal prefill of the clean stream, and a denoise
+# step per noisy block whose cache is the clean stream before it.
+# ---------------------------------------------------------------------------
+
+def _two_stream_dense_mask(Lc, Ln, spans, D):
+    """[L][L] mask, L = Lc + Ln, from the rules: clean rows causal over clean keys
+    (M_C2C); for each response (start c, length m) at noisy offset o, blocks of D
+    from its start with the last one cut at c + m (auto-truncation); a noisy block
+    sees clean keys before its start (M_N2C) and itself (M_N2N)."""
+    L = Lc + Ln
+    mask = np.zeros((L, L), bool)
+    mask[:Lc, :Lc] = np.tril(np.ones((Lc, Lc), bool))
+    o = 0
+    for c, m in spans:
+        for k0 in range(0, m, D):
+            k1 = min(k0 + D, m)
+            rows = slice(Lc + o + k0, Lc + o + k1)
+            mask[rows, :c + k0] = True
+            mask[rows, Lc + o + k0:Lc + o + k1] = True
+        o += m
+    return mask
+
+
+@pytest.mark.parametrize("cfg_seed", [0, 1, 2])
+def test_two_stream_matches_dense_mask(cfg_seed):
+    p = dict(synth.TWO_STREAM_CONFIGS[2])
+    st = synth.make_two_stream(p, 500 + cfg_seed)
+    Lc, Ln = st["Lc"], st["Ln"]
+    out = oracle.two_stream_attention(st["q"], st["k"], st["v"], st["spans"], st["n_spans"], Lc, p["D"])
+    L, G = Lc + Ln, p["Hq"] // p["Hkv"]
+    for it in range(p["n_seq"]):
+        sp = [tuple(x) for x in st["spans"][it, :st["n_spans"][it]]]
+        mask = _two_stream_dense_mask(Lc, Ln, sp, p["D"])
+        live = mask.any(axis=1)
+        Q = np.swapaxes(_widen(st["q"][it]), 0, 1)                  # [Hq][L][d]
+        K = _widen(st["k"][it][:, :L])                               # [Hkv][L][d]
+        V = np.swapaxes(_widen(st["v"][it][:, :, :L]), 1, 2)
+        ref = _sdpa(Q[:, live], K, V, mask[live], G)
+        np.testing.assert_allclose(out[it][live], np.swapaxes(ref, 0, 1), rtol=0, atol=1e-12)
+        assert np.all(out[it][~live] == 0.0)                         # noisy padding sees nothing
+
+
+def test_two_stream_equals_prefill_and_per_block_denoise():
+    """Clean rows = causal prefill (CAUSAL block steps over chunks of the clean
+    stream); each noisy block = a BIDIR step whose cache is the clean stream
+    before the block and whose block is that noisy block (truncated blocks
+    included)."""
+    p = dict(synth.TWO_STREAM_CONFIGS[2])
+    st = synth.make_two_stream(p, 77)
+    Lc, Ln, D = st["Lc"], st["Ln"], p["D"]
+    out = oracle.two_stream_attention(st["q"], st["k"], st["v"], st["spans"], st["n_spans"], Lc, D)
+    for it in range(p["n_seq"]):
+        Kseq = np.swapaxes(st["k"][it], 0, 1)                        # [cap][Hkv][d]
+        Vseq = np.transpose(st["v"][it], (2, 0, 1))                  # [cap][Hkv][d]
+        kc, vc = st["k"][it:it + 1], st["v"][it:it + 1]
+        for c0 in range(0, Lc, 7):                                    # clean chunks of 7 positions
+            c1 = min(c0 + 7, Lc)
+            ref = oracle.attention(st["q"][it:it + 1, c0:c1], Kseq[None, c0:c1], Vseq[None, c0:c1], kc, vc,
+                                   np.array([c0], np.int32), CAUSAL)
+            np.testing.assert_allclose(out[it:it + 1, c0:c1], ref, rtol=0, atol=1e-12)
+        o = 0
+        for c, m in st["spans"][it, :st["n_spans"][it]]:
+            for k0 in range(0, m, D):
+                k1 = min(k0 + D, m)
+                rows = slice(Lc + o + k0, Lc + o + k1)
+                ref = oracle.attention(st["q"][it:it + 1, rows], Kseq[None, rows], Vseq[None, rows], kc, vc,
+                                       np.array([c + k0], np.int32), BIDIR)
+                np.testing.assert_allclose(out[it:it + 1, rows], ref, rtol=0, atol=1e-12)
+            o += m
