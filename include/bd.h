@@ -219,6 +219,49 @@ bd_status bd_lmhead_confidence_commit(const bd_lmhead_desc *desc, const void *hi
                                       uint8_t *committed, int32_t *n_committed, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* Shape of one two-stream training-attention call ([FD] 4.1, 4.3, 4.4; [FD2] Fig. 3).
+ *  n_seq      sequences, >= 1
+ *  Lc         clean-stream length (vision, prompts and responses), >= 1
+ *  Ln         noisy-stream length (the responses' corrupted tokens), >= 0
+ *  cap        positions held by k and v, a multiple of 32, >= Lc + Ln
+ *  D          block size of the noisy stream, 1..4096
+ *  Hq, Hkv    query / KV heads, Hq % Hkv == 0 (head h uses KV head h / (Hq/Hkv))
+ *  d          head dim, 64 or 128
+ *  max_spans  response spans per sequence (rows of `spans`), 0..256 (0 only if Ln == 0)
+ *  scale      softmax scale, finite and > 0 */
+typedef struct {
+    int32_t n_seq, Lc, Ln, cap, D, Hq, Hkv, d, max_spans;
+    float scale;
+} bd_two_stream_desc;
+
+/* Workspace bytes bd_two_stream_attn needs (0 if none); SIZE_MAX if desc is invalid. */
+size_t bd_two_stream_workspace_bytes(const bd_two_stream_desc *desc);
+
+/* Two-stream training attention over [clean stream x ; noisy stream w] ([FD] 4.1:
+ * causal-context attention with the masks M_N2N, M_N2C, M_C2C; [FD] 4.3: blocks cut at
+ * response ends; [FD] 4.4: vision tokens only in the clean stream).  Sequence s has
+ * L = Lc + Ln positions, clean positions 0..Lc-1 then noisy positions Lc..L-1.  Its
+ * responses are spans[s][r] = (clean start c_r, length len_r), r < n_spans[s], in
+ * order; w holds their tokens in the same order, response r at noisy offset
+ * o_r = len_0 + ... + len_{r-1}.  Each response is cut into blocks of D tokens from
+ * its start, the last block ending at the response end.
+ *   clean position p         sees clean positions 0..p                       (M_C2C)
+ *   noisy token of response r, block k, covering clean positions [b0, b1):
+ *                            sees clean positions 0..b0-1                   (M_N2C)
+ *                            and the noisy tokens of its own block            (M_N2N)
+ *   noisy positions past the last response see nothing and get 0;
+ *   out = softmax(scale * q k^T) v over the visible keys.
+ * Layouts (bf16, row-major): q, out [n_seq][L][Hq][d]; k [n_seq][Hkv][cap][d];
+ * v [n_seq][Hkv][d][cap] (d-major, as the decode cache); spans int32
+ * [n_seq][max_spans][2], n_spans int32 [n_seq] (device).  k and v positions
+ * L..cap-1 are read (as parts of 32-key tiles) but never weighted; they must hold
+ * finite values (zeros, say).  Span values out of range are clamped into the
+ * sequence, never read outside it.
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH. */
+bd_status bd_two_stream_attn(const bd_two_stream_desc *desc, const void *q, const void *k, const void *v,
+                             const int32_t *spans, const int32_t *n_spans, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *bd_status_string(bd_status status);
 

@@ -29,9 +29,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ["bd_attn_step", "bd_attn_step_fp8kv", "bd_confidence_commit", "bd_spec_verify", "bd_kv_append",
-                 "bd_lmhead_confidence_commit"]:
+                 "bd_lmhead_confidence_commit", "bd_two_stream_attn"]:
         assert must in names
-    assert len(names) >= 10
+    assert len(names) >= 12
 
 
 def test_library_exports_every_declared_symbol(bd):
@@ -143,6 +143,50 @@ def test_quad_mode_validation(bd):
                                None) == bd.BD_E_PARAM
     assert bd.lib.bd_kv_append(ctypes.byref(_attn(bd, mode=bd.BD_BLOCK_QUAD, D=33)), fake, fake, fake, fake, fake,
                                None, None, None) == bd.BD_E_SHAPE
+
+
+def _ts(bd, **kw):
+    base = dict(n_seq=8, Lc=2048, Ln=832, cap=2880, D=32, Hq=16, Hkv=2, d=128, max_spans=2, scale=0.0884)
+    base.update(kw)
+    return bd.BdTwoStreamDesc(*[base[f] for f, _ in bd.BdTwoStreamDesc._fields_])
+
+
+BAD_TWO_STREAM = [
+    (dict(n_seq=0), "BD_E_SHAPE"), (dict(Lc=0), "BD_E_SHAPE"), (dict(Ln=-1), "BD_E_SHAPE"), (dict(D=0), "BD_E_SHAPE"),
+    (dict(D=4097), "BD_E_SHAPE"), (dict(cap=2848), "BD_E_SHAPE"), (dict(cap=2888), "BD_E_SHAPE"),
+    (dict(Hq=15), "BD_E_SHAPE"), (dict(d=96), "BD_E_SHAPE"), (dict(max_spans=0), "BD_E_SHAPE"),
+    (dict(max_spans=257), "BD_E_SHAPE"), (dict(scale=float("nan")), "BD_E_PARAM"), (dict(scale=-1.0), "BD_E_PARAM"),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_TWO_STREAM)
+def test_two_stream_validation(bd, kw, code):
+    desc = _ts(bd, **kw)
+    fake = 1 << 20
+    st = bd.lib.bd_two_stream_attn(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, 1 << 30, None)
+    assert st == getattr(bd, code)
+    assert bd.lib.bd_two_stream_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
+
+
+def test_two_stream_null_alignment_and_workspace(bd):
+    fake = 1 << 20
+    desc = _ts(bd)
+    need = bd.lib.bd_two_stream_workspace_bytes(ctypes.byref(desc))
+    assert need < bd.SIZE_MAX
+    call = lambda *a: bd.lib.bd_two_stream_attn(ctypes.byref(desc), *a)
+    assert bd.lib.bd_two_stream_attn(None, fake, fake, fake, fake, fake, fake, fake, need, None) == bd.BD_E_NULL
+    assert call(fake, fake, fake, None, fake, fake, fake, need, None) == bd.BD_E_NULL
+    assert call(fake, fake, fake, fake, None, fake, fake, need, None) == bd.BD_E_NULL
+    assert call(fake, fake, fake, fake, fake, None, fake, need, None) == bd.BD_E_NULL
+    assert call(fake + 2, fake, fake, fake, fake, fake, fake, need, None) == bd.BD_E_PARAM
+    if need > 0:
+        assert call(fake, fake, fake, fake, fake, fake, fake, need - 1, None) == bd.BD_E_WORKSPACE
+    # Without responses (plain causal prefill) the span arrays are not needed.
+    plain = _ts(bd, Ln=0, max_spans=0, cap=2048)
+    assert bd.lib.bd_two_stream_workspace_bytes(ctypes.byref(plain)) < bd.SIZE_MAX
+    # Few, long sequences split their keys (workspace); many sequences fill the GPU without.
+    few = _ts(bd, n_seq=1, Hq=2, Hkv=1, Lc=4096, Ln=0, max_spans=0, cap=4096)
+    assert bd.lib.bd_two_stream_workspace_bytes(ctypes.byref(few)) > 0
 
 
 BAD_COMMIT = [

@@ -299,6 +299,76 @@ def test_quad_append_accepted_drafts(dev):
 
 
 # ---------------------------------------------------------------------------
+# Two-stream training attention (bd_two_stream_attn): clean stream causal, each
+# noisy response block sees the clean positions before it and itself; blocks
+# are cut at response ends.  Same bar as the bf16 attention.
+# ---------------------------------------------------------------------------
+
+def _run_two_stream(dev, st, label, items=None):
+    torch, bd = dev["torch"], dev["bd"]
+    p = st["params"]
+    n, L, Hq, d = st["q"].shape
+    _say("two-stream %s n=%d Lc=%d Ln=%d D=%d Hq=%d Hkv=%d d=%d spans=%s" % (
+        label, n, st["Lc"], st["Ln"], p["D"], Hq, p["Hkv"], d, st["n_spans"].tolist()))
+    c = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+    q, k, v, sp, ns = c(st["q"]), c(st["k"]), c(st["v"]), c(st["spans"]), c(st["n_spans"])
+    out = torch.empty_like(q)
+    desc = bd.two_stream_desc(n, st["Lc"], st["Ln"], st["cap"], p["D"], Hq, p["Hkv"], d, st["spans"].shape[1])
+    ws = torch.zeros(max(bd.bd_two_stream_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
+    bd.bd_two_stream_attn(desc, q, k, v, sp, ns, out, ws)
+    torch.cuda.synchronize()
+    got = synth.bf16_bits_to_f32(out.cpu().numpy().view(np.uint16)).astype(np.float64)
+    sel = list(range(n)) if items is None else items
+    ref = oracle.two_stream_attention(*[np.ascontiguousarray(st[x][sel]) for x in ("q", "k", "v", "spans", "n_spans")],
+                                      st["Lc"], p["D"])
+    _check_attention(got[sel], ref, label)
+    return got, (desc, q, k, v, sp, ns, out, ws)
+
+
+def test_two_stream_small_config(dev):
+    _run_two_stream(dev, synth.two_stream_step(2), "two_stream_small")
+
+
+def test_two_stream_3b_training_shape_sampled(dev):
+    """The 3B training shape (8 sequences, clean 2048 with 1024 vision tokens, noisy
+    832, D = 32) in one launch; the oracle checks two whole sequences of it."""
+    _run_two_stream(dev, synth.two_stream_step(1), "two_stream_3b", items=[0, 7])
+
+
+TWO_STREAM_CASES = [
+    ("no_noisy_prefill", dict(turns=[(10, 0)], vision=100)),
+    ("one_response_exact_blocks", dict(turns=[(7, 32)], D=8)),
+    ("D1", dict(D=1, turns=[(4, 9), (3, 5)])),
+    ("D_larger_than_responses", dict(D=64, turns=[(4, 30), (3, 17)])),
+    ("G7_rows", dict(Hq=14, Hkv=2, d=128, turns=[(20, 70), (8, 41)])),
+    ("d128_long", dict(d=128, vision=300, turns=[(33, 250), (12, 77)], D=32)),
+    ("empty_span_and_padding", dict(turns=[[(5, 0), (6, 23)], [(2, 40)]], D=16)),
+]
+
+
+@pytest.mark.parametrize("label,ov", TWO_STREAM_CASES, ids=[c[0] for c in TWO_STREAM_CASES])
+def test_two_stream_edge_cases(dev, label, ov):
+    p = dict(synth.TWO_STREAM_CONFIGS[2])
+    p.update(ov)
+    st = synth.make_two_stream(p, zlib.crc32(("ts" + label).encode()) % 10000)
+    _run_two_stream(dev, st, "two_stream_" + label)
+
+
+def test_two_stream_deterministic(dev):
+    torch, bd = dev["torch"], dev["bd"]
+    st = synth.make_two_stream(dict(synth.TWO_STREAM_CONFIGS[2], n_seq=1, Hq=2, Hkv=1, vision=2000,
+                                    turns=[(30, 500)], D=32), 11)
+    _, args = _run_two_stream(dev, st, "two_stream_split")
+    desc, q, k, v, sp, ns, out, ws = args
+    first = out.clone()
+    for _ in range(3):
+        out.zero_()
+        bd.bd_two_stream_attn(desc, q, k, v, sp, ns, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+
+
+# ---------------------------------------------------------------------------
 # Confidence + commit
 # ---------------------------------------------------------------------------
 

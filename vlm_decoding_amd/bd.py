@@ -35,6 +35,12 @@ class BdLmheadDesc(ctypes.Structure):
                 ("H", ctypes.c_int32), ("S", ctypes.c_int32), ("tau", ctypes.c_float)]
 
 
+class BdTwoStreamDesc(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("Lc", ctypes.c_int32), ("Ln", ctypes.c_int32), ("cap", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("max_spans", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
 class BdError(RuntimeError):
     def __init__(self, fn, status, lib):
         msg = lib.bd_status_string(status).decode()
@@ -59,6 +65,7 @@ def _load():
     AD = ctypes.POINTER(BdAttnDesc)
     CD = ctypes.POINTER(BdCommitDesc)
     LD = ctypes.POINTER(BdLmheadDesc)
+    TD = ctypes.POINTER(BdTwoStreamDesc)
     sig = {
         "bd_attn_workspace_bytes": (sz, [AD]),
         "bd_attn_step": (i32, [AD, P, P, P, P, P, P, P, P, sz, P]),
@@ -70,6 +77,8 @@ def _load():
         "bd_kv_append": (i32, [AD, P, P, P, P, P, P, P, P]),
         "bd_lmhead_workspace_bytes": (sz, [LD]),
         "bd_lmhead_confidence_commit": (i32, [LD, P, P, P, P, P, P, P, P, P, sz, P]),
+        "bd_two_stream_workspace_bytes": (sz, [TD]),
+        "bd_two_stream_attn": (i32, [TD, P, P, P, P, P, P, P, sz, P]),
         "bd_status_string": (ctypes.c_char_p, [i32]),
         "bd_last_hip_error": (i32, []),
     }
@@ -183,3 +192,19 @@ def bd_lmhead_confidence_commit(desc, hidden, weight, masked, tokens, conf=None,
     _check("bd_lmhead_confidence_commit", lib.bd_lmhead_confidence_commit(
         ctypes.byref(desc), _ptr(hidden), _ptr(weight), _ptr(masked), _ptr(tokens), _ptr(conf), _ptr(argmax),
         _ptr(committed), _ptr(n_committed), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def two_stream_desc(n_seq, Lc, Ln, cap, D, Hq, Hkv, d, max_spans, scale=None):
+    return BdTwoStreamDesc(n_seq, Lc, Ln, cap, D, Hq, Hkv, d, max_spans, (1.0 / d ** 0.5) if scale is None else scale)
+
+
+def bd_two_stream_workspace_bytes(desc):
+    return lib.bd_two_stream_workspace_bytes(ctypes.byref(desc))
+
+
+def bd_two_stream_attn(desc, q, k, v, spans, n_spans, out, workspace=None, workspace_bytes=None, stream=None):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bd_two_stream_attn", lib.bd_two_stream_attn(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(spans), _ptr(n_spans), _ptr(out), _ptr(workspace),
+        workspace_bytes, _stream(stream)))

@@ -55,6 +55,19 @@ bd_status check_lmhead_desc(const bd_lmhead_desc *d) {
     return BD_OK;
 }
 
+bd_status check_two_stream_desc(const bd_two_stream_desc *d) {
+    if (!d) return BD_E_NULL;
+    if (!(d->scale > 0.f) || !isfinite(d->scale)) return BD_E_PARAM;
+    if (d->n_seq < 1 || d->Lc < 1 || d->Ln < 0 || d->D < 1 || d->D > 4096) return BD_E_SHAPE;
+    if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return BD_E_SHAPE;
+    if (d->d != 64 && d->d != 128) return BD_E_SHAPE;
+    const int64_t L = (int64_t)d->Lc + d->Ln;
+    if (d->cap < L || d->cap % 32 != 0) return BD_E_SHAPE;
+    if (d->max_spans < 0 || d->max_spans > 256 || (d->Ln > 0 && d->max_spans < 1)) return BD_E_SHAPE;
+    if (L * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
+    return BD_OK;
+}
+
 bd_status launched(hipError_t e) {
     if (e != hipSuccess) {
         g_last_hip_error = (int32_t)e;
@@ -268,5 +281,49 @@ const char *bd_status_string(bd_status s) {
 }
 
 int32_t bd_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"
+
+extern "C" {
+
+size_t bd_two_stream_workspace_bytes(const bd_two_stream_desc *desc) {
+    if (check_two_stream_desc(desc) != BD_OK) return SIZE_MAX;
+    const bd::AttnPlan pl = bd::plan_attention(desc->n_seq, desc->Lc + desc->Ln, desc->Hq, desc->Hkv, desc->d,
+                                               BD_BF16, 0, true);
+    return pl.ws_bytes;
+}
+
+bd_status bd_two_stream_attn(const bd_two_stream_desc *desc, const void *q, const void *k, const void *v,
+                             const int32_t *spans, const int32_t *n_spans, void *out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+    bd_status st = check_two_stream_desc(desc);
+    if (st != BD_OK) return st;
+    if (!q || !k || !v || !out) return BD_E_NULL;
+    if (desc->max_spans > 0 && (!spans || !n_spans)) return BD_E_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return BD_E_PARAM;
+    const bd::AttnPlan pl = bd::plan_attention(desc->n_seq, desc->Lc + desc->Ln, desc->Hq, desc->Hkv, desc->d,
+                                               BD_BF16, 0, true);
+    if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+        return BD_E_WORKSPACE;
+    bd::AttnArgs a{};
+    a.q = q;
+    a.k_cache = k;
+    a.v_cache = v;
+    a.out = out;
+    a.ws = workspace;
+    a.n = desc->n_seq;
+    a.D = desc->Lc + desc->Ln;
+    a.Hq = desc->Hq;
+    a.Hkv = desc->Hkv;
+    a.d = desc->d;
+    a.cap = desc->cap;
+    a.scale = desc->scale;
+    a.spans = spans;
+    a.n_spans = n_spans;
+    a.Lc = desc->Lc;
+    a.max_spans = desc->max_spans;
+    a.Dblk = desc->D;
+    return launched(bd::launch_attention_mfma(pl, a, (hipStream_t)stream));
+}
 
 }  // extern "C"

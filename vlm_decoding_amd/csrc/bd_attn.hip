@@ -47,6 +47,11 @@ struct MfmaParams {
     int B;  // quadratic mode: draft block size (D = B (B + 3) / 2 slots)
     int R, row_blocks, max_splits, tiles_per_split, total_logical;
     float c;  // scale * log2(e)
+    // Two-stream (whole-sequence) mode: D = L = Lc + Ln positions per item, the
+    // clean stream then the noisy stream; response spans (clean start, length).
+    const int32_t *spans, *n_spans;
+    int *unit_splits;  // [units]: split count of each unit, for the merge kernel
+    int Lc, max_spans, Dblk;
 };
 
 // Block slots a query slot may attend to, as two half-open slot ranges
@@ -74,6 +79,37 @@ __device__ __forceinline__ SlotRanges block_ranges(int mode, int slot, int D, in
 // Bitwise, not short-circuit: the result feeds a select, with no branches.
 __device__ __forceinline__ bool in_ranges(const SlotRanges &r, int b) {
     return (b < r.hi1) | ((b >= r.lo2) & (b < r.hi2));
+}
+
+// Two-stream training attention (Fast-dVLM write-up, sections 4.1, 4.3, 4.4;
+// summary page Fig. 3): the keys a sequence position sees, as key-position
+// ranges [0, hi1) and [lo2, hi2) of [clean stream ; noisy stream].
+//  clean position p          : clean keys 0..p (token causal);
+//  noisy position Lc + i     : i falls in response r (noisy offset o, clean
+//                              start c, length len), block k = (i - o) / Dblk;
+//                              clean keys before c + k Dblk, and the noisy keys
+//                              of its block, cut at the response end;
+//  noisy positions past the last response see nothing.
+// Spans come from device memory: every bound is clamped into the sequence.
+__device__ __forceinline__ SlotRanges seq_ranges(const MfmaParams &p, int it, int pos) {
+    if (pos < p.Lc) return {pos + 1, 0, 0};
+    const int L = p.D;
+    const int i = pos - p.Lc;
+    const int32_t *sp = p.spans + (size_t)it * p.max_spans * 2;
+    const int ns = min(max(p.n_spans[it], 0), p.max_spans);
+    int o = 0;
+    for (int r = 0; r < ns; ++r) {
+        const int c = sp[2 * r], len = max(sp[2 * r + 1], 0);
+        if (i < o + len) {
+            const int k = (i - o) / p.Dblk;
+            const int b0 = min(max(c + k * p.Dblk, 0), p.Lc);
+            const int w0 = o + k * p.Dblk;
+            const int bl = min(p.Dblk, len - k * p.Dblk);
+            return {b0, min(p.Lc + w0, L), min(p.Lc + w0 + bl, L)};
+        }
+        o += len;
+    }
+    return {0, 0, 0};
 }
 
 // Row permutations of the K operand.  A-row rho (= lane % 32) of a 32-key
@@ -181,8 +217,12 @@ __device__ __forceinline__ bf16x8 bd_e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 // bytes per stage), converted to bf16 right after each LDS read; the K scale
 // is folded into the softmax constant and the V scale into the final
 // normalisation.
-template <int HD, int NW, bool KV8>
+// SEQ = true: two-stream training attention over whole sequences (bf16 K/V):
+// every key tile comes from the item's K/V arrays by the same copy pipeline,
+// and tiles that some row of the workgroup only partly sees are masked.
+template <int HD, int NW, bool KV8, bool SEQ>
 __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(MfmaParams p) {
+    static_assert(!(SEQ && KV8), "the sequence mode is bf16 only");
     constexpr int NT = NW * 64;
     constexpr int EB = KV8 ? 1 : 2;     // bytes per K / V element
     constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;  // keys per tile
@@ -252,7 +292,8 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const bool wave_active = rb * RPG + w * 32 < p.R;
     const int slot = r / p.G;
     const int head = g * p.G + (r - slot * p.G);
-    const SlotRanges vis = row_valid ? block_ranges(p.mode, slot, p.D, p.B) : SlotRanges{0, 0, 0};
+    SlotRanges vis{0, 0, 0};
+    if (row_valid) vis = SEQ ? seq_ranges(p, it, slot) : block_ranges(p.mode, slot, p.D, p.B);
     bf16x8 qf[KC];
     {
         const uint16_t *qp = p.q + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
@@ -272,18 +313,59 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     }
 
     // Prefix lengths are clamped into [0, cap] so that no access leaves the cache.
-    const int P = min(max(p.prefix[it], 0), p.cap);
+    const int P = SEQ ? 0 : min(max(p.prefix[it], 0), p.cap);
     const int Pb = P & ~(TK - 1);  // cache positions in whole tiles
-    // A prefix above the host's max_prefix widens the splits instead of
-    // overrunning the workspace (at most max_splits per unit).
-    const UnitSplit us = unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
-    const int nsplit = us.nsplit;
-    if (split >= nsplit) return;
-    const bool is_tail = split == nsplit - 1;
-    const int t0 = us.t0;
-    const int nb_split = us.nb;
-    const int tail_len = is_tail ? (P - Pb) + p.D : 0;
-    const int ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
+    int nsplit, t0, nb_split, tail_len = 0, ntail = 0;
+    // Sequence mode: the workgroup's key tiles are segment A, tiles 0..nA-1 of
+    // the clean stream (the first nU of them seen whole by every row), then
+    // segment B, the noisy tiles from bB on; each row's ranges decide the rest.
+    int nU = 0, nA = 0, bB = 0;
+    if constexpr (SEQ) {
+        __shared__ int red[4];
+        if (tid == 0) {
+            red[0] = 0x7fffffff;
+            red[1] = 0;
+            red[2] = 0x7fffffff;
+            red[3] = 0;
+        }
+        bd_barrier_lds();
+        if (row_valid) {
+            atomicMin(&red[0], vis.hi1);
+            atomicMax(&red[1], vis.hi1);
+            if (vis.hi2 > vis.lo2) {
+                atomicMin(&red[2], vis.lo2);
+                atomicMax(&red[3], vis.hi2);
+            }
+        }
+        bd_barrier_lds();
+        const int min_hi1 = red[0], max_hi1 = red[1], min_lo2 = red[2], max_hi2 = red[3];
+        nU = min_hi1 == 0x7fffffff ? 0 : min_hi1 / TK;
+        nA = (max_hi1 + TK - 1) / TK;
+        int nB = 0;
+        if (max_hi2 > min_lo2) {
+            bB = max(min_lo2 / TK, nA);
+            nB = max(0, (max_hi2 + TK - 1) / TK - bB);
+        }
+        const int nt = nA + nB;
+        nsplit = nt == 0 ? 1 : max(1, min(min(p.max_splits, nt), (nt + p.tiles_per_split - 1) / p.tiles_per_split));
+        if (split == 0 && tid == 0 && p.unit_splits) p.unit_splits[unit] = nsplit;
+        if (split >= nsplit) return;
+        t0 = (int)((unsigned)(split * nt) / (unsigned)nsplit);
+        nb_split = (int)((unsigned)((split + 1) * nt) / (unsigned)nsplit) - t0;
+    } else {
+        // A prefix above the host's max_prefix widens the splits instead of
+        // overrunning the workspace (at most max_splits per unit).
+        const UnitSplit us = unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
+        nsplit = us.nsplit;
+        if (split >= nsplit) return;
+        const bool is_tail = split == nsplit - 1;
+        t0 = us.t0;
+        nb_split = us.nb;
+        tail_len = is_tail ? (P - Pb) + p.D : 0;
+        ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
+    }
+    // Key tile of list entry k (sequence mode) or bulk tile k.
+    auto tile_of = [&](int k) __attribute__((always_inline)) { return SEQ && k >= nA ? bB + (k - nA) : k; };
 
     // Byte offsets of this (item, KV head)'s cache rows.
     const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD * EB;   // [cap][HD]
@@ -302,7 +384,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // lane's source address.  No VGPRs hold tile data.
     static_assert(K_UNITS % NT == 0 && V_UNITS % NT == 0, "tile units must split evenly over lanes");
     auto issue_bulk = [&](int t, int st, bool real) __attribute__((always_inline)) {
-        const int key0 = t * TK;
+        const int key0 = tile_of(t) * TK;
 #pragma unroll
         for (int j = 0; j < LK; ++j) {
             const int base = (j * NW + w) * 64;
@@ -421,7 +503,8 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         }
     };
 
-    auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */) __attribute__((always_inline)) {
+    auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */,
+                       int mkey0 /* sequence mode: first key of a masked tile, else -1 */) __attribute__((always_inline)) {
         const uint8_t *Kt = kbuf(st);
         const uint8_t *Vt = vbuf(st);
         floatx16 s[KB];
@@ -444,7 +527,16 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
                 }
             }
         }
-        if (tt >= 0) {
+        if (SEQ && mkey0 >= 0) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int kin = 16 * (i >> 3) + 8 * half + (i & 7);
+                    s[kb][i] = in_ranges(vis, mkey0 + kb * 32 + kin) ? s[kb][i] : -INFINITY;
+                }
+        }
+        if (!SEQ && tt >= 0) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -515,7 +607,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
         load_tail(0, tt);
         bd_barrier_lds();
-        if (wave_active) compute(0, tt);
+        if (wave_active) compute(0, tt, -1);
     }
     // Bulk tiles through NS stages, all NS filled up front: tiles tl+1 ..
     // tl+NS-1 are in flight while tile tl is computed.  Every step has the same
@@ -538,7 +630,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         constexpr int ST = decltype(stage)::value;
         bd_wait_vmcnt<(NS - 1) * (LK + LV)>();  // tile tl's copies have landed
         bd_barrier_lds();                        // ... and are visible to every wave
-        if (wave_active && tl < nb_split) compute(ST, -1);
+        if (wave_active && tl < nb_split) compute(ST, -1, SEQ && t0 + tl >= nU ? tile_of(t0 + tl) * TK : -1);
         bd_barrier_lds();  // every wave is done with stage ST, which is refilled now
         issue_bulk(t0 + tl + NS, ST, tl + NS < nb_split);
     };
@@ -555,7 +647,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // half h holds d = mb*32 + 8*(i/4) + 4*h + (i%4) of this lane's row.
     if (nsplit == 1) {
         if (row_valid) {
-            const float inv = vs / l_tot;
+            const float inv = l_tot > 0.f ? vs / l_tot : 0.f;  // a row that sees nothing outputs 0
             uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -603,7 +695,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 //   M = max_s m_s,  c_s = 2^(m_s - M) l_s,  o = sum_s c_s (o_s / l_s) / sum_s c_s,
 // summed in split order.  The merged 32 rows are staged in LDS and written
 // out as whole rows (HD * 2 contiguous bytes each).
-template <int HD, int NW, int TK>
+template <int HD, int NW, int TK, bool SEQ>
 __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
     constexpr int NT_TILE = NW * 64;    // threads of the tile kernel's block
     constexpr int MB = HD / 32;
@@ -637,8 +729,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
 #pragma unroll
             for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t];
         }
-    const int P = min(max(p.prefix[it], 0), p.cap);
-    const int nsplit = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
+    int nsplit;
+    if constexpr (SEQ) {
+        nsplit = p.unit_splits[unit];  // written by the unit's first split
+    } else {
+        const int P = min(max(p.prefix[it], 0), p.cap);
+        nsplit = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
+    }
     if (nsplit == 1) return;  // single split: written by the tile kernel
     float M = -INFINITY;
 #pragma unroll
@@ -774,8 +871,9 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
 
 }  // namespace
 
-AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix) {
+AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix, bool seq) {
     AttnPlan pl{};
+    pl.seq = seq;
     pl.mfma = (dtype == 1 || dtype == 2);
     pl.fp8 = (dtype == 2);
     pl.tk = pl.fp8 ? 2 * kTileKeys : kTileKeys;
@@ -803,6 +901,13 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     const int ntail_max = (pl.tk - 1 + D + pl.tk - 1) / pl.tk;
     const int work_max = ntiles_max + kTailCost * ntail_max;
     pl.tiles_per_split = std::max(1, (work_max + pl.max_splits - 1) / pl.max_splits);
+    if (seq) {
+        // Whole sequences of D positions: a unit has at most D / tk key tiles,
+        // all streamed the same way; the split count only fills the GPU.
+        const int nt = (D + pl.tk - 1) / pl.tk;
+        pl.max_splits = std::max(1, std::min(std::min(want, nt), kMaxSplits));
+        pl.tiles_per_split = std::max(1, (nt + pl.max_splits - 1) / pl.max_splits);
+    }
     const long total = (long)pl.units * pl.max_splits;
     pl.grid = (int)((total + 7) / 8 * 8);
     if (pl.max_splits > 1) {
@@ -817,21 +922,24 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
         const size_t lanes = (size_t)pl.units * pl.max_splits * pl.nw * 64;
         pl.ws_ml_off = take(sizeof(float) * 2 * lanes);
         pl.ws_o_off = take(sizeof(uint16_t) * (size_t)(d / 2) * lanes);
+        if (seq) pl.ws_splits_off = take(sizeof(int) * (size_t)pl.units);
         pl.ws_bytes = off;
     }
     return pl;
 }
 
 namespace {
-template <bool KV8>
+template <bool KV8, bool SEQ>
 void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge) {
     constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;
     if (d == 128) {
-        *tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4, KV8> : (const void *)attn_mfma_kernel<128, 8, KV8>;
-        *merge = pl.nw == 4 ? (const void *)attn_merge_kernel<128, 4, TK> : (const void *)attn_merge_kernel<128, 8, TK>;
+        *tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4, KV8, SEQ>
+                           : (const void *)attn_mfma_kernel<128, 8, KV8, SEQ>;
+        *merge = pl.nw == 4 ? (const void *)attn_merge_kernel<128, 4, TK, SEQ>
+                            : (const void *)attn_merge_kernel<128, 8, TK, SEQ>;
     } else {
-        *tile = (const void *)attn_mfma_kernel<64, 4, KV8>;
-        *merge = (const void *)attn_merge_kernel<64, 4, TK>;
+        *tile = (const void *)attn_mfma_kernel<64, 4, KV8, SEQ>;
+        *merge = (const void *)attn_merge_kernel<64, 4, TK, SEQ>;
     }
 }
 }  // namespace
@@ -850,6 +958,12 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     char *ws = (char *)a.ws;
     p.ws_ml = pl.max_splits > 1 ? (float2 *)(ws + pl.ws_ml_off) : nullptr;
     p.ws_o = pl.max_splits > 1 ? (float *)(ws + pl.ws_o_off) : nullptr;
+    p.unit_splits = pl.max_splits > 1 && pl.seq ? (int *)(ws + pl.ws_splits_off) : nullptr;
+    p.spans = a.spans;
+    p.n_spans = a.n_spans;
+    p.Lc = a.Lc;
+    p.max_spans = a.max_spans;
+    p.Dblk = a.Dblk;
     p.n = a.n;
     p.D = a.D;
     p.Hq = a.Hq;
@@ -866,10 +980,12 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.c = a.scale * BD_LOG2E;
     dim3 block(pl.nw * 64);
     const void *tile, *merge;
-    if (pl.fp8)
-        pick_kernels<true>(pl, a.d, &tile, &merge);
+    if (pl.seq)
+        pick_kernels<false, true>(pl, a.d, &tile, &merge);
+    else if (pl.fp8)
+        pick_kernels<true, false>(pl, a.d, &tile, &merge);
     else
-        pick_kernels<false>(pl, a.d, &tile, &merge);
+        pick_kernels<false, false>(pl, a.d, &tile, &merge);
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
     if (e != hipSuccess || pl.max_splits == 1) return e;

@@ -15,6 +15,7 @@ constexpr int kMaxSplits = 16;      // split-K pieces per unit (merge registers)
 struct AttnPlan {
     bool mfma;            // MFMA path: bf16, or bf16 queries with E4M3 K/V (else the fp32 vector path)
     bool fp8;             // E4M3 K/V (64-key tiles)
+    bool seq;             // two-stream mode: whole sequences, per-row key ranges
     int tk;               // keys per tile
     int nw;               // waves per workgroup (MFMA path)
     int rows;             // grouped query rows per (item, KV head) = D * Hq/Hkv
@@ -24,7 +25,7 @@ struct AttnPlan {
     int tiles_per_split;
     int max_splits;
     int grid;             // workgroups launched
-    size_t ws_ml_off, ws_o_off, ws_bytes;
+    size_t ws_ml_off, ws_o_off, ws_splits_off, ws_bytes;
 };
 
 struct AttnArgs {
@@ -36,9 +37,12 @@ struct AttnArgs {
     int n, D, Hq, Hkv, d, cap, mode;
     int B;  // quadratic mode: draft block size (D is then the slot count B (B + 3) / 2)
     float scale;
+    // two-stream mode (D = Lc + Ln positions per sequence)
+    const int32_t *spans, *n_spans;
+    int Lc, max_spans, Dblk;
 };
 
-AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix);
+AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix, bool seq = false);
 hipError_t launch_attention_mfma(const AttnPlan &plan, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s);
 
