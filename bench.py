@@ -22,7 +22,8 @@ measures).  ``value`` is steps over the wall time of all timed steps.
 measure the next rows of the path beside the headline: the LM head fused with
 the confidence + commit (``lm_head_confidence_commit``) and the same attention
 call over an E4M3 KV cache (``fp8kv_attention``), and the quadratic
-self-speculative step (``quad_spec_attention``).
+self-speculative step (``quad_spec_attention``), and the two-stream training
+attention (``two_stream_attention``).
 """
 
 import argparse
@@ -301,6 +302,60 @@ def bench_quad_attention(torch, stream, calls=50, warmup=5):
                 linear_draft_plus_verify_us=round(linear_us, 2), calls=calls)
 
 
+def bench_two_stream(torch, stream, calls=30, warmup=3):
+    """Two-stream training attention beside the headline: the 3B training shape
+    (8 sequences; clean stream 2048 = 1024 vision + two turns; noisy stream 832;
+    D = 32; 16q/2kv, d = 128, bf16) in one bd_two_stream_attn call.  MFMA-bound:
+    the figure of merit is bf16 TFLOP/s over the algorithmic flops, 4 d per
+    visible (row, key) pair."""
+    import synth
+    from vlm_decoding_amd import bd
+    st = synth.two_stream_step(1)
+    p = st["params"]
+    n, L, Hq, d = st["q"].shape
+    c = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+    sets = []
+    for k in range(N_SETS):
+        s_k = st if k == 0 else synth.make_two_stream(p, synth.two_stream_seed_of(1) + 1000 * k)
+        sets.append([c(s_k[x]) for x in ("q", "k", "v", "spans", "n_spans")])
+    out = torch.empty_like(sets[0][0])
+    desc = bd.two_stream_desc(n, st["Lc"], st["Ln"], st["cap"], p["D"], Hq, p["Hkv"], d, st["spans"].shape[1])
+    ws = torch.zeros(max(bd.bd_two_stream_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
+    import ctypes
+    args = [(ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), sp.data_ptr(), ns.data_ptr(),
+             out.data_ptr(), ws.data_ptr(), ws.numel(), stream.cuda_stream) for q, k, v, sp, ns in sets]
+    status = 0
+    for i in range(warmup):
+        status |= bd.lib.bd_two_stream_attn(*args[i % N_SETS])
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(calls):
+        status |= bd.lib.bd_two_stream_attn(*args[i % N_SETS])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    if status:
+        raise RuntimeError("bd_two_stream_attn failed (status %d)" % status)
+    us = t0.elapsed_time(t1) * 1e3 / calls
+    # Visible (row, key) pairs per head: clean rows see 1..Lc keys; a noisy block
+    # row sees the clean positions before its block plus its block.
+    Lc, D = st["Lc"], p["D"]
+    vis = 0
+    for it in range(n):
+        pairs = Lc * (Lc + 1) // 2
+        for c0, m in st["spans"][it, :st["n_spans"][it]]:
+            for k0 in range(0, int(m), D):
+                bl = min(D, int(m) - k0)
+                pairs += bl * (int(c0) + k0 + bl)
+        vis += pairs
+    flops = 4.0 * d * vis * Hq
+    tflops = flops / (us * 1e-6) / 1e12
+    return dict(workload="two-stream training attention, 8 sequences x (clean 2048 = 1024 vision + 2 turns, "
+                         "noisy 832), D=32, 16q/2kv, d128, bf16",
+                us_per_call=round(us, 2), algorithmic_tflop=round(flops / 1e12, 4), achieved_tflops=round(tflops, 1),
+                peak_tflops=MFMA_BF16_PEAK_TFLOPS, frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), calls=calls)
+
+
 def copy_calibration(n_bytes=256 << 20, reps=5):
     """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
     WRITE_SIZE for this copy kernel give the scale between counter readings and
@@ -327,6 +382,8 @@ def main():
                     help="timed calls of the E4M3 KV-cache attention variant (0 to skip)")
     ap.add_argument("--quad-calls", type=int, default=50,
                     help="timed calls of the quadratic self-speculative attention step (0 to skip)")
+    ap.add_argument("--two-stream-calls", type=int, default=30,
+                    help="timed calls of the two-stream training attention (0 to skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -448,6 +505,7 @@ def main():
     lmhead = bench_lmhead(torch, stream, calls=args.lmhead_calls) if args.lmhead_calls > 0 else None
     fp8kv = bench_fp8kv_attention(torch, stream, calls=args.fp8kv_calls) if args.fp8kv_calls > 0 else None
     quad = bench_quad_attention(torch, stream, calls=args.quad_calls) if args.quad_calls > 0 else None
+    two_stream = bench_two_stream(torch, stream, calls=args.two_stream_calls) if args.two_stream_calls > 0 else None
 
     cpu = None
     if args.cpu_budget > 0:
@@ -487,6 +545,7 @@ def main():
         "lm_head_confidence_commit": lmhead,
         "fp8kv_attention": fp8kv,
         "quad_spec_attention": quad,
+        "two_stream_attention": two_stream,
     }
     print(json.dumps(out), flush=True)
 
