@@ -356,6 +356,45 @@ def bench_two_stream(torch, stream, calls=30, warmup=3):
                 peak_tflops=MFMA_BF16_PEAK_TFLOPS, frac=round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), calls=calls)
 
 
+def bench_layer_serial(torch, stream, sets, steps=100, warmup=5):
+    """The headline step as a model runs it, beside the batched headline: the 36
+    layers' attention as 36 dependent bd_attn_step launches of one layer each, then
+    the confidence + commit, captured once per input set in a HIP graph (with two
+    small copies that restore the block state) and replayed."""
+    graphs = [ds.capture_layer_serial() for ds in sets]
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / steps
+    return dict(workload="headline step, layer-serial: 36 x bd_attn_step(n_items=1) + bd_confidence_commit "
+                         "in one HIP graph per input set",
+                us_per_step=round(us, 2), steps_per_s=round(1e6 / us, 1), steps=steps)
+
+
+def copy_bandwidth(torch, n_bytes=1 << 30, reps=5):
+    """Measured device-to-device copy rate (torch copy of 1 GiB, read + write),
+    the practical HBM ceiling the roofline fractions can be read against."""
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * n_bytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    return round(gbps, 1)
+
+
 def copy_calibration(n_bytes=256 << 20, reps=5):
     """Plain device-to-device copies of a known size: rocprofv3's FETCH_SIZE and
     WRITE_SIZE for this copy kernel give the scale between counter readings and
@@ -384,6 +423,8 @@ def main():
                     help="timed calls of the quadratic self-speculative attention step (0 to skip)")
     ap.add_argument("--two-stream-calls", type=int, default=30,
                     help="timed calls of the two-stream training attention (0 to skip)")
+    ap.add_argument("--layer-serial-steps", type=int, default=100,
+                    help="timed replays of the layer-serial graph of the headline step (0 to skip)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -502,6 +543,11 @@ def main():
                                        round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
                     algorithmic_bytes_per_launch=attn_bytes)
 
+    layer_serial = (bench_layer_serial(torch, stream, sets, steps=args.layer_serial_steps)
+                    if args.layer_serial_steps > 0 else None)
+    copy_gbps = copy_bandwidth(torch)
+    roofline["copy_gbps_measured"] = copy_gbps
+    roofline["frac_of_copy"] = round(achieved / copy_gbps, 4)
     lmhead = bench_lmhead(torch, stream, calls=args.lmhead_calls) if args.lmhead_calls > 0 else None
     fp8kv = bench_fp8kv_attention(torch, stream, calls=args.fp8kv_calls) if args.fp8kv_calls > 0 else None
     quad = bench_quad_attention(torch, stream, calls=args.quad_calls) if args.quad_calls > 0 else None
@@ -542,6 +588,7 @@ def main():
         "event_stride": stride,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "layer_serial_graph": layer_serial,
         "lm_head_confidence_commit": lmhead,
         "fp8kv_attention": fp8kv,
         "quad_spec_attention": quad,

@@ -143,6 +143,35 @@ def test_attention_deterministic_and_workspace_reuse(dev):
     assert torch.equal(first, ds.out)
 
 
+def test_layer_serial_graph_replays_match_eager(dev):
+    """The step with one bd_attn_step per layer, captured in a HIP graph: every
+    replay (with other eager work and synchronisations in between) reproduces the
+    eager layer-serial results bit for bit, and those match the oracle."""
+    torch = dev["torch"]
+    p = synth.params_for(3, n_items=4, prefix=("list", [0, 100, 700, 2000]), V=3001, n_masked=8, plant=None)
+    st = synth.make_step(p, 321)
+    ds = dev["step"].DeviceStep(st)
+    ds.reset_block_state()
+    ds.layer_serial_step()
+    torch.cuda.synchronize()
+    ref = [ds.out.clone(), ds.masked.clone(), ds.tokens.clone(), ds.conf.clone()]
+    _check_attention(_out_host(dev, ds), _reference(st, p["mode"]), "layer_serial")
+    g = ds.capture_layer_serial()
+    for r in range(3):
+        ds.out.zero_()
+        ds.masked.fill_(3)
+        ds.attn()  # eager work between replays (the batched call) ...
+        torch.cuda.synchronize()
+        ds.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [ds.out, ds.masked, ds.tokens, ds.conf]
+        for a, b in zip(got, ref):
+            if a.dtype == torch.float32:  # conf holds NaN at unmasked slots: compare bits
+                a, b = a.view(torch.int32), b.view(torch.int32)
+            assert torch.equal(a, b), r
+
+
 def test_attention_rejects_bad_arguments_before_launch(dev):
     bd = dev["bd"]
     ds = dev["step"].DeviceStep(synth.config_step(2))

@@ -6,6 +6,8 @@ the library calls on those buffers.  torch supplies device memory and the
 stream; the arithmetic runs in libbd.so.
 """
 
+import ctypes
+
 import numpy as np
 import torch
 
@@ -105,6 +107,51 @@ class DeviceStep:
         """One denoise step: block attention, then confidence + commit."""
         self.attn(stream=stream)
         self.confidence_commit(stream=stream)
+
+    def layer_attn_args(self, it, stream=None):
+        """bd_attn_step arguments for item ``it`` alone (one layer of a model), as a
+        tuple for the raw C call: the descriptor has n_items = 1 and every pointer
+        is offset to the item's slice."""
+        a = self.adesc
+        if not hasattr(self, "_layer_desc"):
+            self._layer_desc = bd.attn_desc(1, a.D, a.Hq, a.Hkv, a.d, a.cap, a.dtype, a.mode, a.max_prefix,
+                                            a.scale)
+        eb = self.q.element_size()
+        S = self.q.shape[1]  # block slots per item
+        qo = it * S * a.Hq * a.d * eb
+        bo = it * S * a.Hkv * a.d * eb
+        co = it * a.Hkv * a.cap * a.d * eb
+        return (ctypes.byref(self._layer_desc), self.q.data_ptr() + qo, self.k_blk.data_ptr() + bo,
+                self.v_blk.data_ptr() + bo, self.k_cache.data_ptr() + co, self.v_cache.data_ptr() + co,
+                self.prefix.data_ptr() + 4 * it, self.out.data_ptr() + qo, self.attn_ws.data_ptr(),
+                self.attn_ws.numel(), bd._stream(stream))
+
+    def layer_serial_step(self, stream=None):
+        """The step as a model runs it: one bd_attn_step per item (layer), one after
+        another on the stream, then confidence + commit."""
+        for it in range(self.adesc.n_items):
+            bd._check("bd_attn_step", bd.lib.bd_attn_step(*self.layer_attn_args(it, stream)))
+        self.confidence_commit(stream=stream)
+
+    def capture_layer_serial(self, restore_state=True):
+        """A HIP graph of layer_serial_step (captured through torch): 36 dependent
+        attention launches plus the commit become one replayable unit.  With
+        ``restore_state`` the graph first copies the block's initial masked /
+        tokens state back, so every replay does the same work."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.layer_serial_step(stream=side)  # warm-up outside the capture
+            if restore_state:
+                self.reset_block_state()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            if restore_state:
+                self.reset_block_state()
+            self.layer_serial_step(stream=side)
+        return g
 
     def verify(self, logits=None, draft=None, stream=None):
         p = self.p
