@@ -503,11 +503,9 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         }
     };
 
-    auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */,
-                       int mkey0 /* sequence mode: first key of a masked tile, else -1 */) __attribute__((always_inline)) {
+    // S^T = K . Q^T for the tile in stage st.
+    auto qk = [&](int st, floatx16 (&s)[KB]) __attribute__((always_inline)) {
         const uint8_t *Kt = kbuf(st);
-        const uint8_t *Vt = vbuf(st);
-        floatx16 s[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             s[kb] = floatx16{};
@@ -527,6 +525,10 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
                 }
             }
         }
+    };
+    // Scores a row may not use become -inf: tail tiles (tt >= 0) of the block
+    // modes, or a masked tile of the sequence mode (first key mkey0 >= 0).
+    auto apply_mask = [&](floatx16 (&s)[KB], int tt, int mkey0) __attribute__((always_inline)) {
         if (SEQ && mkey0 >= 0) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -548,6 +550,10 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
                     s[kb][i] = ok ? s[kb][i] : -INFINITY;
                 }
         }
+    };
+    // Online softmax of one tile's scores and O^T += V^T . P^T.
+    auto softmax_pv = [&](int st, floatx16 (&s)[KB]) __attribute__((always_inline)) {
+        const uint8_t *Vt = vbuf(st);
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -600,6 +606,13 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
                 }
             }
         }
+    };
+    auto compute = [&](int st, int tt /* tail tile index, -1 for bulk */,
+                       int mkey0 /* sequence mode: first key of a masked tile, else -1 */) __attribute__((always_inline)) {
+        floatx16 s[KB];
+        qk(st, s);
+        apply_mask(s, tt, mkey0);
+        softmax_pv(st, s);
     };
 
     // Tail split: gather and compute its (one to three) tiles.
