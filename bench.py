@@ -44,6 +44,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 METRIC = "denoise steps/sec + achieved HBM GB/s (%peak), 3B-shape block-16, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_cfg3_traffic.json")
+HEADLINE_KERNELS = ("attn_mfma_kernel<128, 4, false, false>", "attn_merge_kernel<128, 4, 32, false>")
+FP8KV_KERNELS = ("attn_mfma_kernel<128, 4, true, false>", "attn_merge_kernel<128, 4, 64, false>")
 ATTN_SOURCES = ["vlm_decoding_amd/csrc/bd_attn.hip", "vlm_decoding_amd/csrc/bd_common.h",
                 "vlm_decoding_amd/csrc/bd_internal.h"]
 
@@ -130,14 +132,14 @@ def write_traffic(pmc_dir, copy_bytes=256 << 20):
             acc.setdefault(name, []).append(v * 1024.0 * sc)
         for name, vals in acc.items():
             per_kernel.setdefault(name, {})[counter.lower() + "_bytes"] = sum(vals) / len(vals)
-    # The headline call is the bf16 instance pair (tile kernel <.., false>, merge
-    # <.., 32>); the E4M3 pair (<.., true>, <.., 64>) is summed on its own.
-    def launch_bytes(tags):
+    # The headline call is the bf16 block-mode instance pair; the E4M3 pair is
+    # summed on its own.
+    def launch_bytes(names):
         return sum(v.get("fetch_size_bytes", 0.0) + v.get("write_size_bytes", 0.0)
-                   for k, v in per_kernel.items() if k.endswith(tags))
+                   for k, v in per_kernel.items() if k in names)
     out = {
-        "bytes_per_launch": round(launch_bytes((", false>", ", 32>"))),
-        "fp8kv_bytes_per_launch": round(launch_bytes((", true>", ", 64>"))),
+        "bytes_per_launch": round(launch_bytes(HEADLINE_KERNELS)),
+        "fp8kv_bytes_per_launch": round(launch_bytes(FP8KV_KERNELS)),
         "per_kernel": {k: {kk: round(vv) for kk, vv in v.items()} for k, v in per_kernel.items()},
         "fetch_scale": f_scale, "write_scale": w_scale,
         "calibration": "FETCH_SIZE/WRITE_SIZE over plain %d-byte device copies (bench.py --copy-calibration)" % copy_bytes,
@@ -537,7 +539,7 @@ def main():
     tr = traffic_per_launch()
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=tr,
-                    kernel="bd_attn_step (attn_mfma_kernel<128, 4, false> + attn_merge_kernel<128, 4, 32>)",
+                    kernel="bd_attn_step (%s + %s)" % HEADLINE_KERNELS,
                     kernel_avg_us=round(attn_avg_s * 1e6, 2),
                     kernel_p10_p90_us=[round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
                                        round(float(np.percentile(attn_ms, 90)) * 1e3, 2)],
