@@ -700,25 +700,35 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     }
 }
 
+// Waves per merge block: each merges one (unit, 32-row group, quarter of the
+// columns) per wave, so a launch has 4 / kMergeWaves blocks per row group.
+constexpr int kMergeWaves = 1;
+
 // Merge of the split-K partials (second launch; the kernel boundary orders
-// the partial stores before these loads).  One 256-thread block per (unit,
-// 32-row group): the group's rows are the rows one wave of the tile kernel
-// owned.  Thread (j, lane) merges 16-byte partial units qq = j * QPT .. of
-// lane `lane` of that wave:
+// the partial stores before these loads).  Each wave of a block handles one
+// (unit, 32-row group, quarter of the columns): the group's rows are the rows
+// one wave of the tile kernel owned.  Wave j, lane `lane` merges 16-byte
+// partial units qq = jq * QPT .. of lane `lane` of that wave:
 //   M = max_s m_s,  c_s = 2^(m_s - M) l_s,  o = sum_s c_s (o_s / l_s) / sum_s c_s,
-// summed in split order.  The merged 32 rows are staged in LDS and written
-// out as whole rows (HD * 2 contiguous bytes each).
+// summed in split order.  The merged rows are staged in LDS and written out
+// as row segments of WPB * HD / 4 contiguous elements.
 template <int HD, int NW, int TK, bool SEQ>
-__global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
+__global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams p) {
+    constexpr int WPB = kMergeWaves;    // waves per block
     constexpr int NT_TILE = NW * 64;    // threads of the tile kernel's block
     constexpr int MB = HD / 32;
     constexpr int QQ = MB * 2;          // 16-byte partial units per lane
     constexpr int QPT = QQ / 4;         // units per thread here
+    constexpr int DQ = HD / 4;          // output columns of one quarter (QPT units)
     constexpr int MAXS = kMaxSplits;
-    constexpr int RS = HD + 8;          // LDS row stride (elements), staggers banks
+    constexpr int RS = DQ * WPB + 8;    // LDS row stride (elements), staggers banks
     __shared__ __attribute__((aligned(16))) uint16_t rows_lds[32 * RS];
-    const int unit = blockIdx.x / NW;
-    const int wv = blockIdx.x - unit * NW;
+    // Block = (unit, wave wv of the tile kernel's block, WPB of its four column quarters).
+    constexpr int QB = 4 / WPB;         // blocks per (unit, wave)
+    const int unit = blockIdx.x / (NW * QB);
+    const int rem = blockIdx.x - unit * (NW * QB);
+    const int wv = rem / QB;
+    const int qb = rem - wv * QB;
     const int rb = unit % p.row_blocks;
     const int pair = unit / p.row_blocks;
     const int g = pair % p.Hkv;
@@ -726,7 +736,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
     const int row0 = rb * (NW * 32) + wv * 32;
     if (row0 >= p.R) return;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, jq = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int lane = tid & 63, jl = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int jq = qb * WPB + jl;           // column quarter of this thread
     const int src_t = wv * 64 + lane;      // thread of the tile kernel's block
     const size_t base = (size_t)unit * p.max_splits;
     const uint4 *wo = reinterpret_cast<const uint4 *>(p.ws_o);
@@ -770,11 +781,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
             }
         }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    // Unit qq holds d = mb*32 + 16*(qq%2) + 4*half + {0..3} and the same + 8.
+    // Unit qq holds d = mb*32 + 16*(qq%2) + 4*half + {0..3} and the same + 8;
+    // in this block's LDS rows, column d - qb * WPB * DQ.
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
         const int qq = jq * QPT + j;
-        const int d0 = (qq >> 1) * 32 + 16 * (qq & 1) + 4 * half;
+        const int d0 = (qq >> 1) * 32 + 16 * (qq & 1) + 4 * half - qb * WPB * DQ;
 #pragma unroll
         for (int h8 = 0; h8 < 2; ++h8) {
             uint2 o;
@@ -784,9 +796,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
         }
     }
     __syncthreads();
-    // Whole rows out: HD/8 threads per row, 16 bytes each.
-    constexpr int TPR = HD / 8;
-    constexpr int RPP = 256 / TPR;  // rows per pass
+    // The block's columns of each row out: TPR threads per row, 16 bytes each.
+    constexpr int TPR = WPB * DQ / 8;
+    constexpr int RPP = WPB * 64 / TPR;  // rows per pass
 #pragma unroll
     for (int r0 = 0; r0 < 32; r0 += RPP) {
         const int rr = r0 + tid / TPR, u = tid % TPR;
@@ -794,7 +806,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MfmaParams p) {
         if (r < p.R) {
             const int slot = r / p.G;
             const int head = g * p.G + (r - slot * p.G);
-            uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD + u * 8;
+            uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD + qb * WPB * DQ + u * 8;
             bd_store_nt(op, *reinterpret_cast<const uint4 *>(&rows_lds[rr * RS + u * 8]));
         }
     }
@@ -1002,7 +1014,7 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
     if (e != hipSuccess || pl.max_splits == 1) return e;
-    return hipLaunchKernel(merge, dim3(pl.units * pl.nw), dim3(256), args, 0, s);
+    return hipLaunchKernel(merge, dim3(pl.units * pl.nw * (4 / kMergeWaves)), dim3(kMergeWaves * 64), args, 0, s);
 }
 
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {
