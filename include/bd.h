@@ -30,8 +30,11 @@
  *    BD_E_LAUNCH means the HIP runtime rejected a launch (bd_last_hip_error()).
  *  - Workspaces: size them with the matching *_workspace_bytes() call and
  *    zero-fill them once before first use.  Each call leaves the counter area
- *    it uses zeroed again, so a workspace can be reused by later calls on the
- *    same stream.  Calls that overlap in time must not share a workspace.
+ *    it uses zeroed again, so later calls with the same descriptor on the same
+ *    stream can reuse the workspace.  The counter area's place depends on the
+ *    descriptor: a workspace used with another descriptor, or for anything
+ *    else, must be zero-filled again before such a call.  Calls that overlap
+ *    in time must not share a workspace.
  *  - bf16 data is raw 16-bit storage (round-to-nearest-even when produced).
  *    Accumulation is fp32.  Results do not depend on scheduling: every
  *    reduction runs in a fixed order.  bd_attn_step may split a long
