@@ -914,8 +914,11 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     pl.rows_per_group = pl.nw * 32;
     pl.row_blocks = (pl.rows + pl.rows_per_group - 1) / pl.rows_per_group;
     pl.units = n * Hkv * pl.row_blocks;
-    // Resident workgroups: LDS (kStages tile stages) bounds them per CU.
-    const int slots = kCUs * occupancy_for(d);
+    // Workgroups to launch: as many as hold two waves per SIMD.  LDS (kStages
+    // tile stages) allows two workgroups per CU, which is that many for 4-wave
+    // workgroups; 8-wave workgroups are sized for one per CU, since a second one
+    // (four waves per SIMD) slowed the 8-item 7B step by 15%.
+    const int slots = kCUs * occupancy_for(d) * 4 / pl.nw;
     const int ntiles_max = max_prefix / pl.tk;
     const int want = std::max(1, slots / pl.units);
     // Splits per unit (the device side derives each unit's count from its own
