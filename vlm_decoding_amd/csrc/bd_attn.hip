@@ -703,6 +703,9 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
 // Waves per merge block: each merges one (unit, 32-row group, quarter of the
 // columns) per wave, so a launch has 4 / kMergeWaves blocks per row group.
 constexpr int kMergeWaves = 1;
+// The merge grid, units * nw * (4 / kMergeWaves) with nw >= 4, must be a
+// multiple of 8 for the XCD-aware block decode.
+static_assert((4 * (4 / kMergeWaves)) % 8 == 0, "merge grid must be a multiple of 8");
 
 // Merge of the split-K partials (second launch; the kernel boundary orders
 // the partial stores before these loads).  Each wave of a block handles one
@@ -725,8 +728,12 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams
     __shared__ __attribute__((aligned(16))) uint16_t rows_lds[32 * RS];
     // Block = (unit, wave wv of the tile kernel's block, WPB of its four column quarters).
     constexpr int QB = 4 / WPB;         // blocks per (unit, wave)
-    const int unit = blockIdx.x / (NW * QB);
-    const int rem = blockIdx.x - unit * (NW * QB);
+    // XCD-aware decode (the grid is a multiple of 16): a unit's blocks share an
+    // XCD, so the four column quarters of a row group fetch its (m, l) pairs
+    // through one L2.
+    const int lb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int unit = lb / (NW * QB);
+    const int rem = lb - unit * (NW * QB);
     const int wv = rem / QB;
     const int qb = rem - wv * QB;
     const int rb = unit % p.row_blocks;
