@@ -120,6 +120,61 @@ def test_attention_edge_cases(dev, label, ov, mode):
     _run_attention(dev, synth.make_step(p, seed=zlib.crc32(label.encode()) % 10000), mode=mode, label=label)
 
 
+# Seeded random sweep over small shapes: dtype (bf16, E4M3 cache, fp32), mask
+# mode (bidirectional, causal, quadratic), head layout, d, block length and
+# ragged prefixes drawn together, and for about half the cases a plan sized
+# for a longer context than any prefix (its surplus workgroups must exit and
+# the rest must not read past a prefix: cache slots there hold NaN).
+N_SWEEP = 32
+
+
+def _sweep_case(i):
+    rng = np.random.default_rng(5000 + i)
+
+    def one_prefix():
+        kind = int(rng.integers(0, 3))
+        if kind == 0:
+            return 0 if rng.random() < 0.5 else int(rng.integers(1, 40))
+        if kind == 1:
+            return int(rng.integers(1, 1300))
+        return int(64 * rng.integers(1, 20) + rng.integers(-1, 2))  # at and around tile edges
+
+    while True:
+        dtype = int(rng.choice([BF16, BF16, FP8KV, F32]))
+        mode = int(rng.choice([BIDIR, CAUSAL, QUAD]))
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 3, 4, 7, 8]))
+        n = int(rng.integers(1, 6))
+        B = int(rng.integers(1, 11)) if mode == QUAD else None
+        D = synth.quad_slot_count(B) if mode == QUAD else int(rng.integers(1, 65))
+        prefix = [one_prefix() for _ in range(n)]
+        host_max = max(prefix) + (int(rng.integers(1, 700)) if rng.random() < 0.5 else 0)
+        if n * Hq * D * (max(prefix) + D) * d <= 1.5e8:  # keeps the fp64 oracle within seconds
+            break
+    p = dict(n_items=n, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, prefix=("list", prefix),
+             cap=synth.cache_capacity(host_max, D))
+    if mode == QUAD:
+        st = synth.make_quad_step(dict(synth.QUAD_CONFIGS[2], B=B, **p), 5000 + i)
+    else:
+        st = synth.make_step(synth.params_for(3, D=D, mode=mode, n_masked=D // 2, V=1000, plant=None, **p),
+                             5000 + i)
+    return st, host_max
+
+
+@pytest.mark.parametrize("i", range(N_SWEEP))
+def test_attention_random_sweep(dev, i):
+    st, host_max = _sweep_case(i)
+    p = st["params"]
+    label = "sweep%d" % i
+    _say("attention %s n=%d D=%d B=%s Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s max_prefix=%d cap=%d" % (
+        label, p["n_items"], p["D"], p.get("B"), p["Hq"], p["Hkv"], p["d"], p["dtype"], p["mode"],
+        st["prefix"].tolist(), host_max, st["cap"]))
+    ds = dev["step"].DeviceStep(st, max_prefix=host_max)
+    ds.attn()
+    _check_attention(_out_host(dev, ds), _reference(st, p["mode"]), label)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
 def test_attention_fp32_vector_path(dev, d, mode):

@@ -34,14 +34,16 @@ def to_host(t: torch.Tensor, like=None) -> np.ndarray:
 class DeviceStep:
     """One step's inputs resident in HBM, with outputs and workspaces."""
 
-    def __init__(self, step: dict, device="cuda"):
+    def __init__(self, step: dict, device="cuda", max_prefix=None):
+        """``max_prefix`` (default: the longest prefix of ``step``) is the host-side
+        bound the attention plan is sized for; it must not exceed the cache capacity."""
         p = step["params"]
         self.p = p
         self.dtype = p["dtype"]
         self.device = device
         n, D, Hq, Hkv, d = p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"]
         self.cap = int(step["cap"])
-        self.max_prefix = int(step["prefix"].max())
+        self.max_prefix = int(step["prefix"].max()) if max_prefix is None else int(max_prefix)
         self.q = to_device(step["q"], device)
         self.k_blk = to_device(step["k_blk"], device)
         self.v_blk = to_device(step["v_blk"], device)
