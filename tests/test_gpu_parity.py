@@ -438,6 +438,35 @@ def test_two_stream_edge_cases(dev, label, ov):
     _run_two_stream(dev, st, "two_stream_" + label)
 
 
+# Seeded random sweep of two-stream shapes: 1-3 sequences with their own turn
+# lists (empty prompts and empty responses included), block lengths from 1 to
+# longer than every response, GQA layouts with 1-8 query heads per KV head.
+N_TS_SWEEP = 16
+
+
+def _two_stream_sweep_case(i):
+    rng = np.random.default_rng(6000 + i)
+    while True:
+        n = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2]))
+        Hq = Hkv * int(rng.choice([1, 2, 4, 7, 8]))
+        d = int(rng.choice([64, 128]))
+        D = int(rng.choice([1, 2, 5, 8, 16, 32, 48]))
+        turns = [[(int(rng.integers(0, 40)), int(rng.choice([0, rng.integers(1, 20), rng.integers(20, 160)])))
+                  for _ in range(int(rng.integers(1, 4)))] for _ in range(n)]
+        p = dict(synth.TWO_STREAM_CONFIGS[2], n_seq=n, Hq=Hq, Hkv=Hkv, d=d, D=D,
+                 vision=int(rng.integers(1, 200)), turns=turns)
+        Lc = p["vision"] + max(sum(a + b for a, b in t) for t in turns)
+        L = Lc + max(sum(b for _, b in t) for t in turns)
+        if n * L * L * Hq * d <= 3e8:  # keeps the fp64 oracle within seconds
+            return synth.make_two_stream(p, 6000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_TS_SWEEP))
+def test_two_stream_random_sweep(dev, i):
+    _run_two_stream(dev, _two_stream_sweep_case(i), "two_stream_sweep%d" % i)
+
+
 def test_two_stream_deterministic(dev):
     torch, bd = dev["torch"], dev["bd"]
     st = synth.make_two_stream(dict(synth.TWO_STREAM_CONFIGS[2], n_seq=1, Hq=2, Hkv=1, vision=2000,
