@@ -627,6 +627,54 @@ def test_confidence_ties_and_equal_rows(dev):
     assert ds.committed.cpu().numpy()[0].tolist() == [1, 0, 0, 0, 1, 0]   # k = 2: slot 4, then slot 0
 
 
+# Seeded random sweep of the row kernels' shapes: request count, block length,
+# vocabulary (odd sizes and sizes at 1024-multiples included), masked count,
+# S, tau and logit scale drawn together; a quarter of the cases plant a peak.
+N_ROW_SWEEP = 16
+
+
+def _row_sweep_params(i):
+    rng = np.random.default_rng(7000 + i)
+    while True:
+        n_req = int(rng.integers(1, 9))
+        D = int(rng.choice([1, 2, 7, 8, 16, 31, 32, 64]))
+        V = int(rng.choice([2, int(rng.integers(3, 5000)), 1024 * int(rng.integers(1, 160)) + int(rng.integers(-1, 2)),
+                            int(rng.integers(5000, 160000))], p=[0.1, 0.3, 0.3, 0.3]))
+        if n_req * D * V <= 2e7:
+            break
+    return dict(n_items=1, n_req=n_req, D=D, V=V, n_masked=int(rng.integers(0, D + 1)),
+                S=int(rng.integers(1, D + 1)), tau=float(rng.choice([0.01, 0.2, 0.5, 0.9, 1.5])),
+                logit_sigma2=float(rng.choice([0.25, 1.0, 4.0, 16.0])), plant="peak8" if rng.random() < 0.25 else None,
+                prefix=("fixed", 8), Hq=2, Hkv=1, d=64, dtype=F32)
+
+
+@pytest.mark.parametrize("i", range(N_ROW_SWEEP))
+def test_confidence_commit_random_sweep(dev, i):
+    p = synth.params_for(1, **_row_sweep_params(i))
+    s = synth.make_step(p, seed=7000 + i)
+    label = "commit_sweep%d" % i
+    _say("%s n_req=%d D=%d V=%d masked=%d S=%d tau=%g sigma2=%g plant=%s" % (
+        label, p["n_req"], p["D"], p["V"], p["n_masked"], p["S"], p["tau"], p["logit_sigma2"], p["plant"]))
+    ds = dev["step"].DeviceStep(s)
+    ds.confidence_commit()
+    _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], label)
+
+
+@pytest.mark.parametrize("i", range(N_ROW_SWEEP))
+def test_verify_random_sweep(dev, i):
+    q = _row_sweep_params(100 + i)
+    p = synth.params_for(4, **dict(q, plant="geom0.3", D=min(q["D"], 32)))
+    s = synth.make_step(p, seed=7100 + i)
+    _say("verify_sweep%d n_req=%d D=%d V=%d planted=%s" % (i, p["n_req"], p["D"], p["V"], s["planted_L"].tolist()))
+    ds = dev["step"].DeviceStep(s)
+    L = ds.verify()
+    dev["torch"].cuda.synchronize()
+    L_ref, amax_ref = oracle.spec_verify(s["logits"], s["draft"])
+    np.testing.assert_array_equal(L.cpu().numpy(), L_ref)
+    np.testing.assert_array_equal(L_ref, s["planted_L"])
+    np.testing.assert_array_equal(ds.argmax.cpu().numpy(), amax_ref)
+
+
 # ---------------------------------------------------------------------------
 # Speculative verify and KV append
 # ---------------------------------------------------------------------------
