@@ -850,6 +850,39 @@ def test_lmhead_edge_cases(dev, label, ov):
     _compare_lmhead(dev, g, st, label)
 
 
+# Seeded random sweep of LM-head shapes: hidden size (multiples of 256 up to
+# 4096), vocabulary (tiny, odd, and past several 16-row tiles), requests,
+# block length, masked count, S, tau and the number of planted peaks.
+N_LMHEAD_SWEEP = 8
+
+
+def _lmhead_sweep_case(i):
+    rng = np.random.default_rng(8000 + i)
+    while True:
+        H = 256 * int(rng.integers(1, 17))
+        V = int(rng.choice([int(rng.integers(2, 40)), int(rng.integers(40, 5000)), int(rng.integers(5000, 40000))]))
+        D = int(rng.choice([1, 4, 8, 16]))
+        n_req = int(rng.integers(1, 16 // D + 1))  # at most 16 slots per call
+        if n_req * D * H * V <= 4e8:  # keeps the fp64 oracle within seconds
+            break
+    n_masked = int(rng.integers(0, D + 1))
+    p = dict(synth.LMHEAD_CONFIGS[2], H=H, V=V, n_req=n_req, D=D, n_masked=n_masked, S=int(rng.integers(1, D + 1)),
+             tau=float(rng.choice([0.05, 0.5, 0.9, 1.2])), plants=int(rng.integers(0, n_masked + 1)))
+    return synth.make_lmhead(p, seed=8000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_LMHEAD_SWEEP))
+def test_lmhead_random_sweep(dev, i):
+    st = _lmhead_sweep_case(i)
+    p = st["params"]
+    label = "lmhead_sweep%d" % i
+    _say("%s n_req=%d D=%d V=%d H=%d masked=%d S=%d tau=%g plants=%d" % (
+        label, p["n_req"], p["D"], p["V"], p["H"], p["n_masked"], p["S"], p["tau"], p["plants"]))
+    g = _LmDev(dev, st)
+    g.run()
+    _compare_lmhead(dev, g, st, label)
+
+
 def test_lmhead_deterministic_and_reusable_workspace(dev):
     torch = dev["torch"]
     st = synth.lmhead_step(2)
