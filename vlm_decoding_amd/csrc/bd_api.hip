@@ -18,6 +18,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Block slots per item: D, or B (B + 3) / 2 for the quadratic mode (D = B).
 int block_slots(const bd_attn_desc *d) { return d->mode == BD_BLOCK_QUAD ? d->D * (d->D + 3) / 2 : d->D; }
 
+// Launch sizes stay within 32-bit grid and index arithmetic: at most
+// kMaxSplits workgroups per (item, KV head, 128-row block) on the MFMA path,
+// one wave per query row on the vector path.  Called once slots * Hq <= 2^20.
+bool launch_fits(int64_t n, int64_t slots, int64_t Hq, int64_t Hkv) {
+    const int64_t row_blocks = (slots * (Hq / Hkv) + 127) / 128;
+    int64_t units = 0, rows = 0;
+    if (__builtin_mul_overflow(n, Hkv * row_blocks, &units) || units > INT32_MAX / bd::kMaxSplits - 1) return false;
+    if (__builtin_mul_overflow(n, slots * Hq, &rows) || rows / 4 >= INT32_MAX) return false;
+    return true;
+}
+
 bd_status check_attn_desc(const bd_attn_desc *d) {
     if (!d) return BD_E_NULL;
     if (d->dtype != BD_F32 && d->dtype != BD_BF16 && d->dtype != BD_FP8KV) return BD_E_DTYPE;
@@ -30,6 +41,7 @@ bd_status check_attn_desc(const bd_attn_desc *d) {
     if (d->max_prefix < 0 || d->max_prefix > d->cap) return BD_E_SHAPE;
     // Index arithmetic in the kernels uses 32-bit ints for per-item quantities.
     if ((int64_t)block_slots(d) * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
+    if (!launch_fits(d->n_items, block_slots(d), d->Hq, d->Hkv)) return BD_E_SHAPE;
     return BD_OK;
 }
 
@@ -65,6 +77,7 @@ bd_status check_two_stream_desc(const bd_two_stream_desc *d) {
     if (d->cap < L || d->cap % 32 != 0) return BD_E_SHAPE;
     if (d->max_spans < 0 || d->max_spans > 256 || (d->Ln > 0 && d->max_spans < 1)) return BD_E_SHAPE;
     if (L * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
+    if (!launch_fits(d->n_seq, L, d->Hq, d->Hkv)) return BD_E_SHAPE;
     return BD_OK;
 }
 
