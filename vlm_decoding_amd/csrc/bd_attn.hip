@@ -160,7 +160,7 @@ __device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_spli
     const int w = (work + u.nsplit - 1) / u.nsplit;                    // target work per split
     const int tail_bulk = nbs == 0 ? nbulk : max(0, nbulk - nbs * w);  // bulk tiles of the tail split
     const int shared = nbulk - tail_bulk;                              // >= nbs: every bulk split gets one
-    // 32-bit arithmetic is enough: split < 16 and shared <= cap / TK < 2^19.
+    // 32-bit arithmetic is enough: split < kMaxSplits = 32 and shared <= cap / TK < 2^19.
     if (split < nbs) {
         u.t0 = (int)((unsigned)(split * shared) / (unsigned)nbs);
         u.nb = (int)((unsigned)((split + 1) * shared) / (unsigned)nbs) - u.t0;
@@ -700,36 +700,38 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     }
 }
 
-// Waves per merge block: each merges one (unit, 32-row group, quarter of the
-// columns) per wave, so a launch has 4 / kMergeWaves blocks per row group.
+// Waves per merge block: each merges one (unit, 32-row group, column part)
+// per wave, so a launch has NP / kMergeWaves blocks per row group.
 constexpr int kMergeWaves = 1;
-// The merge grid, units * nw * (4 / kMergeWaves) with nw >= 4, must be a
-// multiple of 8 for the XCD-aware block decode.
+// The merge grid, units * nw * (NP / kMergeWaves) with nw >= 4 and NP >= 4,
+// must be a multiple of 8 for the XCD-aware block decode.
 static_assert((4 * (4 / kMergeWaves)) % 8 == 0, "merge grid must be a multiple of 8");
 
 // Merge of the split-K partials (second launch; the kernel boundary orders
 // the partial stores before these loads).  Each wave of a block handles one
-// (unit, 32-row group, quarter of the columns): the group's rows are the rows
-// one wave of the tile kernel owned.  Wave j, lane `lane` merges 16-byte
+// (unit, 32-row group, part jq of NP column parts): the group's rows are the
+// rows one wave of the tile kernel owned.  Wave j, lane `lane` merges 16-byte
 // partial units qq = jq * QPT .. of lane `lane` of that wave:
 //   M = max_s m_s,  c_s = 2^(m_s - M) l_s,  o = sum_s c_s (o_s / l_s) / sum_s c_s,
 // summed in split order.  The merged rows are staged in LDS and written out
-// as row segments of WPB * HD / 4 contiguous elements.
-template <int HD, int NW, int TK, bool SEQ>
+// as row segments of WPB * HD / NP contiguous elements.  Every split slot of a
+// lane is loaded at once, QPT * MAXS 16-byte units: NP = 4 with up to 16
+// splits, or one unit per split (NP = HD / 16) with up to 32.
+template <int HD, int NW, int TK, bool SEQ, int NP, int MAXS>
 __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams p) {
     constexpr int WPB = kMergeWaves;    // waves per block
     constexpr int NT_TILE = NW * 64;    // threads of the tile kernel's block
     constexpr int MB = HD / 32;
     constexpr int QQ = MB * 2;          // 16-byte partial units per lane
-    constexpr int QPT = QQ / 4;         // units per thread here
-    constexpr int DQ = HD / 4;          // output columns of one quarter (QPT units)
-    constexpr int MAXS = kMaxSplits;
+    constexpr int QPT = QQ / NP;        // units per thread here
+    constexpr int DQ = HD / NP;         // output columns of one part (QPT units)
+    static_assert(QPT >= 1 && QQ % NP == 0 && MAXS <= kMaxSplits, "merge shape");
     constexpr int RS = DQ * WPB + 8;    // LDS row stride (elements), staggers banks
     __shared__ __attribute__((aligned(16))) uint16_t rows_lds[32 * RS];
-    // Block = (unit, wave wv of the tile kernel's block, WPB of its four column quarters).
-    constexpr int QB = 4 / WPB;         // blocks per (unit, wave)
+    // Block = (unit, wave wv of the tile kernel's block, WPB of its NP column parts).
+    constexpr int QB = NP / WPB;        // blocks per (unit, wave)
     // XCD-aware decode (the grid is a multiple of 16): a unit's blocks share an
-    // XCD, so the four column quarters of a row group fetch its (m, l) pairs
+    // XCD, so the column parts of a row group fetch its (m, l) pairs
     // through one L2.
     const int lb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     const int unit = lb / (NW * QB);
@@ -744,7 +746,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams
     if (row0 >= p.R) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, jl = tid >> 6, half = lane >> 5, col = lane & 31;
-    const int jq = qb * WPB + jl;           // column quarter of this thread
+    const int jq = qb * WPB + jl;           // column part of this thread
     const int src_t = wv * 64 + lane;      // thread of the tile kernel's block
     const size_t base = (size_t)unit * p.max_splits;
     const uint4 *wo = reinterpret_cast<const uint4 *>(p.ws_o);
@@ -929,8 +931,12 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     const int ntiles_max = max_prefix / pl.tk;
     const int want = std::max(1, slots / pl.units);
     // Splits per unit (the device side derives each unit's count from its own
-    // prefix): sized so that a unit at max_prefix gets about `want` splits.
-    pl.max_splits = ntiles_max == 0 ? 1 : std::max(2, std::min(std::min(want, ntiles_max + 1), kMaxSplits));
+    // prefix): sized so that a unit at max_prefix gets about `want` splits, at
+    // most kNarrowSplits; up to kMaxSplits while each workgroup still has a CU
+    // of its own (few units, where a lone wave per SIMD makes the tile loop
+    // latency-bound and shorter splits pay).
+    const int cap = (long)pl.units * kMaxSplits <= kCUs ? kMaxSplits : kNarrowSplits;
+    pl.max_splits = ntiles_max == 0 ? 1 : std::max(2, std::min(std::min(want, ntiles_max + 1), cap));
     // Work of a unit at max_prefix in bulk-tile units: its bulk tiles plus
     // kTailCost per tail tile (up to tk - 1 cache positions and the D slots).
     const int ntail_max = (pl.tk - 1 + D + pl.tk - 1) / pl.tk;
@@ -940,7 +946,7 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
         // Whole sequences of D positions: a unit has at most D / tk key tiles,
         // all streamed the same way; the split count only fills the GPU.
         const int nt = (D + pl.tk - 1) / pl.tk;
-        pl.max_splits = std::max(1, std::min(std::min(want, nt), kMaxSplits));
+        pl.max_splits = std::max(1, std::min(std::min(want, nt), cap));
         pl.tiles_per_split = std::max(1, (nt + pl.max_splits - 1) / pl.max_splits);
     }
     const long total = (long)pl.units * pl.max_splits;
@@ -964,18 +970,26 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
 }
 
 namespace {
+// The merge instance holds every split slot of a lane in registers: four
+// column parts for up to kNarrowSplits splits, one 16-byte unit per split
+// (HD / 16 parts) beyond.
+template <int HD, int NW, int TK, bool SEQ>
+const void *pick_merge(const AttnPlan &pl) {
+    if (pl.max_splits <= kNarrowSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, 4, kNarrowSplits>;
+    return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kMaxSplits>;
+}
 template <bool KV8, bool SEQ>
-void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge) {
+void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge, int *parts) {
     constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;
     if (d == 128) {
         *tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4, KV8, SEQ>
                            : (const void *)attn_mfma_kernel<128, 8, KV8, SEQ>;
-        *merge = pl.nw == 4 ? (const void *)attn_merge_kernel<128, 4, TK, SEQ>
-                            : (const void *)attn_merge_kernel<128, 8, TK, SEQ>;
+        *merge = pl.nw == 4 ? pick_merge<128, 4, TK, SEQ>(pl) : pick_merge<128, 8, TK, SEQ>(pl);
     } else {
         *tile = (const void *)attn_mfma_kernel<64, 4, KV8, SEQ>;
-        *merge = (const void *)attn_merge_kernel<64, 4, TK, SEQ>;
+        *merge = pick_merge<64, 4, TK, SEQ>(pl);
     }
+    *parts = pl.max_splits <= kNarrowSplits ? 4 : d / 16;
 }
 }  // namespace
 
@@ -1015,16 +1029,17 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.c = a.scale * BD_LOG2E;
     dim3 block(pl.nw * 64);
     const void *tile, *merge;
+    int parts;
     if (pl.seq)
-        pick_kernels<false, true>(pl, a.d, &tile, &merge);
+        pick_kernels<false, true>(pl, a.d, &tile, &merge, &parts);
     else if (pl.fp8)
-        pick_kernels<true, false>(pl, a.d, &tile, &merge);
+        pick_kernels<true, false>(pl, a.d, &tile, &merge, &parts);
     else
-        pick_kernels<false, false>(pl, a.d, &tile, &merge);
+        pick_kernels<false, false>(pl, a.d, &tile, &merge, &parts);
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
     if (e != hipSuccess || pl.max_splits == 1) return e;
-    return hipLaunchKernel(merge, dim3(pl.units * pl.nw * (4 / kMergeWaves)), dim3(kMergeWaves * 64), args, 0, s);
+    return hipLaunchKernel(merge, dim3(pl.units * pl.nw * (parts / kMergeWaves)), dim3(kMergeWaves * 64), args, 0, s);
 }
 
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {

@@ -10,7 +10,8 @@ namespace bd {
 // ---- block attention -------------------------------------------------------
 constexpr int kTileKeys = 32;       // keys per LDS tile (bf16; E4M3 tiles hold twice as many)
 constexpr int kCUs = 256;           // compute units of an MI355X
-constexpr int kMaxSplits = 16;      // split-K pieces per unit (merge registers)
+constexpr int kNarrowSplits = 16;   // split-K pieces per unit in general
+constexpr int kMaxSplits = 32;      // ... and when every workgroup has a CU of its own
 
 struct AttnPlan {
     bool mfma;            // MFMA path: bf16, or bf16 queries with E4M3 K/V (else the fp32 vector path)
