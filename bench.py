@@ -44,8 +44,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 METRIC = "denoise steps/sec + achieved HBM GB/s (%peak), 3B-shape block-16, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_cfg3_traffic.json")
-HEADLINE_KERNELS = ("attn_mfma_kernel<128, 4, false, false>", "attn_merge_kernel<128, 4, 32, false, 4, 16>")
-FP8KV_KERNELS = ("attn_mfma_kernel<128, 4, true, false>", "attn_merge_kernel<128, 4, 64, false, 4, 16>")
+HEADLINE_KERNELS = ("attn_mfma_kernel<128, 4, false, false>", "attn_merge_kernel<128, 4, 32, false, 4, 16, 1>")
+FP8KV_KERNELS = ("attn_mfma_kernel<128, 4, true, false>", "attn_merge_kernel<128, 4, 64, false, 4, 16, 1>")
 ATTN_SOURCES = ["vlm_decoding_amd/csrc/bd_attn.hip", "vlm_decoding_amd/csrc/bd_common.h",
                 "vlm_decoding_amd/csrc/bd_internal.h"]
 

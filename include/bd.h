@@ -88,7 +88,7 @@ enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1, BD_BLOCK_QUAD = 2 };
  * Size limits (BD_E_SHAPE otherwise), with S = block slots per item (D, or
  * B (B + 3) / 2 for BD_BLOCK_QUAD): S * Hq <= 2^20, cap * d <= 2^30, and the
  * launch fits 32-bit grids: n_items * Hkv * ceil(S * (Hq/Hkv) / 128) <
- * 2^31 / 32 and n_items * S * Hq / 4 < 2^31. */
+ * 2^31 / 64 and n_items * S * Hq / 4 < 2^31. */
 typedef struct {
     int32_t n_items, D, Hq, Hkv, d, cap, dtype, mode, max_prefix;
     float scale;
@@ -237,7 +237,7 @@ bd_status bd_lmhead_confidence_commit(const bd_lmhead_desc *desc, const void *hi
  *  max_spans  response spans per sequence (rows of `spans`), 0..256 (0 only if Ln == 0)
  *  scale      softmax scale, finite and > 0
  * Size limits (BD_E_SHAPE otherwise), with L = Lc + Ln: L * Hq <= 2^20,
- * cap * d <= 2^30, n_seq * Hkv * ceil(L * (Hq/Hkv) / 128) < 2^31 / 32 and
+ * cap * d <= 2^30, n_seq * Hkv * ceil(L * (Hq/Hkv) / 128) < 2^31 / 64 and
  * n_seq * L * Hq / 4 < 2^31. */
 typedef struct {
     int32_t n_seq, Lc, Ln, cap, D, Hq, Hkv, d, max_spans;

@@ -52,7 +52,7 @@ BAD_ATTN = [
     (dict(max_prefix=5000), "BD_E_SHAPE"), (dict(max_prefix=-1), "BD_E_SHAPE"), (dict(n_items=0), "BD_E_SHAPE"),
     (dict(dtype=7), "BD_E_DTYPE"), (dict(mode=3), "BD_E_PARAM"), (dict(scale=float("nan")), "BD_E_PARAM"),
     (dict(scale=0.0), "BD_E_PARAM"), (dict(scale=float("inf")), "BD_E_PARAM"),
-    # launches past 32-bit grids: 2^27 items x 2 KV heads x 32 splits; 2^29 items x 64 slots x 128 heads
+    # launches past 32-bit grids: 2^27 items x 2 KV heads x 64 splits; 2^29 items x 64 slots x 128 heads
     (dict(n_items=1 << 27), "BD_E_SHAPE"), (dict(n_items=(1 << 29) - 1, D=64, Hq=128, Hkv=128, max_prefix=0), "BD_E_SHAPE"),
 ]
 

@@ -160,7 +160,7 @@ __device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_spli
     const int w = (work + u.nsplit - 1) / u.nsplit;                    // target work per split
     const int tail_bulk = nbs == 0 ? nbulk : max(0, nbulk - nbs * w);  // bulk tiles of the tail split
     const int shared = nbulk - tail_bulk;                              // >= nbs: every bulk split gets one
-    // 32-bit arithmetic is enough: split < kMaxSplits = 32 and shared <= cap / TK < 2^19.
+    // 32-bit arithmetic is enough: split < kMaxSplits = 64 and shared <= cap / TK < 2^19.
     if (split < nbs) {
         u.t0 = (int)((unsigned)(split * shared) / (unsigned)nbs);
         u.nb = (int)((unsigned)((split + 1) * shared) / (unsigned)nbs) - u.t0;
@@ -716,16 +716,20 @@ static_assert((4 * (4 / kMergeWaves)) % 8 == 0, "merge grid must be a multiple o
 // summed in split order.  The merged rows are staged in LDS and written out
 // as row segments of WPB * HD / NP contiguous elements.  Every split slot of a
 // lane is loaded at once, QPT * MAXS 16-byte units: NP = 4 with up to 16
-// splits, or one unit per split (NP = HD / 16) with up to 32.
-template <int HD, int NW, int TK, bool SEQ, int NP, int MAXS>
-__global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams p) {
+// splits, or one unit per split (NP = HD / 16) with up to 32.  With SW = 2
+// split waves a block holds up to 64 splits: wave w takes splits 32 w ..
+// 32 w + 31, both use the max over all splits, and wave 0 adds wave 1's sums
+// to its own (the sum over the first 32 splits, then the rest).
+template <int HD, int NW, int TK, bool SEQ, int NP, int MAXS, int SW>
+__global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaParams p) {
     constexpr int WPB = kMergeWaves;    // waves per block
     constexpr int NT_TILE = NW * 64;    // threads of the tile kernel's block
     constexpr int MB = HD / 32;
     constexpr int QQ = MB * 2;          // 16-byte partial units per lane
     constexpr int QPT = QQ / NP;        // units per thread here
     constexpr int DQ = HD / NP;         // output columns of one part (QPT units)
-    static_assert(QPT >= 1 && QQ % NP == 0 && MAXS <= kMaxSplits, "merge shape");
+    static_assert(QPT >= 1 && QQ % NP == 0 && MAXS * SW <= kMaxSplits, "merge shape");
+    static_assert(SW == 1 || WPB == 1, "split waves take one column part per block");
     constexpr int RS = DQ * WPB + 8;    // LDS row stride (elements), staggers banks
     __shared__ __attribute__((aligned(16))) uint16_t rows_lds[32 * RS];
     // Block = (unit, wave wv of the tile kernel's block, WPB of its NP column parts).
@@ -745,10 +749,12 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams
     const int row0 = rb * (NW * 32) + wv * 32;
     if (row0 >= p.R) return;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, jl = tid >> 6, half = lane >> 5, col = lane & 31;
+    const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+    const int jl = SW > 1 ? 0 : tid >> 6;   // column part within the block
+    const int sw = SW > 1 ? tid >> 6 : 0;   // split wave: splits MAXS sw ..
     const int jq = qb * WPB + jl;           // column part of this thread
     const int src_t = wv * 64 + lane;      // thread of the tile kernel's block
-    const size_t base = (size_t)unit * p.max_splits;
+    const size_t base = (size_t)unit * p.max_splits + (size_t)sw * MAXS;
     const uint4 *wo = reinterpret_cast<const uint4 *>(p.ws_o);
     // Every workspace slot of the unit is requested before the prefix length
     // (which decides how many of them hold this call's partials) arrives;
@@ -757,7 +763,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams
     uint4 v[QPT][MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
-        if (s < p.max_splits) {
+        if (sw * MAXS + s < p.max_splits) {
             ml[s] = p.ws_ml[(base + s) * NT_TILE + src_t];
 #pragma unroll
             for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t];
@@ -770,15 +776,23 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams
         nsplit = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
     }
     if (nsplit == 1) return;  // single split: written by the tile kernel
+    const int ns = nsplit - sw * MAXS;  // splits of this wave (may be <= 0)
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
-        if (s < nsplit) M = fmaxf(M, ml[s].x);
+        if (s < ns) M = fmaxf(M, ml[s].x);
+    if constexpr (SW > 1) {
+        __shared__ float m_x[SW][64];
+        m_x[sw][lane] = M;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < SW; ++w) M = fmaxf(M, m_x[w][lane]);
+    }
     float L = 0.f;
     float acc[QPT][8] = {};
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
-        if (s < nsplit) {
+        if (s < ns) {
             const float c = (ml[s].x == -INFINITY) ? 0.f : bd_exp2(ml[s].x - M) * ml[s].y;
             L += c;
 #pragma unroll
@@ -789,11 +803,32 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams
                     acc[j][e] += c * bd_bf16_to_f32((uint16_t)(w4[e >> 1] >> (16 * (e & 1))));
             }
         }
+    if constexpr (SW > 1) {
+        __shared__ float sum_x[SW][QPT * 8 + 1][64];
+        sum_x[sw][0][lane] = L;
+#pragma unroll
+        for (int j = 0; j < QPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sum_x[sw][1 + j * 8 + e][lane] = acc[j][e];
+        __syncthreads();
+        if (sw == 0) {
+#pragma unroll
+            for (int w = 1; w < SW; ++w) {
+                L += sum_x[w][0][lane];
+#pragma unroll
+                for (int j = 0; j < QPT; ++j)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[j][e] += sum_x[w][1 + j * 8 + e][lane];
+            }
+        }
+    }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     // Unit qq holds d = mb*32 + 16*(qq%2) + 4*half + {0..3} and the same + 8;
-    // in this block's LDS rows, column d - qb * WPB * DQ.
+    // in this block's LDS rows, column d - qb * WPB * DQ.  With split waves,
+    // wave 0 alone holds the sums and writes the rows.
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
+        if (sw != 0) continue;
         const int qq = jq * QPT + j;
         const int d0 = (qq >> 1) * 32 + 16 * (qq & 1) + 4 * half - qb * WPB * DQ;
 #pragma unroll
@@ -805,6 +840,7 @@ __global__ __launch_bounds__(kMergeWaves * 64) void attn_merge_kernel(MfmaParams
         }
     }
     __syncthreads();
+    if (sw != 0) return;
     // The block's columns of each row out: TPR threads per row, 16 bytes each.
     constexpr int TPR = WPB * DQ / 8;
     constexpr int RPP = WPB * 64 / TPR;  // rows per pass
@@ -932,10 +968,14 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     const int want = std::max(1, slots / pl.units);
     // Splits per unit (the device side derives each unit's count from its own
     // prefix): sized so that a unit at max_prefix gets about `want` splits, at
-    // most kNarrowSplits; up to kMaxSplits while each workgroup still has a CU
-    // of its own (few units, where a lone wave per SIMD makes the tile loop
-    // latency-bound and shorter splits pay).
-    const int cap = (long)pl.units * kMaxSplits <= kCUs ? kMaxSplits : kNarrowSplits;
+    // most kNarrowSplits; up to kWideSplits or kMaxSplits while each workgroup
+    // still has a CU of its own (few units, where a lone wave per SIMD makes
+    // the tile loop latency-bound and shorter splits pay).
+    // kMaxSplits only where each split keeps two bulk tiles or more: with one
+    // the tail split and the larger merge cost more than the shorter splits save.
+    const int cap = (long)pl.units * kMaxSplits <= kCUs && ntiles_max >= 2 * kMaxSplits ? kMaxSplits
+                    : (long)pl.units * kWideSplits <= kCUs                               ? kWideSplits
+                                                                                          : kNarrowSplits;
     pl.max_splits = ntiles_max == 0 ? 1 : std::max(2, std::min(std::min(want, ntiles_max + 1), cap));
     // Work of a unit at max_prefix in bulk-tile units: its bulk tiles plus
     // kTailCost per tail tile (up to tk - 1 cache positions and the D slots).
@@ -972,14 +1012,16 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
 namespace {
 // The merge instance holds every split slot of a lane in registers: four
 // column parts for up to kNarrowSplits splits, one 16-byte unit per split
-// (HD / 16 parts) beyond.
+// (HD / 16 parts) up to kWideSplits, and two such split waves per block
+// beyond.
 template <int HD, int NW, int TK, bool SEQ>
 const void *pick_merge(const AttnPlan &pl) {
-    if (pl.max_splits <= kNarrowSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, 4, kNarrowSplits>;
-    return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kMaxSplits>;
+    if (pl.max_splits <= kNarrowSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, 4, kNarrowSplits, 1>;
+    if (pl.max_splits <= kWideSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kWideSplits, 1>;
+    return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kWideSplits, kMaxSplits / kWideSplits>;
 }
 template <bool KV8, bool SEQ>
-void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge, int *parts) {
+void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge, int *parts, int *waves) {
     constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;
     if (d == 128) {
         *tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4, KV8, SEQ>
@@ -990,6 +1032,7 @@ void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **mer
         *merge = pick_merge<64, 4, TK, SEQ>(pl);
     }
     *parts = pl.max_splits <= kNarrowSplits ? 4 : d / 16;
+    *waves = pl.max_splits <= kWideSplits ? 1 : kMaxSplits / kWideSplits;
 }
 }  // namespace
 
@@ -1029,17 +1072,18 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.c = a.scale * BD_LOG2E;
     dim3 block(pl.nw * 64);
     const void *tile, *merge;
-    int parts;
+    int parts, waves;
     if (pl.seq)
-        pick_kernels<false, true>(pl, a.d, &tile, &merge, &parts);
+        pick_kernels<false, true>(pl, a.d, &tile, &merge, &parts, &waves);
     else if (pl.fp8)
-        pick_kernels<true, false>(pl, a.d, &tile, &merge, &parts);
+        pick_kernels<true, false>(pl, a.d, &tile, &merge, &parts, &waves);
     else
-        pick_kernels<false, false>(pl, a.d, &tile, &merge, &parts);
+        pick_kernels<false, false>(pl, a.d, &tile, &merge, &parts, &waves);
     void *args[] = {&p};
     hipError_t e = hipLaunchKernel(tile, dim3(pl.grid), block, args, 0, s);
     if (e != hipSuccess || pl.max_splits == 1) return e;
-    return hipLaunchKernel(merge, dim3(pl.units * pl.nw * (parts / kMergeWaves)), dim3(kMergeWaves * 64), args, 0, s);
+    return hipLaunchKernel(merge, dim3(pl.units * pl.nw * (parts / kMergeWaves)), dim3(kMergeWaves * waves * 64), args, 0,
+                           s);
 }
 
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s) {

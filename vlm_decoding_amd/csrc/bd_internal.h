@@ -11,7 +11,8 @@ namespace bd {
 constexpr int kTileKeys = 32;       // keys per LDS tile (bf16; E4M3 tiles hold twice as many)
 constexpr int kCUs = 256;           // compute units of an MI355X
 constexpr int kNarrowSplits = 16;   // split-K pieces per unit in general
-constexpr int kMaxSplits = 32;      // ... and when every workgroup has a CU of its own
+constexpr int kWideSplits = 32;     // ... and when every workgroup has a CU of its own
+constexpr int kMaxSplits = 64;      // ... and when even 64 per unit leave that so
 
 struct AttnPlan {
     bool mfma;            // MFMA path: bf16, or bf16 queries with E4M3 K/V (else the fp32 vector path)
