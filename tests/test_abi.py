@@ -278,3 +278,19 @@ def test_status_strings(bd):
         assert bd.lib.bd_status_string(code)
     assert bd.lib.bd_status_string(99) == b"unknown status"
     assert bd.lib.bd_last_hip_error() == 0
+
+
+def test_binding_refuses_to_run_without_the_library(tmp_path):
+    """No fallback: the package copied without libbd.so raises on import, for the
+    binding and for the step helper built on it."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "vlm_decoding_amd"
+    pkg.mkdir()
+    for f in ("__init__.py", "bd.py", "step.py"):
+        shutil.copy(os.path.join(ROOT, "vlm_decoding_amd", f), str(pkg / f))
+    for mod in ("vlm_decoding_amd.bd", "vlm_decoding_amd.step"):
+        r = subprocess.run([sys.executable, "-c", "import " + mod], cwd=str(tmp_path), capture_output=True, text=True,
+                           env=dict(os.environ, PYTHONPATH=str(tmp_path)), timeout=300)
+        assert r.returncode != 0 and "libbd.so is not built" in r.stderr, (mod, r.stderr[-500:])
