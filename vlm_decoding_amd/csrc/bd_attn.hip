@@ -622,10 +622,11 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         bd_barrier_lds();
         if (wave_active) compute(0, tt, -1);
     }
-    // Bulk tiles through NS stages, all NS filled up front: tiles tl+1 ..
+    // Bulk tiles through NS stages, NS-1 filled up front: tiles tl+1 ..
     // tl+NS-1 are in flight while tile tl is computed.  Every step has the same
-    // shape - wait for all but the last NS-1 copy groups, compute, refill the
-    // stage just freed with tile tl+NS - and the
+    // shape - wait for all but the last NS-2 copy groups, one barrier (after
+    // which no wave still reads tile tl-1's stage), refill that stage with tile
+    // tl+NS-1, compute tile tl - and the
     // step count is rounded up to a multiple of NS, with dummy copy groups
     // (each lane reading one fixed, cached 16-byte unit into a stage nobody
     // reads) past the split's last tile.  The compiler can then prove that a
@@ -637,15 +638,14 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     if (nb_split > 0) {
         if (ntail > 0) bd_barrier_lds();  // every wave is done with the tail tile in stage 0
 #pragma unroll
-        for (int i = 0; i < NS; ++i) issue_bulk(t0 + i, i, i < nb_split);
+        for (int i = 0; i < NS - 1; ++i) issue_bulk(t0 + i, i, i < nb_split);
     }
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
-        bd_wait_vmcnt<(NS - 1) * (LK + LV)>();  // tile tl's copies have landed
-        bd_barrier_lds();                        // ... and are visible to every wave
+        bd_wait_vmcnt<(NS - 2) * (LK + LV)>();  // tile tl's copies have landed
+        bd_barrier_lds();  // ... and are visible to every wave, which is done with tile tl - 1
+        issue_bulk(t0 + tl + NS - 1, (ST + NS - 1) % NS, tl + NS - 1 < nb_split);  // into tile tl - 1's stage
         if (wave_active && tl < nb_split) compute(ST, -1, SEQ && t0 + tl >= nU ? tile_of(t0 + tl) * TK : -1);
-        bd_barrier_lds();  // every wave is done with stage ST, which is refilled now
-        issue_bulk(t0 + tl + NS, ST, tl + NS < nb_split);
     };
     for (int tl = 0; tl < nb_round; tl += NS) {
         step(std::integral_constant<int, 0>{}, tl);
