@@ -405,12 +405,22 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         }
     };
     // Tail tiles: the last P % TK cache positions followed by the D block slots,
-    // zero past the end (at most three tiles, in the unit's last split).  K rows
-    // and cache V^T rows are gathered as 16-byte units.  Block V rows arrive
-    // d-contiguous ([slot][Hkv][d]); they are loaded as 16-byte units and
-    // scattered transposed into the V^T tile after the other units are written.
+    // zero past the end (in the unit's last split).  K rows and cache V^T rows
+    // are gathered as 16-byte units.  Block V rows arrive d-contiguous
+    // ([slot][Hkv][d]); they are loaded as 16-byte units and scattered
+    // transposed into the V^T tile after the other units are written.  All of
+    // a tail tile's loads are issued first; for the first tail tile the first
+    // bulk copies follow them, so those are in flight while the tail is stored
+    // and computed.
     constexpr int BU = HD * EB / 16;  // 16-byte units per block V row
-    auto load_tail = [&](int st, int tt) __attribute__((always_inline)) {
+    // The first NS-1 bulk tiles into stages 0 .. NS-2 (the tail uses stage NS-1).
+    auto first_fill = [&]() __attribute__((always_inline)) {
+        if (nb_split > 0) {
+#pragma unroll
+            for (int i = 0; i < NS - 1; ++i) issue_bulk(t0 + i, i, i < nb_split);
+        }
+    };
+    auto load_tail = [&](int st, int tt, bool fill) __attribute__((always_inline)) {
         const int pc = P - Pb;  // cache positions in the tail
         u32x4 kr[LK], vr[LV];
 #pragma unroll
@@ -456,19 +466,6 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             }
             vr[i] = v;
         }
-#pragma unroll
-        for (int i = 0; i < LK; ++i) {
-            const int u = tid + i * NT;
-            const int key = u / KU, lu = u % KU;
-            *reinterpret_cast<u32x4 *>(kbuf(st) + k_at(key, lu)) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < LV; ++i) {
-            const int u = tid + i * NT;
-            const int dd = u / VU, lu = u % VU;
-            *reinterpret_cast<u32x4 *>(vbuf(st) + v_at(dd, lu)) = vr[i];
-        }
-        bd_barrier_lds();  // the scatter below overwrites zeros written above
         // Block V units that land in this tile: slot b covers tail position pc + b,
         // so this tile holds slots b0 .. b0 + TK - 1 (those in 0..D-1).
         constexpr int VB_N = (TK * BU + NT - 1) / NT;
@@ -484,6 +481,20 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             if (bkey[i] >= 0)
                 br[i] = *reinterpret_cast<const u32x4 *>(p.vb + (((size_t)it * p.D + b) * p.Hkv + g) * HD * EB + du * 16);
         }
+        if (fill) first_fill();  // in flight while the tail is stored and computed
+#pragma unroll
+        for (int i = 0; i < LK; ++i) {
+            const int u = tid + i * NT;
+            const int key = u / KU, lu = u % KU;
+            *reinterpret_cast<u32x4 *>(kbuf(st) + k_at(key, lu)) = kr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < LV; ++i) {
+            const int u = tid + i * NT;
+            const int dd = u / VU, lu = u % VU;
+            *reinterpret_cast<u32x4 *>(vbuf(st) + v_at(dd, lu)) = vr[i];
+        }
+        bd_barrier_lds();  // the scatter below overwrites zeros written above
 #pragma unroll
         for (int i = 0; i < VB_N; ++i) {
             if (bkey[i] < 0) continue;
@@ -615,13 +626,14 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         softmax_pv(st, s);
     };
 
-    // Tail split: gather and compute its (one to three) tiles.
+    // Tail split: gather and compute its (one to three) tiles in stage NS-1.
     for (int tt = 0; tt < ntail; ++tt) {
         if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
-        load_tail(0, tt);
+        load_tail(NS - 1, tt, tt == 0);
         bd_barrier_lds();
-        if (wave_active) compute(0, tt, -1);
+        if (wave_active) compute(NS - 1, tt, -1);
     }
+    if (ntail == 0) first_fill();
     // Bulk tiles through NS stages, NS-1 filled up front: tiles tl+1 ..
     // tl+NS-1 are in flight while tile tl is computed.  Every step has the same
     // shape - wait for all but the last NS-2 copy groups, one barrier (after
@@ -635,11 +647,6 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // The Q loads, issued before the first copies, are retired by the first
     // fixed-count wait.
     const int nb_round = (nb_split + NS - 1) / NS * NS;
-    if (nb_split > 0) {
-        if (ntail > 0) bd_barrier_lds();  // every wave is done with the tail tile in stage 0
-#pragma unroll
-        for (int i = 0; i < NS - 1; ++i) issue_bulk(t0 + i, i, i < nb_split);
-    }
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
         bd_wait_vmcnt<(NS - 2) * (LK + LV)>();  // tile tl's copies have landed
