@@ -120,6 +120,28 @@ def test_attention_edge_cases(dev, label, ov, mode):
     _run_attention(dev, synth.make_step(p, seed=zlib.crc32(label.encode()) % 10000), mode=mode, label=label)
 
 
+# Few items with long prefixes: the plan gives such calls 32 or 64 splits per
+# unit (every workgroup on a CU of its own) and merges them with the 32-slot
+# merge instance or its two-split-wave form.  Ragged prefixes give units with
+# fewer splits than the plan's maximum.
+FEW_ITEM_CASES = [
+    ("one_item_4096_64_splits", dict(n_items=1, prefix=("fixed", 4096))),
+    ("two_items_ragged_64_splits", dict(n_items=2, prefix=("list", [4096, 2050]))),
+    ("two_items_4133_tail", dict(n_items=2, prefix=("list", [4133, 4127]))),
+    ("four_items_32_splits", dict(n_items=4, prefix=("list", [2048, 1100, 31, 2047]))),
+    ("one_item_fp8_32_splits", dict(n_items=1, prefix=("fixed", 4096), dtype=FP8KV)),
+]
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("label,ov", FEW_ITEM_CASES, ids=[c[0] for c in FEW_ITEM_CASES])
+def test_attention_few_items_many_splits(dev, label, ov, mode):
+    base = dict(Hq=16, Hkv=2, d=128, dtype=BF16, D=16, n_masked=8, V=1000, plant=None)
+    base.update(ov)
+    p = synth.params_for(3, **base)
+    _run_attention(dev, synth.make_step(p, seed=zlib.crc32(label.encode()) % 10000), mode=mode, label=label)
+
+
 # Seeded random sweep over small shapes: dtype (bf16, E4M3 cache, fp32), mask
 # mode (bidirectional, causal, quadratic), head layout, d, block length and
 # ragged prefixes drawn together, and for about half the cases a plan sized
