@@ -449,6 +449,8 @@ TWO_STREAM_CASES = [
     ("G7_rows", dict(Hq=14, Hkv=2, d=128, turns=[(20, 70), (8, 41)])),
     ("d128_long", dict(d=128, vision=300, turns=[(33, 250), (12, 77)], D=32)),
     ("empty_span_and_padding", dict(turns=[[(5, 0), (6, 23)], [(2, 40)]], D=16)),
+    # 6 units (one sequence, one KV head, 1420 positions): 32 splits, the 32-slot merge
+    ("few_units_32_splits", dict(n_seq=1, Hq=1, Hkv=1, d=128, vision=600, turns=[(20, 400)], D=16)),
 ]
 
 
