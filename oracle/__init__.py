@@ -49,7 +49,7 @@ def _load():
         lib.bdo_confidence_row.argtypes = [i32, P, P, P, P, P]
         lib.bdo_commit_k.argtypes = [i32, i32, i32]
         lib.bdo_commit_k.restype = i32
-        lib.bdo_confidence_commit.argtypes = [i32, i32, i32, i32, ctypes.c_float] + [P] * 7
+        lib.bdo_confidence_commit.argtypes = [i32, i32, i32, i32, ctypes.c_double] + [P] * 7
         lib.bdo_spec_verify.argtypes = [i32, i32, i32, P, P, P, P]
         lib.bdo_kv_append.argtypes = [i32] * 6 + [P] * 7
         lib.bdo_num_threads.restype = i32
@@ -132,7 +132,7 @@ def confidence_commit(logits, masked, tokens, S, tau):
     amax = np.zeros((n_req, D), np.int32)
     committed = np.zeros((n_req, D), np.uint8)
     ncom = np.zeros(n_req, np.int32)
-    lib.bdo_confidence_commit(n_req, D, V, int(S), ctypes.c_float(tau), _ptr(logits), _ptr(masked),
+    lib.bdo_confidence_commit(n_req, D, V, int(S), float(tau), _ptr(logits), _ptr(masked),
                               _ptr(tokens), _ptr(conf), _ptr(amax), _ptr(committed), _ptr(ncom))
     return dict(conf=conf, argmax=amax, committed=committed, n_committed=ncom,
                 masked=masked, tokens=tokens)

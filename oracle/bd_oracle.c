@@ -33,8 +33,9 @@
  * notes): scale 1/sqrt(d) is passed in; GQA head h uses KV head
  * h / (Hq/Hkv); Q and K are already position-encoded; the greedy token is
  * the argmax with the lowest index on ties; "greater than tau" is strict;
- * positions are ranked by (confidence desc, index asc); the commit decision
- * is taken on confidences rounded to fp32, the precision the GPU decides in.
+ * positions are ranked by (confidence desc, index asc).  The commit decision
+ * is taken on the fp64 confidences themselves (the rule is stated on the
+ * model's probabilities); tau is compared as given, in double precision.
  */
 #include <math.h>
 #include <stdint.h>
@@ -271,8 +272,8 @@ int bdo_commit_k(int D, int S, int n_masked) {
     return k < n_masked ? k : n_masked;
 }
 
-/* a ranks before b: higher fp32 confidence first, lower index on equal confidence. */
-static int ranks_before(float ca, int ia, float cb, int ib) {
+/* a ranks before b: higher confidence first, lower index on equal confidence. */
+static int ranks_before(double ca, int ia, double cb, int ib) {
     return (ca > cb) || (ca == cb && ia < ib);
 }
 
@@ -284,15 +285,14 @@ static int ranks_before(float ca, int ia, float cb, int ib) {
  *   H = { i in M : conf_i > tau };  commit C = T u H:
  *   tokens[i] = a_i, masked[i] = 0, committed[i] = 1.
  * Positions outside M are not read and never change.
- * conf_out (double, NaN outside M) and argmax_out (-1 outside M) report
- * the fp64 values; the ranking and threshold use them rounded to fp32.
+ * conf_out (NaN outside M) and argmax_out (-1 outside M) report the values
+ * the ranking and the threshold were decided on.
  */
-void bdo_confidence_commit(int n_req, int D, int V, int S, float tau, const float *logits,
+void bdo_confidence_commit(int n_req, int D, int V, int S, double tau, const float *logits,
                            uint8_t *masked, int32_t *tokens, double *conf_out,
                            int32_t *argmax_out, uint8_t *committed_out,
                            int32_t *n_committed_out) {
     double *conf = (double *)malloc(sizeof(double) * (size_t)D);
-    float *c32 = (float *)malloc(sizeof(float) * (size_t)D);
     int32_t *amax = (int32_t *)malloc(sizeof(int32_t) * (size_t)D);
     uint8_t *take = (uint8_t *)malloc((size_t)D);
     for (int r = 0; r < n_req; ++r) {
@@ -306,15 +306,14 @@ void bdo_confidence_commit(int n_req, int D, int V, int S, float tau, const floa
                 bdo_confidence_row(V, logits + ((size_t)r * D + i) * (size_t)V, &conf[i], &amax[i],
                                    NULL, NULL);
             }
-            c32[i] = (float)conf[i];
         }
         int k = bdo_commit_k(D, S, n_m);
         for (int i = 0; i < D; ++i) {
             if (!masked[(size_t)r * D + i]) continue;
             int rank = 0;
             for (int j = 0; j < D; ++j)
-                if (j != i && masked[(size_t)r * D + j] && ranks_before(c32[j], j, c32[i], i)) ++rank;
-            if (rank < k || c32[i] > tau) take[i] = 1;
+                if (j != i && masked[(size_t)r * D + j] && ranks_before(conf[j], j, conf[i], i)) ++rank;
+            if (rank < k || conf[i] > tau) take[i] = 1;
         }
         int cnt = 0;
         for (int i = 0; i < D; ++i) {
@@ -331,7 +330,6 @@ void bdo_confidence_commit(int n_req, int D, int V, int S, float tau, const floa
         if (n_committed_out) n_committed_out[r] = cnt;
     }
     free(conf);
-    free(c32);
     free(amax);
     free(take);
 }
