@@ -194,6 +194,8 @@ bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logit
  *    that mode) and L <= B accepted drafts, slots 0..L-1, are appended.
  * If L is outside 0..D or P + L > cap, item i is left untouched and *dev_err
  * (optional device int32) is set to 1.
+ * Size limits (BD_E_SHAPE otherwise): cap * d <= 2^30 and, with S block slots
+ * per item, S * Hkv * d <= 2^30.
  * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_LAUNCH. */
 bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache,
                        int32_t *prefix_len, const void *k_blk, const void *v_blk,

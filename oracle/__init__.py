@@ -53,6 +53,7 @@ def _load():
         lib.bdo_spec_verify.argtypes = [i32, i32, i32, P, P, P, P]
         lib.bdo_kv_append.argtypes = [i32] * 6 + [P] * 7
         lib.bdo_num_threads.restype = i32
+        lib.bdo_set_num_threads.argtypes = [i32]
         lib.bdo_softmax_partial.argtypes = [i32, i32, P, P, P, P, P]
         lib.bdo_merge_partials.argtypes = [i32, i32, P, P, P, P]
         lib.bdo_lm_head_logits.argtypes = [i32, i32, i32, P, P, P]
@@ -77,6 +78,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(_load().bdo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops (independent query rows) use from now on."""
+    _load().bdo_set_num_threads(int(n))
 
 
 def attention(q, k_blk, v_blk, k_cache, v_cache, prefix, mode, scale=None):

@@ -80,6 +80,15 @@ int bdo_num_threads(void) {
 #endif
 }
 
+/* Threads the parallel loops use from now on (>= 1). */
+void bdo_set_num_threads(int n) {
+#ifdef _OPENMP
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Block attention ([FD] 4.1, 5.3; [FD2] Fig. 3).
  *

@@ -234,6 +234,14 @@ def test_verify_and_append_validation(bd):
     assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_SHAPE
     desc = _attn(bd)
     assert bd.lib.bd_kv_append(ctypes.byref(desc), None, fake, fake, fake, fake, None, None, None) == bd.BD_E_NULL
+    # A block of 64 slots x 2^19 KV heads x d 128 (2^32 elements per item) would
+    # overflow 32-bit index arithmetic: refused before any launch.
+    desc = _attn(bd, D=64, Hq=1 << 19, Hkv=1 << 19)
+    assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_SHAPE
+    desc = _attn(bd, D=64, Hq=1 << 16, Hkv=1 << 16)   # 2^29 elements: within the limit
+    assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, None, fake, fake, None, None, None) == bd.BD_E_NULL
+    desc = _attn(bd, cap=(1 << 23) + 8)               # cap * d > 2^30
+    assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_SHAPE
 
 
 BAD_LMHEAD = [

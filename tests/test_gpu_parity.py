@@ -7,16 +7,23 @@ Bars:
   * greedy tokens, committed sets, accepted lengths, appended bytes: exact.
     A commit decision is excluded (and counted) only where the oracle's own
     fp64 values put it within 1e-4 of a tie: the k-th / (k+1)-th confidence
-    boundary, or the threshold tau.  The GPU's committed set must in addition
-    equal the rule applied exactly to the GPU's own confidences.
+    boundary, or the threshold tau (tests/acceptance.py; the counts per
+    config are in tests/golden/fragile_counts.json).  The GPU's committed set
+    must in addition equal the rule applied exactly to the GPU's own
+    confidences.
+  * every buffer the library writes sits between canary bands that must be
+    intact after the test, and outputs start poisoned.
 """
 
+import json
+import os
 import sys
 import zlib
 
 import numpy as np
 import pytest
 
+import acceptance
 import oracle
 import synth
 from synth import BF16, BIDIR, CAUSAL, F32, FP8KV, QUAD
@@ -26,7 +33,12 @@ pytestmark = pytest.mark.gpu
 ATTN_MAX_ABS = 2e-2
 ATTN_REL = 1e-2
 CONF_ABS = 1e-5
-FRAGILE = 1e-4
+GUARD = 4096  # canary bytes on each side of every buffer the library writes
+
+with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fragile_counts.json")) as _f:
+    FRAGILE_COUNTS = json.load(_f)["configs"]
+
+_LIVE = []  # guarded buffer sets created by the running test
 
 
 @pytest.fixture(scope="module")
@@ -35,6 +47,31 @@ def dev():
     assert torch.cuda.is_available(), "GPU tests need a visible GPU"
     from vlm_decoding_amd import bd, step  # raises if libbd.so is missing
     return dict(torch=torch, bd=bd, step=step)
+
+
+@pytest.fixture(autouse=True)
+def _guards_intact():
+    """After every test: no buffer the library wrote may have been written past its ends."""
+    _LIVE.clear()
+    yield
+    damaged = []
+    for g in _LIVE:
+        damaged += g.damaged()
+    _LIVE.clear()
+    assert not damaged, "guard bands overwritten: %s" % damaged
+
+
+def _ds(dev, st, **kw):
+    """DeviceStep with canary bands around every buffer the library writes."""
+    ds = dev["step"].DeviceStep(st, guard_bytes=GUARD, **kw)
+    _LIVE.append(ds.gb)
+    return ds
+
+
+def _guarded(dev):
+    g = dev["step"].GuardedBuffers("cuda", GUARD)
+    _LIVE.append(g)
+    return g
 
 
 def _say(msg):
@@ -62,7 +99,7 @@ def _check_attention(got, ref, label):
 
 
 def _run_attention(dev, step_np, mode=None, label=""):
-    ds = dev["step"].DeviceStep(step_np)
+    ds = _ds(dev, step_np)
     p = step_np["params"]
     mode = p["mode"] if mode is None else mode
     _say("attention %s n=%d D=%d Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s" % (
@@ -108,6 +145,11 @@ ATTN_CASES = [
     ("G7_rows224", dict(Hq=28, Hkv=4, D=32, prefix=("list", [70, 500]), n_items=2)),
     ("d64_bf16", dict(d=64, prefix=("fixed", 333))),
     ("many_items", dict(n_items=40, prefix=("fixed", 150))),
+    # capacities that are multiples of 8 but not of 64: d-major value rows start
+    # on 16-byte (not 128-byte) boundaries
+    ("cap1016", dict(prefix=("fixed", 1000), cap=1016)),
+    ("cap1016_ragged", dict(prefix=("list", [1, 63, 517, 1000]), n_items=4, cap=1016)),
+    ("cap40_short", dict(prefix=("list", [0, 7, 24]), n_items=3, cap=40)),
 ]
 
 
@@ -174,8 +216,10 @@ def _sweep_case(i):
         host_max = max(prefix) + (int(rng.integers(1, 700)) if rng.random() < 0.5 else 0)
         if n * Hq * D * (max(prefix) + D) * d <= 1.5e8:  # keeps the fp64 oracle within seconds
             break
+    # the smallest capacity the ABI accepts: a multiple of 8 (16 for E4M3)
+    al = 16 if dtype == FP8KV else 8
     p = dict(n_items=n, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, prefix=("list", prefix),
-             cap=synth.cache_capacity(host_max, D))
+             cap=(host_max + D + al - 1) // al * al)
     if mode == QUAD:
         st = synth.make_quad_step(dict(synth.QUAD_CONFIGS[2], B=B, **p), 5000 + i)
     else:
@@ -192,7 +236,7 @@ def test_attention_random_sweep(dev, i):
     _say("attention %s n=%d D=%d B=%s Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s max_prefix=%d cap=%d" % (
         label, p["n_items"], p["D"], p.get("B"), p["Hq"], p["Hkv"], p["d"], p["dtype"], p["mode"],
         st["prefix"].tolist(), host_max, st["cap"]))
-    ds = dev["step"].DeviceStep(st, max_prefix=host_max)
+    ds = _ds(dev, st, max_prefix=host_max)
     ds.attn()
     _check_attention(_out_host(dev, ds), _reference(st, p["mode"]), label)
 
@@ -209,7 +253,7 @@ def test_attention_deterministic_and_workspace_reuse(dev):
     merge runs in a fixed order and the ticket counters reset themselves)."""
     torch = dev["torch"]
     s = synth.config_step(3)
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     ds.attn()
     torch.cuda.synchronize()
     first = ds.out.clone()
@@ -227,7 +271,7 @@ def test_layer_serial_graph_replays_match_eager(dev):
     torch = dev["torch"]
     p = synth.params_for(3, n_items=4, prefix=("list", [0, 100, 700, 2000]), V=3001, n_masked=8, plant=None)
     st = synth.make_step(p, 321)
-    ds = dev["step"].DeviceStep(st)
+    ds = _ds(dev, st)
     ds.reset_block_state()
     ds.layer_serial_step()
     torch.cuda.synchronize()
@@ -251,7 +295,7 @@ def test_layer_serial_graph_replays_match_eager(dev):
 
 def test_attention_rejects_bad_arguments_before_launch(dev):
     bd = dev["bd"]
-    ds = dev["step"].DeviceStep(synth.config_step(2))
+    ds = _ds(dev, synth.config_step(2))
     bad = bd.attn_desc(1, 8, 16, 2, 96, ds.cap, BF16, BIDIR, 1024)
     with pytest.raises(bd.BdError) as e:
         bd.bd_attn_step(bad, ds.q, ds.k_blk, ds.v_blk, ds.k_cache, ds.v_cache, ds.prefix, ds.out, ds.attn_ws)
@@ -286,6 +330,9 @@ FP8_CASES = [
     ("d64", dict(d=64, prefix=("fixed", 333))),
     ("d64_ragged", dict(d=64, D=32, prefix=("list", [0, 64, 65, 700]), n_items=4)),
     ("many_items", dict(n_items=40, prefix=("fixed", 150))),
+    # capacities that are multiples of 16 but not of 64
+    ("cap1008", dict(prefix=("fixed", 990), cap=1008)),
+    ("cap1008_ragged", dict(prefix=("list", [0, 65, 500, 990]), n_items=4, cap=1008)),
 ]
 
 
@@ -306,7 +353,7 @@ def test_fp8kv_deterministic_append_and_reattend(dev):
     p = synth.params_for(3, n_items=3, dtype=FP8KV, D=16, prefix=("list", [100, 64, 1500]), V=1000,
                          n_masked=8, plant=None)
     s = synth.make_step(p, seed=4242)
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     ds.attn()
     torch.cuda.synchronize()
     first = ds.out.clone()
@@ -332,6 +379,31 @@ def test_fp8kv_deterministic_append_and_reattend(dev):
     _check_attention(got, ref, "fp8kv_after_append")
 
 
+@pytest.mark.parametrize("dtype,cap", [(BF16, 2072), (FP8KV, 2080)])
+def test_append_and_reattend_unaligned_cap(dev, dtype, cap):
+    """Append into caches whose capacity is a multiple of 8 (bf16) or 16 (E4M3) but
+    not of 64, up to the last slot; the grown caches are the oracle's bit for bit
+    and attention over them matches the oracle."""
+    torch = dev["torch"]
+    p = synth.params_for(3, n_items=3, dtype=dtype, D=16, prefix=("list", [cap - 16, 1000, 77]), cap=cap, V=1000,
+                         n_masked=8, plant=None)
+    s = synth.make_step(p, seed=cap + dtype)
+    ds = _ds(dev, s, max_prefix=cap)
+    acc = np.array([16, 9, 1], np.int32)
+    ds.append(n_accept=torch.from_numpy(acc).cuda())
+    torch.cuda.synchronize()
+    kc, vc, pref, err = oracle.kv_append(s["k_cache"], s["v_cache"], s["prefix"], s["k_blk"], s["v_blk"], acc)
+    assert err == 0 and int(ds.dev_err.cpu()[0]) == 0
+    np.testing.assert_array_equal(ds.prefix.cpu().numpy(), pref)
+    assert pref[0] == cap
+    assert ds.k_cache.cpu().numpy().tobytes() == kc.tobytes()
+    assert ds.v_cache.cpu().numpy().tobytes() == vc.tobytes()
+    ds.attn()
+    got = _out_host(dev, ds)
+    s2 = dict(s, k_cache=kc, v_cache=vc, prefix=pref)
+    _check_attention(got, _reference(s2, BIDIR), "append_cap%d_dtype%d" % (cap, dtype))
+
+
 # ---------------------------------------------------------------------------
 # Quadratic self-speculative attention (BD_BLOCK_QUAD): B drafts, causal among
 # themselves, then B groups of mask tokens, group g seeing drafts 0..g-1 and
@@ -347,7 +419,7 @@ def test_quad_3b_sampled_items(dev):
     slots): the GPU computes every layer in the launch that bench.py times; the
     oracle checks three whole layers of it."""
     st = synth.quad_step(1)
-    ds = dev["step"].DeviceStep(st)
+    ds = _ds(dev, st)
     p = st["params"]
     _say("quad 3b: n=%d slots=%d B=%d" % (p["n_items"], p["D"], p["B"]))
     ds.attn()
@@ -389,7 +461,7 @@ def test_quad_append_accepted_drafts(dev):
     torch = dev["torch"]
     B = 5
     st = synth.make_quad_step(dict(synth.QUAD_CONFIGS[2], B=B), 123)
-    ds = dev["step"].DeviceStep(st)
+    ds = _ds(dev, st)
     acc = np.array([B, 0, 3], np.int32)
     ds.append(n_accept=torch.from_numpy(acc).cuda())
     torch.cuda.synchronize()
@@ -418,9 +490,10 @@ def _run_two_stream(dev, st, label, items=None):
         label, n, st["Lc"], st["Ln"], p["D"], Hq, p["Hkv"], d, st["n_spans"].tolist()))
     c = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
     q, k, v, sp, ns = c(st["q"]), c(st["k"]), c(st["v"]), c(st["spans"]), c(st["n_spans"])
-    out = torch.empty_like(q)
+    g = _guarded(dev)
+    out = g.make("out", q.shape, q.dtype, fill=dev["step"].POISON)
     desc = bd.two_stream_desc(n, st["Lc"], st["Ln"], st["cap"], p["D"], Hq, p["Hkv"], d, st["spans"].shape[1])
-    ws = torch.zeros(max(bd.bd_two_stream_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
+    ws = g.make("ws", (max(bd.bd_two_stream_workspace_bytes(desc), 16),), torch.uint8, fill=0)
     bd.bd_two_stream_attn(desc, q, k, v, sp, ns, out, ws)
     torch.cuda.synchronize()
     got = synth.bf16_bits_to_f32(out.cpu().numpy().view(np.uint16)).astype(np.float64)
@@ -510,39 +583,26 @@ def test_two_stream_deterministic(dev):
 # ---------------------------------------------------------------------------
 
 def _rule_commit(conf32, masked, k, tau):
-    """Top-k by (conf desc, index asc) plus {conf > tau}, on fp32 values."""
+    """Top-k by (conf desc, index asc) plus {conf > tau}, on the GPU's fp32 values."""
     idx = [i for i in range(len(masked)) if masked[i]]
     order = sorted(idx, key=lambda i: (-float(conf32[i]), i))
     take = set(order[:k]) | {i for i in idx if conf32[i] > np.float32(tau)}
     return take
 
 
-def _fragile(conf64, masked, k, tau):
-    """Positions whose commit decision sits within 1e-4 of a tie in the oracle's values."""
-    idx = [i for i in range(len(masked)) if masked[i]]
-    frag = set()
-    for i in idx:
-        if abs(conf64[i] - tau) < FRAGILE:
-            frag.add(i)
-    if 0 < k < len(idx):
-        order = sorted(idx, key=lambda i: (-conf64[i], i))
-        kth, nxt = conf64[order[k - 1]], conf64[order[k]]
-        if kth - nxt < FRAGILE:
-            frag |= {i for i in idx if abs(conf64[i] - kth) < FRAGILE or abs(conf64[i] - nxt) < FRAGILE}
-    return frag
-
-
 def _compare_commit(dev, ds, p, masked_in, tokens_in, logits_np, label):
+    """GPU confidence + commit outputs (in ``ds``) against the oracle on the same
+    inputs.  Returns (fragile counts, oracle result)."""
     torch = dev["torch"]
     torch.cuda.synchronize()
     ref = oracle.confidence_commit(logits_np, masked_in, tokens_in, p["S"], p["tau"])
+    frag = acceptance.step_fragility(logits_np, masked_in, p["S"], p["tau"], ref)
     g_conf = ds.conf.cpu().numpy()
     g_arg = ds.argmax.cpu().numpy()
     g_com = ds.committed.cpu().numpy()
     g_ncom = ds.n_committed.cpu().numpy()
     g_mask = ds.masked.cpu().numpy()
     g_tok = ds.tokens.cpu().numpy()
-    excluded = 0
     for r in range(p["n_req"]):
         m = masked_in[r].astype(bool)
         nm = int(m.sum())
@@ -551,15 +611,14 @@ def _compare_commit(dev, ds, p, masked_in, tokens_in, logits_np, label):
         if nm:
             err = np.abs(g_conf[r][m].astype(np.float64) - ref["conf"][r][m])
             assert err.max() <= CONF_ABS, (label, r, err.max())
-            np.testing.assert_array_equal(g_arg[r][m], ref["argmax"][r][m])
+            np.testing.assert_array_equal(g_arg[r][m], ref["argmax"][r][m])  # margin rows included
         # The GPU applies the rule exactly to its own fp32 confidences ...
         own = _rule_commit(g_conf[r], m, k, p["tau"])
         assert set(np.nonzero(g_com[r])[0].tolist()) == own, (label, r)
         # ... and agrees with the oracle wherever the decision is not within 1e-4 of a tie.
-        frag = _fragile(ref["conf"][r], m, k, p["tau"])
-        excluded += len(frag)
+        excl = frag[r]["rank"] | frag[r]["tau"]
         for i in range(p["D"]):
-            if i in frag:
+            if i in excl:
                 continue
             assert g_com[r, i] == ref["committed"][r, i], (label, r, i)
             assert g_mask[r, i] == ref["masked"][r, i]
@@ -568,7 +627,7 @@ def _compare_commit(dev, ds, p, masked_in, tokens_in, logits_np, label):
         untouched = ~m
         np.testing.assert_array_equal(g_tok[r][untouched], tokens_in[r][untouched])
         np.testing.assert_array_equal(g_mask[r][untouched], 0)
-    return excluded, ref
+    return acceptance.counts(frag), ref
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
@@ -576,36 +635,97 @@ def test_confidence_commit_configs(dev, cfg):
     s = synth.config_step(cfg)
     p = s["params"]
     _say("confidence_commit cfg%d n_req=%d D=%d V=%d" % (cfg, p["n_req"], p["D"], p["V"]))
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     ds.confidence_commit()
-    excl, _ = _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], "cfg%d" % cfg)
-    _say("cfg%d excluded fragile decisions: %d" % (cfg, excl))
+    c, _ = _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], "cfg%d" % cfg)
+    _say("cfg%d fragile decisions: %s" % (cfg, c))
+    want = FRAGILE_COUNTS[str(cfg)]["first_step"]
+    assert {k: c[k] for k in ("margin", "rank", "tau", "excluded")} == \
+        {k: want[k] for k in ("margin", "rank", "tau", "excluded")}
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
-def test_multistep_block_parity(dev, cfg):
-    """The whole S-step loop of one block: at every step both sides start from the
-    oracle's state, decide, and must agree (DiffusionVL notes, Algorithm 1)."""
+def test_block_loop_on_own_state(dev, cfg):
+    """The whole denoising loop of one block on the GPU's own state (DiffusionVL
+    notes, cached block decoding and Algorithm 1): the GPU's masked / tokens are
+    never reset between steps; each step gets the next seeded logits.  After
+    every step the GPU's decisions match the oracle's on the same state (fragile
+    ones excluded), its trajectory equals the oracle's own loop unless a counted
+    fragile decision went the other way, committed tokens never change, each step
+    commits at least min(k, |M|), and the block finishes within S steps."""
     torch = dev["torch"]
     s = synth.config_step(cfg)
     p = s["params"]
-    ds = dev["step"].DeviceStep(s)
-    rng = np.random.Generator(np.random.PCG64(4242 + cfg))
-    masked, tokens, logits = s["masked"].copy(), s["tokens"].copy(), s["logits"]
-    steps, excluded = 0, 0
-    while masked.sum() > 0:
-        _say("cfg%d step %d masked=%d" % (cfg, steps + 1, int(masked.sum())))
-        ds.masked.copy_(torch.from_numpy(masked))
-        ds.tokens.copy_(torch.from_numpy(tokens))
-        lg = torch.from_numpy(np.ascontiguousarray(logits)).cuda()
-        ds.confidence_commit(logits=lg)
-        e, ref = _compare_commit(dev, ds, p, masked, tokens, logits, "cfg%d step%d" % (cfg, steps + 1))
-        excluded += e
-        masked, tokens = ref["masked"], ref["tokens"]
+    ds = _ds(dev, s)
+    nxt = acceptance.block_loop_logits(p, cfg)
+    logits = nxt(s["logits"])
+    o_masked, o_tokens = s["masked"].copy(), s["tokens"].copy()   # the oracle's own loop
+    steps, diverged_at = 0, None
+    total = dict(margin=0, rank=0, tau=0, excluded=0)
+    while True:
+        torch.cuda.synchronize()
+        gm, gt = ds.masked.cpu().numpy().copy(), ds.tokens.cpu().numpy().copy()
+        if gm.sum() == 0:
+            break
         steps += 1
-        logits = synth.fresh_logits(p, rng)
-    assert steps <= p["S"]
-    _say("cfg%d finished in %d steps, excluded %d" % (cfg, steps, excluded))
+        _say("cfg%d step %d masked=%d" % (cfg, steps, int(gm.sum())))
+        assert steps <= p["S"], "block not finished within S steps"
+        if diverged_at is None:
+            np.testing.assert_array_equal(gm, o_masked)
+            np.testing.assert_array_equal(gt, o_tokens)
+        ds.confidence_commit(logits=torch.from_numpy(np.ascontiguousarray(logits)).cuda())
+        c, ref = _compare_commit(dev, ds, p, gm, gt, logits, "cfg%d step%d" % (cfg, steps))
+        for key in total:
+            total[key] += c[key]
+        torch.cuda.synchronize()
+        nm, nt = ds.masked.cpu().numpy(), ds.tokens.cpu().numpy()
+        for r in range(p["n_req"]):
+            kept = gm[r] == 0
+            np.testing.assert_array_equal(nt[r][kept], gt[r][kept])     # committed tokens stay
+            assert np.all(nm[r][kept] == 0)                              # never re-masked
+            k = oracle.commit_k(p["D"], p["S"], int(gm[r].sum()))
+            assert int(gm[r].sum()) - int(nm[r].sum()) >= k
+        if diverged_at is None:
+            o_masked, o_tokens = ref["masked"], ref["tokens"]
+            if not (np.array_equal(nm, o_masked) and np.array_equal(nt, o_tokens)):
+                diverged_at = steps   # only possible at an excluded (counted) position
+                _say("cfg%d: trajectory left the oracle's at step %d through a fragile decision" % (cfg, steps))
+        logits = nxt(None)
+    _say("cfg%d finished in %d steps; fragile %s" % (cfg, steps, total))
+    if diverged_at is None:
+        want = FRAGILE_COUNTS[str(cfg)]["block_loop"]
+        assert steps == want["steps"]
+        assert total == {k: want[k] for k in ("margin", "rank", "tau", "excluded")}
+    else:
+        assert total["excluded"] > 0
+
+
+def test_commit_last_step_with_slot0_committed(dev):
+    """The last step of a block whose slot 0 is already committed and whose every
+    remaining masked slot commits now (|M| <= k): every output is written by the
+    finishing workgroup, after all workgroups of the launch have read the masked
+    flags that it rewrites."""
+    torch = dev["torch"]
+    p = synth.params_for(1, n_items=1, n_req=3, D=16, n_masked=3, V=151936, S=4, tau=1.5,
+                         logit_sigma2=4.0, prefix=("fixed", 8), Hq=2, Hkv=1, d=64, dtype=F32)
+    s = synth.make_step(p, seed=616)
+    for r, slots in enumerate([[3, 7, 11], [1, 2, 15], [5, 6, 9]]):
+        s["masked"][r] = 0
+        s["masked"][r, slots] = 1                  # slot 0 committed in every request
+        s["tokens"][r] = np.where(s["masked"][r] == 1, -1, 1000 + r)
+    ds = _ds(dev, s)
+    for rep in range(3):
+        ds.reset_block_state()
+        ds.conf.fill_(0.5)
+        ds.argmax.fill_(7)
+        ds.committed.fill_(9)
+        ds.n_committed.fill_(9)
+        ds.confidence_commit()
+        _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], "last_step_%d" % rep)
+        torch.cuda.synchronize()
+        assert ds.n_committed.cpu().numpy().tolist() == [3, 3, 3]
+        assert int(ds.masked.sum()) == 0
+        assert np.array_equal(ds.committed.cpu().numpy(), s["masked"])
 
 
 COMMIT_CASES = [
@@ -628,7 +748,7 @@ def test_confidence_commit_edge_cases(dev, label, ov):
     p = synth.params_for(1, **base)
     s = synth.make_step(p, seed=len(label) * 31)
     _say("confidence_commit %s" % label)
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     ds.confidence_commit()
     _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], label)
 
@@ -641,7 +761,7 @@ def test_confidence_ties_and_equal_rows(dev):
     s = synth.make_step(p, seed=5)
     s["logits"][:] = 0.25
     s["logits"][0, 4, [100, 7, 4000]] = 3.0
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     ds.confidence_commit()
     torch.cuda.synchronize()
     conf = ds.conf.cpu().numpy()[0]
@@ -679,7 +799,7 @@ def test_confidence_commit_random_sweep(dev, i):
     label = "commit_sweep%d" % i
     _say("%s n_req=%d D=%d V=%d masked=%d S=%d tau=%g sigma2=%g plant=%s" % (
         label, p["n_req"], p["D"], p["V"], p["n_masked"], p["S"], p["tau"], p["logit_sigma2"], p["plant"]))
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     ds.confidence_commit()
     _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], label)
 
@@ -690,7 +810,7 @@ def test_verify_random_sweep(dev, i):
     p = synth.params_for(4, **dict(q, plant="geom0.3", D=min(q["D"], 32)))
     s = synth.make_step(p, seed=7100 + i)
     _say("verify_sweep%d n_req=%d D=%d V=%d planted=%s" % (i, p["n_req"], p["D"], p["V"], s["planted_L"].tolist()))
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     L = ds.verify()
     dev["torch"].cuda.synchronize()
     L_ref, amax_ref = oracle.spec_verify(s["logits"], s["draft"])
@@ -710,7 +830,7 @@ def test_verify_then_append_cfg4(dev, seed):
     s = synth.make_step(synth.params_for(4), synth.seed_of(4) + seed, plant_L=forced)
     p = s["params"]
     _say("verify+append cfg4 seed=%d planted L=%d" % (seed, int(s["planted_L"][0])))
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     ds.attn()
     L_gpu = ds.verify()
     ds.append(n_accept=L_gpu)
@@ -729,7 +849,7 @@ def test_verify_ragged_requests(dev):
     torch = dev["torch"]
     p = synth.params_for(4, n_req=6, n_items=1, D=13, V=3001, prefix=("fixed", 8))
     s = synth.make_step(p, seed=9)
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     L = ds.verify()
     torch.cuda.synchronize()
     L_ref, amax_ref = oracle.spec_verify(s["logits"], s["draft"])
@@ -744,7 +864,7 @@ def test_append_overflow_and_partial(dev, dtype):
     p = synth.params_for(1, n_items=3, D=8, dtype=dtype, prefix=("list", [10, 0, 50]), Hq=4, Hkv=2,
                          d=64, cap=64)
     s = synth.make_step(p, seed=3)
-    ds = dev["step"].DeviceStep(s)
+    ds = _ds(dev, s)
     acc = np.array([3, 8, 8], np.int32)     # item 2: 50 + 8 > 56? no: cap 64 -> fits
     acc[2] = 8
     s_prefix = s["prefix"].copy()
@@ -779,19 +899,21 @@ class _LmDev:
         p = st["params"]
         self.p = p
         c = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        g = _guarded(dev)
+        poison = dev["step"].POISON
         self.hidden = c(st["hidden"].view(np.int16))
         self.weight = c(st["weight"].view(np.int16))
-        self.masked = c(st["masked"])
-        self.tokens = c(st["tokens"])
+        self.masked = g.make("masked", st["masked"].shape, torch.uint8, init=c(st["masked"]))
+        self.tokens = g.make("tokens", st["tokens"].shape, torch.int32, init=c(st["tokens"]))
         nr, D = p["n_req"], p["D"]
-        self.conf = torch.empty((nr, D), dtype=torch.float32, device="cuda")
-        self.argmax = torch.empty((nr, D), dtype=torch.int32, device="cuda")
-        self.committed = torch.empty((nr, D), dtype=torch.uint8, device="cuda")
-        self.n_committed = torch.empty((nr,), dtype=torch.int32, device="cuda")
+        self.conf = g.make("conf", (nr, D), torch.float32, fill=poison)
+        self.argmax = g.make("argmax", (nr, D), torch.int32, fill=poison)
+        self.committed = g.make("committed", (nr, D), torch.uint8, fill=poison)
+        self.n_committed = g.make("n_committed", (nr,), torch.int32, fill=poison)
         self.desc = bd.lmhead_desc(nr, D, p["V"], p["H"], p["S"], p["tau"])
         need = bd.bd_lmhead_workspace_bytes(self.desc)
         assert need < bd.SIZE_MAX
-        self.ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+        self.ws = g.make("ws", (max(need, 16),), torch.uint8, fill=0)
         self.bd = bd
 
     def run(self):
@@ -804,7 +926,9 @@ def _compare_lmhead(dev, g, st, label):
     torch.cuda.synchronize()
     p = st["params"]
     logits64 = oracle.lm_head_logits(st["hidden"], st["weight"])
-    ref = oracle.confidence_commit(logits64.astype(np.float32), st["masked"], st["tokens"], p["S"], p["tau"])
+    logits32 = logits64.astype(np.float32)
+    ref = oracle.confidence_commit(logits32, st["masked"], st["tokens"], p["S"], p["tau"])
+    frag_sets = acceptance.step_fragility(logits32, st["masked"], p["S"], p["tau"], ref)
     g_conf, g_arg = g.conf.cpu().numpy(), g.argmax.cpu().numpy()
     g_com, g_ncom = g.committed.cpu().numpy(), g.n_committed.cpu().numpy()
     g_mask, g_tok = g.masked.cpu().numpy(), g.tokens.cpu().numpy()
@@ -814,7 +938,7 @@ def _compare_lmhead(dev, g, st, label):
         nm = int(m.sum())
         k = min(-(-p["D"] // p["S"]), nm)
         assert np.all(np.isnan(g_conf[r][~m])) and np.all(g_arg[r][~m] == -1)
-        frag = _fragile(ref["conf"][r], m, k, p["tau"])
+        frag = frag_sets[r]["rank"] | frag_sets[r]["tau"]
         for i in np.flatnonzero(m):
             top2 = np.partition(logits64[r, i], -2)[-2:]
             if top2[1] - top2[0] < LOGIT_GAP:

@@ -54,7 +54,15 @@ def _load():
     # torch ships its own libamdhip64.so.7.  Load it first, so libbd.so binds to
     # the same HIP runtime that owns torch's device memory and streams (both
     # libraries carry the same soname; whichever loads first serves the process).
-    import torch  # noqa: F401
+    import torch
+    # Start that runtime before libbd.so is loaded.  Loading libbd.so registers
+    # its code objects with the runtime and an exit handler that unregisters
+    # them (hipcc's module constructor calls atexit); exit handlers run in the
+    # reverse order of registration, so this one then runs before any handler
+    # registered while the runtime started (a profiler's finalisation, say),
+    # while the runtime is still whole.  On a machine without a GPU this only
+    # reports that there is none.
+    torch.cuda.is_available()
     if not os.path.exists(LIB_PATH):
         raise ImportError("libbd.so is not built (%s); run __graft_entry__.build() or "
                           "python vlm_decoding_amd/build.py" % LIB_PATH)

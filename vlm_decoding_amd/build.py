@@ -22,9 +22,11 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every HIP source into libbd.so next to this file.  ``extra`` holds
+    further hipcc arguments (e.g. -D definitions of the tuning constants)."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
@@ -33,4 +35,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, extra=[a for a in sys.argv[1:] if a.startswith("-D")]))

@@ -236,6 +236,10 @@ bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache, i
         return BD_E_SHAPE;
     if (desc->d != 64 && desc->d != 128) return BD_E_SHAPE;
     if (desc->cap < 1 || desc->cap % (desc->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
+    // The limits bd_attn_step puts on a cache and a block: one item's cache and
+    // one item's block K (or V) hold at most 2^30 elements.
+    if ((int64_t)desc->cap * desc->d > (1ll << 30)) return BD_E_SHAPE;
+    if ((int64_t)block_slots(desc) * desc->Hkv * desc->d > (1ll << 30)) return BD_E_SHAPE;
     if (!k_cache || !v_cache || !prefix_len || !k_blk || !v_blk) return BD_E_NULL;
     // Quadratic mode: the block holds B (B + 3) / 2 slots, of which the first B
     // (the drafts) can be accepted.

@@ -9,13 +9,24 @@
 // the accepted length is the first slot whose greedy token differs from
 // the draft.
 //
-// Each row is split into chunks of whole 1024-float strides; one 256-thread
-// workgroup streams one chunk with 16-byte loads, keeping a running
-// (max, index of first max, sum of exp(x - max)) per thread.  Partials are
-// combined in a fixed tree inside the workgroup; the last workgroup of a
-// request (one atomic ticket per request) merges every row's chunk partials
-// in chunk order and runs the one-wave commit / verify tail.  No float atomics, so
-// results are identical run to run.
+// Work split.  Each request gets G workgroups of 256 threads (G sized by the
+// host as if every slot took part).  Every workgroup first reads the
+// request's masked flags (one 64-byte line) and learns the rows that take
+// part - the masked slots, or every slot for verify - and their number nm.
+// The G workgroups are then dealt out over those rows, cpr = G / nm chunks
+// of contiguous columns per row, so every launched workgroup streams logits
+// of a participating row whatever the masked set is, and no byte of an
+// unmasked row is read.  A workgroup streams its chunk with 16-byte loads
+// (up to 16 per thread in flight) into a running (max, index of first max,
+// sum of exp(x - max)) per thread, combined in a fixed tree.
+//
+// Hand-off.  Every workgroup of the request - idle ones included - takes one
+// ticket on the request's counter after publishing its partial, so the last
+// one to arrive (the finisher) starts only after every workgroup of the
+// launch has read the masked flags it rewrites.  The finisher stages the
+// request's partials in LDS, merges each row's chunks in chunk order (16
+// lanes per row, a fixed tree) and runs the one-wave commit / verify tail.
+// No float atomics, so results are identical run to run.
 #include "bd_common.h"
 #include "bd_internal.h"
 #include "bd_rowreduce.h"
@@ -24,7 +35,15 @@ namespace bd {
 namespace {
 
 constexpr int NT = 256;
-constexpr int kRowLoads = 16;  // float4 loads per thread per chunk (chunk <= 16 x 1024 floats)
+constexpr int kBatch = 16;          // 16-byte loads per thread in flight at once
+#ifndef BD_ROW_WG_TARGET
+#define BD_ROW_WG_TARGET 512
+#endif
+constexpr int kWgTarget = BD_ROW_WG_TARGET;  // workgroups a call aims for (two per CU)
+constexpr int kMaxGroups = 1024;    // workgroups per request (the finisher stages their partials in LDS)
+constexpr int kMaxChunk = 16384;    // floats per workgroup, upper target when every slot takes part
+constexpr int kMinChunk = 1024;     // ... lower bound of the plan (one 16-byte load per thread)
+constexpr int kMinChunkRun = 256;   // lower bound when few slots take part
 
 struct RowParams {
     const float *logits;
@@ -36,120 +55,155 @@ struct RowParams {
     int32_t *n_committed;
     const int32_t *draft;
     int32_t *accepted_len;
-    float *part_m, *part_s;
-    int *part_i;
-    int *req_cnt;
-    int n_req, D, V, S, chunks, chunk_elems;
+    float2 *part_ms;  // [n_req][G] (max, sum of exp(x - max))
+    int *part_i;      // [n_req][G] index of the first max
+    int *req_cnt;     // [n_req] tickets
+    int n_req, D, V, S, G, max_cpr;
     float tau;
 };
 
+template <bool WITH_SUM>
+__device__ __forceinline__ void push4(Part &acc, float4 v, int e) {
+    push<WITH_SUM>(acc, v.x, e);
+    push<WITH_SUM>(acc, v.y, e + 1);
+    push<WITH_SUM>(acc, v.z, e + 2);
+    push<WITH_SUM>(acc, v.w, e + 3);
+}
+
 template <bool VERIFY>
 __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
+    __shared__ float2 s_ms[kMaxGroups];
+    __shared__ int s_i[kMaxGroups];
     __shared__ Part s_part[NT / 64];
     __shared__ __attribute__((aligned(16))) float s_conf[64];
     __shared__ int s_arg[64];
-    __shared__ int s_done, s_nm;
-    __shared__ unsigned long long s_mask;
+    __shared__ int s_slot[64];
+    __shared__ int s_done;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int row = blockIdx.x / p.chunks;
-    const int chunk = blockIdx.x - row * p.chunks;
-    const int r = row / p.D;
-    const int slot = row - r * p.D;
+    const int r = blockIdx.x / p.G;
+    const int b = blockIdx.x - r * p.G;
     const size_t ob = (size_t)r * p.D;
 
-    // The masked flags are requested first and the chunk's logits right behind
-    // them (all of a thread's loads in flight together), so deciding whether this
-    // row takes part costs no extra round trip; rows that do not take part drop
-    // their loads.
-    bool mk = false;
-    if (!VERIFY && w == 0) mk = lane < p.D && p.masked[ob + lane] != 0;
-    const float *x = p.logits + (size_t)row * p.V;
-    const int beg = chunk * p.chunk_elems;
-    const int end = min(p.V, beg + p.chunk_elems);
-    const bool vec = (p.V & 3) == 0;
-    float4 v[kRowLoads];
-    if (vec) {
-#pragma unroll
-        for (int u = 0; u < kRowLoads; ++u) {
-            const int e = beg + tid * 4 + u * NT * 4;
-            if (e < end) v[u] = *reinterpret_cast<const float4 *>(x + e);
-        }
-    }
-    if (!VERIFY) {
-        if (w == 0) {
-            const unsigned long long b = __builtin_amdgcn_ballot_w64(mk);
-            if (lane == 0) {
-                s_mask = b;
-                s_nm = __popcll(b);
-            }
-        }
-        __syncthreads();
-        if (!((s_mask >> slot) & 1ull)) {
-            // A request with nothing masked still reports an empty commit.
-            if (s_nm == 0 && slot == 0 && chunk == 0 && w == 0 && lane < p.D) {
-                if (p.conf) p.conf[ob + lane] = __int_as_float(0x7fc00000);
-                if (p.argmax) p.argmax[ob + lane] = -1;
-                if (p.committed) p.committed[ob + lane] = 0;
-                if (p.n_committed && lane == 0) p.n_committed[r] = 0;
-            }
-            return;
-        }
-    }
+    // The rows that take part and the j-th of them.  Each wave reads the flags
+    // itself, so no barrier is needed before the loads.
+    unsigned long long mask;
+    if (VERIFY)
+        mask = p.D == 64 ? ~0ull : (1ull << p.D) - 1ull;
+    else
+        mask = __builtin_amdgcn_ballot_w64(lane < p.D && p.masked[ob + lane] != 0);
+    const int nm = __popcll(mask);
+    // rank of this lane's slot among the participating slots
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    const bool in_mask = (mask >> lane) & 1ull;
+    const int cpr = nm == 0 ? 0 : min(p.G / nm, p.max_cpr);  // chunks per participating row
+    const bool active = b < nm * cpr;
 
-    // Reduce this chunk of the row.
     Part acc{-INFINITY, 0.f, 0x7fffffff};
-    if (vec) {
+    if (active) {
+        const int j = b / cpr;
+        const int c = b - j * cpr;
+        const int slot = __builtin_ctzll(__builtin_amdgcn_ballot_w64(in_mask && rank == j));
+        const float *x = p.logits + (ob + slot) * (size_t)p.V;
+        if ((p.V & 3) == 0) {
+            const int V4 = p.V >> 2;
+            const int beg = (int)((long long)V4 * c / cpr);
+            const int end = (int)((long long)V4 * (c + 1) / cpr);
+            const float4 *x4 = reinterpret_cast<const float4 *>(x);
+            for (int u0 = beg; u0 < end; u0 += NT * kBatch) {
+                float4 v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kRowLoads; ++u) {
-            const int e = beg + tid * 4 + u * NT * 4;
-            if (e < end) {
-                push<!VERIFY>(acc, v[u].x, e);
-                push<!VERIFY>(acc, v[u].y, e + 1);
-                push<!VERIFY>(acc, v[u].z, e + 2);
-                push<!VERIFY>(acc, v[u].w, e + 3);
+                for (int k = 0; k < kBatch; ++k) {
+                    const int u = u0 + k * NT + tid;
+                    if (u < end) v[k] = x4[u];
+                }
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const int u = u0 + k * NT + tid;
+                    if (u < end) push4<!VERIFY>(acc, v[k], 4 * u);
+                }
+            }
+        } else {
+            const int beg = (int)((long long)p.V * c / cpr);
+            const int end = (int)((long long)p.V * (c + 1) / cpr);
+            for (int e0 = beg; e0 < end; e0 += NT * kBatch) {
+                float v[kBatch];
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const int e = e0 + k * NT + tid;
+                    if (e < end) v[k] = x[e];
+                }
+#pragma unroll
+                for (int k = 0; k < kBatch; ++k) {
+                    const int e = e0 + k * NT + tid;
+                    if (e < end) push<!VERIFY>(acc, v[k], e);
+                }
             }
         }
-    } else {
-        for (int e = beg + tid; e < end; e += NT) push<!VERIFY>(acc, x[e], e);
     }
     acc = wave_reduce(acc);
     if (lane == 0) s_part[w] = acc;
     __syncthreads();
     if (tid == 0) {
-        Part t = s_part[0];
+        if (active) {
+            Part t = s_part[0];
 #pragma unroll
-        for (int k = 1; k < NT / 64; ++k) t = combine(t, s_part[k]);
-        const size_t o = (size_t)row * p.chunks + chunk;
-        bd_coherent_store(p.part_m + o, t.m);
-        bd_coherent_store(p.part_s + o, t.s);
-        bd_coherent_store(p.part_i + o, t.i);
-        bd_wait_all_memory();
-        // One ticket per request: the last of its (rows x chunks) workgroups finishes it.
-        const int need = (VERIFY ? p.D : s_nm) * p.chunks;
-        s_done = bd_ticket(&p.req_cnt[r]) == need - 1;
+            for (int k = 1; k < NT / 64; ++k) t = combine(t, s_part[k]);
+            const size_t o = (size_t)r * p.G + b;
+            bd_coherent_store2(reinterpret_cast<float *>(&p.part_ms[o]), t.m, t.s);
+            bd_coherent_store(p.part_i + o, t.i);
+        }
+        bd_wait_all_memory();  // the partial (and this workgroup's flag reads) precede the ticket
+        s_done = bd_ticket(&p.req_cnt[r]) == p.G - 1;
     }
     __syncthreads();
     if (!s_done) return;
 
-    // Last workgroup of request r.  Sixteen lanes per row merge that row's chunk
-    // partials (lane c takes chunks c, c + 16, ... in order, then a fixed
-    // 16-lane tree), four rows per wave, sixteen rows per pass.
-    for (int r0 = 0; r0 < p.D; r0 += 16) {
-        const int i = r0 + w * 4 + (lane >> 4);
-        const bool act = i < p.D && (VERIFY || ((s_mask >> i) & 1ull));
-        Part t{-INFINITY, 0.f, 0x7fffffff};
-        if (act) {
-            const size_t o = (ob + i) * p.chunks;
-            for (int c = lane & 15; c < p.chunks; c += 16)
-                t = combine(t, Part{bd_coherent_load(p.part_m + o + c), bd_coherent_load(p.part_s + o + c),
-                                    bd_coherent_load(p.part_i + o + c)});
+    // Finisher of request r.  Stage the nm * cpr partials (chunk c of row j at
+    // j * cpr + c) in LDS with one round of coherent loads.
+    const int n_part = nm * cpr;
+    const size_t pb = (size_t)r * p.G;
+    {
+        constexpr int PER = kMaxGroups / NT;
+        float2 ms[PER];
+        int ix[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int q = tid + k * NT;
+            if (q < n_part) {
+                ms[k] = bd_coherent_load2(reinterpret_cast<const float *>(&p.part_ms[pb + q]));
+                ix[k] = bd_coherent_load(p.part_i + pb + q);
+            }
         }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int q = tid + k * NT;
+            if (q < n_part) {
+                s_ms[q] = ms[k];
+                s_i[q] = ix[k];
+            }
+        }
+    }
+    if (w == 0 && in_mask) s_slot[rank] = lane;
+    __syncthreads();
+    // Sixteen lanes per row: lane c takes chunks c, c + 16, ... in order, then a
+    // fixed 16-lane tree; sixteen rows per pass.
+    for (int j0 = 0; j0 < nm; j0 += NT / 16) {
+        const int j = j0 + (tid >> 4);
+        const int c0 = tid & 15;
+        Part t{-INFINITY, 0.f, 0x7fffffff};
+        if (j < nm)
+            for (int c = c0; c < cpr; c += 16) {
+                const float2 m2 = s_ms[j * cpr + c];
+                t = combine(t, Part{m2.x, m2.y, s_i[j * cpr + c]});
+            }
         t = reduce16(t);
-        if (act && (lane & 15) == 0) {
-            s_conf[i] = 1.0f / t.s;
-            s_arg[i] = t.i;
+        if (j < nm && c0 == 0) {
+            const int slot = s_slot[j];
+            s_conf[slot] = 1.0f / t.s;
+            s_arg[slot] = t.i;
         }
     }
     __syncthreads();
@@ -157,15 +211,15 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     if (VERIFY) {
         const int a = lane < p.D ? s_arg[lane] : 0;
         const bool bad = lane < p.D && a != p.draft[ob + lane];
-        const unsigned long long b = __builtin_amdgcn_ballot_w64(bad);
+        const unsigned long long bb = __builtin_amdgcn_ballot_w64(bad);
         if (lane < p.D && p.argmax) p.argmax[ob + lane] = a;
         if (lane == 0) {
-            p.accepted_len[r] = b ? (__ffsll((long long)b) - 1) : p.D;
+            p.accepted_len[r] = bb ? (__ffsll((long long)bb) - 1) : p.D;
             bd_coherent_store(p.req_cnt + r, 0);
         }
         return;
     }
-    const unsigned long long tb = commit_request(s_conf, s_arg, s_mask, s_nm, p.D, p.S, p.tau, lane, p.masked + ob,
+    const unsigned long long tb = commit_request(s_conf, s_arg, mask, nm, p.D, p.S, p.tau, lane, p.masked + ob,
                                                  p.tokens + ob, p.conf ? p.conf + ob : nullptr,
                                                  p.argmax ? p.argmax + ob : nullptr,
                                                  p.committed ? p.committed + ob : nullptr);
@@ -187,17 +241,15 @@ RowParams make_params(const RowPlan &pl, const RowArgs &a) {
     p.draft = a.draft;
     p.accepted_len = a.accepted_len;
     char *ws = (char *)a.ws;
-    const size_t np = (size_t)pl.rows * pl.chunks;
-    p.part_m = (float *)(ws + pl.part_off);
-    p.part_s = p.part_m + np;
-    p.part_i = (int *)(p.part_s + np);
+    p.part_ms = (float2 *)(ws + pl.part_off);
+    p.part_i = (int *)(ws + pl.idx_off);
     p.req_cnt = (int *)(ws + pl.cnt_off);
     p.n_req = a.n_req;
     p.D = a.D;
     p.V = a.V;
     p.S = a.S;
-    p.chunks = pl.chunks;
-    p.chunk_elems = pl.chunk_elems;
+    p.G = pl.groups;
+    p.max_cpr = pl.max_cpr;
     p.tau = a.tau;
     return p;
 }
@@ -206,26 +258,25 @@ RowParams make_params(const RowPlan &pl, const RowArgs &a) {
 
 RowPlan plan_rows(int n_req, int D, int V) {
     RowPlan pl{};
-    pl.rows = n_req * D;
-    // Chunks of about 16 strides of 1024 floats (64 KB): enough bytes per
-    // workgroup to keep its loads streaming, few enough workgroups per request
-    // that its ticket counter is not a point of contention.  Rows that are
-    // short or few get smaller chunks so that at least ~256 workgroups run.
-    const int strides = (V + 1023) / 1024;  // 1024-float strides per row
-    int chunks = std::max(1, (strides + 15) / 16);
-    const int want = std::max(1, (256 + pl.rows - 1) / pl.rows);
-    chunks = std::min(strides, std::max(chunks, want));
-    const int per = (strides + chunks - 1) / chunks;
-    pl.chunk_elems = per * 1024;
-    pl.chunks = (V + pl.chunk_elems - 1) / pl.chunk_elems;
-    pl.ok = (size_t)pl.rows * pl.chunks * NT < (1ull << 32);  // HIP grid limit
+    // Chunks per row if every slot took part: enough workgroups for the call to
+    // fill the GPU (kWgTarget), no chunk above kMaxChunk floats where the rows
+    // allow, none below kMinChunk, and at most kMaxGroups workgroups per request.
+    const long long c_lo = ((long long)V + kMaxChunk - 1) / kMaxChunk;
+    const long long c_hi = std::max(1ll, ((long long)V + kMinChunk - 1) / kMinChunk);
+    const long long c_want = ((long long)kWgTarget + (long long)n_req * D - 1) / ((long long)n_req * D);
+    long long c0 = std::min(std::max(c_want, c_lo), c_hi);
+    c0 = std::max(1ll, std::min(c0, (long long)(kMaxGroups / D)));
+    pl.groups = (int)(D * c0);
+    pl.max_cpr = std::max((int)c0, V / kMinChunkRun);
+    pl.ok = (long long)n_req * pl.groups * NT < (1ll << 32);  // HIP grid limit
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t o = off;
         off += (bytes + 255) / 256 * 256;
         return o;
     };
-    pl.part_off = take((size_t)pl.rows * pl.chunks * 12);
+    pl.part_off = take((size_t)n_req * pl.groups * 8);
+    pl.idx_off = take((size_t)n_req * pl.groups * 4);
     pl.cnt_off = take((size_t)n_req * 4);
     pl.ws_bytes = off;
     return pl;
@@ -233,13 +284,13 @@ RowPlan plan_rows(int n_req, int D, int V) {
 
 hipError_t launch_confidence_commit(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
     RowParams p = make_params(pl, a);
-    hipLaunchKernelGGL((row_kernel<false>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((row_kernel<false>), dim3(a.n_req * pl.groups), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_spec_verify(const RowPlan &pl, const RowArgs &a, hipStream_t s) {
     RowParams p = make_params(pl, a);
-    hipLaunchKernelGGL((row_kernel<true>), dim3(pl.rows * pl.chunks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((row_kernel<true>), dim3(a.n_req * pl.groups), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
@@ -260,11 +311,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(int D, int S, int Hkv, i
         if (threadIdx.x == 0 && dev_err) *dev_err = 1;
         return;
     }
-    const int per_t = Hkv * d;
-    for (int e = threadIdx.x; e < L * per_t; e += blockDim.x) {
-        const int t = e / per_t;
-        const int g = (e / d) % Hkv;
-        const int dd = e % d;
+    const long long per_t = (long long)Hkv * d;
+    for (long long e = threadIdx.x; e < L * per_t; e += blockDim.x) {
+        const int t = (int)(e / per_t);
+        const int g = (int)((e / d) % Hkv);
+        const int dd = (int)(e % d);
         const size_t src = (((size_t)it * S + t) * Hkv + g) * d + dd;
         k_cache[(((size_t)it * Hkv + g) * cap + (P + t)) * d + dd] = k_blk[src];
         v_cache[(((size_t)it * Hkv + g) * d + dd) * cap + (P + t)] = v_blk[src];

@@ -4,6 +4,11 @@
 include/bd.h) to HBM once, sizes and zero-fills the workspaces, and exposes
 the library calls on those buffers.  torch supplies device memory and the
 stream; the arithmetic runs in libbd.so.
+
+With ``guard_bytes > 0`` every buffer the library writes (outputs, block
+state, caches, prefix lengths, workspaces) sits between two bands of canary
+bytes, and outputs start filled with a poison pattern; ``check_guards()``
+then names every buffer whose bands were overwritten.
 """
 
 import ctypes
@@ -13,8 +18,44 @@ import torch
 
 from . import bd
 
-_TORCH = {np.float32: torch.float32, np.uint16: torch.int16, np.uint8: torch.uint8,
-          np.int32: torch.int32}
+CANARY = 0xA7   # guard-band byte
+POISON = 0x5A   # initial bytes of outputs (finite as fp32 / bf16, never a valid result here)
+
+
+class GuardedBuffers:
+    """Device tensors carved out of larger byte buffers with canary bands on both sides."""
+
+    def __init__(self, device, guard_bytes):
+        assert guard_bytes % 256 == 0
+        self.device = device
+        self.guard = guard_bytes
+        self.bufs = []  # (name, raw uint8 tensor, interior bytes)
+
+    def make(self, name, shape, dtype, init=None, fill=None):
+        """A tensor of ``shape``/``dtype``: a copy of ``init`` (a device tensor), or
+        filled with the byte ``fill``, or uninitialised."""
+        elem = torch.empty((), dtype=dtype).element_size()
+        n = int(np.prod(shape)) * elem
+        if self.guard == 0:
+            t = torch.empty(shape, dtype=dtype, device=self.device)
+        else:
+            raw = torch.full((n + 2 * self.guard,), CANARY, dtype=torch.uint8, device=self.device)
+            t = raw[self.guard:self.guard + n].view(dtype).view(shape)
+            self.bufs.append((name, raw, n))
+        if init is not None:
+            t.copy_(init.reshape(shape))
+        elif fill is not None:
+            t.view(torch.uint8).fill_(fill)
+        return t
+
+    def damaged(self):
+        """Names of the buffers whose guard bands no longer hold the canary."""
+        bad = []
+        for name, raw, n in self.bufs:
+            g = self.guard
+            if bool((raw[:g] != CANARY).any()) or bool((raw[g + n:] != CANARY).any()):
+                bad.append(name)
+        return bad
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -22,6 +63,12 @@ def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
     if a.dtype == np.uint16:
         a = a.view(np.int16)
     return torch.from_numpy(a).to(device)
+
+
+def _dt(a: np.ndarray):
+    """torch dtype of the device copy of a host array (bf16 bits travel as int16)."""
+    return {np.dtype(np.float32): torch.float32, np.dtype(np.uint16): torch.int16, np.dtype(np.uint8): torch.uint8,
+            np.dtype(np.int32): torch.int32}[a.dtype]
 
 
 def to_host(t: torch.Tensor, like=None) -> np.ndarray:
@@ -34,10 +81,14 @@ def to_host(t: torch.Tensor, like=None) -> np.ndarray:
 class DeviceStep:
     """One step's inputs resident in HBM, with outputs and workspaces."""
 
-    def __init__(self, step: dict, device="cuda", max_prefix=None):
+    def __init__(self, step: dict, device="cuda", max_prefix=None, guard_bytes=0):
         """``max_prefix`` (default: the longest prefix of ``step``) is the host-side
-        bound the attention plan is sized for; it must not exceed the cache capacity."""
+        bound the attention plan is sized for; it must not exceed the cache capacity.
+        ``guard_bytes`` > 0 puts canary bands of that size around every buffer the
+        library writes (see check_guards)."""
         p = step["params"]
+        self.gb = GuardedBuffers(device, guard_bytes)
+        mk = self.gb.make
         self.p = p
         self.dtype = p["dtype"]
         self.device = device
@@ -47,9 +98,9 @@ class DeviceStep:
         self.q = to_device(step["q"], device)
         self.k_blk = to_device(step["k_blk"], device)
         self.v_blk = to_device(step["v_blk"], device)
-        self.k_cache = to_device(step["k_cache"], device)
-        self.v_cache = to_device(step["v_cache"], device)
-        self.prefix = to_device(step["prefix"], device)
+        self.k_cache = mk("k_cache", step["k_cache"].shape, _dt(step["k_cache"]), init=to_device(step["k_cache"], device))
+        self.v_cache = mk("v_cache", step["v_cache"].shape, _dt(step["v_cache"]), init=to_device(step["v_cache"], device))
+        self.prefix = mk("prefix", step["prefix"].shape, torch.int32, init=to_device(step["prefix"], device))
         # E4M3 K/V carry one fp32 scale per (item, KV head) for keys and for values.
         self.fp8kv = self.dtype == bd.BD_FP8KV
         self.k_scale = to_device(step["k_scale"], device) if self.fp8kv else None
@@ -57,10 +108,10 @@ class DeviceStep:
         self.logits = to_device(step["logits"], device)
         self.masked0 = to_device(step["masked"], device)
         self.tokens0 = to_device(step["tokens"], device)
-        self.masked = self.masked0.clone()
-        self.tokens = self.tokens0.clone()
+        self.masked = mk("masked", self.masked0.shape, torch.uint8, init=self.masked0)
+        self.tokens = mk("tokens", self.tokens0.shape, torch.int32, init=self.tokens0)
         self.draft = to_device(step["draft"], device) if "draft" in step else None
-        self.out = torch.empty_like(self.q)
+        self.out = mk("out", self.q.shape, self.q.dtype, fill=POISON)
         # The quadratic mode's descriptor takes the draft block size B; its tensors hold D = B (B + 3) / 2 slots.
         d_desc = p["B"] if p["mode"] == bd.BD_BLOCK_QUAD else D
         self.adesc = bd.attn_desc(n, d_desc, Hq, Hkv, d, self.cap, self.dtype, p["mode"], self.max_prefix)
@@ -72,16 +123,23 @@ class DeviceStep:
         # slot count) leaves their workspaces minimal; those calls then report it.
         cb = 16 if cb == bd.SIZE_MAX else cb
         vb = 16 if vb == bd.SIZE_MAX else vb
-        self.attn_ws = torch.zeros(max(ab, 16), dtype=torch.uint8, device=device)
-        self.commit_ws = torch.zeros(max(cb, 16), dtype=torch.uint8, device=device)
-        self.verify_ws = torch.zeros(max(vb, 16), dtype=torch.uint8, device=device)
+        self.attn_ws = mk("attn_ws", (max(ab, 16),), torch.uint8, fill=0)
+        self.commit_ws = mk("commit_ws", (max(cb, 16),), torch.uint8, fill=0)
+        self.verify_ws = mk("verify_ws", (max(vb, 16),), torch.uint8, fill=0)
         nr = p["n_req"]
-        self.conf = torch.empty((nr, D), dtype=torch.float32, device=device)
-        self.argmax = torch.empty((nr, D), dtype=torch.int32, device=device)
-        self.committed = torch.empty((nr, D), dtype=torch.uint8, device=device)
-        self.n_committed = torch.empty((nr,), dtype=torch.int32, device=device)
-        self.accepted = torch.empty((nr,), dtype=torch.int32, device=device)
-        self.dev_err = torch.zeros((1,), dtype=torch.int32, device=device)
+        self.conf = mk("conf", (nr, D), torch.float32, fill=POISON)
+        self.argmax = mk("argmax", (nr, D), torch.int32, fill=POISON)
+        self.committed = mk("committed", (nr, D), torch.uint8, fill=POISON)
+        self.n_committed = mk("n_committed", (nr,), torch.int32, fill=POISON)
+        self.accepted = mk("accepted", (nr,), torch.int32, fill=POISON)
+        self.dev_err = mk("dev_err", (1,), torch.int32, fill=0)
+
+    def check_guards(self):
+        """Names of the buffers whose canary bands were overwritten (empty if none,
+        or if the step was built without guards)."""
+        if torch.device(self.device).type == "cuda":
+            torch.cuda.synchronize(self.device)
+        return self.gb.damaged()
 
     def reset_block_state(self):
         self.masked.copy_(self.masked0)
