@@ -23,7 +23,7 @@ event record (hipEventDisableSystemFence), which would cost the GPU several
 microseconds per record.
 
 Beside the headline (extra keys): the same step timed cold, one step after
-each untimed 1 GiB flush write (``cold_step``); the other configurations of
+each untimed 1 GiB flush read (``cold_step``); the other configurations of
 the workload table (``configs``: the 3B single layer, the 3B verify chain -
 causal attention, speculative verify, KV append of the accepted prefix - and
 the 7B batch of 8 ragged requests); the layer-serial form of the headline
@@ -110,16 +110,18 @@ def dist_us(ms_list):
 
 def timed_calls(torch, stream, calls, iters, flush=None, before=None, sets=1):
     """Time ``iters`` iterations of ``calls(i)`` (a list of C-ABI calls issued on
-    ``stream``), each bracketed by HIP events.  ``flush`` (a 1 GiB tensor) is
-    written before every iteration outside the events, so nothing it follows stays
-    in any cache; ``before(i)`` runs untimed work (state restores) first.
-    Returns the per-iteration event times in ms."""
+    ``stream``), each bracketed by HIP events.  ``flush`` (a 1 GiB tensor) is read
+    in full before every iteration outside the events, so none of the data the
+    iteration touches is left in the L2s or the 256 MB last-level cache (a read,
+    not a write: a written flush would leave that cache full of dirty lines for
+    the timed iteration to write back); ``before(i)`` runs untimed work (state
+    restores) after it.  Returns the per-iteration event times in ms."""
     ev = HipEvents(2 * iters)
     sh = stream.cuda_stream
     status = 0
     for i in range(iters):
         if flush is not None:
-            flush.fill_(float(i & 7))
+            torch.sum(flush)
         if before is not None:
             before(i)
         ev.record(2 * i, sh)
@@ -354,7 +356,7 @@ def leg_denoise_config(torch, stream, flush, cfg, iters):
     med_s = dist["median"] * 1e-6
     out = dict(workload=p["name"], step_us=dist, steps_per_s=round(1.0 / med_s, 1), algorithmic_bytes=total,
                attn_bytes=a_b, logits_bytes=l_b, achieved_gbps=round(total / med_s / 1e9, 1),
-               frac=round(total / med_s / 1e9 / HBM_PEAK_GBS, 4), timing="cold: 1 GiB flush before each step")
+               frac=round(total / med_s / 1e9 / HBM_PEAK_GBS, 4), timing="cold: 1 GiB flush read before each step")
     del ds
     return out
 
@@ -395,7 +397,7 @@ def leg_verify_chain(torch, stream, flush, iters):
                attn_bytes=a_b, logits_bytes_read=logits_read, logits_bytes_algorithmic=logits_alg, append_bytes=app_b,
                algorithmic_bytes=total, achieved_gbps=round(total / med_s / 1e9, 1),
                frac=round(total / med_s / 1e9 / HBM_PEAK_GBS, 4),
-               timing="cold: 1 GiB flush before each chain; all 16 logits rows read (verify needs every row "
+               timing="cold: 1 GiB flush read before each chain; all 16 logits rows read (verify needs every row "
                       "until the first mismatch is known on the device)")
     del ds
     return out
@@ -746,7 +748,7 @@ def main():
                     algorithmic_bytes_per_launch=a_bytes,
                     achieved_at_median_gbps=round(a_bytes / (attn_d["median"] * 1e-6) / 1e9, 1))
 
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     cold = None
     if args.cold_steps > 0:
         ds0 = sets[0]
@@ -756,7 +758,7 @@ def main():
         cold = dict(step_us=cd, steps_per_s=round(1e6 / cd["median"], 1),
                     step_gbps=round(step_bytes / (cd["median"] * 1e-6) / 1e9, 1),
                     step_frac=round(step_bytes / (cd["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                    timing="each step alone after an untimed 1 GiB flush write, between HIP events")
+                    timing="each step alone after an untimed 1 GiB flush read, between HIP events")
     configs = None
     if args.config_iters > 0:
         configs = {"cfg2_3b_single_layer": leg_denoise_config(torch, stream, flush, 2, args.config_iters),

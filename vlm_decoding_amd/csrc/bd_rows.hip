@@ -21,12 +21,15 @@
 // sum of exp(x - max)) per thread, combined in a fixed tree.
 //
 // Hand-off.  Every workgroup of the request - idle ones included - takes one
-// ticket on the request's counter after publishing its partial, so the last
-// one to arrive (the finisher) starts only after every workgroup of the
-// launch has read the masked flags it rewrites.  The finisher stages the
-// request's partials in LDS, merges each row's chunks in chunk order (16
-// lanes per row, a fixed tree) and runs the one-wave commit / verify tail.
-// No float atomics, so results are identical run to run.
+// ticket after publishing its partial, so the last one to arrive (the
+// finisher) starts only after every workgroup of the launch has read the
+// masked flags it rewrites.  Tickets on one address are served one after
+// another (about 10 ns each, measured), so they go in two levels: a
+// workgroup tickets its group of kTicketGroup workgroups, the last of a group
+// tickets the request; every counter has a 256-byte line of its own.  The
+// finisher stages the request's partials in LDS, merges each row's chunks in
+// chunk order (16 lanes per row, a fixed tree) and runs the one-wave commit /
+// verify tail.  No float atomics, so results are identical run to run.
 #include "bd_common.h"
 #include "bd_internal.h"
 #include "bd_rowreduce.h"
@@ -41,9 +44,14 @@ constexpr int kBatch = 16;          // 16-byte loads per thread in flight at onc
 #endif
 constexpr int kWgTarget = BD_ROW_WG_TARGET;  // workgroups a call aims for (two per CU)
 constexpr int kMaxGroups = 1024;    // workgroups per request (the finisher stages their partials in LDS)
-constexpr int kMaxChunk = 16384;    // floats per workgroup, upper target when every slot takes part
+#ifndef BD_ROW_MAX_CHUNK
+#define BD_ROW_MAX_CHUNK 32768
+#endif
+constexpr int kMaxChunk = BD_ROW_MAX_CHUNK;  // floats per workgroup, upper target when every slot takes part
 constexpr int kMinChunk = 1024;     // ... lower bound of the plan (one 16-byte load per thread)
 constexpr int kMinChunkRun = 256;   // lower bound when few slots take part
+constexpr int kTicketGroup = 16;    // workgroups per first-level ticket counter
+constexpr int kCounterStride = 64;  // ints between counters (a 256-byte line each)
 
 struct RowParams {
     const float *logits;
@@ -57,17 +65,30 @@ struct RowParams {
     int32_t *accepted_len;
     float2 *part_ms;  // [n_req][G] (max, sum of exp(x - max))
     int *part_i;      // [n_req][G] index of the first max
-    int *req_cnt;     // [n_req] tickets
-    int n_req, D, V, S, G, max_cpr;
+    int *grp_cnt;     // [n_req][NG] first-level tickets, kCounterStride apart
+    int *req_cnt;     // [n_req] second-level tickets, kCounterStride apart
+    int n_req, D, V, S, G, NG, max_cpr;
     float tau;
 };
 
+// Four consecutive logits (indices e..e+3) into a running state: one max over
+// the four, the rare rescale only when the running maximum grows (the new
+// argmax is the first of the four equal to it: every earlier element this
+// thread saw is below it), then the four exponentials.
 template <bool WITH_SUM>
 __device__ __forceinline__ void push4(Part &acc, float4 v, int e) {
-    push<WITH_SUM>(acc, v.x, e);
-    push<WITH_SUM>(acc, v.y, e + 1);
-    push<WITH_SUM>(acc, v.z, e + 2);
-    push<WITH_SUM>(acc, v.w, e + 3);
+    const float lm = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    if (lm > acc.m) {
+        const int k = v.x == lm ? 0 : v.y == lm ? 1 : v.z == lm ? 2 : 3;
+        if (WITH_SUM) acc.s *= bd_exp2((acc.m - lm) * BD_LOG2E);  // 0 while acc.m is -inf
+        acc.m = lm;
+        acc.i = e + k;
+    }
+    if (WITH_SUM) {
+        const float m = acc.m;
+        acc.s += (bd_exp2((v.x - m) * BD_LOG2E) + bd_exp2((v.y - m) * BD_LOG2E)) +
+                 (bd_exp2((v.z - m) * BD_LOG2E) + bd_exp2((v.w - m) * BD_LOG2E));
+    }
 }
 
 template <bool VERIFY>
@@ -112,18 +133,31 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
             const int beg = (int)((long long)V4 * c / cpr);
             const int end = (int)((long long)V4 * (c + 1) / cpr);
             const float4 *x4 = reinterpret_cast<const float4 *>(x);
-            for (int u0 = beg; u0 < end; u0 += NT * kBatch) {
-                float4 v[kBatch];
+            // Two batches of kBatch / 2 loads per thread alternate: the next
+            // batch is in flight while the current one is reduced.
+            constexpr int HB = kBatch / 2;
+            constexpr int STEP = NT * HB;
+            float4 va[HB], vb[HB];
+            auto load = [&](float4(&v)[HB], int u0) __attribute__((always_inline)) {
 #pragma unroll
-                for (int k = 0; k < kBatch; ++k) {
+                for (int k = 0; k < HB; ++k) {
                     const int u = u0 + k * NT + tid;
                     if (u < end) v[k] = x4[u];
                 }
+            };
+            auto reduce = [&](const float4(&v)[HB], int u0) __attribute__((always_inline)) {
 #pragma unroll
-                for (int k = 0; k < kBatch; ++k) {
+                for (int k = 0; k < HB; ++k) {
                     const int u = u0 + k * NT + tid;
                     if (u < end) push4<!VERIFY>(acc, v[k], 4 * u);
                 }
+            };
+            load(va, beg);
+            for (int u0 = beg; u0 < end; u0 += 2 * STEP) {
+                if (u0 + STEP < end) load(vb, u0 + STEP);
+                reduce(va, u0);
+                if (u0 + 2 * STEP < end) load(va, u0 + 2 * STEP);
+                if (u0 + STEP < end) reduce(vb, u0 + STEP);
             }
         } else {
             const int beg = (int)((long long)p.V * c / cpr);
@@ -156,7 +190,16 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
             bd_coherent_store(p.part_i + o, t.i);
         }
         bd_wait_all_memory();  // the partial (and this workgroup's flag reads) precede the ticket
-        s_done = bd_ticket(&p.req_cnt[r]) == p.G - 1;
+        const int grp = b / kTicketGroup;
+        const int gsize = min(kTicketGroup, p.G - grp * kTicketGroup);
+        int *gc = p.grp_cnt + ((size_t)r * p.NG + grp) * kCounterStride;
+        bool last = false;
+        if (bd_ticket(gc) == gsize - 1) {
+            bd_coherent_store(gc, 0);  // every ticket of the group is taken: reset for the next call
+            // one group: its last workgroup is the request's last
+            last = p.NG == 1 || bd_ticket(p.req_cnt + (size_t)r * kCounterStride) == p.NG - 1;
+        }
+        s_done = last;
     }
     __syncthreads();
     if (!s_done) return;
@@ -215,7 +258,7 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         if (lane < p.D && p.argmax) p.argmax[ob + lane] = a;
         if (lane == 0) {
             p.accepted_len[r] = bb ? (__ffsll((long long)bb) - 1) : p.D;
-            bd_coherent_store(p.req_cnt + r, 0);
+            bd_coherent_store(p.req_cnt + (size_t)r * kCounterStride, 0);
         }
         return;
     }
@@ -225,7 +268,7 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
                                                  p.committed ? p.committed + ob : nullptr);
     if (lane == 0) {
         if (p.n_committed) p.n_committed[r] = __popcll(tb);
-        bd_coherent_store(p.req_cnt + r, 0);
+        bd_coherent_store(p.req_cnt + (size_t)r * kCounterStride, 0);
     }
 }
 
@@ -243,12 +286,14 @@ RowParams make_params(const RowPlan &pl, const RowArgs &a) {
     char *ws = (char *)a.ws;
     p.part_ms = (float2 *)(ws + pl.part_off);
     p.part_i = (int *)(ws + pl.idx_off);
+    p.grp_cnt = (int *)(ws + pl.grp_off);
     p.req_cnt = (int *)(ws + pl.cnt_off);
     p.n_req = a.n_req;
     p.D = a.D;
     p.V = a.V;
     p.S = a.S;
     p.G = pl.groups;
+    p.NG = (pl.groups + kTicketGroup - 1) / kTicketGroup;
     p.max_cpr = pl.max_cpr;
     p.tau = a.tau;
     return p;
@@ -277,7 +322,9 @@ RowPlan plan_rows(int n_req, int D, int V) {
     };
     pl.part_off = take((size_t)n_req * pl.groups * 8);
     pl.idx_off = take((size_t)n_req * pl.groups * 4);
-    pl.cnt_off = take((size_t)n_req * 4);
+    const int ng = (pl.groups + kTicketGroup - 1) / kTicketGroup;
+    pl.grp_off = take((size_t)n_req * ng * kCounterStride * 4);
+    pl.cnt_off = take((size_t)n_req * kCounterStride * 4);
     pl.ws_bytes = off;
     return pl;
 }
