@@ -70,6 +70,7 @@ typedef int32_t bd_status;
 #define BD_E_PARAM 4     /* unknown mode, S < 1, NaN tau or scale, ... */
 #define BD_E_WORKSPACE 5 /* workspace missing or too small */
 #define BD_E_LAUNCH 6    /* the HIP runtime rejected a launch */
+#define BD_E_SCRATCH 7   /* bd_attn_step_noalloc: the call needs more than its fixed scratch */
 
 enum { BD_F32 = 0, BD_BF16 = 1, BD_FP8KV = 2 };
 enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1, BD_BLOCK_QUAD = 2 };
@@ -128,6 +129,29 @@ bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_bl
                        const void *v_blk, const void *k_cache, const void *v_cache,
                        const int32_t *prefix_len, void *out, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* bd_attn_step for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments, results and errors as bd_attn_step (BD_F32 / BD_BF16,
+ * every mode), with no workspace argument.  The split-K exchange goes through
+ * a fixed device array of BD_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * nothing and calls no allocating routine.
+ *  - A call whose workspace (bd_attn_workspace_bytes) exceeds that size
+ *    returns BD_E_SCRATCH before anything is launched.
+ *  - The array's address on a device is looked up on the first call on that
+ *    device (hipGetSymbolAddress); `stream` must belong to the current device
+ *    (BD_E_LAUNCH otherwise).  Nothing in the array needs to start at zero.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap in time
+ *    on one GPU (on different streams, or from different threads) race and
+ *    give wrong results.  Calls in order on one stream are safe. */
+#define BD_NOALLOC_SCRATCH_BYTES (64u << 20)
+bd_status bd_attn_step_noalloc(const bd_attn_desc *desc, const void *q, const void *k_blk,
+                               const void *v_blk, const void *k_cache, const void *v_cache,
+                               const int32_t *prefix_len, void *out, void *stream);
+
+/* BD_NOALLOC_SCRATCH_BYTES, as the library was built. */
+size_t bd_attn_noalloc_max_scratch_bytes(void);
 
 /* Block attention over an FP8 KV cache (desc->dtype == BD_FP8KV).  The same
  * operation, masks and layouts as bd_attn_step (for BD_FP8KV,

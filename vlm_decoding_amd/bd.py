@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbd.so")
 
-BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH = range(7)
+BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH, BD_E_SCRATCH = range(8)
 BD_F32, BD_BF16, BD_FP8KV = 0, 1, 2
 BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL, BD_BLOCK_QUAD = 0, 1, 2
 SIZE_MAX = (1 << 64) - 1
@@ -78,6 +78,8 @@ def _load():
         "bd_attn_workspace_bytes": (sz, [AD]),
         "bd_attn_step": (i32, [AD, P, P, P, P, P, P, P, P, sz, P]),
         "bd_attn_step_fp8kv": (i32, [AD, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "bd_attn_step_noalloc": (i32, [AD, P, P, P, P, P, P, P, P]),
+        "bd_attn_noalloc_max_scratch_bytes": (sz, []),
         "bd_commit_workspace_bytes": (sz, [CD]),
         "bd_confidence_commit": (i32, [CD, P, P, P, P, P, P, P, P, sz, P]),
         "bd_verify_workspace_bytes": (sz, [i32, i32, i32]),
@@ -141,6 +143,12 @@ def bd_attn_step(desc, q, k_blk, v_blk, k_cache, v_cache, prefix_len, out, works
     _check("bd_attn_step", lib.bd_attn_step(
         ctypes.byref(desc), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache),
         _ptr(prefix_len), _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def bd_attn_step_noalloc(desc, q, k_blk, v_blk, k_cache, v_cache, prefix_len, out, stream=None):
+    _check("bd_attn_step_noalloc", lib.bd_attn_step_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+        _ptr(out), _stream(stream)))
 
 
 def bd_attn_step_fp8kv(desc, q, k_blk, v_blk, k_cache, v_cache, k_scale, v_scale, prefix_len, out,

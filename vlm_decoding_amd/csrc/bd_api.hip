@@ -5,9 +5,15 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/bd.h"
 #include "bd_internal.h"
+
+// Fixed device memory of bd_attn_step_noalloc: the split-K exchange of one
+// call at a time per GPU.  Every GPU the library runs on holds its own copy
+// (64 MiB) until the process ends.
+static __device__ __align__(256) unsigned char scratch[BD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -89,6 +95,35 @@ bd_status launched(hipError_t e) {
     return BD_OK;
 }
 
+// Device address of the current device's copy of `scratch`, looked up once per
+// device.  In host code `scratch` names a host-side stand-in; only this address
+// may be handed to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (stream) {
+        hipDevice_t sdev = 0;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return e;
+        if (sdev != dev) return hipErrorInvalidDevice;  // the stream must belong to the current device
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,6 +182,30 @@ bd_status bd_attn_step(const bd_attn_desc *desc, const void *q, const void *k_bl
     return attn_common(desc, q, k_blk, v_blk, k_cache, v_cache, nullptr, nullptr, prefix_len, out, workspace,
                        workspace_bytes, stream);
 }
+
+bd_status bd_attn_step_noalloc(const bd_attn_desc *desc, const void *q, const void *k_blk, const void *v_blk,
+                               const void *k_cache, const void *v_cache, const int32_t *prefix_len, void *out,
+                               void *stream) {
+    bd_status st = check_attn_desc(desc);
+    if (st != BD_OK) return st;
+    if (desc->dtype == BD_FP8KV) return BD_E_DTYPE;
+    if (!q || !k_blk || !v_blk || !k_cache || !v_cache || !prefix_len || !out) return BD_E_NULL;
+    if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out))
+        return BD_E_PARAM;
+    const bd::AttnPlan pl = bd::plan_attention(desc->n_items, block_slots(desc), desc->Hq, desc->Hkv, desc->d,
+                                               desc->dtype, desc->max_prefix);
+    if (pl.ws_bytes > BD_NOALLOC_SCRATCH_BYTES) return BD_E_SCRATCH;
+    void *ws = nullptr;
+    if (pl.ws_bytes > 0) {
+        const hipError_t e = scratch_address((hipStream_t)stream, &ws);
+        if (e != hipSuccess) return launched(e);
+    }
+    return attn_common(desc, q, k_blk, v_blk, k_cache, v_cache, nullptr, nullptr, prefix_len, out, ws,
+                       BD_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+size_t bd_attn_noalloc_max_scratch_bytes(void) { return BD_NOALLOC_SCRATCH_BYTES; }
 
 bd_status bd_attn_step_fp8kv(const bd_attn_desc *desc, const void *q, const void *k_blk, const void *v_blk,
                              const void *k_cache, const void *v_cache, const float *k_scale,
@@ -293,6 +352,7 @@ const char *bd_status_string(bd_status s) {
         case BD_E_PARAM: return "invalid parameter (mode, S, tau, scale or alignment)";
         case BD_E_WORKSPACE: return "workspace missing, misaligned or too small";
         case BD_E_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case BD_E_SCRATCH: return "the call needs more than the fixed device scratch of bd_attn_step_noalloc";
         default: return "unknown status";
     }
 }
