@@ -81,7 +81,7 @@ struct LhPlan {
     int tiles_per_wave;
     int G;               // workgroups
     size_t lds;          // dynamic LDS: the hidden states, 16 rows of H + 8
-    size_t ms_off, i_off, cnt_off, ws_bytes;
+    size_t ms_off, i_off, grp_off, cnt_off, ws_bytes;
     bool ok;             // G within the finisher's reach
 };
 LhPlan plan_lmhead(int n_req, int D, int V, int H);

@@ -20,7 +20,7 @@
 // steps); the hidden states sit in LDS (rows padded by 16 bytes, so the 16
 // rows of one MFMA operand fall in distinct banks).  The
 // workgroup's per-slot partials go out with write-through stores; the last
-// workgroup (one ticket) merges them in workgroup order and commits.  No float
+// workgroup (two levels of tickets) merges them in workgroup order and commits.  No float
 // atomics: results are identical run to run.
 #include "bd_common.h"
 #include "bd_internal.h"
@@ -34,6 +34,11 @@ constexpr int LH_SLOTS = 16;    // MFMA N dimension (slots, zero-padded)
 constexpr int LH_BLK = 256;     // hidden columns per pipeline step (eight MFMAs)
 constexpr int LH_RING = 4;      // register ring: loads run LH_RING - 1 steps ahead
 constexpr int LH_LPS = LH_BLK / 32;  // 16-byte loads (and MFMAs) per lane and step
+// Tickets on one address are served one after another (about 10 ns each), so
+// workgroups ticket a counter per group of kLhTicketGroup and the last of a
+// group tickets the call; each counter has a 256-byte line of its own.
+constexpr int kLhTicketGroup = 16;
+constexpr int kLhCounterStride = 64;
 
 struct LhParams {
     const uint16_t *hidden, *weight;
@@ -45,8 +50,9 @@ struct LhParams {
     int32_t *n_committed;
     float2 *part_ms;  // [G][16] (max, sum)
     int *part_i;      // [G][16] first argmax
-    int *cnt;         // ticket
-    int n_req, D, R, V, H, S, tiles, tiles_per_wave, G;
+    int *grp_cnt;     // [NG] first-level tickets, kLhCounterStride ints apart
+    int *cnt;         // second-level ticket
+    int n_req, D, R, V, H, S, tiles, tiles_per_wave, G, NG;
     float tau;
 };
 
@@ -152,7 +158,17 @@ __global__ __launch_bounds__(LH_NT, 2) void lmhead_kernel(LhParams p) {
     }
     bd_wait_all_memory();
     __syncthreads();
-    if (tid == 0) s_done = bd_ticket(p.cnt) == p.G - 1;
+    if (tid == 0) {
+        const int grp = blockIdx.x / kLhTicketGroup;
+        const int gsize = min(kLhTicketGroup, p.G - grp * kLhTicketGroup);
+        int *gc = p.grp_cnt + (size_t)grp * kLhCounterStride;
+        bool last = false;
+        if (bd_ticket(gc) == gsize - 1) {
+            bd_coherent_store(gc, 0);  // every ticket of the group is taken: reset for the next call
+            last = p.NG == 1 || bd_ticket(p.cnt) == p.NG - 1;
+        }
+        s_done = last;
+    }
     __syncthreads();
     if (!s_done) return;
 
@@ -222,6 +238,7 @@ LhPlan plan_lmhead(int n_req, int D, int V, int H) {
     };
     pl.ms_off = take(sizeof(float) * 2 * LH_SLOTS * (size_t)pl.G);
     pl.i_off = take(sizeof(int) * LH_SLOTS * (size_t)pl.G);
+    pl.grp_off = take(sizeof(int) * kLhCounterStride * (size_t)((pl.G + kLhTicketGroup - 1) / kLhTicketGroup));
     pl.cnt_off = take(sizeof(int));
     pl.ws_bytes = off;
     pl.ok = pl.G <= 512;
@@ -241,6 +258,7 @@ hipError_t launch_lmhead(const LhPlan &pl, const LhArgs &a, hipStream_t s) {
     char *ws = (char *)a.ws;
     p.part_ms = (float2 *)(ws + pl.ms_off);
     p.part_i = (int *)(ws + pl.i_off);
+    p.grp_cnt = (int *)(ws + pl.grp_off);
     p.cnt = (int *)(ws + pl.cnt_off);
     p.n_req = a.n_req;
     p.D = a.D;
@@ -251,6 +269,7 @@ hipError_t launch_lmhead(const LhPlan &pl, const LhArgs &a, hipStream_t s) {
     p.tiles = pl.tiles;
     p.tiles_per_wave = pl.tiles_per_wave;
     p.G = pl.G;
+    p.NG = (pl.G + kLhTicketGroup - 1) / kLhTicketGroup;
     p.tau = a.tau;
     if (pl.lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute((const void *)lmhead_kernel,

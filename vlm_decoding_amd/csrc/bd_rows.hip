@@ -344,13 +344,21 @@ hipError_t launch_spec_verify(const RowPlan &pl, const RowArgs &a, hipStream_t s
 // ---------------------------------------------------------------------------
 // KV append (Fast-dVLM write-up, section 5.3: crop the cache to the accepted
 // prefix; DiffusionVL notes: a finished block joins the history cache).
-// One workgroup per item; the prefix length is read on the device, so no
-// host round trip is needed between verify and append.
+// One workgroup per item, so the prefix length it reads and advances has a
+// single reader and writer; no host round trip is needed between verify and
+// append.  Keys are copied token by token (the d elements of a token are
+// contiguous on both sides); values go into the d-major cache with the L
+// accepted positions of each (head, d) row contiguous, so both writes are
+// runs of consecutive addresses.  The host bounds S * Hkv * d by 2^30, so the
+// element indices fit 32 bits.
 // ---------------------------------------------------------------------------
+constexpr int kAppendThreads = 512;
+
 template <typename E>
-__global__ __launch_bounds__(256) void kv_append_kernel(int D, int S, int Hkv, int d, int cap, E *k_cache, E *v_cache,
-                                                        int32_t *prefix, const E *k_blk, const E *v_blk,
-                                                        const int32_t *n_accept, int32_t *dev_err) {
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(int D, int S, int Hkv, int d, int cap, E *k_cache,
+                                                                   E *v_cache, int32_t *prefix, const E *k_blk,
+                                                                   const E *v_blk, const int32_t *n_accept,
+                                                                   int32_t *dev_err) {
     const int it = blockIdx.x;
     const int P = prefix[it];
     const int L = n_accept ? n_accept[it] : D;
@@ -358,16 +366,20 @@ __global__ __launch_bounds__(256) void kv_append_kernel(int D, int S, int Hkv, i
         if (threadIdx.x == 0 && dev_err) *dev_err = 1;
         return;
     }
-    const long long per_t = (long long)Hkv * d;
-    for (long long e = threadIdx.x; e < L * per_t; e += blockDim.x) {
-        const int t = (int)(e / per_t);
-        const int g = (int)((e / d) % Hkv);
-        const int dd = (int)(e % d);
-        const size_t src = (((size_t)it * S + t) * Hkv + g) * d + dd;
-        k_cache[(((size_t)it * Hkv + g) * cap + (P + t)) * d + dd] = k_blk[src];
-        v_cache[(((size_t)it * Hkv + g) * d + dd) * cap + (P + t)] = v_blk[src];
+    const int per_g = L * d;    // elements of one KV head
+    const int n = per_g * Hkv;  // <= 2^30
+    const E *kb = k_blk + (size_t)it * S * Hkv * d;
+    const E *vb = v_blk + (size_t)it * S * Hkv * d;
+    E *kc = k_cache + (size_t)it * Hkv * cap * d;
+    E *vc = v_cache + (size_t)it * Hkv * d * cap;
+    for (int e = threadIdx.x; e < n; e += kAppendThreads) {
+        const int g = e / per_g, r = e - g * per_g;
+        const int t = r / d, dd = r - t * d;  // keys: dd fastest
+        kc[((size_t)g * cap + P + t) * d + dd] = kb[((size_t)t * Hkv + g) * d + dd];
+        const int dv = r / L, tv = r - dv * L;  // values: t fastest
+        vc[((size_t)g * d + dv) * cap + P + tv] = vb[((size_t)tv * Hkv + g) * d + dv];
     }
-    __syncthreads();
+    __syncthreads();  // every thread has read P
     if (threadIdx.x == 0) prefix[it] = P + L;
 }
 
@@ -375,15 +387,15 @@ hipError_t launch_kv_append(int n, int D, int S, int Hkv, int d, int cap, int el
                             int32_t *prefix, const void *k_blk, const void *v_blk, const int32_t *n_accept,
                             int32_t *dev_err, hipStream_t s) {
     if (elem_bytes == 4)
-        hipLaunchKernelGGL((kv_append_kernel<uint32_t>), dim3(n), dim3(256), 0, s, D, S, Hkv, d, cap,
+        hipLaunchKernelGGL((kv_append_kernel<uint32_t>), dim3(n), dim3(kAppendThreads), 0, s, D, S, Hkv, d, cap,
                            (uint32_t *)k_cache, (uint32_t *)v_cache, prefix, (const uint32_t *)k_blk,
                            (const uint32_t *)v_blk, n_accept, dev_err);
     else if (elem_bytes == 2)
-        hipLaunchKernelGGL((kv_append_kernel<uint16_t>), dim3(n), dim3(256), 0, s, D, S, Hkv, d, cap,
+        hipLaunchKernelGGL((kv_append_kernel<uint16_t>), dim3(n), dim3(kAppendThreads), 0, s, D, S, Hkv, d, cap,
                            (uint16_t *)k_cache, (uint16_t *)v_cache, prefix, (const uint16_t *)k_blk,
                            (const uint16_t *)v_blk, n_accept, dev_err);
     else
-        hipLaunchKernelGGL((kv_append_kernel<uint8_t>), dim3(n), dim3(256), 0, s, D, S, Hkv, d, cap,
+        hipLaunchKernelGGL((kv_append_kernel<uint8_t>), dim3(n), dim3(kAppendThreads), 0, s, D, S, Hkv, d, cap,
                            (uint8_t *)k_cache, (uint8_t *)v_cache, prefix, (const uint8_t *)k_blk,
                            (const uint8_t *)v_blk, n_accept, dev_err);
     return hipGetLastError();
