@@ -61,11 +61,17 @@ __device__ __forceinline__ bool bd_wave_any(bool p) {
 }
 
 // Cross-workgroup hand-off without whole-cache maintenance.  Partial results
-// are written with agent-scope relaxed atomic stores (write-through, "sc1")
-// and read back with agent-scope relaxed atomic loads (coherent reads).  The
-// writer waits for its stores to complete (s_waitcnt 0) before the workgroup
-// takes its ticket, so a device-scope fence (which would write back and
-// invalidate the whole L2) is never needed.
+// are written with agent-scope relaxed atomic stores, which gfx950 performs
+// at the agent's coherence point (through the L2, not kept only in one XCD's
+// L2), and read back with agent-scope relaxed atomic loads, which read from
+// that point.  The writer waits until its stores are acknowledged
+// (s_waitcnt 0) before its workgroup takes a ticket, and the ticket is an
+// agent-scope atomic performed at the same point.  The workgroup whose ticket
+// completes the count therefore comes after every other workgroup's ticket,
+// each of which came after that workgroup's stores had completed; its
+// coherent loads, issued after it has seen the count, observe them.  Only the
+// hand-off locations need ordering, so no release / acquire fence (which on
+// gfx950 writes back or invalidates the whole L2 at agent scope) is used.
 __device__ __forceinline__ void bd_coherent_store2(float *p, float a, float b) {
     const uint64_t v = ((uint64_t)__float_as_uint(b) << 32) | (uint64_t)__float_as_uint(a);
     __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -110,8 +116,14 @@ __device__ __forceinline__ void bd_store_nt(void *p, uint2 v) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2 *>(p));
 }
-// Wait until every memory operation this thread issued has completed.
-__device__ __forceinline__ void bd_wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// Wait until every memory operation this thread issued has completed (for a
+// store: acknowledged by the memory side).  The empty asm statements keep the
+// compiler from moving any memory access across the wait.
+__device__ __forceinline__ void bd_wait_all_memory() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+}
 // Relaxed agent-scope ticket: returns the previous count.
 __device__ __forceinline__ int bd_ticket(int *counter) {
     return __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
