@@ -337,15 +337,16 @@ def commit_call(ds, masked_ptr=None, tokens_ptr=None):
              ds.n_committed.data_ptr(), ds.commit_ws.data_ptr(), ds.commit_ws.numel(), ds.stream_handle))
 
 
-def leg_denoise_config(torch, stream, flush, cfg, iters):
+def leg_denoise_config(torch, stream, flush, cfg, iters, balanced=False):
     """One denoise step (attention + confidence/commit) of a configuration, timed
     cold: each iteration follows an untimed 1 GiB flush and starts from the
-    initial block state."""
+    initial block state.  ``balanced`` marks the batch as ragged (the attention
+    plan then balances key splits across items from their prefix lengths)."""
     import synth
     from vlm_decoding_amd.step import DeviceStep
     st = synth.config_step(cfg)
     p = st["params"]
-    ds = DeviceStep(st)
+    ds = DeviceStep(st, balanced=balanced)
     ds.stream_handle = stream.cuda_stream
     ms = timed_calls(torch, stream, lambda i: [attn_call(ds), commit_call(ds)], iters, flush=flush,
                      before=lambda i: ds.reset_block_state())
@@ -354,7 +355,8 @@ def leg_denoise_config(torch, stream, flush, cfg, iters):
     total = a_b + l_b + s_b
     dist = dist_us(ms)
     med_s = dist["median"] * 1e-6
-    out = dict(workload=p["name"], step_us=dist, steps_per_s=round(1.0 / med_s, 1), algorithmic_bytes=total,
+    out = dict(workload=p["name"] + (", ragged-batch plan (BD_PLAN_BALANCED)" if balanced else ""), step_us=dist,
+               steps_per_s=round(1.0 / med_s, 1), algorithmic_bytes=total,
                attn_bytes=a_b, logits_bytes=l_b, achieved_gbps=round(total / med_s / 1e9, 1),
                frac=round(total / med_s / 1e9 / HBM_PEAK_GBS, 4), timing="cold: 1 GiB flush read before each step")
     del ds
@@ -763,7 +765,8 @@ def main():
     if args.config_iters > 0:
         configs = {"cfg2_3b_single_layer": leg_denoise_config(torch, stream, flush, 2, args.config_iters),
                    "cfg4_3b_verify_chain": leg_verify_chain(torch, stream, flush, args.config_iters),
-                   "cfg5_7b_batched": leg_denoise_config(torch, stream, flush, 5, args.config_iters)}
+                   "cfg5_7b_batched": leg_denoise_config(torch, stream, flush, 5, args.config_iters, balanced=True),
+                   "cfg5_7b_batched_plain_plan": leg_denoise_config(torch, stream, flush, 5, args.config_iters)}
     del flush
 
     layer_serial = (bench_layer_serial(torch, stream, sets, steps=args.layer_serial_steps)

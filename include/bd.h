@@ -74,6 +74,16 @@ typedef int32_t bd_status;
 
 enum { BD_F32 = 0, BD_BF16 = 1, BD_FP8KV = 2 };
 enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1, BD_BLOCK_QUAD = 2 };
+/* Plan flag, or-ed into bd_attn_desc.mode: the batch is ragged (items with
+ * different prefix lengths).  With at most 64 items, bd_attn_step then sizes
+ * each item's key splits from the device-side prefix lengths, so that every
+ * split of the call carries about the same number of keys; otherwise the
+ * split plan follows max_prefix alone (a short item then gets few splits and
+ * part of the GPU idles while the long ones finish).  Same results within the
+ * bf16 bar (the splits, hence the rounding of the exchange, differ); results
+ * still do not depend on scheduling.  Ignored beyond 64 items, by the vector
+ * (BD_F32) path and by bd_kv_append. */
+#define BD_PLAN_BALANCED 0x100
 
 /* Shape of one block-attention call.
  *  n_items    independent (request, layer) items, >= 1
@@ -83,7 +93,7 @@ enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1, BD_BLOCK_QUAD = 2 };
  *  cap        cache capacity in tokens, a multiple of 8 (of 16 for BD_FP8KV)
  *  dtype      BD_BF16 (MFMA path), BD_F32 (vector path) or BD_FP8KV (bf16
  *             queries and outputs, E4M3 keys and values: bd_attn_step_fp8kv)
- *  mode       BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL or BD_BLOCK_QUAD
+ *  mode       BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL or BD_BLOCK_QUAD, optionally | BD_PLAN_BALANCED
  *  max_prefix host-side upper bound of every prefix_len[i], 0..cap; sizes the grid
  *  scale      softmax scale (normally 1/sqrt(d)); finite and > 0
  * Size limits (BD_E_SHAPE otherwise), with S = block slots per item (D, or

@@ -66,6 +66,29 @@ def test_attn_validation(bd, kw, code):
     assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
 
 
+def test_balanced_plan_flag(bd):
+    """BD_PLAN_BALANCED is a flag on the mode: accepted with every mask mode, other
+    high bits refused; with it a ragged batch of up to 64 items may use more
+    split slots per unit (a larger workspace), never fewer."""
+    fake = 1 << 20
+    for mode in (0, 1, 2):
+        plain = _attn(bd, n_items=8, mode=mode, D=8 if mode == 2 else 16)
+        flagged = _attn(bd, n_items=8, mode=mode | bd.BD_PLAN_BALANCED, D=8 if mode == 2 else 16)
+        a, b = bd.bd_attn_workspace_bytes(plain), bd.bd_attn_workspace_bytes(flagged)
+        assert a < bd.SIZE_MAX and a <= b < bd.SIZE_MAX, (mode, a, b)
+    for bad in (0x200, bd.BD_PLAN_BALANCED | 3, 0x101 | 0x400):
+        desc = _attn(bd, mode=bad)
+        assert bd.bd_attn_workspace_bytes(desc) == bd.SIZE_MAX
+        st = bd.lib.bd_attn_step(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 30, None)
+        assert st == bd.BD_E_PARAM
+    # the append reads the flagged descriptor's mask mode
+    desc = _attn(bd, mode=bd.BD_BLOCK_QUAD | bd.BD_PLAN_BALANCED, D=33)
+    assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_SHAPE
+    # beyond 64 items the flag is ignored: the plain plan's workspace
+    big_plain, big_flag = _attn(bd, n_items=65), _attn(bd, n_items=65, mode=bd.BD_PLAN_BALANCED)
+    assert bd.bd_attn_workspace_bytes(big_plain) == bd.bd_attn_workspace_bytes(big_flag)
+
+
 def test_attn_null_and_workspace_errors(bd):
     desc = _attn(bd)
     fake = 1 << 20

@@ -98,13 +98,13 @@ def _check_attention(got, ref, label):
     assert max(rels) <= ATTN_REL, (label, max(rels))
 
 
-def _run_attention(dev, step_np, mode=None, label=""):
-    ds = _ds(dev, step_np)
+def _run_attention(dev, step_np, mode=None, label="", balanced=False):
+    ds = _ds(dev, step_np, balanced=balanced)
     p = step_np["params"]
     mode = p["mode"] if mode is None else mode
-    _say("attention %s n=%d D=%d Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s" % (
+    _say("attention %s n=%d D=%d Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s balanced=%s" % (
         label, p["n_items"], p["D"], p["Hq"], p["Hkv"], p["d"], p["dtype"], mode,
-        np.unique(step_np["prefix"])[:8].tolist()))
+        np.unique(step_np["prefix"])[:8].tolist(), balanced))
     ds.attn(mode=mode)
     got = _out_host(dev, ds)
     ref = _reference(step_np, mode)
@@ -162,6 +162,57 @@ def test_attention_edge_cases(dev, label, ov, mode):
     _run_attention(dev, synth.make_step(p, seed=zlib.crc32(label.encode()) % 10000), mode=mode, label=label)
 
 
+# The balanced plan of ragged batches (BD_PLAN_BALANCED): every item's split
+# count comes from the device-side prefix lengths.  The 7B batch (8 ragged
+# items, 8-wave workgroups) in bf16 and over an E4M3 cache, the uniform 3B step
+# (the plan reduces to the plain one), and ragged edge cases in both modes.
+@pytest.mark.parametrize("cfg,dtype", [(5, BF16), (5, FP8KV), (3, BF16)])
+def test_attention_balanced_configs(dev, cfg, dtype):
+    _run_attention(dev, synth.config_step(cfg, dtype=dtype), label="balanced_cfg%d_dtype%d" % (cfg, dtype),
+                   balanced=True)
+
+
+BALANCED_CASES = [
+    ("P_ragged", dict(prefix=("list", [1, 63, 64, 65, 200, 511, 640, 1000]), n_items=8)),
+    ("P_ragged_wide", dict(prefix=("list", [0, 4096, 31, 2050, 17, 3000]), n_items=6)),
+    ("two_items_4133_9", dict(n_items=2, prefix=("list", [4133, 9]))),
+    ("G7_rows224", dict(Hq=28, Hkv=4, D=32, prefix=("list", [70, 2500, 900]), n_items=3)),
+    ("many_items_64", dict(n_items=64, prefix=("list", [(37 * i) % 700 for i in range(64)]))),
+    ("d64", dict(d=64, prefix=("list", [333, 1, 1500]), n_items=3)),
+    ("fp8_ragged", dict(dtype=FP8KV, prefix=("list", [0, 63, 64, 1000, 2049]), n_items=5)),
+]
+
+
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("label,ov", BALANCED_CASES, ids=[c[0] for c in BALANCED_CASES])
+def test_attention_balanced_edge_cases(dev, label, ov, mode):
+    base = dict(n_items=2, Hq=16, Hkv=2, d=128, dtype=BF16, D=16, n_masked=8, V=1000, plant=None)
+    base.update(ov)
+    p = synth.params_for(3, **base)
+    _run_attention(dev, synth.make_step(p, seed=zlib.crc32(("bal" + label).encode()) % 10000), mode=mode,
+                   label="balanced_" + label, balanced=True)
+
+
+def test_attention_balanced_deterministic_and_quad(dev):
+    """Repeated balanced calls are bitwise identical; the quadratic mode with ragged
+    prefixes under the balanced plan matches the oracle."""
+    torch = dev["torch"]
+    p = synth.params_for(5, n_items=4, prefix=("list", [300, 5000, 64, 2048]), V=1000, plant=None)
+    s = synth.make_step(p, seed=55)
+    ds = _ds(dev, s, balanced=True)
+    ds.attn()
+    torch.cuda.synchronize()
+    first = ds.out.clone()
+    for _ in range(3):
+        ds.out.zero_()
+        ds.attn()
+    torch.cuda.synchronize()
+    assert torch.equal(first, ds.out)
+    _check_attention(_out_host(dev, ds), _reference(s, p["mode"]), "balanced_7b_ragged")
+    q = dict(synth.QUAD_CONFIGS[2], B=16, n_items=4, prefix=("list", [0, 95, 96, 1200]))
+    _run_attention(dev, synth.make_quad_step(q, 66), label="balanced_quad_B16", balanced=True)
+
+
 # Few items with long prefixes: the plan gives such calls 32 or 64 splits per
 # unit (every workgroup on a CU of its own) and merges them with the 32-slot
 # merge instance or its two-split-wave form.  Ragged prefixes give units with
@@ -216,6 +267,7 @@ def _sweep_case(i):
         host_max = max(prefix) + (int(rng.integers(1, 700)) if rng.random() < 0.5 else 0)
         if n * Hq * D * (max(prefix) + D) * d <= 1.5e8:  # keeps the fp64 oracle within seconds
             break
+    balanced = bool(rng.random() < 0.5)  # drawn after the shape, so the shapes of the sweep stay put
     # the smallest capacity the ABI accepts: a multiple of 8 (16 for E4M3)
     al = 16 if dtype == FP8KV else 8
     p = dict(n_items=n, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, prefix=("list", prefix),
@@ -225,18 +277,18 @@ def _sweep_case(i):
     else:
         st = synth.make_step(synth.params_for(3, D=D, mode=mode, n_masked=D // 2, V=1000, plant=None, **p),
                              5000 + i)
-    return st, host_max
+    return st, host_max, balanced
 
 
 @pytest.mark.parametrize("i", range(N_SWEEP))
 def test_attention_random_sweep(dev, i):
-    st, host_max = _sweep_case(i)
+    st, host_max, balanced = _sweep_case(i)
     p = st["params"]
     label = "sweep%d" % i
-    _say("attention %s n=%d D=%d B=%s Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s max_prefix=%d cap=%d" % (
+    _say("attention %s n=%d D=%d B=%s Hq=%d Hkv=%d d=%d dtype=%d mode=%d prefix=%s max_prefix=%d cap=%d balanced=%s" % (
         label, p["n_items"], p["D"], p.get("B"), p["Hq"], p["Hkv"], p["d"], p["dtype"], p["mode"],
-        st["prefix"].tolist(), host_max, st["cap"]))
-    ds = _ds(dev, st, max_prefix=host_max)
+        st["prefix"].tolist(), host_max, st["cap"], balanced))
+    ds = _ds(dev, st, max_prefix=host_max, balanced=balanced)
     ds.attn()
     _check_attention(_out_host(dev, ds), _reference(st, p["mode"]), label)
 

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libbd.so")
 BD_OK, BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_WORKSPACE, BD_E_LAUNCH, BD_E_SCRATCH = range(8)
 BD_F32, BD_BF16, BD_FP8KV = 0, 1, 2
 BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL, BD_BLOCK_QUAD = 0, 1, 2
+BD_PLAN_BALANCED = 0x100
 SIZE_MAX = (1 << 64) - 1
 
 

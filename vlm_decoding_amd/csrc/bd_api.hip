@@ -21,8 +21,12 @@ thread_local int32_t g_last_hip_error = 0;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The mask mode without the plan flag.
+int mask_mode(const bd_attn_desc *d) { return d->mode & ~BD_PLAN_BALANCED; }
+bool balanced_hint(const bd_attn_desc *d) { return (d->mode & BD_PLAN_BALANCED) != 0; }
+
 // Block slots per item: D, or B (B + 3) / 2 for the quadratic mode (D = B).
-int block_slots(const bd_attn_desc *d) { return d->mode == BD_BLOCK_QUAD ? d->D * (d->D + 3) / 2 : d->D; }
+int block_slots(const bd_attn_desc *d) { return mask_mode(d) == BD_BLOCK_QUAD ? d->D * (d->D + 3) / 2 : d->D; }
 
 // Launch sizes stay within 32-bit grid and index arithmetic: at most
 // kMaxSplits workgroups per (item, KV head, 128-row block) on the MFMA path,
@@ -38,9 +42,10 @@ bool launch_fits(int64_t n, int64_t slots, int64_t Hq, int64_t Hkv) {
 bd_status check_attn_desc(const bd_attn_desc *d) {
     if (!d) return BD_E_NULL;
     if (d->dtype != BD_F32 && d->dtype != BD_BF16 && d->dtype != BD_FP8KV) return BD_E_DTYPE;
-    if (d->mode != BD_BLOCK_BIDIR && d->mode != BD_BLOCK_CAUSAL && d->mode != BD_BLOCK_QUAD) return BD_E_PARAM;
+    const int m = mask_mode(d);
+    if (m != BD_BLOCK_BIDIR && m != BD_BLOCK_CAUSAL && m != BD_BLOCK_QUAD) return BD_E_PARAM;
     if (!(d->scale > 0.f) || !isfinite(d->scale)) return BD_E_PARAM;
-    if (d->n_items < 1 || d->D < 1 || d->D > (d->mode == BD_BLOCK_QUAD ? 32 : 64)) return BD_E_SHAPE;
+    if (d->n_items < 1 || d->D < 1 || d->D > (m == BD_BLOCK_QUAD ? 32 : 64)) return BD_E_SHAPE;
     if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return BD_E_SHAPE;
     if (d->d != 64 && d->d != 128) return BD_E_SHAPE;
     if (d->cap < 1 || d->cap % (d->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
@@ -131,7 +136,7 @@ extern "C" {
 size_t bd_attn_workspace_bytes(const bd_attn_desc *desc) {
     if (check_attn_desc(desc) != BD_OK) return SIZE_MAX;
     const bd::AttnPlan pl = bd::plan_attention(desc->n_items, block_slots(desc), desc->Hq, desc->Hkv, desc->d,
-                                               desc->dtype, desc->max_prefix);
+                                               desc->dtype, desc->max_prefix, false, balanced_hint(desc));
     return pl.ws_bytes;
 }
 
@@ -141,7 +146,7 @@ bd_status attn_common(const bd_attn_desc *desc, const void *q, const void *k_blk
                       const int32_t *prefix_len, void *out, void *workspace, size_t workspace_bytes,
                       void *stream) {
     const bd::AttnPlan pl = bd::plan_attention(desc->n_items, block_slots(desc), desc->Hq, desc->Hkv, desc->d,
-                                               desc->dtype, desc->max_prefix);
+                                               desc->dtype, desc->max_prefix, false, balanced_hint(desc));
     if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
         return BD_E_WORKSPACE;
     bd::AttnArgs a{};
@@ -157,12 +162,12 @@ bd_status attn_common(const bd_attn_desc *desc, const void *q, const void *k_blk
     a.ws = workspace;
     a.n = desc->n_items;
     a.D = block_slots(desc);
-    a.B = desc->mode == BD_BLOCK_QUAD ? desc->D : 0;
+    a.B = mask_mode(desc) == BD_BLOCK_QUAD ? desc->D : 0;
     a.Hq = desc->Hq;
     a.Hkv = desc->Hkv;
     a.d = desc->d;
     a.cap = desc->cap;
-    a.mode = desc->mode;
+    a.mode = mask_mode(desc);
     a.scale = desc->scale;
     hipStream_t s = (hipStream_t)stream;
     return launched(pl.mfma ? bd::launch_attention_mfma(pl, a, s) : bd::launch_attention_vec(a, desc->dtype, s));
@@ -194,7 +199,7 @@ bd_status bd_attn_step_noalloc(const bd_attn_desc *desc, const void *q, const vo
         !aligned16(v_cache) || !aligned16(out))
         return BD_E_PARAM;
     const bd::AttnPlan pl = bd::plan_attention(desc->n_items, block_slots(desc), desc->Hq, desc->Hkv, desc->d,
-                                               desc->dtype, desc->max_prefix);
+                                               desc->dtype, desc->max_prefix, false, balanced_hint(desc));
     if (pl.ws_bytes > BD_NOALLOC_SCRATCH_BYTES) return BD_E_SCRATCH;
     void *ws = nullptr;
     if (pl.ws_bytes > 0) {
@@ -290,8 +295,9 @@ bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache, i
                        void *stream) {
     if (!desc) return BD_E_NULL;
     if (desc->dtype != BD_F32 && desc->dtype != BD_BF16 && desc->dtype != BD_FP8KV) return BD_E_DTYPE;
-    if (desc->mode != BD_BLOCK_BIDIR && desc->mode != BD_BLOCK_CAUSAL && desc->mode != BD_BLOCK_QUAD) return BD_E_PARAM;
-    if (desc->n_items < 1 || desc->D < 1 || desc->D > (desc->mode == BD_BLOCK_QUAD ? 32 : 64) || desc->Hkv < 1)
+    const int m = mask_mode(desc);
+    if (m != BD_BLOCK_BIDIR && m != BD_BLOCK_CAUSAL && m != BD_BLOCK_QUAD) return BD_E_PARAM;
+    if (desc->n_items < 1 || desc->D < 1 || desc->D > (m == BD_BLOCK_QUAD ? 32 : 64) || desc->Hkv < 1)
         return BD_E_SHAPE;
     if (desc->d != 64 && desc->d != 128) return BD_E_SHAPE;
     if (desc->cap < 1 || desc->cap % (desc->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;

@@ -46,6 +46,8 @@ struct MfmaParams {
     int n, D, Hq, Hkv, G, cap, mode;
     int B;  // quadratic mode: draft block size (D = B (B + 3) / 2 slots)
     int R, row_blocks, max_splits, tiles_per_split, total_logical;
+    int balanced;       // ragged-batch plan: split counts from the device-side prefix lengths
+    int balance_slots;  // ... workgroups the plan may use
     float c;  // scale * log2(e)
     // Two-stream (whole-sequence) mode: D = L = Lc + Ln positions per item, the
     // clean stream then the noisy stream; response spans (clean start, length).
@@ -149,13 +151,14 @@ __device__ __forceinline__ int unit_nsplit(int P, int D, int tiles_per_split, in
     const int work = nbulk + kTailCost * ntail;
     return max(1, min(min(max_splits, nbulk + 1), (work + tiles_per_split - 1) / tiles_per_split));
 }
+// The split of a unit with `nsplit` splits (1 <= nsplit <= nbulk + 1).
 template <int TK>
-__device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_split, int max_splits, int split) {
+__device__ __forceinline__ UnitSplit unit_split_n(int P, int D, int nsplit, int split) {
     UnitSplit u;
     const int nbulk = P / TK;
     const int ntail = ((P - nbulk * TK) + D + TK - 1) / TK;
     const int work = nbulk + kTailCost * ntail;
-    u.nsplit = unit_nsplit<TK>(P, D, tiles_per_split, max_splits);
+    u.nsplit = nsplit;
     const int nbs = u.nsplit - 1;                                      // bulk-only splits
     const int w = (work + u.nsplit - 1) / u.nsplit;                    // target work per split
     const int tail_bulk = nbs == 0 ? nbulk : max(0, nbulk - nbs * w);  // bulk tiles of the tail split
@@ -169,6 +172,83 @@ __device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_spli
         u.nb = tail_bulk;
     }
     return u;
+}
+template <int TK>
+__device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_split, int max_splits, int split) {
+    return unit_split_n<TK>(P, D, unit_nsplit<TK>(P, D, tiles_per_split, max_splits), split);
+}
+
+// Sum and max over the 64 lanes of a wave with DPP row operations and lane
+// swaps (no LDS round trip); every lane receives the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false); }
+__device__ __forceinline__ int wave_sum_i(int x) {
+    x += dpp_i<0xB1>(x);
+    x += dpp_i<0x4E>(x);
+    x += dpp_i<0x141>(x);
+    x += dpp_i<0x140>(x);
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = (int)(a[0] + a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return (int)(b[0] + b[1]);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+    x = max(x, dpp_i<0xB1>(x));
+    x = max(x, dpp_i<0x4E>(x));
+    x = max(x, dpp_i<0x141>(x));
+    x = max(x, dpp_i<0x140>(x));
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    x = max((int)a[0], (int)a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return max((int)b[0], (int)b[1]);
+}
+
+// Split plan of a ragged batch (items with different prefix lengths, at most
+// 64 of them: one lane per item).  Every unit of item i gets
+//   n_i = min(cap_i, ceil(work_i / T)) splits,   cap_i = min(max_splits, nbulk_i + 1),
+// with T the smallest whole number of tiles for which the splits of all units
+// fit `balance_slots` workgroups, so the longest split of the call is as short
+// as that many workgroups allow (a plan sized from the host's max_prefix gives
+// short items few splits and leaves CUs idle).  It depends only on the
+// prefix lengths, so every wave that computes it gets the same plan and the
+// results do not depend on scheduling.  Lane i returns n_i and the first
+// logical workgroup of item i's units (unit-major: units of item i, in order,
+// n_i splits each); `total` is the workgroup count.
+struct ItemPlan {
+    int nsplit, start, total;
+};
+template <int TK>
+__device__ __forceinline__ ItemPlan balanced_plan(const MfmaParams &p, int lane) {
+    const bool has = lane < p.n;
+    const int P = has ? min(max(p.prefix[lane], 0), p.cap) : 0;
+    const int nbulk = P / TK;
+    const int ntail = ((P - nbulk * TK) + p.D + TK - 1) / TK;
+    const int work = has ? nbulk + kTailCost * ntail : 0;
+    const int capi = min(p.max_splits, nbulk + 1);
+    const int upi = p.Hkv * p.row_blocks;  // units per item
+    // count(T) = upi * sum_i min(cap_i, ceil(work_i / T)) falls as T grows; at
+    // T = max work it is the unit count, which the host keeps <= balance_slots.
+    int lo = 1, hi = max(1, wave_max_i(work));
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const int c = has ? min(capi, (work + mid - 1) / mid) : 0;
+        if (wave_sum_i(c) * upi <= p.balance_slots)
+            hi = mid;
+        else
+            lo = mid + 1;
+    }
+    ItemPlan ip;
+    ip.nsplit = has ? min(capi, (work + lo - 1) / lo) : 0;
+    const int cnt = ip.nsplit * upi;
+    int incl = cnt;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    ip.start = incl - cnt;
+    ip.total = __shfl(incl, 63, 64);
+    return ip;
 }
 
 // 16-byte-unit XOR swizzles of the LDS tiles.  A tile row of U units shares
@@ -274,9 +354,26 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // XCD-aware decode: consecutive logical ids (the splits of one unit) share an XCD.
     const int nb = gridDim.x;
     const int logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
-    if (logical >= p.total_logical) return;
-    const int unit = logical / p.max_splits;
-    const int split = logical - unit * p.max_splits;
+    int unit, split, nsplit_b = 0;  // nsplit_b: the balanced plan's split count of this unit
+    if (!SEQ && p.balanced) {
+        const ItemPlan ip = balanced_plan<TK>(p, lane);
+        if (logical >= ip.total) return;  // the whole workgroup: every wave has the same plan
+        const int upi = p.Hkv * p.row_blocks;
+        const unsigned long long hit =
+            __builtin_amdgcn_ballot_w64(lane < p.n && logical >= ip.start && logical < ip.start + ip.nsplit * upi);
+        const int item = __builtin_ctzll(hit);
+        nsplit_b = __shfl(ip.nsplit, item, 64);
+        const int rloc = logical - __shfl(ip.start, item, 64);
+        const int uin = rloc / nsplit_b;
+        split = rloc - uin * nsplit_b;
+        unit = item * upi + uin;
+        // The merge kernel reads the count here instead of recomputing the plan.
+        if (split == 0 && tid == 0) p.unit_splits[unit] = nsplit_b;
+    } else {
+        if (logical >= p.total_logical) return;
+        unit = logical / p.max_splits;
+        split = logical - unit * p.max_splits;
+    }
     const int rb = unit % p.row_blocks;
     const int pair = unit / p.row_blocks;
     const int g = pair % p.Hkv;
@@ -355,7 +452,8 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     } else {
         // A prefix above the host's max_prefix widens the splits instead of
         // overrunning the workspace (at most max_splits per unit).
-        const UnitSplit us = unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
+        const UnitSplit us = p.balanced ? unit_split_n<TK>(P, p.D, nsplit_b, split)
+                                        : unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
         nsplit = us.nsplit;
         if (split >= nsplit) return;
         const bool is_tail = split == nsplit - 1;
@@ -765,12 +863,19 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
     const uint4 *wo = reinterpret_cast<const uint4 *>(p.ws_o);
     // Every workspace slot of the unit is requested before the prefix length
     // (which decides how many of them hold this call's partials) arrives;
-    // slots past the unit's split count are read but not used.
+    // slots past the unit's split count are read but not used.  A balanced
+    // plan (up to twice the average split count per unit) first reads the
+    // count that the unit's first split stored and requests only those slots.
+    int slots_to_load = p.max_splits, nsplit_b = 0;
+    if (!SEQ && p.balanced) {
+        nsplit_b = p.unit_splits[unit];
+        slots_to_load = nsplit_b;
+    }
     float2 ml[MAXS];
     uint4 v[QPT][MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
-        if (sw * MAXS + s < p.max_splits) {
+        if (sw * MAXS + s < slots_to_load) {
             ml[s] = p.ws_ml[(base + s) * NT_TILE + src_t];
 #pragma unroll
             for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t];
@@ -778,6 +883,8 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
     int nsplit;
     if constexpr (SEQ) {
         nsplit = p.unit_splits[unit];  // written by the unit's first split
+    } else if (p.balanced) {
+        nsplit = nsplit_b;
     } else {
         const int P = min(max(p.prefix[it], 0), p.cap);
         nsplit = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
@@ -948,7 +1055,7 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
 
 }  // namespace
 
-AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix, bool seq) {
+AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix, bool seq, bool balanced) {
     AttnPlan pl{};
     pl.seq = seq;
     pl.mfma = (dtype == 1 || dtype == 2);
@@ -989,6 +1096,15 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     const int ntail_max = (pl.tk - 1 + D + pl.tk - 1) / pl.tk;
     const int work_max = ntiles_max + kTailCost * ntail_max;
     pl.tiles_per_split = std::max(1, (work_max + pl.max_splits - 1) / pl.max_splits);
+    // Ragged batch (caller's hint): the device balances split counts across
+    // items from their prefix lengths, each unit getting up to twice the
+    // average (at most the cap above), within the same number of workgroups.
+    if (balanced && !seq && n <= kBalancedMaxItems && ntiles_max >= 1 && pl.units <= slots) {
+        pl.balanced = true;
+        pl.balance_slots = slots;
+        pl.max_splits = std::max(2, std::min(std::min(2 * want, cap), ntiles_max + 1));
+        pl.tiles_per_split = 1;  // unused: the device plan sets each unit's split count
+    }
     if (seq) {
         // Whole sequences of D positions: a unit has at most D / tk key tiles,
         // all streamed the same way; the split count only fills the GPU.
@@ -996,7 +1112,7 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
         pl.max_splits = std::max(1, std::min(std::min(want, nt), cap));
         pl.tiles_per_split = std::max(1, (nt + pl.max_splits - 1) / pl.max_splits);
     }
-    const long total = (long)pl.units * pl.max_splits;
+    const long total = pl.balanced ? (long)pl.balance_slots : (long)pl.units * pl.max_splits;
     pl.grid = (int)((total + 7) / 8 * 8);
     if (pl.max_splits > 1) {
         size_t off = 0;
@@ -1010,7 +1126,7 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
         const size_t lanes = (size_t)pl.units * pl.max_splits * pl.nw * 64;
         pl.ws_ml_off = take(sizeof(float) * 2 * lanes);
         pl.ws_o_off = take(sizeof(uint16_t) * (size_t)(d / 2) * lanes);
-        if (seq) pl.ws_splits_off = take(sizeof(int) * (size_t)pl.units);
+        if (seq || pl.balanced) pl.ws_splits_off = take(sizeof(int) * (size_t)pl.units);
         pl.ws_bytes = off;
     }
     return pl;
@@ -1057,7 +1173,7 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     char *ws = (char *)a.ws;
     p.ws_ml = pl.max_splits > 1 ? (float2 *)(ws + pl.ws_ml_off) : nullptr;
     p.ws_o = pl.max_splits > 1 ? (float *)(ws + pl.ws_o_off) : nullptr;
-    p.unit_splits = pl.max_splits > 1 && pl.seq ? (int *)(ws + pl.ws_splits_off) : nullptr;
+    p.unit_splits = pl.max_splits > 1 && (pl.seq || pl.balanced) ? (int *)(ws + pl.ws_splits_off) : nullptr;
     p.spans = a.spans;
     p.n_spans = a.n_spans;
     p.Lc = a.Lc;
@@ -1076,6 +1192,8 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.max_splits = pl.max_splits;
     p.tiles_per_split = pl.tiles_per_split;
     p.total_logical = pl.units * pl.max_splits;
+    p.balanced = pl.balanced ? 1 : 0;
+    p.balance_slots = pl.balance_slots;
     p.c = a.scale * BD_LOG2E;
     dim3 block(pl.nw * 64);
     const void *tile, *merge;

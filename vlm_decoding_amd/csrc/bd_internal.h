@@ -26,6 +26,8 @@ struct AttnPlan {
     int units;            // n_items * Hkv * row_blocks
     int tiles_per_split;
     int max_splits;
+    bool balanced;        // ragged-batch plan: split counts from the device-side prefix lengths
+    int balance_slots;    // ... workgroups it may use
     int grid;             // workgroups launched
     size_t ws_ml_off, ws_o_off, ws_splits_off, ws_bytes;
 };
@@ -44,7 +46,9 @@ struct AttnArgs {
     int Lc, max_spans, Dblk;
 };
 
-AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix, bool seq = false);
+constexpr int kBalancedMaxItems = 64;  // the balanced plan keeps one lane per item
+AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix, bool seq = false,
+                        bool balanced = false);
 hipError_t launch_attention_mfma(const AttnPlan &plan, const AttnArgs &a, hipStream_t s);
 hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s);
 

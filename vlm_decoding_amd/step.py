@@ -81,11 +81,12 @@ def to_host(t: torch.Tensor, like=None) -> np.ndarray:
 class DeviceStep:
     """One step's inputs resident in HBM, with outputs and workspaces."""
 
-    def __init__(self, step: dict, device="cuda", max_prefix=None, guard_bytes=0):
+    def __init__(self, step: dict, device="cuda", max_prefix=None, guard_bytes=0, balanced=False):
         """``max_prefix`` (default: the longest prefix of ``step``) is the host-side
         bound the attention plan is sized for; it must not exceed the cache capacity.
         ``guard_bytes`` > 0 puts canary bands of that size around every buffer the
-        library writes (see check_guards)."""
+        library writes (see check_guards).  ``balanced`` marks the batch as ragged
+        (BD_PLAN_BALANCED in the attention descriptor's mode)."""
         p = step["params"]
         self.gb = GuardedBuffers(device, guard_bytes)
         mk = self.gb.make
@@ -114,7 +115,9 @@ class DeviceStep:
         self.out = mk("out", self.q.shape, self.q.dtype, fill=POISON)
         # The quadratic mode's descriptor takes the draft block size B; its tensors hold D = B (B + 3) / 2 slots.
         d_desc = p["B"] if p["mode"] == bd.BD_BLOCK_QUAD else D
-        self.adesc = bd.attn_desc(n, d_desc, Hq, Hkv, d, self.cap, self.dtype, p["mode"], self.max_prefix)
+        self.plan_flag = bd.BD_PLAN_BALANCED if balanced else 0
+        self.adesc = bd.attn_desc(n, d_desc, Hq, Hkv, d, self.cap, self.dtype, p["mode"] | self.plan_flag,
+                                  self.max_prefix)
         self.cdesc = bd.commit_desc(p["n_req"], D, p["V"], p["S"], p["tau"])
         ab = bd.bd_attn_workspace_bytes(self.adesc)
         cb = bd.bd_commit_workspace_bytes(self.cdesc)
@@ -147,9 +150,9 @@ class DeviceStep:
 
     def attn(self, mode=None, stream=None):
         desc = self.adesc
-        if mode is not None and mode != desc.mode:
+        if mode is not None and (mode | self.plan_flag) != desc.mode:
             desc = bd.attn_desc(desc.n_items, desc.D, desc.Hq, desc.Hkv, desc.d, desc.cap, desc.dtype,
-                                mode, desc.max_prefix, desc.scale)
+                                mode | self.plan_flag, desc.max_prefix, desc.scale)
         if self.fp8kv:
             bd.bd_attn_step_fp8kv(desc, self.q, self.k_blk, self.v_blk, self.k_cache, self.v_cache, self.k_scale,
                                   self.v_scale, self.prefix, self.out, self.attn_ws, stream=stream)
