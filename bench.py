@@ -78,6 +78,7 @@ class HipEvents:
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventQuery.argtypes = [ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
@@ -88,6 +89,15 @@ class HipEvents:
     def record(self, i, stream_handle):
         if self.hip.hipEventRecord(self.ev[i], ctypes.c_void_p(stream_handle)) != 0:
             raise RuntimeError("hipEventRecord failed")
+
+    def wait(self, i):
+        """Poll event i until it has completed (hipErrorNotReady = 600 until then)."""
+        while True:
+            st = self.hip.hipEventQuery(self.ev[i])
+            if st == 0:
+                return
+            if st != 600:
+                raise RuntimeError("hipEventQuery failed (%d)" % st)
 
     def ms(self, i, j):
         f = ctypes.c_float()
@@ -728,8 +738,12 @@ def main():
         ev.record(3 * n + 2, sh)
     ev.record(outer + 1, sh)
     t_enq = time.perf_counter() - t0
-    torch.cuda.synchronize()
+    # The clock stops when the last event is seen complete by polling: a blocking
+    # synchronize wakes the host up to several ms late now and then, which would
+    # be timed as GPU work.
+    ev.wait(outer + 1)
     elapsed = time.perf_counter() - t0
+    torch.cuda.synchronize()
     if status:
         raise RuntimeError("a library call failed in the timed loop (status %d)" % status)
     attn_ms = [ev.ms(3 * n, 3 * n + 1) for n in range(len(sampled))]

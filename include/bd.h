@@ -46,7 +46,7 @@
  *    q, out     [n][D][Hq][d]        queries / outputs of every block slot
  *    k_blk,v_blk[n][D][Hkv][d]       this step's block keys / values
  *    k_cache    [n][Hkv][cap][d]     frozen keys of prompt and finished blocks
- *    v_cache    [n][Hkv][d][cap]     frozen values, stored d-major (transposed)
+ *    v_cache    [n][Hkv][cap][d]     frozen values of the same positions
  *    prefix_len int32[n]             valid cache length of each item (device)
  *    logits     f32[n_req][D][V]
  *    masked     u8[n_req][D]         1 = still [MASK]
@@ -90,7 +90,7 @@ enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1, BD_BLOCK_QUAD = 2 };
  *  D          block length, 1..64 (BD_BLOCK_QUAD: the draft block size B, 1..32)
  *  Hq, Hkv    query / KV heads, Hq % Hkv == 0; head h uses KV head h / (Hq/Hkv)
  *  d          head dim, 64 or 128
- *  cap        cache capacity in tokens, a multiple of 8 (of 16 for BD_FP8KV)
+ *  cap        cache capacity in tokens, >= 1
  *  dtype      BD_BF16 (MFMA path), BD_F32 (vector path) or BD_FP8KV (bf16
  *             queries and outputs, E4M3 keys and values: bd_attn_step_fp8kv)
  *  mode       BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL or BD_BLOCK_QUAD, optionally | BD_PLAN_BALANCED
@@ -171,8 +171,8 @@ size_t bd_attn_noalloc_max_scratch_bytes(void);
  *   key   = e4m3(k_cache or k_blk byte) * k_scale[i][g]
  *   value = e4m3(v_cache or v_blk byte) * v_scale[i][g]
  * for item i and KV head g.  q and out are bf16 [n][D][Hq][d].
- *   k_blk, v_blk   u8 [n][D][Hkv][d]      k_cache u8 [n][Hkv][cap][d]
- *   v_cache        u8 [n][Hkv][d][cap]    k_scale, v_scale f32 [n][Hkv] (device)
+ *   k_blk, v_blk   u8 [n][D][Hkv][d]      k_cache, v_cache u8 [n][Hkv][cap][d]
+ *   k_scale, v_scale f32 [n][Hkv] (device)
  * E4M3 values are widened to bf16 exactly; products and sums are fp32, the
  * attention weights bf16, as in bd_attn_step.  Every k_scale and v_scale
  * entry must be finite and > 0 (device values, not checked).
@@ -220,8 +220,8 @@ bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logit
  * prefix; [DV] a finished block joins the history cache).  Uses n_items, D, Hkv, d,
  * cap, dtype and mode of `desc`.  For item i with P = prefix_len[i] and
  * L = n_accept ? n_accept[i] : D (device values): cache slots P..P+L-1 receive block
- * slots 0..L-1 bit for bit (keys row-wise, values into the d-major layout) and
- * prefix_len[i] becomes P + L.  Nothing else is written.
+ * slots 0..L-1 bit for bit (one d-element row per slot and KV head, keys and
+ * values alike) and prefix_len[i] becomes P + L.  Nothing else is written.
  *  - BD_FP8KV: the E4M3 bytes are copied; they share the cache's per-(item, KV head)
  *    scales.
  *  - BD_BLOCK_QUAD: k_blk / v_blk hold B (B + 3) / 2 slots per item (the layout of
@@ -230,7 +230,8 @@ bd_status bd_spec_verify(int32_t n_req, int32_t D, int32_t V, const float *logit
  * (optional device int32) is set to 1.
  * Size limits (BD_E_SHAPE otherwise): cap * d <= 2^30 and, with S block slots
  * per item, S * Hkv * d <= 2^30.
- * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM, BD_E_LAUNCH. */
+ * Errors: BD_E_NULL, BD_E_SHAPE, BD_E_DTYPE, BD_E_PARAM (a pointer not 16-byte
+ * aligned), BD_E_LAUNCH. */
 bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache,
                        int32_t *prefix_len, const void *k_blk, const void *v_blk,
                        const int32_t *n_accept, int32_t *dev_err, void *stream);
@@ -297,8 +298,8 @@ size_t bd_two_stream_workspace_bytes(const bd_two_stream_desc *desc);
  *                            and the noisy tokens of its own block            (M_N2N)
  *   noisy positions past the last response see nothing and get 0;
  *   out = softmax(scale * q k^T) v over the visible keys.
- * Layouts (bf16, row-major): q, out [n_seq][L][Hq][d]; k [n_seq][Hkv][cap][d];
- * v [n_seq][Hkv][d][cap] (d-major, as the decode cache); spans int32
+ * Layouts (bf16, row-major): q, out [n_seq][L][Hq][d]; k, v [n_seq][Hkv][cap][d]
+ * (as the decode cache); spans int32
  * [n_seq][max_spans][2], n_spans int32 [n_seq] (device).  k and v positions
  * L..cap-1 are read (as parts of 32-key tiles) but never weighted; they must hold
  * finite values (zeros, say).  Span values out of range are clamped into the

@@ -95,7 +95,7 @@ def attention(q, k_blk, v_blk, k_cache, v_cache, prefix, mode, scale=None):
     el = np.float32 if dtype == F32 else np.uint16
     arrs = [_c(a, el) for a in (q, k_blk, v_blk, k_cache, v_cache)]
     assert k_blk.shape == (n, D, Hkv, d) and v_blk.shape == (n, D, Hkv, d)
-    assert k_cache.shape == (n, Hkv, cap, d) and v_cache.shape == (n, Hkv, d, cap)
+    assert k_cache.shape == (n, Hkv, cap, d) and v_cache.shape == (n, Hkv, cap, d)
     prefix = _c(prefix, np.int32)
     assert prefix.shape == (n,) and np.all(prefix >= 0) and np.all(prefix <= cap)
     if scale is None:
@@ -282,8 +282,8 @@ def two_stream_attention(q, k, v, spans, n_spans, Lc, D, scale=None):
     causal over the clean stream; a noisy query sees the clean positions before its
     block and its own block of the noisy stream (bidirectional), blocks of D tokens
     cut from each response's start and truncated at its end.
-    q [n][L][Hq][d] (L = Lc + Ln), k [n][Hkv][cap][d], v [n][Hkv][d][cap] (bf16 bits
-    or fp32), spans int32 [n][max_spans][2] = (clean start, length) of each response,
+    q [n][L][Hq][d] (L = Lc + Ln), k and v [n][Hkv][cap][d] (bf16 bits or fp32),
+    spans int32 [n][max_spans][2] = (clean start, length) of each response,
     n_spans int32 [n].  Returns float64 [n][L][Hq][d]."""
     lib = _load()
     n, L, Hq, d = q.shape

@@ -101,7 +101,7 @@ void bdo_set_num_threads(int n) {
  * o = sum_j w_j v_j / sum_j w_j,  w_j = exp(s_j - max s),  s_j = scale * <q, k_j>.
  *
  * Layouts: q [n][D][Hq][d], k_blk/v_blk [n][D][Hkv][d],
- * k_cache [n][Hkv][cap][d], v_cache [n][Hkv][d][cap] (transposed),
+ * k_cache and v_cache [n][Hkv][cap][d],
  * out [n][D][Hq][d] double.
  */
 static void attention_impl(int n, int D, int Hq, int Hkv, int d, int cap, int q_dtype, int kv_dtype,
@@ -239,7 +239,7 @@ static void attention_impl(int n, int D, int Hq, int Hkv, int d, int cap, int q_
                 if (s[j] == 0.0) continue;
                 double vv;
                 if (j < P)
-                    vv = widen(v_cache, kv_dtype, (((size_t)it * Hkv + g) * d + t) * (size_t)cap + j);
+                    vv = widen(v_cache, kv_dtype, (((size_t)it * Hkv + g) * cap + j) * (size_t)d + t);
                 else
                     vv = widen(v_blk, kv_dtype, (((size_t)it * D + (j - P)) * Hkv + g) * (size_t)d + t);
                 if (v_scale) vv *= (double)v_scale[(size_t)it * Hkv + g];
@@ -388,10 +388,9 @@ void bdo_kv_append(int n, int D, int Hkv, int d, int cap, int dtype, void *k_cac
             for (int g = 0; g < Hkv; ++g)
                 for (int e = 0; e < d; ++e) {
                     size_t src = (((size_t)it * D + t) * Hkv + g) * (size_t)d + e;
-                    size_t kdst = (((size_t)it * Hkv + g) * cap + (P + t)) * (size_t)d + e;
-                    size_t vdst = (((size_t)it * Hkv + g) * d + e) * (size_t)cap + (P + t);
-                    memcpy((char *)k_cache + kdst * es, (const char *)k_blk + src * es, es);
-                    memcpy((char *)v_cache + vdst * es, (const char *)v_blk + src * es, es);
+                    size_t dst = (((size_t)it * Hkv + g) * cap + (P + t)) * (size_t)d + e;
+                    memcpy((char *)k_cache + dst * es, (const char *)k_blk + src * es, es);
+                    memcpy((char *)v_cache + dst * es, (const char *)v_blk + src * es, es);
                 }
         prefix_len[it] = P + L;
     }
@@ -489,7 +488,7 @@ void bdo_fp8_e4m3_decode(int n, const uint8_t *b, double *out) {
  *   response see nothing and their output is 0.
  *
  * Layouts: q, out [n][L][Hq][d] with L = Lc + Ln (clean positions first);
- * k [n][Hkv][cap][d], v [n][Hkv][d][cap] over the same L positions;
+ * k and v [n][Hkv][cap][d] over the same L positions;
  * spans int32 [n][max_spans][2] = (c_r, len_r), n_spans int32 [n].
  */
 static int ts_noisy_block(const int32_t *sp, int ns, int D, int i, int *b0, int *b1, int *w0) {
@@ -551,7 +550,7 @@ void bdo_two_stream_attention(int n, int Lc, int Ln, int cap, int D, int Hq, int
         for (int t = 0; t < d; ++t) {
             double acc = 0.0;
             for (int j = 0; j < L; ++j)
-                if (s[j] != 0.0) acc += s[j] * widen(v, dtype, (((size_t)it * Hkv + g) * d + t) * (size_t)cap + j);
+                if (s[j] != 0.0) acc += s[j] * widen(v, dtype, (((size_t)it * Hkv + g) * cap + j) * (size_t)d + t);
             out[qoff + t] = denom > 0.0 ? acc / denom : 0.0;
         }
         free(s);

@@ -12,7 +12,7 @@ Layouts (row-major, innermost last):
     k_blk    [n][D][Hkv][d]       this step's block keys
     v_blk    [n][D][Hkv][d]       this step's block values
     k_cache  [n][Hkv][cap][d]     frozen keys of the prompt and finished blocks
-    v_cache  [n][Hkv][d][cap]     frozen values, stored transposed (d-major)
+    v_cache  [n][Hkv][cap][d]     frozen values
     prefix   int32[n]             valid cache length per item
     logits   f32 [n_req][D][V]
     masked   u8  [n_req][D]       1 = still [MASK]
@@ -113,14 +113,13 @@ def make_step(p: dict, seed: int, plant_L=None) -> dict:
 
     q = _normal(rng, (n, D, Hq, d), dtype)
     k_cache = np.full((n, Hkv, cap, d), nan, dtype=elem)
-    v_cache = np.full((n, Hkv, d, cap), nan, dtype=elem)
+    v_cache = np.full((n, Hkv, cap, d), nan, dtype=elem)
     for it in range(n):
         P = int(prefix[it])
         k_cache[it, :, :P, :] = _normal(rng, (Hkv, P, d), dtype)
     for it in range(n):
         P = int(prefix[it])
-        v_nat = _normal(rng, (Hkv, P, d), dtype)
-        v_cache[it, :, :, :P] = np.swapaxes(v_nat, 1, 2)
+        v_cache[it, :, :P, :] = _normal(rng, (Hkv, P, d), dtype)
     k_blk = _normal(rng, (n, D, Hkv, d), dtype)
     v_blk = _normal(rng, (n, D, Hkv, d), dtype)
 
@@ -237,14 +236,14 @@ def _make_step_fp8kv(p, rng, prefix, cap, plant_L, seed):
             k_scale[it, g] = max(float(np.abs(kf[it][g]).max(initial=0.0)), float(np.abs(kbf[it, :, g]).max())) / 448.0
             v_scale[it, g] = max(float(np.abs(vf[it][g]).max(initial=0.0)), float(np.abs(vbf[it, :, g]).max())) / 448.0
     k_cache = np.full((n, Hkv, cap, d), E4M3_NAN, dtype=np.uint8)
-    v_cache = np.full((n, Hkv, d, cap), E4M3_NAN, dtype=np.uint8)
+    v_cache = np.full((n, Hkv, cap, d), E4M3_NAN, dtype=np.uint8)
     k_blk = np.zeros((n, D, Hkv, d), np.uint8)
     v_blk = np.zeros((n, D, Hkv, d), np.uint8)
     for it in range(n):
         P = int(prefix[it])
         for g in range(Hkv):
             k_cache[it, g, :P, :] = f32_to_e4m3_bits(kf[it][g] / k_scale[it, g])
-            v_cache[it, g, :, :P] = f32_to_e4m3_bits(vf[it][g] / v_scale[it, g]).T
+            v_cache[it, g, :P, :] = f32_to_e4m3_bits(vf[it][g] / v_scale[it, g])
             k_blk[it, :, g, :] = f32_to_e4m3_bits(kbf[it, :, g] / k_scale[it, g])
             v_blk[it, :, g, :] = f32_to_e4m3_bits(vbf[it, :, g] / v_scale[it, g])
     rest = make_step(dict(p, dtype=BF16, n_items=1, prefix=("fixed", 0), Hq=1, Hkv=1, d=8), seed + 7919)
@@ -286,8 +285,8 @@ def make_two_stream(p: dict, seed: int) -> dict:
     noisy stream = the responses' tokens in order (padding after them when a
     sequence has fewer response tokens than the longest).  Lc and Ln are the
     maxima over sequences; a shorter clean stream ends in plain clean tokens.
-    Arrays: q [n][L][Hq][d] with L = Lc + Ln; k [n][Hkv][cap][d] and v
-    [n][Hkv][d][cap] (cap = L rounded up to 64, zeros past L); spans int32
+    Arrays: q [n][L][Hq][d] with L = Lc + Ln; k and v [n][Hkv][cap][d]
+    (cap = L rounded up to 64, zeros past L); spans int32
     [n][max_spans][2] = (clean start, length) of each response; n_spans [n].
     Draw order: q, then k, then v, as N(0, 1) rounded to bf16.
     """
@@ -319,9 +318,9 @@ def make_two_stream(p: dict, seed: int) -> dict:
     elem = np.uint16 if dtype == BF16 else np.float32
     q = _normal(rng, (n, L, Hq, d), dtype)
     k = np.zeros((n, Hkv, cap, d), elem)
-    v = np.zeros((n, Hkv, d, cap), elem)
+    v = np.zeros((n, Hkv, cap, d), elem)
     k[:, :, :L, :] = _normal(rng, (n, Hkv, L, d), dtype)
-    v[:, :, :, :L] = np.swapaxes(_normal(rng, (n, Hkv, L, d), dtype), 2, 3)
+    v[:, :, :L, :] = _normal(rng, (n, Hkv, L, d), dtype)
     return dict(params=dict(p, Lc=Lc, Ln=Ln, L=L), seed=seed, q=q, k=k, v=v, spans=spans, n_spans=n_spans,
                 cap=cap, Lc=Lc, Ln=Ln)
 

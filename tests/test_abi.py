@@ -48,7 +48,7 @@ def _attn(bd, **kw):
 
 BAD_ATTN = [
     (dict(d=96), "BD_E_SHAPE"), (dict(D=0), "BD_E_SHAPE"), (dict(D=65), "BD_E_SHAPE"),
-    (dict(Hq=15), "BD_E_SHAPE"), (dict(Hkv=0), "BD_E_SHAPE"), (dict(cap=4161), "BD_E_SHAPE"),
+    (dict(Hq=15), "BD_E_SHAPE"), (dict(Hkv=0), "BD_E_SHAPE"), (dict(cap=0), "BD_E_SHAPE"),
     (dict(max_prefix=5000), "BD_E_SHAPE"), (dict(max_prefix=-1), "BD_E_SHAPE"), (dict(n_items=0), "BD_E_SHAPE"),
     (dict(dtype=7), "BD_E_DTYPE"), (dict(mode=3), "BD_E_PARAM"), (dict(scale=float("nan")), "BD_E_PARAM"),
     (dict(scale=0.0), "BD_E_PARAM"), (dict(scale=float("inf")), "BD_E_PARAM"),
@@ -64,6 +64,15 @@ def test_attn_validation(bd, kw, code):
     st = bd.lib.bd_attn_step(ctypes.byref(desc), fake, fake, fake, fake, fake, fake, fake, fake, 1 << 30, None)
     assert st == getattr(bd, code)
     assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_any_cache_capacity_is_accepted(bd, dtype):
+    """K and V caches are both [cap][d] rows of d * element-size bytes (a multiple of
+    16), so no capacity needs rounding: odd and small ones are valid shapes."""
+    for cap in (4096, 4097, 4099, 4103):
+        assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(_attn(bd, cap=cap, dtype=dtype))) != bd.SIZE_MAX
+    assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(_attn(bd, cap=1, max_prefix=1, dtype=dtype))) != bd.SIZE_MAX
 
 
 def test_balanced_plan_flag(bd):
@@ -116,10 +125,9 @@ def _fp8_call(bd, desc, k_scale=1 << 20, v_scale=1 << 20, ws_bytes=1 << 30, q=1 
                                      k_scale, v_scale, fake, fake, ws, ws_bytes, None)
 
 
-@pytest.mark.parametrize("kw,code", BAD_ATTN + [(dict(cap=4168), "BD_E_SHAPE")])
+@pytest.mark.parametrize("kw,code", BAD_ATTN)
 def test_fp8kv_attn_validation(bd, kw, code):
-    # The shape rules of bd_attn_step, plus a cache capacity that is a multiple of 16
-    # (each d-major E4M3 value row starts on a 16-byte boundary).
+    # The shape rules of bd_attn_step.
     desc = _attn(bd, **dict(dict(dtype=bd.BD_FP8KV), **kw))
     assert _fp8_call(bd, desc) == getattr(bd, code)
     assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == bd.SIZE_MAX
@@ -144,9 +152,10 @@ def test_fp8kv_dtype_routing_and_errors(bd):
     for mp in (0, 32, 63):
         desc = _attn(bd, n_items=1, max_prefix=mp, cap=128, dtype=bd.BD_FP8KV)
         assert bd.lib.bd_attn_workspace_bytes(ctypes.byref(desc)) == 0
-    # kv_append copies E4M3 bytes; its capacity rule follows the dtype.
-    assert bd.lib.bd_kv_append(ctypes.byref(_attn(bd, dtype=bd.BD_FP8KV, cap=4168)), fake, fake, fake, fake, fake,
-                               None, None, None) == bd.BD_E_SHAPE
+    # kv_append copies E4M3 bytes; any capacity is a valid shape (a NULL prefix
+    # pointer is what it then refuses).
+    assert bd.lib.bd_kv_append(ctypes.byref(_attn(bd, dtype=bd.BD_FP8KV, cap=4169)), fake, fake, None, fake, fake,
+                               None, None, None) == bd.BD_E_NULL
 
 
 def test_quad_mode_validation(bd):
@@ -253,8 +262,15 @@ def test_verify_and_append_validation(bd):
     assert bd.lib.bd_spec_verify(1, 65, 151936, fake, fake, fake, None, fake, need, None) == bd.BD_E_SHAPE
     desc = _attn(bd, dtype=5)
     assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_DTYPE
-    desc = _attn(bd, cap=100)
+    desc = _attn(bd, cap=0)
     assert bd.lib.bd_kv_append(ctypes.byref(desc), fake, fake, fake, fake, fake, None, None, None) == bd.BD_E_SHAPE
+    # Rows are copied as 16-byte units: every cache and block pointer must be 16-byte aligned.
+    desc = _attn(bd, cap=4099)
+    for i in range(4):
+        ptrs = [fake] * 4
+        ptrs[i] = fake + 8
+        kc, vc, kb, vb = ptrs
+        assert bd.lib.bd_kv_append(ctypes.byref(desc), kc, vc, fake, kb, vb, None, None, None) == bd.BD_E_PARAM
     desc = _attn(bd)
     assert bd.lib.bd_kv_append(ctypes.byref(desc), None, fake, fake, fake, fake, None, None, None) == bd.BD_E_NULL
     # A block of 64 slots x 2^19 KV heads x d 128 (2^32 elements per item) would

@@ -145,11 +145,12 @@ ATTN_CASES = [
     ("G7_rows224", dict(Hq=28, Hkv=4, D=32, prefix=("list", [70, 500]), n_items=2)),
     ("d64_bf16", dict(d=64, prefix=("fixed", 333))),
     ("many_items", dict(n_items=40, prefix=("fixed", 150))),
-    # capacities that are multiples of 8 but not of 64: d-major value rows start
-    # on 16-byte (not 128-byte) boundaries
+    # capacities that are not multiples of 64 (nor of 8): each (item, KV head)'s
+    # cache rows then start at an odd multiple of the row size
     ("cap1016", dict(prefix=("fixed", 1000), cap=1016)),
-    ("cap1016_ragged", dict(prefix=("list", [1, 63, 517, 1000]), n_items=4, cap=1016)),
-    ("cap40_short", dict(prefix=("list", [0, 7, 24]), n_items=3, cap=40)),
+    ("cap1001", dict(prefix=("fixed", 1000), cap=1001)),
+    ("cap1019_ragged", dict(prefix=("list", [1, 63, 517, 1000]), n_items=4, cap=1019)),
+    ("cap25_short", dict(prefix=("list", [0, 7, 24]), n_items=3, cap=25)),
 ]
 
 
@@ -268,10 +269,8 @@ def _sweep_case(i):
         if n * Hq * D * (max(prefix) + D) * d <= 1.5e8:  # keeps the fp64 oracle within seconds
             break
     balanced = bool(rng.random() < 0.5)  # drawn after the shape, so the shapes of the sweep stay put
-    # the smallest capacity the ABI accepts: a multiple of 8 (16 for E4M3)
-    al = 16 if dtype == FP8KV else 8
-    p = dict(n_items=n, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, prefix=("list", prefix),
-             cap=(host_max + D + al - 1) // al * al)
+    # the smallest capacity that holds the largest prefix plus one block
+    p = dict(n_items=n, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, prefix=("list", prefix), cap=host_max + D)
     if mode == QUAD:
         st = synth.make_quad_step(dict(synth.QUAD_CONFIGS[2], B=B, **p), 5000 + i)
     else:
@@ -382,9 +381,10 @@ FP8_CASES = [
     ("d64", dict(d=64, prefix=("fixed", 333))),
     ("d64_ragged", dict(d=64, D=32, prefix=("list", [0, 64, 65, 700]), n_items=4)),
     ("many_items", dict(n_items=40, prefix=("fixed", 150))),
-    # capacities that are multiples of 16 but not of 64
+    # capacities that are not multiples of 64 (1003: not even of 2)
     ("cap1008", dict(prefix=("fixed", 990), cap=1008)),
-    ("cap1008_ragged", dict(prefix=("list", [0, 65, 500, 990]), n_items=4, cap=1008)),
+    ("cap1003", dict(prefix=("fixed", 990), cap=1003)),
+    ("cap1003_ragged", dict(prefix=("list", [0, 65, 500, 990]), n_items=4, cap=1003)),
 ]
 
 
@@ -431,10 +431,10 @@ def test_fp8kv_deterministic_append_and_reattend(dev):
     _check_attention(got, ref, "fp8kv_after_append")
 
 
-@pytest.mark.parametrize("dtype,cap", [(BF16, 2072), (FP8KV, 2080)])
+@pytest.mark.parametrize("dtype,cap", [(BF16, 2072), (BF16, 2069), (FP8KV, 2080), (FP8KV, 2071)])
 def test_append_and_reattend_unaligned_cap(dev, dtype, cap):
-    """Append into caches whose capacity is a multiple of 8 (bf16) or 16 (E4M3) but
-    not of 64, up to the last slot; the grown caches are the oracle's bit for bit
+    """Append into caches whose capacity is not a multiple of 64 (2069 and 2071 not
+    even of 8), up to the last slot; the grown caches are the oracle's bit for bit
     and attention over them matches the oracle."""
     torch = dev["torch"]
     p = synth.params_for(3, n_items=3, dtype=dtype, D=16, prefix=("list", [cap - 16, 1000, 77]), cap=cap, V=1000,

@@ -35,14 +35,14 @@ def _rand(rng, shape, dtype):
 
 
 def _pack_cache(k_seq, v_seq, cap, dtype):
-    """k_seq/v_seq: [Hkv][P][d] -> cache layouts [1][Hkv][cap][d] and [1][Hkv][d][cap] (NaN tail)."""
+    """k_seq/v_seq: [Hkv][P][d] -> cache layout [1][Hkv][cap][d] (NaN tail)."""
     Hkv, P, d = k_seq.shape
     el = np.uint16 if dtype == BF16 else np.float32
     nan = synth.gen.BF16_NAN if dtype == BF16 else np.float32(np.nan)
     kc = np.full((1, Hkv, cap, d), nan, el)
-    vc = np.full((1, Hkv, d, cap), nan, el)
+    vc = np.full((1, Hkv, cap, d), nan, el)
     kc[0, :, :P, :] = k_seq
-    vc[0, :, :, :P] = np.swapaxes(v_seq, 1, 2)
+    vc[0, :, :P, :] = v_seq
     return kc, vc
 
 
@@ -207,18 +207,18 @@ def _random_step(rng, n, D, Hq, Hkv, d, P, dtype, cap=None):
     el = np.uint16 if dtype == BF16 else np.float32
     nan = synth.gen.BF16_NAN if dtype == BF16 else np.float32(np.nan)
     kc = np.full((n, Hkv, cap, d), nan, el)
-    vc = np.full((n, Hkv, d, cap), nan, el)
+    vc = np.full((n, Hkv, cap, d), nan, el)
     for it in range(n):
         p = int(prefix[it])
         kc[it, :, :p] = _rand(rng, (Hkv, p, d), dtype)
-        vc[it, :, :, :p] = _rand(rng, (Hkv, d, p), dtype)
+        vc[it, :, :p] = _rand(rng, (Hkv, p, d), dtype)
     return q, kb, vb, kc, vc, prefix
 
 
 def _keys_natural(kc, vc, kb, vb, it, P):
     """Key/value sequences [Hkv][P+D][d] of item ``it`` in natural layout."""
     k = np.concatenate([kc[it, :, :P], np.swapaxes(kb[it], 0, 1)], axis=1)
-    v = np.concatenate([np.swapaxes(vc[it, :, :, :P], 1, 2), np.swapaxes(vb[it], 0, 1)], axis=1)
+    v = np.concatenate([vc[it, :, :P], np.swapaxes(vb[it], 0, 1)], axis=1)
     return k, v
 
 
@@ -268,7 +268,7 @@ def test_attention_invariants():
     # Constant values give that constant, whatever the scores.
     vc2, vb2 = vc.copy(), vb.copy()
     for it in range(n):
-        vc2[it, :, :, :prefix[it]] = 0.75
+        vc2[it, :, :prefix[it]] = 0.75
     vb2[:] = 0.75
     const = oracle.attention(q, kb, vb2, kc, vc2, prefix, BIDIR)
     np.testing.assert_allclose(const, 0.75, rtol=0, atol=1e-14)
@@ -278,7 +278,7 @@ def test_attention_invariants():
         P = int(prefix[it])
         perm = rng.permutation(P)
         kc3[it, :, :P] = kc[it, :, perm].swapaxes(0, 1)
-        vc3[it, :, :, :P] = vc[it, :, :, perm].transpose(1, 2, 0)
+        vc3[it, :, :P] = vc[it, :, perm].swapaxes(0, 1)
     perm_out = oracle.attention(q, kb, vb, kc3, vc3, prefix, BIDIR)
     np.testing.assert_allclose(perm_out, base, rtol=0, atol=1e-12)
     # CAUSAL differs from BIDIR only in the block: the last slot sees the whole block either way.
@@ -505,12 +505,12 @@ def test_kv_append_is_bitwise_and_bounded(dtype):
     for it in range(n):
         P, L = int(prefix[it]), int(acc[it])
         np.testing.assert_array_equal(kc2[it, :, P:P + L], np.swapaxes(kb[it, :L], 0, 1))
-        np.testing.assert_array_equal(vc2[it, :, :, P:P + L], np.transpose(vb[it, :L], (1, 2, 0)))
+        np.testing.assert_array_equal(vc2[it, :, P:P + L], np.swapaxes(vb[it, :L], 0, 1))
         untouched_k = np.ones(kc.shape[2], bool)
         untouched_k[P:P + L] = False
         bits = lambda a: np.ascontiguousarray(a).view(np.uint8)
         np.testing.assert_array_equal(bits(kc2[it][:, untouched_k]), bits(kc[it][:, untouched_k]))
-        np.testing.assert_array_equal(bits(vc2[it][:, :, untouched_k]), bits(vc[it][:, :, untouched_k]))
+        np.testing.assert_array_equal(bits(vc2[it][:, untouched_k]), bits(vc[it][:, untouched_k]))
     # Overflow: that item is skipped and the error word is set.
     kc3, vc3, p3, err = oracle.kv_append(kc, vc, np.array([12, 0, 0], np.int32), kb, vb, None)
     assert err == 1 and p3.tolist() == [12, 6, 6]
@@ -522,7 +522,7 @@ def test_kv_append_fp8_bytes():
     rng = np.random.Generator(np.random.PCG64(52))
     n, D, Hkv, d, cap = 2, 5, 2, 16, 32
     kc = rng.integers(0, 256, size=(n, Hkv, cap, d), dtype=np.uint8)
-    vc = rng.integers(0, 256, size=(n, Hkv, d, cap), dtype=np.uint8)
+    vc = rng.integers(0, 256, size=(n, Hkv, cap, d), dtype=np.uint8)
     kb = rng.integers(0, 256, size=(n, D, Hkv, d), dtype=np.uint8)
     vb = rng.integers(0, 256, size=(n, D, Hkv, d), dtype=np.uint8)
     prefix = np.array([3, 27], np.int32)
@@ -531,11 +531,11 @@ def test_kv_append_fp8_bytes():
     for it in range(n):
         P = int(prefix[it])
         np.testing.assert_array_equal(kc2[it, :, P:P + D], np.swapaxes(kb[it], 0, 1))
-        np.testing.assert_array_equal(vc2[it, :, :, P:P + D], np.transpose(vb[it], (1, 2, 0)))
+        np.testing.assert_array_equal(vc2[it, :, P:P + D], np.swapaxes(vb[it], 0, 1))
         keep = np.ones(cap, bool)
         keep[P:P + D] = False
         np.testing.assert_array_equal(kc2[it][:, keep], kc[it][:, keep])
-        np.testing.assert_array_equal(vc2[it][:, :, keep], vc[it][:, :, keep])
+        np.testing.assert_array_equal(vc2[it][:, keep], vc[it][:, keep])
 
 
 # ---------------------------------------------------------------------------
@@ -589,7 +589,7 @@ def test_merge_matches_split_attention_rows():
                            st["prefix"], oracle.BIDIR)
     q = st["q"][0, 2, 1].astype(np.float64)
     K = np.concatenate([st["k_cache"][0, 0, :40], st["k_blk"][0, :, 0]]).astype(np.float64)
-    Vv = np.concatenate([st["v_cache"][0, 0, :, :40].T, st["v_blk"][0, :, 0]]).astype(np.float64)
+    Vv = np.concatenate([st["v_cache"][0, 0, :40], st["v_blk"][0, :, 0]]).astype(np.float64)
     sc = K @ q / np.sqrt(64)
     parts = [oracle.softmax_partial(sc[a:b], Vv[a:b]) for a, b in ((0, 17), (17, 40), (40, 44))]
     np.testing.assert_allclose(oracle.merge_partials(parts), out[0, 2, 1], atol=1e-12)
@@ -722,7 +722,7 @@ def test_two_stream_matches_dense_mask(cfg_seed):
         live = mask.any(axis=1)
         Q = np.swapaxes(_widen(st["q"][it]), 0, 1)                  # [Hq][L][d]
         K = _widen(st["k"][it][:, :L])                               # [Hkv][L][d]
-        V = np.swapaxes(_widen(st["v"][it][:, :, :L]), 1, 2)
+        V = _widen(st["v"][it][:, :L])                               # [Hkv][L][d]
         ref = _sdpa(Q[:, live], K, V, mask[live], G)
         np.testing.assert_allclose(out[it][live], np.swapaxes(ref, 0, 1), rtol=0, atol=1e-12)
         assert np.all(out[it][~live] == 0.0)                         # noisy padding sees nothing
@@ -739,7 +739,7 @@ def test_two_stream_equals_prefill_and_per_block_denoise():
     out = oracle.two_stream_attention(st["q"], st["k"], st["v"], st["spans"], st["n_spans"], Lc, D)
     for it in range(p["n_seq"]):
         Kseq = np.swapaxes(st["k"][it], 0, 1)                        # [cap][Hkv][d]
-        Vseq = np.transpose(st["v"][it], (2, 0, 1))                  # [cap][Hkv][d]
+        Vseq = np.swapaxes(st["v"][it], 0, 1)                        # [cap][Hkv][d]
         kc, vc = st["k"][it:it + 1], st["v"][it:it + 1]
         for c0 in range(0, Lc, 7):                                    # clean chunks of 7 positions
             c1 = min(c0 + 7, Lc)

@@ -48,7 +48,7 @@ bd_status check_attn_desc(const bd_attn_desc *d) {
     if (d->n_items < 1 || d->D < 1 || d->D > (m == BD_BLOCK_QUAD ? 32 : 64)) return BD_E_SHAPE;
     if (d->Hq < 1 || d->Hkv < 1 || d->Hq % d->Hkv != 0) return BD_E_SHAPE;
     if (d->d != 64 && d->d != 128) return BD_E_SHAPE;
-    if (d->cap < 1 || d->cap % (d->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
+    if (d->cap < 1) return BD_E_SHAPE;
     if (d->max_prefix < 0 || d->max_prefix > d->cap) return BD_E_SHAPE;
     // Index arithmetic in the kernels uses 32-bit ints for per-item quantities.
     if ((int64_t)block_slots(d) * d->Hq > (1 << 20) || (int64_t)d->cap * d->d > (1ll << 30)) return BD_E_SHAPE;
@@ -300,12 +300,14 @@ bd_status bd_kv_append(const bd_attn_desc *desc, void *k_cache, void *v_cache, i
     if (desc->n_items < 1 || desc->D < 1 || desc->D > (m == BD_BLOCK_QUAD ? 32 : 64) || desc->Hkv < 1)
         return BD_E_SHAPE;
     if (desc->d != 64 && desc->d != 128) return BD_E_SHAPE;
-    if (desc->cap < 1 || desc->cap % (desc->dtype == BD_FP8KV ? 16 : 8) != 0) return BD_E_SHAPE;
+    if (desc->cap < 1) return BD_E_SHAPE;
     // The limits bd_attn_step puts on a cache and a block: one item's cache and
     // one item's block K (or V) hold at most 2^30 elements.
     if ((int64_t)desc->cap * desc->d > (1ll << 30)) return BD_E_SHAPE;
     if ((int64_t)block_slots(desc) * desc->Hkv * desc->d > (1ll << 30)) return BD_E_SHAPE;
     if (!k_cache || !v_cache || !prefix_len || !k_blk || !v_blk) return BD_E_NULL;
+    // Rows are copied as 16-byte units.
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_blk) || !aligned16(v_blk)) return BD_E_PARAM;
     // Quadratic mode: the block holds B (B + 3) / 2 slots, of which the first B
     // (the drafts) can be accepted.
     return launched(bd::launch_kv_append(desc->n_items, desc->D, block_slots(desc), desc->Hkv, desc->d, desc->cap,

@@ -14,11 +14,12 @@
 // so that each lane holds one query row: the softmax max is an in-lane
 // reduction plus one exchange between the two 32-lane halves.  K rows are
 // fed to the first MFMA in a permuted order so that the scores a lane holds
-// for each 16-key chunk are consecutive keys; the second MFMA then reads its
-// V^T operand as one 16-byte LDS load per lane from the d-major value tile.
-// K and V^T tiles (32 bf16 or 64 E4M3 keys, 8 KB each at d = 128) stream
-// through four LDS stages with XOR swizzles that keep 16-lane read phases
-// conflict-free.  E4M3 K/V (the FP8 rung of the Fast-dVLM write-up, section
+// for each 16-key chunk are consecutive keys; the second MFMA then takes its
+// V^T operand from the row-major [key][d] value tile through gfx950's LDS
+// transpose loads (two 8-byte loads per lane and MFMA), so values are cached
+// in the same [cap][d] layout as keys.  K and V tiles (32 bf16 or 64 E4M3
+// keys, 8 KB each at d = 128) stream through four LDS stages with XOR
+// swizzles that keep every read phase conflict-free.  E4M3 K/V (the FP8 rung of the Fast-dVLM write-up, section
 // 5.4 and Table 4, applied to the cache) are widened to bf16 exactly, right
 // after each LDS read, with one fp32 scale per (item, KV head) for K and V.
 // The online softmax (Milakov & Gimelshein, "Online normalizer calculation
@@ -255,7 +256,7 @@ __device__ __forceinline__ ItemPlan balanced_plan(const MfmaParams &p, int lane)
 // one 256-byte bank span (16 units) with 16/U - 1 other rows.  One ds_read_b128
 // phase serves 16 lanes that read the same logical unit of 16 different rows;
 // the swizzle sends those 16 reads to 16 different unit slots of the span.
-// V^T rows (and bf16 K rows) are read 16 consecutive rows at a time.
+// bf16 K rows are read 16 consecutive rows at a time.
 template <int U>
 __device__ __forceinline__ int row_swz(int row) { return (row / (16 / U)) & (U - 1); }
 // E4M3 K rows are read in key_perm8 order: the 16 keys of a phase differ in
@@ -265,6 +266,37 @@ __device__ __forceinline__ int k_swz(int key) {
     if constexpr (!KV8) return row_swz<HD / 8>(key);
     else if constexpr (HD == 128) return ((key >> 1) & 3) | ((key >> 2) & 4);  // 2 rows per span
     else return ((key >> 2) & 1) | ((key >> 3) & 2);                             // 4 rows per span
+}
+// V rows ([key][d], U units each) are read by LDS transpose loads: in every
+// 32-lane phase, bf16 reads cover 4 consecutive rows x 64 bytes and E4M3 reads
+// 8 consecutive rows x 32 bytes.  The swizzle moves the 64- (32-) byte column
+// chunk of each of those rows to its own quarter (eighth) of the 256-byte bank
+// span.  It depends on key mod 4 (bf16) or key mod 8 (E4M3) only.
+template <int HD, bool KV8>
+__device__ __forceinline__ int v_swz(int key) {
+    constexpr int U = HD * (KV8 ? 1 : 2) / 16;  // 16-byte units per row
+    constexpr int RPS = 16 / U;                 // rows per 256-byte span
+    if constexpr (!KV8) return 4 * ((key / RPS) % (U / 4));
+    else return 2 * ((key / RPS) % (U / 2));
+}
+
+// LDS transpose loads of gfx950.  In each group of 16 lanes every lane fetches
+// 8 bytes at its own address; ds_read_b64_tr_b16 then gives lane r, element j
+// (0..3) the 16-bit element r % 4 of lane 4 j + r / 4's fetch, and
+// ds_read_b64_tr_b8 gives lane r, byte j (0..7) the byte r % 8 of lane
+// 2 j + r / 8's fetch.  So when the 16 lanes fetch 4 (8) consecutive rows of a
+// row-major [key][d] tile, 4 (2) lanes per row over 16 consecutive columns,
+// lane r receives column r of those 4 (8) rows: the k-contiguous operand an
+// MFMA takes.
+typedef short bd_s16x4 __attribute__((ext_vector_type(4)));
+typedef int bd_i32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bd_s16x4 bd_lds_tr16(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) bd_s16x4 *)(__attribute__((address_space(3))) uint8_t *)p);
+}
+__device__ __forceinline__ bd_i32x2 bd_lds_tr8(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) bd_i32x2 *)(__attribute__((address_space(3))) uint8_t *)p);
 }
 
 // Tile pipeline depth: NS LDS stages per workgroup, so NS - 1 tiles stay in
@@ -306,14 +338,11 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     constexpr int NT = NW * 64;
     constexpr int EB = KV8 ? 1 : 2;     // bytes per K / V element
     constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;  // keys per tile
-    constexpr int EPU = 16 / EB;        // elements per 16-byte unit
-    constexpr int KU = HD * EB / 16;    // 16-byte units per K row
-    constexpr int VU = TK * EB / 16;    // 16-byte units per V^T row
+    constexpr int KU = HD * EB / 16;    // 16-byte units per K (or V) row
     constexpr int SB = TK * HD * EB;    // bytes per K (or V) stage
-    constexpr int K_UNITS = TK * KU;
-    constexpr int V_UNITS = HD * VU;
+    constexpr int K_UNITS = TK * KU;    // ... and V units: both tiles are [TK][HD]
     constexpr int LK = (K_UNITS + NT - 1) / NT;
-    constexpr int LV = (V_UNITS + NT - 1) / NT;
+    constexpr int LV = LK;
     constexpr int KC = HD / 16;         // d-chunks of the first MFMA
     constexpr int MB = HD / 32;         // d-blocks of the second MFMA
     constexpr int RPG = NW * 32;        // rows per workgroup
@@ -341,9 +370,9 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     auto vbuf = [&](int st) __attribute__((always_inline)) -> uint8_t * {
         return st == 0 ? lds_v0 : st == 1 ? lds_v1 : st == 2 ? lds_v2 : lds_v3;
     };
-    // Byte offsets of 16-byte unit lu of K row `key` / V^T row `dd` in a stage.
+    // Byte offsets of 16-byte unit lu of K / V row `key` in a stage.
     auto k_at = [](int key, int lu) __attribute__((always_inline)) { return (key * KU + (lu ^ k_swz<HD, KV8>(key))) * 16; };
-    auto v_at = [](int dd, int lu) __attribute__((always_inline)) { return (dd * VU + (lu ^ row_swz<VU>(dd))) * 16; };
+    auto v_at = [](int key, int lu) __attribute__((always_inline)) { return (key * KU + (lu ^ v_swz<HD, KV8>(key))) * 16; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -401,6 +430,23 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
                 qf[kc] = *reinterpret_cast<const bf16x8 *>(qp + d0);
             else
                 qf[kc] = bf16x8{};
+        }
+    }
+    // Transpose-load offsets of this lane in a V stage, per 32-column block mb.
+    // In its group of 16 lanes (s = lane % 16), lane s fetches 8 bytes of row
+    // rho = 8 half + s / 4 (bf16) or 16 half + s / 2 (E4M3) at column
+    // 32 mb + 16 grp + 4 (s % 4) (bf16) or + 8 (s % 2) (E4M3), grp = lane / 16 % 2;
+    // the tile's other rows for this lane are rho plus multiples of 4 (8), which
+    // v_swz maps the same way.
+    int v_lane[MB];
+    {
+        const int s16 = lane & 15, grp = (lane >> 4) & 1;
+        const int rho = KV8 ? 16 * half + (s16 >> 1) : 8 * half + (s16 >> 2);
+        const int cbyte = KV8 ? 16 * grp + 8 * (s16 & 1) : (16 * grp + 4 * (s16 & 3)) * 2;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int c = mb * 32 * EB + cbyte;  // byte column in the row
+            v_lane[mb] = v_at(rho, c >> 4) + (c & 15);
         }
     }
     float cs = p.c, vs = 1.0f;
@@ -465,10 +511,8 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // Key tile of list entry k (sequence mode) or bulk tile k.
     auto tile_of = [&](int k) __attribute__((always_inline)) { return SEQ && k >= nA ? bB + (k - nA) : k; };
 
-    // Byte offsets of this (item, KV head)'s cache rows.
-    const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD * EB;   // [cap][HD]
-    const size_t vc_base = ((size_t)it * p.Hkv + g) * HD * p.cap * EB;   // [HD][cap]
-    const size_t row_v = (size_t)p.cap * EB;                              // bytes per V^T cache row
+    // Byte offset of this (item, KV head)'s K and V cache rows ([cap][HD] each).
+    const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD * EB;
 
     floatx16 o[MB];
 #pragma unroll
@@ -480,7 +524,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // (global_load_lds_dwordx4): each instruction fills 64 consecutive 16-byte
     // LDS slots, one per lane, so the XOR swizzle is applied by choosing every
     // lane's source address.  No VGPRs hold tile data.
-    static_assert(K_UNITS % NT == 0 && V_UNITS % NT == 0, "tile units must split evenly over lanes");
+    static_assert(K_UNITS % NT == 0, "tile units must split evenly over lanes");
     auto issue_bulk = [&](int t, int st, bool real) __attribute__((always_inline)) {
         const int key0 = tile_of(t) * TK;
 #pragma unroll
@@ -496,21 +540,18 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         for (int j = 0; j < LV; ++j) {
             const int base = (j * NW + w) * 64;
             const int u = base + lane;
-            const int dd = u / VU, pu = u % VU;
-            const int lu = pu ^ row_swz<VU>(dd);
-            const uint8_t *src = real ? p.vc + vc_base + (size_t)dd * row_v + (size_t)key0 * EB + lu * 16 : p.kc + kc_base;
+            const int key = u / KU, pu = u % KU;
+            const int lu = pu ^ v_swz<HD, KV8>(key);
+            const uint8_t *src = real ? p.vc + kc_base + (size_t)(key0 + key) * HD * EB + lu * 16 : p.kc + kc_base;
             __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 16], 16, 0, 0);
         }
     };
     // Tail tiles: the last P % TK cache positions followed by the D block slots,
-    // zero past the end (in the unit's last split).  K rows and cache V^T rows
-    // are gathered as 16-byte units.  Block V rows arrive d-contiguous
-    // ([slot][Hkv][d]); they are loaded as 16-byte units and scattered
-    // transposed into the V^T tile after the other units are written.  All of
-    // a tail tile's loads are issued first; for the first tail tile the first
-    // bulk copies follow them, so those are in flight while the tail is stored
-    // and computed.
-    constexpr int BU = HD * EB / 16;  // 16-byte units per block V row
+    // zero past the end (in the unit's last split).  K and V rows, of the
+    // cache or of the block ([slot][Hkv][d]), are gathered as 16-byte units
+    // through registers.  All of a tail tile's loads are issued first; for the
+    // first tail tile the first bulk copies follow them, so those are in
+    // flight while the tail is stored and computed.
     // The first NS-1 bulk tiles into stages 0 .. NS-2 (the tail uses stage NS-1).
     auto first_fill = [&]() __attribute__((always_inline)) {
         if (nb_split > 0) {
@@ -519,7 +560,6 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         }
     };
     auto load_tail = [&](int st, int tt, bool fill) __attribute__((always_inline)) {
-        const int pc = P - Pb;  // cache positions in the tail
         u32x4 kr[LK], vr[LV];
 #pragma unroll
         for (int i = 0; i < LK; ++i) {
@@ -527,57 +567,15 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             const int key = u / KU, lu = u % KU;
             const int j = tt * TK + key;
             const int pos = Pb + j;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = kv;
             if (j < tail_len) {
-                const uint8_t *src = pos < P ? p.kc + kc_base + (size_t)pos * HD * EB + lu * 16
-                                             : p.kb + (((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD * EB + lu * 16;
-                v = *reinterpret_cast<const u32x4 *>(src);
+                const size_t off = pos < P ? kc_base + (size_t)pos * HD * EB + lu * 16
+                                           : (((size_t)it * p.D + (pos - P)) * p.Hkv + g) * HD * EB + lu * 16;
+                kv = *reinterpret_cast<const u32x4 *>((pos < P ? p.kc : p.kb) + off);
+                vv = *reinterpret_cast<const u32x4 *>((pos < P ? p.vc : p.vb) + off);
             }
-            kr[i] = v;
-        }
-#pragma unroll
-        for (int i = 0; i < LV; ++i) {
-            const int u = tid + i * NT;
-            const int dd = u / VU, lu = u % VU;
-            const int j0 = tt * TK + lu * EPU;
-            const uint8_t *row = p.vc + vc_base + (size_t)dd * row_v + (size_t)(Pb + j0) * EB;
-            u32x4 v = u32x4{0u, 0u, 0u, 0u};
-            if (j0 + EPU <= pc) {
-                v = *reinterpret_cast<const u32x4 *>(row);
-            } else if (j0 < pc) {  // unit straddles the end of the cache part
-                // Every lane loads all EPU elements (positions past the cache
-                // part re-read its last one) and zeroes the extra ones after,
-                // so the loads issue back to back with one wait.
-                uint32_t x[EPU];
-#pragma unroll
-                for (int e = 0; e < EPU; ++e) {
-                    const int ee = min(e, pc - 1 - j0);
-                    x[e] = KV8 ? (uint32_t)row[ee] : (uint32_t)reinterpret_cast<const uint16_t *>(row)[ee];
-                }
-#pragma unroll
-                for (int e = 0; e < EPU; ++e)
-                    if (j0 + e >= pc) x[e] = 0u;
-                uint32_t w4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int e = 0; e < EPU; ++e) w4[(e * EB) >> 2] |= x[e] << (8 * ((e * EB) & 3));
-                v = u32x4{w4[0], w4[1], w4[2], w4[3]};
-            }
-            vr[i] = v;
-        }
-        // Block V units that land in this tile: slot b covers tail position pc + b,
-        // so this tile holds slots b0 .. b0 + TK - 1 (those in 0..D-1).
-        constexpr int VB_N = (TK * BU + NT - 1) / NT;
-        const int b0 = tt * TK - pc;
-        u32x4 br[VB_N];
-        int bkey[VB_N];
-#pragma unroll
-        for (int i = 0; i < VB_N; ++i) {
-            const int u = tid + i * NT;
-            const int key = u / BU, du = u % BU;  // key index inside this tile
-            const int b = b0 + key;
-            bkey[i] = (u < TK * BU && b >= 0 && b < p.D) ? key : -1;
-            if (bkey[i] >= 0)
-                br[i] = *reinterpret_cast<const u32x4 *>(p.vb + (((size_t)it * p.D + b) * p.Hkv + g) * HD * EB + du * 16);
+            kr[i] = kv;
+            vr[i] = vv;
         }
         if (fill) first_fill();  // in flight while the tail is stored and computed
 #pragma unroll
@@ -585,30 +583,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             const int u = tid + i * NT;
             const int key = u / KU, lu = u % KU;
             *reinterpret_cast<u32x4 *>(kbuf(st) + k_at(key, lu)) = kr[i];
-        }
-#pragma unroll
-        for (int i = 0; i < LV; ++i) {
-            const int u = tid + i * NT;
-            const int dd = u / VU, lu = u % VU;
-            *reinterpret_cast<u32x4 *>(vbuf(st) + v_at(dd, lu)) = vr[i];
-        }
-        bd_barrier_lds();  // the scatter below overwrites zeros written above
-#pragma unroll
-        for (int i = 0; i < VB_N; ++i) {
-            if (bkey[i] < 0) continue;
-            const int u = tid + i * NT;
-            const int du = u % BU;
-            const int key = bkey[i];
-            const uint32_t w4[4] = {br[i].x, br[i].y, br[i].z, br[i].w};
-#pragma unroll
-            for (int e = 0; e < EPU; ++e) {
-                const int dd = du * EPU + e;
-                uint8_t *dst = vbuf(st) + v_at(dd, key / EPU) + (key % EPU) * EB;
-                if constexpr (KV8)
-                    *dst = (uint8_t)(w4[e >> 2] >> (8 * (e & 3)));
-                else
-                    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
-            }
+            *reinterpret_cast<u32x4 *>(vbuf(st) + v_at(key, lu)) = vr[i];
         }
     };
 
@@ -663,6 +638,31 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // Online softmax of one tile's scores and O^T += V^T . P^T.
     auto softmax_pv = [&](int st, floatx16 (&s)[KB]) __attribute__((always_inline)) {
         const uint8_t *Vt = vbuf(st);
+        // A operands of O^T += V^T . P^T: lane (col, half) needs d = 32 mb + col
+        // of the 8 keys that pb pairs with it, read by transpose loads at the
+        // lane offsets v_lane[mb] plus a row offset known at compile time.  All
+        // of the tile's reads are issued here, ahead of the softmax, which
+        // covers their latency.
+        constexpr int VR = KV8 ? C4 : 2 * C4;  // 8-byte reads per d-block
+        uint32_t vraw[MB][VR][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < VR; ++i) {
+                // bf16: read i covers keys 4 i .. 4 i + 3 of the lane's 16-key chunk
+                // i / 2 rows; E4M3: keys 8 i .. (rows 32 (i / 2) + 8 (i % 2)).
+                const int row = KV8 ? 32 * (i >> 1) + 8 * (i & 1) : 16 * (i >> 1) + 4 * (i & 1);
+                if constexpr (!KV8) {
+                    const bd_s16x4 r = bd_lds_tr16(Vt + v_lane[mb] + row * KU * 16);
+                    const bd_i32x2 w = __builtin_bit_cast(bd_i32x2, r);
+                    vraw[mb][i][0] = (uint32_t)w[0];
+                    vraw[mb][i][1] = (uint32_t)w[1];
+                } else {
+                    const bd_i32x2 w = bd_lds_tr8(Vt + v_lane[mb] + row * KU * 16);
+                    vraw[mb][i][0] = (uint32_t)w[0];
+                    vraw[mb][i][1] = (uint32_t)w[1];
+                }
+            }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -699,20 +699,17 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         l_run += lsum;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            const int dd = mb * 32 + col;
-            if constexpr (!KV8) {
 #pragma unroll
-                for (int c4 = 0; c4 < C4; ++c4) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(Vt + v_at(dd, c4 * 2 + half));
-                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c4], o[mb], 0, 0, 0);
+            for (int c4 = 0; c4 < C4; ++c4) {
+                bf16x8 a;
+                if constexpr (!KV8) {
+                    const u32x4 w = {vraw[mb][2 * c4][0], vraw[mb][2 * c4][1], vraw[mb][2 * c4 + 1][0],
+                                     vraw[mb][2 * c4 + 1][1]};
+                    a = __builtin_bit_cast(bf16x8, w);
+                } else {
+                    a = bd_e4m3x8_to_bf16(vraw[mb][c4][0], vraw[mb][c4][1]);
                 }
-            } else {
-#pragma unroll
-                for (int m = 0; m < C4 / 2; ++m) {
-                    const u32x4 raw = *reinterpret_cast<const u32x4 *>(Vt + v_at(dd, m * 2 + half));
-                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd_e4m3x8_to_bf16(raw.x, raw.y), pb[2 * m], o[mb], 0, 0, 0);
-                    o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bd_e4m3x8_to_bf16(raw.z, raw.w), pb[2 * m + 1], o[mb], 0, 0, 0);
-                }
+                o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c4], o[mb], 0, 0, 0);
             }
         }
     };
@@ -1005,8 +1002,7 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
     const int P = min(max(prefix[it], 0), cap);
     const int nk = P + D;
     const SlotRanges vis = block_ranges(mode, slot, D, B);
-    const size_t kc_base = ((size_t)it * Hkv + g) * cap * HD;
-    const size_t vc_base = ((size_t)it * Hkv + g) * HD * cap;
+    const size_t kc_base = ((size_t)it * Hkv + g) * cap * HD;  // K and V cache rows [cap][HD]
     float m = -INFINITY, l = 0.f, o[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
@@ -1043,7 +1039,7 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
 #pragma unroll
             for (int e = 0; e < PER; ++e) {
                 const int dd = lane + 64 * e;
-                const float vv = key2 < P ? ld(vc, vc_base + (size_t)dd * cap + key2)
+                const float vv = key2 < P ? ld(vc, kc_base + (size_t)key2 * HD + dd)
                                           : ld(vb, (((size_t)it * D + (key2 - P)) * Hkv + g) * HD + dd);
                 o[e] = fmaf(pk, vv, o[e]);
             }

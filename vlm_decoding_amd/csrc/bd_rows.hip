@@ -346,19 +346,14 @@ hipError_t launch_spec_verify(const RowPlan &pl, const RowArgs &a, hipStream_t s
 // prefix; DiffusionVL notes: a finished block joins the history cache).
 // One workgroup per item, so the prefix length it reads and advances has a
 // single reader and writer; no host round trip is needed between verify and
-// append.  Keys are copied token by token (the d elements of a token are
-// contiguous on both sides); values go into the d-major cache with the L
-// accepted positions of each (head, d) row contiguous, so both writes are
-// runs of consecutive addresses.  The host bounds S * Hkv * d by 2^30, so the
-// element indices fit 32 bits.
+// append.  The host bounds S * Hkv * d by 2^30, so unit indices fit 32 bits.
 // ---------------------------------------------------------------------------
 constexpr int kAppendThreads = 512;
 
-template <typename E>
-__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(int D, int S, int Hkv, int d, int cap, E *k_cache,
-                                                                   E *v_cache, int32_t *prefix, const E *k_blk,
-                                                                   const E *v_blk, const int32_t *n_accept,
-                                                                   int32_t *dev_err) {
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(int D, int S, int Hkv, int row_bytes, int cap,
+                                                                   uint8_t *k_cache, uint8_t *v_cache, int32_t *prefix,
+                                                                   const uint8_t *k_blk, const uint8_t *v_blk,
+                                                                   const int32_t *n_accept, int32_t *dev_err) {
     const int it = blockIdx.x;
     const int P = prefix[it];
     const int L = n_accept ? n_accept[it] : D;
@@ -366,18 +361,20 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(int D, int S,
         if (threadIdx.x == 0 && dev_err) *dev_err = 1;
         return;
     }
-    const int per_g = L * d;    // elements of one KV head
-    const int n = per_g * Hkv;  // <= 2^30
-    const E *kb = k_blk + (size_t)it * S * Hkv * d;
-    const E *vb = v_blk + (size_t)it * S * Hkv * d;
-    E *kc = k_cache + (size_t)it * Hkv * cap * d;
-    E *vc = v_cache + (size_t)it * Hkv * d * cap;
+    // K and V rows alike: block [slot][Hkv][d] -> cache [Hkv][cap][d], whole
+    // 16-byte units (a row is 64 to 512 bytes).  Consecutive threads read
+    // consecutive units of the block.
+    const int U = row_bytes / 16;
+    const int per_t = Hkv * U;
+    const int n = L * per_t;  // <= S * Hkv * d * 4 / 16 <= 2^28
+    const size_t src0 = (size_t)it * S * per_t;
     for (int e = threadIdx.x; e < n; e += kAppendThreads) {
-        const int g = e / per_g, r = e - g * per_g;
-        const int t = r / d, dd = r - t * d;  // keys: dd fastest
-        kc[((size_t)g * cap + P + t) * d + dd] = kb[((size_t)t * Hkv + g) * d + dd];
-        const int dv = r / L, tv = r - dv * L;  // values: t fastest
-        vc[((size_t)g * d + dv) * cap + P + tv] = vb[((size_t)tv * Hkv + g) * d + dv];
+        const int t = e / per_t, r = e - t * per_t;
+        const int g = r / U, u = r - g * U;
+        const size_t src = src0 + e;
+        const size_t dst = (((size_t)it * Hkv + g) * cap + P + t) * U + u;
+        reinterpret_cast<uint4 *>(k_cache)[dst] = reinterpret_cast<const uint4 *>(k_blk)[src];
+        reinterpret_cast<uint4 *>(v_cache)[dst] = reinterpret_cast<const uint4 *>(v_blk)[src];
     }
     __syncthreads();  // every thread has read P
     if (threadIdx.x == 0) prefix[it] = P + L;
@@ -386,18 +383,9 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(int D, int S,
 hipError_t launch_kv_append(int n, int D, int S, int Hkv, int d, int cap, int elem_bytes, void *k_cache, void *v_cache,
                             int32_t *prefix, const void *k_blk, const void *v_blk, const int32_t *n_accept,
                             int32_t *dev_err, hipStream_t s) {
-    if (elem_bytes == 4)
-        hipLaunchKernelGGL((kv_append_kernel<uint32_t>), dim3(n), dim3(kAppendThreads), 0, s, D, S, Hkv, d, cap,
-                           (uint32_t *)k_cache, (uint32_t *)v_cache, prefix, (const uint32_t *)k_blk,
-                           (const uint32_t *)v_blk, n_accept, dev_err);
-    else if (elem_bytes == 2)
-        hipLaunchKernelGGL((kv_append_kernel<uint16_t>), dim3(n), dim3(kAppendThreads), 0, s, D, S, Hkv, d, cap,
-                           (uint16_t *)k_cache, (uint16_t *)v_cache, prefix, (const uint16_t *)k_blk,
-                           (const uint16_t *)v_blk, n_accept, dev_err);
-    else
-        hipLaunchKernelGGL((kv_append_kernel<uint8_t>), dim3(n), dim3(kAppendThreads), 0, s, D, S, Hkv, d, cap,
-                           (uint8_t *)k_cache, (uint8_t *)v_cache, prefix, (const uint8_t *)k_blk,
-                           (const uint8_t *)v_blk, n_accept, dev_err);
+    hipLaunchKernelGGL(kv_append_kernel, dim3(n), dim3(kAppendThreads), 0, s, D, S, Hkv, d * elem_bytes, cap,
+                       (uint8_t *)k_cache, (uint8_t *)v_cache, prefix, (const uint8_t *)k_blk, (const uint8_t *)v_blk,
+                       n_accept, dev_err);
     return hipGetLastError();
 }
 
