@@ -286,7 +286,7 @@ def make_two_stream(p: dict, seed: int) -> dict:
     sequence has fewer response tokens than the longest).  Lc and Ln are the
     maxima over sequences; a shorter clean stream ends in plain clean tokens.
     Arrays: q [n][L][Hq][d] with L = Lc + Ln; k and v [n][Hkv][cap][d]
-    (cap = L rounded up to 64, zeros past L); spans int32
+    (cap = L rounded up to p["cap_align"], default 64, zeros past L); spans int32
     [n][max_spans][2] = (clean start, length) of each response; n_spans [n].
     Draw order: q, then k, then v, as N(0, 1) rounded to bf16.
     """
@@ -307,7 +307,8 @@ def make_two_stream(p: dict, seed: int) -> dict:
         ln_l.append(sum(r for _, r in sp))
     Lc, Ln = max(lc_l), max(ln_l)
     L = Lc + Ln
-    cap = (L + 63) // 64 * 64
+    align = int(p.get("cap_align", 64))
+    cap = (L + align - 1) // align * align
     max_spans = max(len(sp) for sp in spans_l)
     spans = np.zeros((n, max_spans, 2), np.int32)
     n_spans = np.zeros(n, np.int32)

@@ -576,6 +576,9 @@ TWO_STREAM_CASES = [
     ("empty_span_and_padding", dict(turns=[[(5, 0), (6, 23)], [(2, 40)]], D=16)),
     # 6 units (one sequence, one KV head, 1420 positions): 32 splits, the 32-slot merge
     ("few_units_32_splits", dict(n_seq=1, Hq=1, Hkv=1, d=128, vision=600, turns=[(20, 400)], D=16)),
+    # L = 200 positions in a 224-slot array: the smallest capacity the ABI takes (a
+    # multiple of 32), so the last tile ends at the array's end
+    ("cap_odd_multiple_of_32", dict(vision=120, turns=[(20, 30)], cap_align=32)),
 ]
 
 

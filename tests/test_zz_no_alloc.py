@@ -54,6 +54,8 @@ CASES = [
     # (label, overrides, mode, items checked against the oracle)
     ("8_layers_prefix_4096", dict(n_items=8, prefix=("fixed", 4096)), BIDIR, [0, 7]),
     ("2_items_ragged_smaller", dict(n_items=2, prefix=("list", [700, 33])), CAUSAL, [0, 1]),
+    # the balanced split plan (a mode flag): its exchange also holds each unit's split count
+    ("4_items_ragged_balanced", dict(n_items=4, prefix=("list", [3000, 150, 1700, 4096])), BIDIR, [1, 3]),
 ]
 
 
@@ -67,7 +69,7 @@ def test_noalloc_matches_bd_attn_step_on_two_calls_in_a_row():
         p = synth.params_for(3, dtype=BF16, D=16, n_masked=8, V=1000, plant=None, mode=mode, **ov)
         st = synth.make_step(p, seed=len(label) * 101)
         _say("noalloc %s n=%d mode=%d prefix=%s" % (label, p["n_items"], mode, st["prefix"].tolist()))
-        ds = DeviceStep(st)
+        ds = DeviceStep(st, balanced=label.endswith("balanced"))
         ds.attn()
         torch.cuda.synchronize()
         want = ds.out.clone()
