@@ -214,6 +214,19 @@ def test_attention_balanced_deterministic_and_quad(dev):
     _run_attention(dev, synth.make_quad_step(q, 66), label="balanced_quad_B16", balanced=True)
 
 
+@pytest.mark.parametrize("n_items", [64, 65])
+def test_attention_balanced_at_the_item_limit(dev, n_items):
+    """The balanced plan takes one lane per item: 64 ragged items (empty prefixes
+    and prefixes shorter than a tile among them) use it, 65 fall back to the plain
+    plan.  Every item of the output against the oracle."""
+    rng = np.random.default_rng(640 + n_items)
+    pre = rng.integers(0, 2400, size=n_items)
+    pre[::9] = 0
+    pre[1::11] = rng.integers(1, 32, size=len(pre[1::11]))
+    p = synth.params_for(3, n_items=n_items, D=16, prefix=("list", pre.tolist()), V=1000, n_masked=8, plant=None)
+    _run_attention(dev, synth.make_step(p, 640 + n_items), label="balanced_%d_items" % n_items, balanced=True)
+
+
 # Few items with long prefixes: the plan gives such calls 32 or 64 splits per
 # unit (every workgroup on a CU of its own) and merges them with the 32-slot
 # merge instance or its two-split-wave form.  Ragged prefixes give units with
