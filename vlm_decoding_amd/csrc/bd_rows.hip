@@ -134,7 +134,8 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
             const int end = (int)((long long)V4 * (c + 1) / cpr);
             const float4 *x4 = reinterpret_cast<const float4 *>(x);
             // Two batches of kBatch / 2 loads per thread alternate: the next
-            // batch is in flight while the current one is reduced.
+            // batch is in flight while the current one is reduced.  Each logit
+            // is read once, so the loads are non-temporal.
             constexpr int HB = kBatch / 2;
             constexpr int STEP = NT * HB;
             float4 va[HB], vb[HB];
@@ -142,7 +143,10 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
 #pragma unroll
                 for (int k = 0; k < HB; ++k) {
                     const int u = u0 + k * NT + tid;
-                    if (u < end) v[k] = x4[u];
+                    if (u < end) {
+                        const floatx4 t = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(x4) + u);
+                        v[k] = make_float4(t[0], t[1], t[2], t[3]);
+                    }
                 }
             };
             auto reduce = [&](const float4(&v)[HB], int u0) __attribute__((always_inline)) {
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
 #pragma unroll
                 for (int k = 0; k < kBatch; ++k) {
                     const int e = e0 + k * NT + tid;
-                    if (e < end) v[k] = x[e];
+                    if (e < end) v[k] = __builtin_nontemporal_load(x + e);
                 }
 #pragma unroll
                 for (int k = 0; k < kBatch; ++k) {
