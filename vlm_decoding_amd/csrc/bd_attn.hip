@@ -873,9 +873,16 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
         if (sw * MAXS + s < slots_to_load) {
-            ml[s] = p.ws_ml[(base + s) * NT_TILE + src_t];
+            // Each partial is read once: non-temporal loads.
+            const floatx2_nt m2 =
+                __builtin_nontemporal_load(reinterpret_cast<const floatx2_nt *>(p.ws_ml) + (base + s) * NT_TILE + src_t);
+            ml[s] = make_float2(m2[0], m2[1]);
 #pragma unroll
-            for (int j = 0; j < QPT; ++j) v[j][s] = wo[((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t];
+            for (int j = 0; j < QPT; ++j) {
+                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wo) +
+                                                           ((base + s) * QQ + jq * QPT + j) * NT_TILE + src_t);
+                v[j][s] = make_uint4(t[0], t[1], t[2], t[3]);
+            }
         }
     int nsplit;
     if constexpr (SEQ) {
