@@ -13,11 +13,13 @@ rotated so that no step finds its K/V in the 256 MB last-level cache: every
 step streams its bytes from HBM.
 
 Prints one JSON line.  ``value`` is timed steps over the wall time of the K
-timed steps (bracketed by device synchronisations).  Inside that region HIP
-events on the launch stream bracket the attention call and the commit call
-of sampled steps (every step when K <= 400, else K / 200 evenly spaced
-ones); ``roofline.achieved`` is the attention call's algorithmic bytes over
-the mean of those samples, and median / p10 / p90 are reported with them.
+timed steps (bracketed by device synchronisations; one event pair around
+them gives the GPU time, ``gpu_event_us_per_step``).  After the timed region
+a sampled pass runs the same step max(20, --event-samples) more times with
+HIP events on the launch stream around the attention call and the commit
+call of every step; ``roofline.achieved`` is the attention call's
+algorithmic bytes over the mean of those samples, and median / p10 / p90
+are reported with them (``steps_per_s_at_median`` = 1 / the step median).
 The events are recorded without the system-scope cache release of a default
 event record (hipEventDisableSystemFence), which would cost the GPU several
 microseconds per record.
@@ -635,7 +637,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--event-samples", type=int, default=200,
-                    help="timed steps whose calls are bracketed by events (all of them when K <= 2x this)")
+                    help="steps of the sampled pass after the timed region, each call between events (at least 20)")
     ap.add_argument("--cold-steps", type=int, default=100,
                     help="headline steps timed one by one after a 1 GiB flush (0 to skip)")
     ap.add_argument("--config-iters", type=int, default=40,
@@ -690,7 +692,8 @@ def main():
     # The commit mutates the block state (masked flags, tokens), so every step
     # gets its own copy of its set's initial state, prepared before timing: one
     # 128-byte row per step (masked at bytes 0..15, tokens at 64..127).
-    total = args.warmup + args.steps
+    n_samples = max(20, args.event_samples)
+    total = args.warmup + args.steps + n_samples
     rows = np.zeros((N_SETS, 128), dtype=np.uint8)
     for k, ds in enumerate(sets):
         rows[k, :16] = ds.masked0.cpu().numpy().reshape(-1)
@@ -717,39 +720,44 @@ def main():
     torch.cuda.synchronize()
     if status:
         raise RuntimeError("a library call failed during warm-up (status %d)" % status)
-    stride = 1 if args.steps <= 2 * args.event_samples else args.steps // args.event_samples
-    sampled = {i: n for n, i in enumerate(range(0, args.steps, stride))}
-    ev = HipEvents(3 * len(sampled) + 2)
-    outer = 3 * len(sampled)
+    # The timed region: exactly K steps, with one event pair around all of them
+    # (per-call events inside it would add their own records to the GPU's work).
+    ev = HipEvents(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev.record(outer, sh)
+    ev.record(0, sh)
     for i in range(args.steps):
         j = args.warmup + i
-        n = sampled.get(i)
-        if n is None:
-            status |= attn_fn(*attn_args[j % N_SETS])
-            status |= commit_fn(*commit_args[j])
-            continue
+        status |= attn_fn(*attn_args[j % N_SETS])
+        status |= commit_fn(*commit_args[j])
+    ev.record(1, sh)
+    t_enq = time.perf_counter() - t0
+    # The clock stops when the last event is seen complete by polling: a blocking
+    # synchronize wakes the host up to several ms late now and then, which would
+    # be timed as GPU work.
+    ev.wait(1)
+    elapsed = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    if status:
+        raise RuntimeError("a library call failed in the timed loop (status %d)" % status)
+    gpu_ms_per_step = ev.ms(0, 1) / args.steps
+    ev.destroy()
+    # The sampled pass, after the timed region and not part of `value`: the same
+    # step, each call between events, for the per-call distributions.
+    ev = HipEvents(3 * n_samples)
+    for n in range(n_samples):
+        j = args.warmup + args.steps + n
         ev.record(3 * n, sh)
         status |= attn_fn(*attn_args[j % N_SETS])
         ev.record(3 * n + 1, sh)
         status |= commit_fn(*commit_args[j])
         ev.record(3 * n + 2, sh)
-    ev.record(outer + 1, sh)
-    t_enq = time.perf_counter() - t0
-    # The clock stops when the last event is seen complete by polling: a blocking
-    # synchronize wakes the host up to several ms late now and then, which would
-    # be timed as GPU work.
-    ev.wait(outer + 1)
-    elapsed = time.perf_counter() - t0
     torch.cuda.synchronize()
     if status:
-        raise RuntimeError("a library call failed in the timed loop (status %d)" % status)
-    attn_ms = [ev.ms(3 * n, 3 * n + 1) for n in range(len(sampled))]
-    conf_ms = [ev.ms(3 * n + 1, 3 * n + 2) for n in range(len(sampled))]
-    step_ms = [ev.ms(3 * n, 3 * n + 2) for n in range(len(sampled))]
-    gpu_ms_per_step = ev.ms(outer, outer + 1) / args.steps
+        raise RuntimeError("a library call failed in the sampled pass (status %d)" % status)
+    attn_ms = [ev.ms(3 * n, 3 * n + 1) for n in range(n_samples)]
+    conf_ms = [ev.ms(3 * n + 1, 3 * n + 2) for n in range(n_samples)]
+    step_ms = [ev.ms(3 * n, 3 * n + 2) for n in range(n_samples)]
     ev.destroy()
     ms_per_step = elapsed * 1e3 / args.steps
     attn_d, conf_d, step_d = dist_us(attn_ms), dist_us(conf_ms), dist_us(step_ms)
@@ -830,7 +838,8 @@ def main():
         "confidence_commit_traffic": traffic.get("commit"),
         "host_enqueue_us_per_step": round(t_enq * 1e6 / args.steps, 2),
         "gpu_event_us_per_step": round(gpu_ms_per_step * 1e3, 2),
-        "event_stride": stride,
+        "event_samples": n_samples,
+        "steps_per_s_at_median": round(1e6 / step_d["median"], 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cold_step": cold,
