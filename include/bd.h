@@ -30,7 +30,8 @@
  *    BD_E_LAUNCH means the HIP runtime rejected a launch (bd_last_hip_error()).
  *  - Workspaces: size them with the matching *_workspace_bytes() call and
  *    zero-fill them once before first use.  Each call leaves the counter area
- *    it uses zeroed again, so later calls with the same descriptor on the same
+ *    it uses (for the confidence and verify calls: the whole workspace)
+ *    zeroed again, so later calls with the same descriptor on the same
  *    stream can reuse the workspace.  The counter area's place depends on the
  *    descriptor: a workspace used with another descriptor, or for anything
  *    else, must be zero-filled again before such a call.  Calls that overlap

@@ -926,6 +926,41 @@ def test_verify_ragged_requests(dev):
     np.testing.assert_array_equal(ds.argmax.cpu().numpy(), amax_ref)
 
 
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_row_calls_leave_workspace_zeroed(dev, cfg):
+    """The confidence / verify kernel publishes its partials into tagged
+    workspace slots; the finishing workgroup clears them, and the ticket
+    counters, before the call ends.  After every call the whole workspace is
+    zero again, and a repeated call on it gives bitwise the same outputs."""
+    torch = dev["torch"]
+    s = synth.config_step(cfg)
+    p = s["params"]
+    ds = _ds(dev, s)
+    outs = []
+    for rep in range(3):
+        _say("cfg%d row call %d" % (cfg, rep))
+        if cfg == 4:
+            L = ds.verify()
+            torch.cuda.synchronize()
+            assert int(ds.verify_ws.count_nonzero()) == 0
+            outs.append([L.cpu().clone(), ds.argmax.cpu().clone()])
+        else:
+            ds.reset_block_state()
+            ds.confidence_commit()
+            torch.cuda.synchronize()
+            assert int(ds.commit_ws.count_nonzero()) == 0
+            outs.append([t.cpu().clone() for t in (ds.conf, ds.argmax, ds.committed, ds.n_committed,
+                                                   ds.masked, ds.tokens)])
+    for later in outs[1:]:
+        for a, b in zip(outs[0], later):
+            assert a.numpy().tobytes() == b.numpy().tobytes()  # bitwise (unmasked confidences are NaN)
+    if cfg == 4:
+        L_ref, amax_ref = oracle.spec_verify(s["logits"], s["draft"])
+        np.testing.assert_array_equal(outs[0][0].numpy(), L_ref)
+    else:
+        _compare_commit(dev, ds, p, s["masked"], s["tokens"], s["logits"], "cfg%d repeated" % cfg)
+
+
 @pytest.mark.parametrize("dtype", [F32, BF16])
 def test_append_overflow_and_partial(dev, dtype):
     torch = dev["torch"]

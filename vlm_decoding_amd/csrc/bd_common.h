@@ -102,6 +102,12 @@ __device__ __forceinline__ uint2 bd_coherent_load_u2(const uint2 *p) {
                                          __HIP_MEMORY_SCOPE_AGENT);
     return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
 }
+__device__ __forceinline__ void bd_coherent_store64(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t bd_coherent_load64(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Non-temporal stores for data the next kernel consumes: the lines are not
 // kept dirty in L2, so the write-back that ends a kernel has little left to
 // do and the next kernel on the stream starts sooner.

@@ -56,7 +56,7 @@ hipError_t launch_attention_vec(const AttnArgs &a, int dtype, hipStream_t s);
 struct RowPlan {
     int groups;    // workgroups per request
     int max_cpr;   // most chunks one participating row is cut into
-    size_t part_off, idx_off, grp_off, cnt_off, ws_bytes;
+    size_t part_off, grp_off, cnt_off, ws_bytes;
     bool ok;       // the grid fits one launch
 };
 RowPlan plan_rows(int n_req, int D, int V);

@@ -20,16 +20,22 @@
 // (up to 16 per thread in flight) into a running (max, index of first max,
 // sum of exp(x - max)) per thread, combined in a fixed tree.
 //
-// Hand-off.  Every workgroup of the request - idle ones included - takes one
-// ticket after publishing its partial, so the last one to arrive (the
-// finisher) starts only after every workgroup of the launch has read the
-// masked flags it rewrites.  Tickets on one address are served one after
-// another (about 10 ns each, measured), so they go in two levels: a
-// workgroup tickets its group of kTicketGroup workgroups, the last of a group
-// tickets the request; every counter has a 256-byte line of its own.  The
-// finisher stages the request's partials in LDS, merges each row's chunks in
-// chunk order (16 lanes per row, a fixed tree) and runs the one-wave commit /
-// verify tail.  No float atomics, so results are identical run to run.
+// Hand-off.  The finisher of a request is elected when the workgroups start:
+// each takes a ticket on its group's counter (kTicketGroup workgroups; tickets
+// on one address are served one after another, about 10 ns each, measured),
+// the last of a group takes one on the request's counter, and the workgroup
+// holding the request's last ticket finishes.  These round trips overlap the
+// logits stream.  Every workgroup - idle ones included - then publishes its
+// partial as two 64-bit atomic stores tagged non-zero, without waiting for
+// them; the finisher polls the request's slots until all are tagged, stages
+// the partials in LDS, clears the slots, merges each row's chunks in chunk
+// order (16 lanes per row, a fixed tree) and runs the one-wave commit /
+// verify tail.  Waiting is safe: when the finisher is known every workgroup of
+// its request has taken its ticket, so has started, and none of them waits.
+// A slot is published after its workgroup's masked-flag reads have returned,
+// so the finisher rewrites the flags only after every reader is done.  Every
+// counter has a 256-byte line of its own.  No float atomics, so results are
+// identical run to run.
 #include "bd_common.h"
 #include "bd_internal.h"
 #include "bd_rowreduce.h"
@@ -52,6 +58,7 @@ constexpr int kMinChunk = 1024;     // ... lower bound of the plan (one 16-byte 
 constexpr int kMinChunkRun = 256;   // lower bound when few slots take part
 constexpr int kTicketGroup = 16;    // workgroups per first-level ticket counter
 constexpr int kCounterStride = 64;  // ints between counters (a 256-byte line each)
+constexpr int kPollLimit = 1 << 20; // bound of the finisher's wait (rounds of loads)
 
 struct RowParams {
     const float *logits;
@@ -63,8 +70,7 @@ struct RowParams {
     int32_t *n_committed;
     const int32_t *draft;
     int32_t *accepted_len;
-    float2 *part_ms;  // [n_req][G] (max, sum of exp(x - max))
-    int *part_i;      // [n_req][G] index of the first max
+    uint64_t *part;   // [n_req][G][2] published partials: (max, index of the first max + 2), (sum, 1)
     int *grp_cnt;     // [n_req][NG] first-level tickets, kCounterStride apart
     int *req_cnt;     // [n_req] second-level tickets, kCounterStride apart
     int n_req, D, V, S, G, NG, max_cpr;
@@ -106,6 +112,17 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     const int r = blockIdx.x / p.G;
     const int b = blockIdx.x - r * p.G;
     const size_t ob = (size_t)r * p.D;
+    const int grp = b / kTicketGroup;
+    const int gsize = min(kTicketGroup, p.G - grp * kTicketGroup);
+    int *gc = p.grp_cnt + ((size_t)r * p.NG + grp) * kCounterStride;
+    int *rc = p.req_cnt + (size_t)r * kCounterStride;
+
+    // Finisher election, at the start: the workgroup that takes the request's
+    // last ticket (the last of its group, then the last group) finishes.  Its
+    // round trips overlap the logits stream, and when it is known every other
+    // workgroup of the request has started, so the finisher may wait for them.
+    int tk = 0;
+    if (tid == 0) tk = bd_ticket(gc);
 
     // The rows that take part and the j-th of them.  Each wave reads the flags
     // itself, so no barrier is needed before the loads.
@@ -121,6 +138,11 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     const bool in_mask = (mask >> lane) & 1ull;
     const int cpr = nm == 0 ? 0 : min(p.G / nm, p.max_cpr);  // chunks per participating row
     const bool active = b < nm * cpr;
+    int rq = 0;
+    if (tid == 0 && tk == gsize - 1) {
+        bd_coherent_store(gc, 0);  // every ticket of the group is taken: reset for the next call
+        if (p.NG > 1) rq = bd_ticket(rc);
+    }
 
     Part acc{-INFINITY, 0.f, 0x7fffffff};
     if (active) {
@@ -185,51 +207,63 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
     if (lane == 0) s_part[w] = acc;
     __syncthreads();
     if (tid == 0) {
-        if (active) {
-            Part t = s_part[0];
+        // Publish: every workgroup, idle ones included (an idle partial is the
+        // identity), writes its slot only after its flag reads have returned
+        // (the partial depends on them).  Each word is one 64-bit atomic store
+        // whose upper half is non-zero, so a reader that sees it non-zero sees
+        // the whole word of this call.
+        Part t = s_part[0];
 #pragma unroll
-            for (int k = 1; k < NT / 64; ++k) t = combine(t, s_part[k]);
-            const size_t o = (size_t)r * p.G + b;
-            bd_coherent_store2(reinterpret_cast<float *>(&p.part_ms[o]), t.m, t.s);
-            bd_coherent_store(p.part_i + o, t.i);
-        }
-        bd_wait_all_memory();  // the partial (and this workgroup's flag reads) precede the ticket
-        const int grp = b / kTicketGroup;
-        const int gsize = min(kTicketGroup, p.G - grp * kTicketGroup);
-        int *gc = p.grp_cnt + ((size_t)r * p.NG + grp) * kCounterStride;
-        bool last = false;
-        if (bd_ticket(gc) == gsize - 1) {
-            bd_coherent_store(gc, 0);  // every ticket of the group is taken: reset for the next call
-            // one group: its last workgroup is the request's last
-            last = p.NG == 1 || bd_ticket(p.req_cnt + (size_t)r * kCounterStride) == p.NG - 1;
-        }
-        s_done = last;
+        for (int k = 1; k < NT / 64; ++k) t = combine(t, s_part[k]);
+        uint64_t *slot = p.part + ((size_t)r * p.G + b) * 2;
+        bd_coherent_store64(slot, ((uint64_t)((uint32_t)t.i + 2u) << 32) | __float_as_uint(t.m));
+        bd_coherent_store64(slot + 1, (1ull << 32) | __float_as_uint(t.s));
+        s_done = tk == gsize - 1 && (p.NG == 1 || rq == p.NG - 1);
     }
     __syncthreads();
     if (!s_done) return;
 
-    // Finisher of request r.  Stage the nm * cpr partials (chunk c of row j at
-    // j * cpr + c) in LDS with one round of coherent loads.
+    // Finisher of request r.  Every ticket is taken: reset the request counter.
+    // Then wait until all G slots are published (which also means every
+    // workgroup has read the masked flags rewritten below) and stage the
+    // nm * cpr partials (chunk c of row j at j * cpr + c) in LDS.  The wait is
+    // bounded so the kernel always ends; it cannot run out, since every
+    // workgroup of the request has started and publishes without waiting.
+    if (tid == 0 && p.NG > 1) bd_coherent_store(rc, 0);
     const int n_part = nm * cpr;
-    const size_t pb = (size_t)r * p.G;
     {
+        uint64_t *pp = p.part + (size_t)r * p.G * 2;
         constexpr int PER = kMaxGroups / NT;
-        float2 ms[PER];
-        int ix[PER];
+        uint64_t wa[PER], wb[PER];
+        unsigned pend = 0;
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int q = tid + k * NT;
-            if (q < n_part) {
-                ms[k] = bd_coherent_load2(reinterpret_cast<const float *>(&p.part_ms[pb + q]));
-                ix[k] = bd_coherent_load(p.part_i + pb + q);
-            }
+            wa[k] = wb[k] = 0;
+            if (tid + k * NT < p.G) pend |= 1u << k;
+        }
+        for (int it = 0; pend != 0 && it < kPollLimit; ++it) {
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                if ((pend >> k) & 1u) {
+                    const int q = tid + k * NT;
+                    wa[k] = bd_coherent_load64(pp + 2 * q);
+                    wb[k] = bd_coherent_load64(pp + 2 * q + 1);
+                }
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                if ((wa[k] >> 32) != 0 && (wb[k] >> 32) != 0) pend &= ~(1u << k);
+            if (pend != 0) __builtin_amdgcn_s_sleep(1);
         }
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int q = tid + k * NT;
             if (q < n_part) {
-                s_ms[q] = ms[k];
-                s_i[q] = ix[k];
+                s_ms[q] = make_float2(__uint_as_float((uint32_t)wa[k]), __uint_as_float((uint32_t)wb[k]));
+                s_i[q] = (int)((uint32_t)(wa[k] >> 32) - 2u);
+            }
+            if (q < p.G) {  // read: clear the slot for the next call
+                bd_coherent_store64(pp + 2 * q, 0);
+                bd_coherent_store64(pp + 2 * q + 1, 0);
             }
         }
     }
@@ -260,20 +294,14 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         const bool bad = lane < p.D && a != p.draft[ob + lane];
         const unsigned long long bb = __builtin_amdgcn_ballot_w64(bad);
         if (lane < p.D && p.argmax) p.argmax[ob + lane] = a;
-        if (lane == 0) {
-            p.accepted_len[r] = bb ? (__ffsll((long long)bb) - 1) : p.D;
-            bd_coherent_store(p.req_cnt + (size_t)r * kCounterStride, 0);
-        }
+        if (lane == 0) p.accepted_len[r] = bb ? (__ffsll((long long)bb) - 1) : p.D;
         return;
     }
     const unsigned long long tb = commit_request(s_conf, s_arg, mask, nm, p.D, p.S, p.tau, lane, p.masked + ob,
                                                  p.tokens + ob, p.conf ? p.conf + ob : nullptr,
                                                  p.argmax ? p.argmax + ob : nullptr,
                                                  p.committed ? p.committed + ob : nullptr);
-    if (lane == 0) {
-        if (p.n_committed) p.n_committed[r] = __popcll(tb);
-        bd_coherent_store(p.req_cnt + (size_t)r * kCounterStride, 0);
-    }
+    if (lane == 0 && p.n_committed) p.n_committed[r] = __popcll(tb);
 }
 
 RowParams make_params(const RowPlan &pl, const RowArgs &a) {
@@ -288,8 +316,7 @@ RowParams make_params(const RowPlan &pl, const RowArgs &a) {
     p.draft = a.draft;
     p.accepted_len = a.accepted_len;
     char *ws = (char *)a.ws;
-    p.part_ms = (float2 *)(ws + pl.part_off);
-    p.part_i = (int *)(ws + pl.idx_off);
+    p.part = (uint64_t *)(ws + pl.part_off);
     p.grp_cnt = (int *)(ws + pl.grp_off);
     p.req_cnt = (int *)(ws + pl.cnt_off);
     p.n_req = a.n_req;
@@ -324,8 +351,7 @@ RowPlan plan_rows(int n_req, int D, int V) {
         off += (bytes + 255) / 256 * 256;
         return o;
     };
-    pl.part_off = take((size_t)n_req * pl.groups * 8);
-    pl.idx_off = take((size_t)n_req * pl.groups * 4);
+    pl.part_off = take((size_t)n_req * pl.groups * 16);
     const int ng = (pl.groups + kTicketGroup - 1) / kTicketGroup;
     pl.grp_off = take((size_t)n_req * ng * kCounterStride * 4);
     pl.cnt_off = take((size_t)n_req * kCounterStride * 4);
