@@ -106,10 +106,11 @@ __device__ __forceinline__ unsigned long long commit_request(const float *conf, 
             cj[4 * q + 3] = c4.w;
         }
         const unsigned mj = (unsigned)(mask >> j0) & 0xffffu;
+        // Bitwise operators, not && / ||: no branch per slot.
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int j = j0 + e;
-            const bool ahead = ((mj >> e) & 1u) && (cj[e] > cf || (cj[e] == cf && j < lane));
+            const bool ahead = (((mj >> e) & 1u) != 0) & ((cj[e] > cf) | ((cj[e] == cf) & (j < lane)));
             rank += ahead ? 1 : 0;
         }
     }

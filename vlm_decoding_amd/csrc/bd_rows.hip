@@ -275,11 +275,26 @@ __global__ __launch_bounds__(NT) void row_kernel(RowParams p) {
         const int j = j0 + (tid >> 4);
         const int c0 = tid & 15;
         Part t{-INFINITY, 0.f, 0x7fffffff};
-        if (j < nm)
-            for (int c = c0; c < cpr; c += 16) {
+        if (j < nm) {
+            // Four chunks' partials are read before they are combined (in
+            // chunk order), so the LDS latency is paid once per four.
+            int c = c0;
+            for (; c + 48 < cpr; c += 64) {
+                float2 m2[4];
+                int ix[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    m2[u] = s_ms[j * cpr + c + 16 * u];
+                    ix[u] = s_i[j * cpr + c + 16 * u];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) t = combine(t, Part{m2[u].x, m2[u].y, ix[u]});
+            }
+            for (; c < cpr; c += 16) {
                 const float2 m2 = s_ms[j * cpr + c];
                 t = combine(t, Part{m2.x, m2.y, s_i[j * cpr + c]});
             }
+        }
         t = reduce16(t);
         if (j < nm && c0 == 0) {
             const int slot = s_slot[j];
