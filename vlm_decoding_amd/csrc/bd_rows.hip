@@ -55,7 +55,15 @@ constexpr int kMaxGroups = 1024;    // workgroups per request (the finisher stag
 #endif
 constexpr int kMaxChunk = BD_ROW_MAX_CHUNK;  // floats per workgroup, upper target when every slot takes part
 constexpr int kMinChunk = 1024;     // ... lower bound of the plan (one 16-byte load per thread)
-constexpr int kMinChunkRun = 256;   // lower bound when few slots take part
+#ifndef BD_ROW_MIN_CHUNK_RUN
+#define BD_ROW_MIN_CHUNK_RUN 8192
+#endif
+// Lower bound of a chunk when few slots take part: the plan's G workgroups
+// are sized for every slot, and a row never gets more than V / kMinChunkRun
+// chunks (nor fewer than the plan's own), so with few masked slots part of
+// the workgroups stay idle instead of streaming slivers, and the finisher
+// merges fewer partials.
+constexpr int kMinChunkRun = BD_ROW_MIN_CHUNK_RUN;
 constexpr int kTicketGroup = 16;    // workgroups per first-level ticket counter
 constexpr int kCounterStride = 64;  // ints between counters (a 256-byte line each)
 constexpr int kPollLimit = 1 << 20; // bound of the finisher's wait (rounds of loads)
