@@ -783,11 +783,16 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // a wave covers one contiguous span.  16-byte unit qq (output quads 2qq and
     // 2qq+1, i.e. block mb = qq/2, quads i4 = 2(qq%2) and 2(qq%2)+1) of thread t
     // of split s of unit u lives at [(u * max_splits + s) * (QUADS/2) + qq][t].
+    // They are stored write-through (sc1): the merge kernel, next on the
+    // stream, then reads them from the last-level cache (non-temporal stores
+    // measured slower there), and the L2 holds nothing dirty for the
+    // kernel-end write-back.
     constexpr int QUADS = MB * 4;
     if (wave_active) {
         const size_t base = ((size_t)unit * p.max_splits + split);
         const float inv = l_tot > 0.f ? vs / l_tot : 0.f;
-        uint4 *wo = reinterpret_cast<uint4 *>(p.ws_o) + base * (QUADS / 2) * NT + tid;
+        const __amdgpu_buffer_rsrc_t ro =
+            bd_region(reinterpret_cast<uint4 *>(p.ws_o) + base * (QUADS / 2) * NT, (QUADS / 2) * NT * 16);
 #pragma unroll
         for (int qq = 0; qq < QUADS / 2; ++qq) {
             const int mb = qq >> 1, i0 = 8 * (qq & 1);
@@ -796,9 +801,9 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
             v.y = bd_f32_to_bf16(o[mb][i0 + 2] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][i0 + 3] * inv) << 16);
             v.z = bd_f32_to_bf16(o[mb][i0 + 4] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][i0 + 5] * inv) << 16);
             v.w = bd_f32_to_bf16(o[mb][i0 + 6] * inv) | ((uint32_t)bd_f32_to_bf16(o[mb][i0 + 7] * inv) << 16);
-            bd_store_nt(&wo[(size_t)qq * NT], v);
+            bd_store_wt(ro, (unsigned)(qq * NT + tid) * 16u, v);
         }
-        bd_store_nt(&p.ws_ml[base * NT + tid], make_float2(m_run, l_tot));
+        bd_store_wt(bd_region(p.ws_ml + base * NT, NT * 8), (unsigned)tid * 8u, make_float2(m_run, l_tot));
     }
 }
 

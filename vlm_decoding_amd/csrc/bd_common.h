@@ -122,6 +122,24 @@ __device__ __forceinline__ void bd_store_nt(void *p, uint2 v) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2 *>(p));
 }
+// Write-through stores (cache policy sc1) of 16 or 8 bytes at byte offset
+// `off` of a region of `bytes` bytes at `base`, through a raw buffer
+// resource (stores past the region are dropped by the range check).  The
+// lines do not stay dirty in L2 for the kernel-end write-back, and unlike
+// non-temporal stores they stay in the last-level cache, where the next
+// kernel on the stream reads them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bd_region(void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, (int)bytes, 0x00020000);
+}
+constexpr int kPolicySc1 = 16;  // buffer-op cache policy bits: sc1
+__device__ __forceinline__ void bd_store_wt(__amdgpu_buffer_rsrc_t r, unsigned off, uint4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, (int)off, 0, kPolicySc1);
+}
+__device__ __forceinline__ void bd_store_wt(__amdgpu_buffer_rsrc_t r, unsigned off, float2 v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v.x), __float_as_uint(v.y)}, r, (int)off, 0,
+                                          kPolicySc1);
+}
 // Wait until every memory operation this thread issued has completed (for a
 // store: acknowledged by the memory side).  The empty asm statements keep the
 // compiler from moving any memory access across the wait.
