@@ -60,9 +60,7 @@ __device__ __forceinline__ bool bd_wave_any(bool p) {
     return __builtin_amdgcn_ballot_w64(p) != 0;
 }
 
-// Cross-workgroup hand-off without whole-cache maintenance (the LM head's;
-// the confidence kernel publishes self-tagged 64-bit words that its finisher
-// polls, with its own argument in bd_rows.hip).  Partial results
+// Cross-workgroup hand-off without whole-cache maintenance.  Partial results
 // are written with agent-scope relaxed atomic stores, which gfx950 performs
 // at the agent's coherence point (through the L2, not kept only in one XCD's
 // L2), and read back with agent-scope relaxed atomic loads, which read from
