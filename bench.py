@@ -120,15 +120,18 @@ def dist_us(ms_list):
                 p90=round(float(np.percentile(a, 90)), 2), mean=round(float(a.mean()), 2), samples=int(a.size))
 
 
-def timed_calls(torch, stream, calls, iters, flush=None, before=None, sets=1):
+def timed_calls(torch, stream, calls, iters, flush=None, before=None, sets=1, per_call=False):
     """Time ``iters`` iterations of ``calls(i)`` (a list of C-ABI calls issued on
     ``stream``), each bracketed by HIP events.  ``flush`` (a 1 GiB tensor) is read
     in full before every iteration outside the events, so none of the data the
     iteration touches is left in the L2s or the 256 MB last-level cache (a read,
     not a write: a written flush would leave that cache full of dirty lines for
     the timed iteration to write back); ``before(i)`` runs untimed work (state
-    restores) after it.  Returns the per-iteration event times in ms."""
-    ev = HipEvents(2 * iters)
+    restores) after it.  Returns the per-iteration event times in ms; with
+    ``per_call`` an event also follows every call, and the result is one list of
+    times per call instead."""
+    n_calls = len(calls(0)) if per_call else 1
+    ev = HipEvents((n_calls + 1) * iters)
     sh = stream.cuda_stream
     status = 0
     for i in range(iters):
@@ -136,15 +139,22 @@ def timed_calls(torch, stream, calls, iters, flush=None, before=None, sets=1):
             torch.sum(flush)
         if before is not None:
             before(i)
-        ev.record(2 * i, sh)
-        for fn, args in calls(i):
+        e0 = (n_calls + 1) * i
+        ev.record(e0, sh)
+        for k, (fn, args) in enumerate(calls(i)):
             status |= fn(*args)
-        ev.record(2 * i + 1, sh)
+            if per_call:
+                ev.record(e0 + 1 + k, sh)
+        if not per_call:
+            ev.record(e0 + 1, sh)
     torch.cuda.synchronize()
     if status:
         ev.destroy()
         raise RuntimeError("a library call failed (status %d)" % status)
-    out = [ev.ms(2 * i, 2 * i + 1) for i in range(iters)]
+    if per_call:
+        out = [[ev.ms((n_calls + 1) * i + k, (n_calls + 1) * i + k + 1) for i in range(iters)] for k in range(n_calls)]
+    else:
+        out = [ev.ms(2 * i, 2 * i + 1) for i in range(iters)]
     ev.destroy()
     return out
 
@@ -362,15 +372,25 @@ def leg_denoise_config(torch, stream, flush, cfg, iters, balanced=False):
     ds.stream_handle = stream.cuda_stream
     ms = timed_calls(torch, stream, lambda i: [attn_call(ds), commit_call(ds)], iters, flush=flush,
                      before=lambda i: ds.reset_block_state())
+    # A second pass with an event between the two calls, for each call's own time
+    # (kept out of step_us, which the extra event would lengthen).
+    a_ms, c_ms = timed_calls(torch, stream, lambda i: [attn_call(ds), commit_call(ds)], iters, flush=flush,
+                             before=lambda i: ds.reset_block_state(), per_call=True)
     a_b = attn_bytes(p, st["prefix"])
     l_b, s_b = commit_bytes(p, int(st["masked"].sum()))
     total = a_b + l_b + s_b
     dist = dist_us(ms)
     med_s = dist["median"] * 1e-6
+    a_d, c_d = dist_us(a_ms), dist_us(c_ms)
+    per = lambda b, d: dict(us=d, gbps_at_median=round(b / (d["median"] * 1e-6) / 1e9, 1),
+                            frac_at_median=round(b / (d["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
     out = dict(workload=p["name"] + (", ragged-batch plan (BD_PLAN_BALANCED)" if balanced else ""), step_us=dist,
                steps_per_s=round(1.0 / med_s, 1), algorithmic_bytes=total,
                attn_bytes=a_b, logits_bytes=l_b, achieved_gbps=round(total / med_s / 1e9, 1),
-               frac=round(total / med_s / 1e9 / HBM_PEAK_GBS, 4), timing="cold: 1 GiB flush read before each step")
+               frac=round(total / med_s / 1e9 / HBM_PEAK_GBS, 4),
+               attention_call=per(a_b, a_d), commit_call=per(l_b + s_b, c_d),
+               timing="cold: 1 GiB flush read before each step; the per-call times come from a second "
+                      "pass with an event between the calls")
     del ds
     return out
 
@@ -398,6 +418,8 @@ def leg_verify_chain(torch, stream, flush, iters):
                                     ds.accepted.data_ptr(), ds.dev_err.data_ptr(), sh))
     ms = timed_calls(torch, stream, lambda i: [attn_call(ds), verify, append], iters, flush=flush,
                      before=lambda i: ds.prefix.copy_(prefix0))
+    per_ms = timed_calls(torch, stream, lambda i: [attn_call(ds), verify, append], iters, flush=flush,
+                         before=lambda i: ds.prefix.copy_(prefix0), per_call=True)
     L = int(ds.accepted.cpu()[0])
     assert L == int(st["planted_L"][0]) and int(ds.dev_err.cpu()[0]) == 0
     a_b = attn_bytes(p, st["prefix"])
@@ -411,8 +433,10 @@ def leg_verify_chain(torch, stream, flush, iters):
                attn_bytes=a_b, logits_bytes_read=logits_read, logits_bytes_algorithmic=logits_alg, append_bytes=app_b,
                algorithmic_bytes=total, achieved_gbps=round(total / med_s / 1e9, 1),
                frac=round(total / med_s / 1e9 / HBM_PEAK_GBS, 4),
+               attention_us=dist_us(per_ms[0]), verify_us=dist_us(per_ms[1]), append_us=dist_us(per_ms[2]),
                timing="cold: 1 GiB flush read before each chain; all 16 logits rows read (verify needs every row "
-                      "until the first mismatch is known on the device)")
+                      "until the first mismatch is known on the device); the per-call times come from a second "
+                      "pass with an event after each call")
     del ds
     return out
 
