@@ -249,6 +249,39 @@ def test_attention_few_items_many_splits(dev, label, ov, mode):
     _run_attention(dev, synth.make_step(p, seed=zlib.crc32(label.encode()) % 10000), mode=mode, label=label)
 
 
+# Paired halves: where two 4-wave workgroups would share every CU (d = 128,
+# fixed split plan, more list slots than CUs), one 8-wave workgroup runs two
+# adjacent list slots and combines them in LDS when both belong to one unit.
+# Ragged prefixes give units with different split counts (pairs across unit
+# boundaries, halves with nothing to stream, units whose only partial is one
+# combined pair, written out directly); an odd list length leaves the last
+# workgroup's second half empty; a plan sized for a much longer context than
+# any prefix leaves whole workgroups empty.
+PAIR_CASES = [
+    ("ragged_40_items", dict(n_items=40, prefix=("list", [(0, 1, 31, 32, 33, 100, 500, 1000, 1500, 2047)[i % 10]
+                                                          for i in range(40)])), 2048),
+    ("odd_list_37_units", dict(n_items=37, Hq=8, Hkv=1, prefix=("list", [(53 * i) % 1000 for i in range(37)])), 1000),
+    ("short_prefixes_long_plan", dict(n_items=36, prefix=("list", [(7 * i) % 70 for i in range(36)])), 4096),
+    ("two_split_units", dict(n_items=64, prefix=("fixed", 40)), 128),
+]
+
+
+@pytest.mark.parametrize("dtype", [BF16, FP8KV])
+@pytest.mark.parametrize("mode", [BIDIR, CAUSAL])
+@pytest.mark.parametrize("label,ov,host_max", PAIR_CASES, ids=[c[0] for c in PAIR_CASES])
+def test_attention_paired_halves(dev, label, ov, host_max, mode, dtype):
+    base = dict(n_items=2, Hq=16, Hkv=2, d=128, dtype=dtype, D=16, n_masked=8, V=1000, plant=None,
+                cap=host_max + 16)
+    base.update(ov)
+    p = synth.params_for(3, **base)
+    st = synth.make_step(p, seed=zlib.crc32(("pair" + label).encode()) % 10000)
+    _say("attention pair_%s n=%d Hq=%d Hkv=%d dtype=%d mode=%d max_prefix=%d" % (
+        label, p["n_items"], p["Hq"], p["Hkv"], dtype, mode, host_max))
+    ds = _ds(dev, st, max_prefix=host_max)
+    ds.attn(mode=mode)
+    _check_attention(_out_host(dev, ds), _reference(st, mode), "pair_" + label)
+
+
 # Seeded random sweep over small shapes: dtype (bf16, E4M3 cache, fp32), mask
 # mode (bidirectional, causal, quadratic), head layout, d, block length and
 # ragged prefixes drawn together, and for about half the cases a plan sized

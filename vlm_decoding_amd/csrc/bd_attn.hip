@@ -49,6 +49,7 @@ struct MfmaParams {
     int R, row_blocks, max_splits, tiles_per_split, total_logical;
     int balanced;       // ragged-batch plan: split counts from the device-side prefix lengths
     int balance_slots;  // ... workgroups the plan may use
+    int pair;           // paired halves: odd list slots after their unit's first may be absorbed
     float c;  // scale * log2(e)
     // Two-stream (whole-sequence) mode: D = L = Lc + Ln positions per item, the
     // clean stream then the noisy stream; response spans (clean start, length).
@@ -305,6 +306,9 @@ __device__ __forceinline__ bd_i32x2 bd_lds_tr8(const uint8_t *p) {
 // per SIMD) share a CU, each keeping three tiles (48 KB) in flight.  Two per
 // CU is also the cap for d = 64, where registers rather than LDS are the limit.
 constexpr int kStages = 4;
+#ifndef BD_PAIR_HALVES
+#define BD_PAIR_HALVES 1
+#endif
 constexpr int kStageBytesPerD = kTileKeys * 2;  // LDS bytes of one K (or V) stage per head-dim element
 constexpr int occupancy_for(int hd) {
     return (160 * 1024) / (kStages * 2 * kStageBytesPerD * hd) < 2 ? (160 * 1024) / (kStages * 2 * kStageBytesPerD * hd)
@@ -332,10 +336,20 @@ __device__ __forceinline__ bf16x8 bd_e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 // SEQ = true: two-stream training attention over whole sequences (bf16 K/V):
 // every key tile comes from the item's K/V arrays by the same copy pipeline,
 // and tiles that some row of the workgroup only partly sees are masked.
-template <int HD, int NW, bool KV8, bool SEQ>
-__global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(MfmaParams p) {
+// PAIR = true (block modes, d = 128): one workgroup per CU of two NW-wave
+// halves.  Half h runs split slot 2 L + h of the call's unit-major slot list
+// (L = the workgroup's logical id) with its own four LDS stages; both halves
+// step through one barrier sequence, sized for the longer of the two, so
+// they keep pace instead of the later-dispatched of two workgroups on a CU
+// falling behind.  When both slots belong to one unit (same rows, adjacent
+// key ranges), the halves combine their (m, l, o) through LDS and the pair
+// leaves one partial; the merge kernel skips the slot it absorbed.
+template <int HD, int NW, bool KV8, bool SEQ, bool PAIR = false>
+__global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void attn_mfma_kernel(MfmaParams p) {
     static_assert(!(SEQ && KV8), "the sequence mode is bf16 only");
-    constexpr int NT = NW * 64;
+    static_assert(!(SEQ && PAIR) && (!PAIR || HD == 128), "paired halves: block modes, d = 128");
+    constexpr int NH = PAIR ? 2 : 1;    // halves per workgroup
+    constexpr int NT = NW * 64;         // threads per half
     constexpr int EB = KV8 ? 1 : 2;     // bytes per K / V element
     constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;  // keys per tile
     constexpr int KU = HD * EB / 16;    // 16-byte units per K (or V) row
@@ -356,25 +370,31 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // One array per stage: the tile loop below is unrolled by NS so that every
     // LDS access names a fixed array, which lets the compiler see that reads of
     // one stage never alias the global->LDS copies in flight into the others.
-    __shared__ __attribute__((aligned(16))) uint8_t lds_k0[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_k1[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_k2[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_k3[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_v0[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_v1[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_v2[SB];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_v3[SB];
-    auto kbuf = [&](int st) __attribute__((always_inline)) -> uint8_t * {
+    // With paired halves each array holds one stage of each half.
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k0[SB * NH];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k1[SB * NH];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k2[SB * NH];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_k3[SB * NH];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v0[SB * NH];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v1[SB * NH];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v2[SB * NH];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_v3[SB * NH];
+    // This thread's half and its index within the half.
+    const int hw = PAIR ? (int)threadIdx.x / NT : 0;
+    const int tid = (int)threadIdx.x - hw * NT;
+    const int hoff = hw * SB;
+    auto kraw = [&](int st) __attribute__((always_inline)) -> uint8_t * {
         return st == 0 ? lds_k0 : st == 1 ? lds_k1 : st == 2 ? lds_k2 : lds_k3;
     };
-    auto vbuf = [&](int st) __attribute__((always_inline)) -> uint8_t * {
+    auto vraw = [&](int st) __attribute__((always_inline)) -> uint8_t * {
         return st == 0 ? lds_v0 : st == 1 ? lds_v1 : st == 2 ? lds_v2 : lds_v3;
     };
+    auto kbuf = [&](int st) __attribute__((always_inline)) -> uint8_t * { return kraw(st) + hoff; };
+    auto vbuf = [&](int st) __attribute__((always_inline)) -> uint8_t * { return vraw(st) + hoff; };
     // Byte offsets of 16-byte unit lu of K / V row `key` in a stage.
     auto k_at = [](int key, int lu) __attribute__((always_inline)) { return (key * KU + (lu ^ k_swz<HD, KV8>(key))) * 16; };
     auto v_at = [](int key, int lu) __attribute__((always_inline)) { return (key * KU + (lu ^ v_swz<HD, KV8>(key))) * 16; };
 
-    const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int half = lane >> 5;
@@ -384,7 +404,14 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     const int nb = gridDim.x;
     const int logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
     int unit, split, nsplit_b = 0;  // nsplit_b: the balanced plan's split count of this unit
-    if (!SEQ && p.balanced) {
+    if (PAIR) {
+        // Slot 2 L + hw of the list; a half past its end takes its partner's
+        // unit for the addresses below and streams nothing.
+        if (2 * logical >= p.total_logical) return;  // both halves: the whole workgroup
+        const int sidx = min(2 * logical + hw, p.total_logical - 1);
+        unit = sidx / p.max_splits;
+        split = sidx - unit * p.max_splits;
+    } else if (!SEQ && p.balanced) {
         const ItemPlan ip = balanced_plan<TK>(p, lane);
         if (logical >= ip.total) return;  // the whole workgroup: every wave has the same plan
         const int upi = p.Hkv * p.row_blocks;
@@ -498,15 +525,51 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     } else {
         // A prefix above the host's max_prefix widens the splits instead of
         // overrunning the workspace (at most max_splits per unit).
-        const UnitSplit us = p.balanced ? unit_split_n<TK>(P, p.D, nsplit_b, split)
-                                        : unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
+        const UnitSplit us = !PAIR && p.balanced ? unit_split_n<TK>(P, p.D, nsplit_b, split)
+                                                 : unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
         nsplit = us.nsplit;
-        if (split >= nsplit) return;
+        if (!PAIR && split >= nsplit) return;
         const bool is_tail = split == nsplit - 1;
         t0 = us.t0;
         nb_split = us.nb;
         tail_len = is_tail ? (P - Pb) + p.D : 0;
         ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
+    }
+    // Paired halves: both halves' plans, computed alike by every wave from the
+    // list slot alone, so the loop counts below (the longer half's tail and
+    // bulk tile counts) and every branch around a barrier are the same in all
+    // eight waves.
+    bool hvalid = true, merged = false;
+    int ntail_all = ntail, nb_all = nb_split;
+    if constexpr (PAIR) {
+        struct SlotPlan {
+            bool valid;
+            int unit, nb, ntail;
+        };
+        auto slot_plan = [&](int s) __attribute__((always_inline)) {
+            SlotPlan sp{false, -1, 0, 0};
+            if (s >= p.total_logical) return sp;
+            sp.unit = s / p.max_splits;
+            const int sl = s - sp.unit * p.max_splits;
+            const int Px = min(max(p.prefix[sp.unit / p.row_blocks / p.Hkv], 0), p.cap);
+            const UnitSplit u = unit_split<TK>(Px, p.D, p.tiles_per_split, p.max_splits, sl);
+            if (sl >= u.nsplit) return sp;
+            sp.valid = true;
+            sp.nb = u.nb;
+            sp.ntail = sl == u.nsplit - 1 ? ((Px - (Px & ~(TK - 1))) + p.D + TK - 1) / TK : 0;
+            return sp;
+        };
+        const SlotPlan s0 = slot_plan(2 * logical), s1 = slot_plan(2 * logical + 1);
+        if (!s0.valid && !s1.valid) return;  // the whole workgroup
+        hvalid = hw == 0 ? s0.valid : s1.valid;
+        ntail_all = max(s0.ntail, s1.ntail);
+        nb_all = max(s0.nb, s1.nb);
+        merged = s0.valid && s1.valid && s0.unit == s1.unit;
+        if (!hvalid) {
+            nb_split = 0;
+            ntail = 0;
+            tail_len = 0;
+        }
     }
     // Key tile of list entry k (sequence mode) or bulk tile k.
     auto tile_of = [&](int k) __attribute__((always_inline)) { return SEQ && k >= nA ? bB + (k - nA) : k; };
@@ -722,13 +785,15 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     };
 
     // Tail split: gather and compute its (one to three) tiles in stage NS-1.
-    for (int tt = 0; tt < ntail; ++tt) {
-        if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
-        load_tail(NS - 1, tt, tt == 0);
-        bd_barrier_lds();
-        if (wave_active) compute(NS - 1, tt, -1);
-    }
+    // A half without a tail starts its bulk copies first and only keeps step
+    // with its partner's tail barriers.
     if (ntail == 0) first_fill();
+    for (int tt = 0; tt < ntail_all; ++tt) {
+        if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
+        if (tt < ntail) load_tail(NS - 1, tt, tt == 0);
+        bd_barrier_lds();
+        if (tt < ntail && wave_active) compute(NS - 1, tt, -1);
+    }
     // Bulk tiles through NS stages, NS-1 filled up front: tiles tl+1 ..
     // tl+NS-1 are in flight while tile tl is computed.  Every step has the same
     // shape - wait for all but the last NS-2 copy groups, one barrier (after
@@ -741,7 +806,7 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
     // varying count it falls back to draining every copy before each tile.
     // The Q loads, issued before the first copies, are retired by the first
     // fixed-count wait.
-    const int nb_round = (nb_split + NS - 1) / NS * NS;
+    const int nb_round = (nb_all + NS - 1) / NS * NS;
     auto step = [&](auto stage, int tl) __attribute__((always_inline)) {
         constexpr int ST = decltype(stage)::value;
         bd_wait_vmcnt<(NS - 2) * (LK + LV)>();  // tile tl's copies have landed
@@ -755,12 +820,54 @@ __global__ __launch_bounds__(NW * 64, occupancy_for(HD)) void attn_mfma_kernel(M
         step(std::integral_constant<int, 2>{}, tl + 2);
         step(std::integral_constant<int, 3>{}, tl + 3);
     }
-    if (nb_split > 0) bd_wait_vmcnt<0>();  // no copy may still target LDS when the workgroup ends
+    if (nb_all > 0) bd_wait_vmcnt<0>();  // no copy may still target LDS when the workgroup ends
 
-    const float l_tot = bd_sum_halves(l_run);
+    float l_tot = bd_sum_halves(l_run);
+    // Partials this unit leaves: its split count, less the slots absorbed by a
+    // paired half (slot s >= 1 whose list index is odd: its partner s - 1 is in
+    // the same workgroup and unit).
+    int eff = nsplit;
+    if constexpr (PAIR) {
+        const int base0 = unit * p.max_splits;
+        eff = nsplit - ((base0 & 1) ? (nsplit - 1) / 2 : nsplit / 2);
+        if (merged) {
+            // Half 1 hands its (m, l, o) to half 0 through LDS: wave w's 64
+            // accumulators of each lane in lds_k<w> ([register][lane], so each
+            // store of a wave fills 256 contiguous bytes), (m, l) in lds_v<w>.
+            // Lane and wave layouts are the same in both halves.
+            static_assert(MB * 16 * 64 * 4 <= SB * NH && NW <= NS, "exchange must fit one stage array per wave");
+            bd_barrier_lds();  // every copy has landed and no wave still reads a stage
+            float *xo = reinterpret_cast<float *>(kraw(w));
+            float *xm = reinterpret_cast<float *>(vraw(w));
+            if (hw == 1 && wave_active) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) xo[(mb * 16 + i) * 64 + lane] = o[mb][i];
+                xm[lane] = m_run;
+                xm[64 + lane] = l_tot;
+            }
+            bd_barrier_lds();
+            if (hw == 1) return;
+            if (wave_active) {
+                // Fixed order: this half's keys come first in the unit.
+                const float m1 = xm[lane], l1 = xm[64 + lane];
+                const float M = fmaxf(m_run, m1);
+                const float a0 = m_run == -INFINITY ? 0.f : bd_exp2(m_run - M);
+                const float a1 = m1 == -INFINITY ? 0.f : bd_exp2(m1 - M);
+                l_tot = l_tot * a0 + l1 * a1;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o[mb][i] = o[mb][i] * a0 + xo[(mb * 16 + i) * 64 + lane] * a1;
+                m_run = M;
+            }
+        }
+        if (!hvalid) return;
+    }
     // Output element mapping of the O^T accumulators: block mb, register i of
     // half h holds d = mb*32 + 8*(i/4) + 4*h + (i%4) of this lane's row.
-    if (nsplit == 1) {
+    if (eff == 1) {
         if (row_valid) {
             const float inv = l_tot > 0.f ? vs / l_tot : 0.f;  // a row that sees nothing outputs 0
             uint16_t *op = p.out + (((size_t)it * p.D + slot) * p.Hq + head) * HD;
@@ -873,11 +980,16 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
         nsplit_b = p.unit_splits[unit];
         slots_to_load = nsplit_b;
     }
+    // Paired halves: slot s >= 1 with an odd list index was absorbed by slot
+    // s - 1 (same workgroup, same unit) and holds nothing of this call.
+    const int list0 = unit * p.max_splits;
+    auto absorbed = [&](int s) __attribute__((always_inline)) { return p.pair && s >= 1 && ((list0 + s) & 1); };
     float2 ml[MAXS];
     uint4 v[QPT][MAXS];
 #pragma unroll
-    for (int s = 0; s < MAXS; ++s)
-        if (sw * MAXS + s < slots_to_load) {
+    for (int s = 0; s < MAXS; ++s) {
+        ml[s] = make_float2(-INFINITY, 0.f);
+        if (sw * MAXS + s < slots_to_load && !absorbed(sw * MAXS + s)) {
             // Each partial is read once: non-temporal loads.
             const floatx2_nt m2 =
                 __builtin_nontemporal_load(reinterpret_cast<const floatx2_nt *>(p.ws_ml) + (base + s) * NT_TILE + src_t);
@@ -889,6 +1001,7 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
                 v[j][s] = make_uint4(t[0], t[1], t[2], t[3]);
             }
         }
+    }
     int nsplit;
     if constexpr (SEQ) {
         nsplit = p.unit_splits[unit];  // written by the unit's first split
@@ -898,12 +1011,14 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
         const int P = min(max(p.prefix[it], 0), p.cap);
         nsplit = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
     }
-    if (nsplit == 1) return;  // single split: written by the tile kernel
+    // A unit left with one partial was written out by the tile kernel.
+    const int eff = p.pair ? nsplit - ((list0 & 1) ? (nsplit - 1) / 2 : nsplit / 2) : nsplit;
+    if (eff == 1) return;
     const int ns = nsplit - sw * MAXS;  // splits of this wave (may be <= 0)
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
-        if (s < ns) M = fmaxf(M, ml[s].x);
+        if (s < ns && !absorbed(sw * MAXS + s)) M = fmaxf(M, ml[s].x);
     if constexpr (SW > 1) {
         __shared__ float m_x[SW][64];
         m_x[sw][lane] = M;
@@ -915,7 +1030,7 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
     float acc[QPT][8] = {};
 #pragma unroll
     for (int s = 0; s < MAXS; ++s)
-        if (s < ns) {
+        if (s < ns && !absorbed(sw * MAXS + s)) {
             const float c = (ml[s].x == -INFINITY) ? 0.f : bd_exp2(ml[s].x - M) * ml[s].y;
             L += c;
 #pragma unroll
@@ -1120,8 +1235,12 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
         pl.max_splits = std::max(1, std::min(std::min(want, nt), cap));
         pl.tiles_per_split = std::max(1, (nt + pl.max_splits - 1) / pl.max_splits);
     }
+    // Where two 4-wave workgroups would share every CU (d = 128 block modes
+    // with the fixed split plan), one 8-wave workgroup runs two list slots.
+    pl.pair = BD_PAIR_HALVES && !seq && !pl.balanced && pl.nw == 4 && d == 128 && pl.max_splits > 1 &&
+              (long)pl.units * pl.max_splits > kCUs;
     const long total = pl.balanced ? (long)pl.balance_slots : (long)pl.units * pl.max_splits;
-    pl.grid = (int)((total + 7) / 8 * 8);
+    pl.grid = (int)(((pl.pair ? (total + 1) / 2 : total) + 7) / 8 * 8);
     if (pl.max_splits > 1) {
         size_t off = 0;
         auto take = [&](size_t bytes) {
@@ -1155,8 +1274,12 @@ template <bool KV8, bool SEQ>
 void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge, int *parts, int *waves) {
     constexpr int TK = KV8 ? 2 * kTileKeys : kTileKeys;
     if (d == 128) {
-        *tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4, KV8, SEQ>
-                           : (const void *)attn_mfma_kernel<128, 8, KV8, SEQ>;
+        if constexpr (!SEQ) {
+            if (pl.pair) *tile = (const void *)attn_mfma_kernel<128, 4, KV8, false, true>;
+        }
+        if (!pl.pair)
+            *tile = pl.nw == 4 ? (const void *)attn_mfma_kernel<128, 4, KV8, SEQ>
+                               : (const void *)attn_mfma_kernel<128, 8, KV8, SEQ>;
         *merge = pl.nw == 4 ? pick_merge<128, 4, TK, SEQ>(pl) : pick_merge<128, 8, TK, SEQ>(pl);
     } else {
         *tile = (const void *)attn_mfma_kernel<64, 4, KV8, SEQ>;
@@ -1202,8 +1325,9 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.total_logical = pl.units * pl.max_splits;
     p.balanced = pl.balanced ? 1 : 0;
     p.balance_slots = pl.balance_slots;
+    p.pair = pl.pair ? 1 : 0;
     p.c = a.scale * BD_LOG2E;
-    dim3 block(pl.nw * 64);
+    dim3 block(pl.nw * 64 * (pl.pair ? 2 : 1));
     const void *tile, *merge;
     int parts, waves;
     if (pl.seq)
