@@ -180,6 +180,16 @@ __device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_spli
     return unit_split_n<TK>(P, D, unit_nsplit<TK>(P, D, tiles_per_split, max_splits), split);
 }
 
+// Paired halves: the key range (split index) that list slot `slot` of `unit`
+// runs.  Odd units take theirs in reverse; slots past the unit's split count
+// stay as they are (they stream nothing).
+template <int TK>
+__device__ __forceinline__ int key_split(const MfmaParams &p, int unit, int P, int slot) {
+    if (!(unit & 1)) return slot;
+    const int ns = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
+    return slot < ns ? ns - 1 - slot : slot;
+}
+
 // Sum and max over the 64 lanes of a wave with DPP row operations and lane
 // swaps (no LDS round trip); every lane receives the result.
 template <int CTRL>
@@ -525,11 +535,17 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     } else {
         // A prefix above the host's max_prefix widens the splits instead of
         // overrunning the workspace (at most max_splits per unit).
+        // Paired halves: the slots of an odd unit take its key ranges in
+        // reverse (slot s runs split nsplit - 1 - s), so with an odd slot count
+        // per unit the two tail splits of units 2k and 2k + 1 share a
+        // workgroup, which then steps through fewer bulk tiles, instead of each
+        // tail holding up a partner with a full share.
+        const int ks = PAIR ? key_split<TK>(p, unit, P, split) : split;
         const UnitSplit us = !PAIR && p.balanced ? unit_split_n<TK>(P, p.D, nsplit_b, split)
-                                                 : unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
+                                                 : unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, ks);
         nsplit = us.nsplit;
         if (!PAIR && split >= nsplit) return;
-        const bool is_tail = split == nsplit - 1;
+        const bool is_tail = ks == nsplit - 1;
         t0 = us.t0;
         nb_split = us.nb;
         tail_len = is_tail ? (P - Pb) + p.D : 0;
@@ -552,11 +568,12 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
             sp.unit = s / p.max_splits;
             const int sl = s - sp.unit * p.max_splits;
             const int Px = min(max(p.prefix[sp.unit / p.row_blocks / p.Hkv], 0), p.cap);
-            const UnitSplit u = unit_split<TK>(Px, p.D, p.tiles_per_split, p.max_splits, sl);
+            const int kx = key_split<TK>(p, sp.unit, Px, sl);
+            const UnitSplit u = unit_split<TK>(Px, p.D, p.tiles_per_split, p.max_splits, kx);
             if (sl >= u.nsplit) return sp;
             sp.valid = true;
             sp.nb = u.nb;
-            sp.ntail = sl == u.nsplit - 1 ? ((Px - (Px & ~(TK - 1))) + p.D + TK - 1) / TK : 0;
+            sp.ntail = kx == u.nsplit - 1 ? ((Px - (Px & ~(TK - 1))) + p.D + TK - 1) / TK : 0;
             return sp;
         };
         const SlotPlan s0 = slot_plan(2 * logical), s1 = slot_plan(2 * logical + 1);
