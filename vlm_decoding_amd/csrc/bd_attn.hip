@@ -49,7 +49,6 @@ struct MfmaParams {
     int R, row_blocks, max_splits, tiles_per_split, total_logical;
     int balanced;       // ragged-batch plan: split counts from the device-side prefix lengths
     int balance_slots;  // ... workgroups the plan may use
-    int pair;           // paired halves: odd list slots after their unit's first may be absorbed
     float c;  // scale * log2(e)
     // Two-stream (whole-sequence) mode: D = L = Lc + Ln positions per item, the
     // clean stream then the noisy stream; response spans (clean start, length).
@@ -802,14 +801,24 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     };
 
     // Tail split: gather and compute its (one to three) tiles in stage NS-1.
-    // A half without a tail starts its bulk copies first and only keeps step
-    // with its partner's tail barriers.
-    if (ntail == 0) first_fill();
-    for (int tt = 0; tt < ntail_all; ++tt) {
-        if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
-        if (tt < ntail) load_tail(NS - 1, tt, tt == 0);
-        bd_barrier_lds();
-        if (tt < ntail && wave_active) compute(NS - 1, tt, -1);
+    if constexpr (PAIR) {
+        // A half without a tail starts its bulk copies first and only keeps
+        // step with its partner's tail barriers.
+        if (ntail == 0) first_fill();
+        for (int tt = 0; tt < ntail_all; ++tt) {
+            if (tt > 0) bd_barrier_lds();
+            if (tt < ntail) load_tail(NS - 1, tt, tt == 0);
+            bd_barrier_lds();
+            if (tt < ntail && wave_active) compute(NS - 1, tt, -1);
+        }
+    } else {
+        for (int tt = 0; tt < ntail; ++tt) {
+            if (tt > 0) bd_barrier_lds();  // every wave is done with the previous tail tile
+            load_tail(NS - 1, tt, tt == 0);
+            bd_barrier_lds();
+            if (wave_active) compute(NS - 1, tt, -1);
+        }
+        if (ntail == 0) first_fill();
     }
     // Bulk tiles through NS stages, NS-1 filled up front: tiles tl+1 ..
     // tl+NS-1 are in flight while tile tl is computed.  Every step has the same
@@ -951,7 +960,8 @@ static_assert((4 * (4 / kMergeWaves)) % 8 == 0, "merge grid must be a multiple o
 // split waves a block holds up to 64 splits: wave w takes splits 32 w ..
 // 32 w + 31, both use the max over all splits, and wave 0 adds wave 1's sums
 // to its own (the sum over the first 32 splits, then the rest).
-template <int HD, int NW, int TK, bool SEQ, int NP, int MAXS, int SW>
+// PAIRED: the partials of paired tile halves (some slots absorbed, see below).
+template <int HD, int NW, int TK, bool SEQ, int NP, int MAXS, int SW, bool PAIRED = false>
 __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaParams p) {
     constexpr int WPB = kMergeWaves;    // waves per block
     constexpr int NT_TILE = NW * 64;    // threads of the tile kernel's block
@@ -1000,12 +1010,12 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
     // Paired halves: slot s >= 1 with an odd list index was absorbed by slot
     // s - 1 (same workgroup, same unit) and holds nothing of this call.
     const int list0 = unit * p.max_splits;
-    auto absorbed = [&](int s) __attribute__((always_inline)) { return p.pair && s >= 1 && ((list0 + s) & 1); };
+    auto absorbed = [&](int s) __attribute__((always_inline)) { return PAIRED && s >= 1 && ((list0 + s) & 1); };
     float2 ml[MAXS];
     uint4 v[QPT][MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
-        ml[s] = make_float2(-INFINITY, 0.f);
+        if (PAIRED) ml[s] = make_float2(-INFINITY, 0.f);
         if (sw * MAXS + s < slots_to_load && !absorbed(sw * MAXS + s)) {
             // Each partial is read once: non-temporal loads.
             const floatx2_nt m2 =
@@ -1029,7 +1039,7 @@ __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaP
         nsplit = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
     }
     // A unit left with one partial was written out by the tile kernel.
-    const int eff = p.pair ? nsplit - ((list0 & 1) ? (nsplit - 1) / 2 : nsplit / 2) : nsplit;
+    const int eff = PAIRED ? nsplit - ((list0 & 1) ? (nsplit - 1) / 2 : nsplit / 2) : nsplit;
     if (eff == 1) return;
     const int ns = nsplit - sw * MAXS;  // splits of this wave (may be <= 0)
     float M = -INFINITY;
@@ -1255,7 +1265,7 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
     // Where two 4-wave workgroups would share every CU (d = 128 block modes
     // with the fixed split plan), one 8-wave workgroup runs two list slots.
     pl.pair = BD_PAIR_HALVES && !seq && !pl.balanced && pl.nw == 4 && d == 128 && pl.max_splits > 1 &&
-              (long)pl.units * pl.max_splits > kCUs;
+              pl.max_splits <= kNarrowSplits && (long)pl.units * pl.max_splits > kCUs;
     const long total = pl.balanced ? (long)pl.balance_slots : (long)pl.units * pl.max_splits;
     pl.grid = (int)(((pl.pair ? (total + 1) / 2 : total) + 7) / 8 * 8);
     if (pl.max_splits > 1) {
@@ -1283,6 +1293,9 @@ namespace {
 // beyond.
 template <int HD, int NW, int TK, bool SEQ>
 const void *pick_merge(const AttnPlan &pl) {
+    // Paired plans have more slots than CUs, so at most kNarrowSplits per unit.
+    if constexpr (!SEQ && HD == 128 && NW == 4)
+        if (pl.pair) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, 4, kNarrowSplits, 1, true>;
     if (pl.max_splits <= kNarrowSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, 4, kNarrowSplits, 1>;
     if (pl.max_splits <= kWideSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kWideSplits, 1>;
     return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kWideSplits, kMaxSplits / kWideSplits>;
@@ -1342,7 +1355,6 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.total_logical = pl.units * pl.max_splits;
     p.balanced = pl.balanced ? 1 : 0;
     p.balance_slots = pl.balance_slots;
-    p.pair = pl.pair ? 1 : 0;
     p.c = a.scale * BD_LOG2E;
     dim3 block(pl.nw * 64 * (pl.pair ? 2 : 1));
     const void *tile, *merge;
