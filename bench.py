@@ -56,8 +56,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 FLUSH_BYTES = 1 << 30
 METRIC = "denoise steps/sec + achieved HBM GB/s (%peak), 3B-shape block-16, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cfg3_step_traffic.json")
-HEADLINE_KERNELS = ("attn_mfma_kernel<128, 4, false, false>", "attn_merge_kernel<128, 4, 32, false, 4, 16, 1>")
-FP8KV_KERNELS = ("attn_mfma_kernel<128, 4, true, false>", "attn_merge_kernel<128, 4, 64, false, 4, 16, 1>")
+HEADLINE_KERNELS = ("attn_mfma_kernel<128, 4, false, false, true>", "attn_merge_kernel<128, 4, 32, false, 4, 16, 1, true>")
+FP8KV_KERNELS = ("attn_mfma_kernel<128, 4, true, false, true>", "attn_merge_kernel<128, 4, 64, false, 4, 16, 1, true>")
 ROW_KERNEL = "row_kernel<false>"
 ATTN_SOURCES = ["vlm_decoding_amd/csrc/bd_attn.hip", "vlm_decoding_amd/csrc/bd_common.h",
                 "vlm_decoding_amd/csrc/bd_internal.h"]
