@@ -179,16 +179,6 @@ __device__ __forceinline__ UnitSplit unit_split(int P, int D, int tiles_per_spli
     return unit_split_n<TK>(P, D, unit_nsplit<TK>(P, D, tiles_per_split, max_splits), split);
 }
 
-// Paired halves: the key range (split index) that list slot `slot` of `unit`
-// runs.  Odd units take theirs in reverse; slots past the unit's split count
-// stay as they are (they stream nothing).
-template <int TK>
-__device__ __forceinline__ int key_split(const MfmaParams &p, int unit, int P, int slot) {
-    if (!(unit & 1)) return slot;
-    const int ns = unit_nsplit<TK>(P, p.D, p.tiles_per_split, p.max_splits);
-    return slot < ns ? ns - 1 - slot : slot;
-}
-
 // Sum and max over the 64 lanes of a wave with DPP row operations and lane
 // swaps (no LDS round trip); every lane receives the result.
 template <int CTRL>
@@ -413,7 +403,13 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     const int nb = gridDim.x;
     const int logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
     int unit, split, nsplit_b = 0;  // nsplit_b: the balanced plan's split count of this unit
+    int pre0 = 0, pre1 = 0;  // paired halves: the prefix lengths of slots 2 L and 2 L + 1
     if (PAIR) {
+        // Every kernel argument the prologue uses, fetched in one batch at
+        // entry rather than in several dependent round trips.
+        asm volatile("" ::"s"(p.total_logical), "s"(p.max_splits), "s"(p.row_blocks), "s"(p.Hkv), "s"(p.G),
+                     "s"(p.R), "s"(p.D), "s"(p.Hq), "s"(p.q), "s"(p.prefix), "s"(p.cap), "s"(p.tiles_per_split),
+                     "s"(p.mode), "s"(p.B), "s"(p.kc), "s"(p.vc), "s"(p.kb), "s"(p.vb), "s"(p.c));
         // Slot 2 L + hw of the list; a half past its end takes its partner's
         // unit for the addresses below and streams nothing.
         if (2 * logical >= p.total_logical) return;  // both halves: the whole workgroup
@@ -468,6 +464,18 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
                 qf[kc] = bf16x8{};
         }
     }
+    if constexpr (PAIR) {
+        // The two prefix lengths (workgroup-uniform addresses) as scalar loads
+        // issued after the query loads and waited for on the scalar counter
+        // alone, so their round trip overlaps the query loads rather than
+        // following them (a vector load's wait would also wait for the queries).
+        const int32_t *a0 = p.prefix + (2 * logical) / p.max_splits / p.row_blocks / p.Hkv;
+        const int32_t *a1 = p.prefix + min(2 * logical + 1, p.total_logical - 1) / p.max_splits / p.row_blocks / p.Hkv;
+        asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                     : "=s"(pre0), "=s"(pre1)
+                     : "s"(a0), "s"(a1)
+                     : "memory");
+    }
     // Transpose-load offsets of this lane in a V stage, per 32-column block mb.
     // In its group of 16 lanes (s = lane % 16), lane s fetches 8 bytes of row
     // rho = 8 half + s / 4 (bf16) or 16 half + s / 2 (E4M3) at column
@@ -492,9 +500,9 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     }
 
     // Prefix lengths are clamped into [0, cap] so that no access leaves the cache.
-    const int P = SEQ ? 0 : min(max(p.prefix[it], 0), p.cap);
+    const int P = SEQ ? 0 : min(max(PAIR ? (hw ? pre1 : pre0) : p.prefix[it], 0), p.cap);
     const int Pb = P & ~(TK - 1);  // cache positions in whole tiles
-    int nsplit, t0, nb_split, tail_len = 0, ntail = 0;
+    int nsplit = 1, t0 = 0, nb_split = 0, tail_len = 0, ntail = 0;
     // Sequence mode: the workgroup's key tiles are segment A, tiles 0..nA-1 of
     // the clean stream (the first nU of them seen whole by every row), then
     // segment B, the noisy tiles from bB on; each row's ranges decide the rest.
@@ -531,61 +539,62 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
         if (split >= nsplit) return;
         t0 = (int)((unsigned)(split * nt) / (unsigned)nsplit);
         nb_split = (int)((unsigned)((split + 1) * nt) / (unsigned)nsplit) - t0;
-    } else {
+    } else if constexpr (!PAIR) {
         // A prefix above the host's max_prefix widens the splits instead of
         // overrunning the workspace (at most max_splits per unit).
-        // Paired halves: the slots of an odd unit take its key ranges in
-        // reverse (slot s runs split nsplit - 1 - s), so with an odd slot count
-        // per unit the two tail splits of units 2k and 2k + 1 share a
-        // workgroup, which then steps through fewer bulk tiles, instead of each
-        // tail holding up a partner with a full share.
-        const int ks = PAIR ? key_split<TK>(p, unit, P, split) : split;
-        const UnitSplit us = !PAIR && p.balanced ? unit_split_n<TK>(P, p.D, nsplit_b, split)
-                                                 : unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, ks);
+        const UnitSplit us = p.balanced ? unit_split_n<TK>(P, p.D, nsplit_b, split)
+                                        : unit_split<TK>(P, p.D, p.tiles_per_split, p.max_splits, split);
         nsplit = us.nsplit;
-        if (!PAIR && split >= nsplit) return;
-        const bool is_tail = ks == nsplit - 1;
+        if (split >= nsplit) return;
+        const bool is_tail = split == nsplit - 1;
         t0 = us.t0;
         nb_split = us.nb;
         tail_len = is_tail ? (P - Pb) + p.D : 0;
         ntail = is_tail ? (tail_len + TK - 1) / TK : 0;
     }
     // Paired halves: both halves' plans, computed alike by every wave from the
-    // list slot alone, so the loop counts below (the longer half's tail and
-    // bulk tile counts) and every branch around a barrier are the same in all
-    // eight waves.
+    // list slots and their prefix lengths alone, so the loop counts below (the
+    // longer half's tail and bulk tile counts) and every branch around a
+    // barrier are the same in all eight waves; each half takes its own.  The
+    // slots of an odd unit take its key ranges in reverse (slot s runs split
+    // nsplit - 1 - s), so with an odd slot count per unit the two tail splits
+    // of units 2k and 2k + 1 share a workgroup, which then steps through fewer
+    // bulk tiles, instead of each tail holding up a partner with a full share.
     bool hvalid = true, merged = false;
     int ntail_all = ntail, nb_all = nb_split;
     if constexpr (PAIR) {
         struct SlotPlan {
             bool valid;
-            int unit, nb, ntail;
+            int unit, nsplit, t0, nb, ntail;
         };
-        auto slot_plan = [&](int s) __attribute__((always_inline)) {
-            SlotPlan sp{false, -1, 0, 0};
+        auto slot_plan = [&](int s, int raw_prefix) __attribute__((always_inline)) {
+            SlotPlan sp{false, -1, 1, 0, 0, 0};
             if (s >= p.total_logical) return sp;
             sp.unit = s / p.max_splits;
             const int sl = s - sp.unit * p.max_splits;
-            const int Px = min(max(p.prefix[sp.unit / p.row_blocks / p.Hkv], 0), p.cap);
-            const int kx = key_split<TK>(p, sp.unit, Px, sl);
-            const UnitSplit u = unit_split<TK>(Px, p.D, p.tiles_per_split, p.max_splits, kx);
-            if (sl >= u.nsplit) return sp;
+            const int Px = min(max(raw_prefix, 0), p.cap);
+            sp.nsplit = unit_nsplit<TK>(Px, p.D, p.tiles_per_split, p.max_splits);
+            if (sl >= sp.nsplit) return sp;
+            const int kx = (sp.unit & 1) ? sp.nsplit - 1 - sl : sl;
+            const UnitSplit u = unit_split_n<TK>(Px, p.D, sp.nsplit, kx);
             sp.valid = true;
+            sp.t0 = u.t0;
             sp.nb = u.nb;
-            sp.ntail = kx == u.nsplit - 1 ? ((Px - (Px & ~(TK - 1))) + p.D + TK - 1) / TK : 0;
+            sp.ntail = kx == sp.nsplit - 1 ? ((Px - (Px & ~(TK - 1))) + p.D + TK - 1) / TK : 0;
             return sp;
         };
-        const SlotPlan s0 = slot_plan(2 * logical), s1 = slot_plan(2 * logical + 1);
+        const SlotPlan s0 = slot_plan(2 * logical, pre0), s1 = slot_plan(2 * logical + 1, pre1);
         if (!s0.valid && !s1.valid) return;  // the whole workgroup
-        hvalid = hw == 0 ? s0.valid : s1.valid;
+        const SlotPlan &me = hw == 0 ? s0 : s1;
+        hvalid = me.valid;
+        nsplit = me.nsplit;
+        t0 = me.t0;
+        nb_split = me.nb;
+        ntail = me.ntail;
+        tail_len = ntail > 0 ? (P - Pb) + p.D : 0;
         ntail_all = max(s0.ntail, s1.ntail);
         nb_all = max(s0.nb, s1.nb);
         merged = s0.valid && s1.valid && s0.unit == s1.unit;
-        if (!hvalid) {
-            nb_split = 0;
-            ntail = 0;
-            tail_len = 0;
-        }
     }
     // Key tile of list entry k (sequence mode) or bulk tile k.
     auto tile_of = [&](int k) __attribute__((always_inline)) { return SEQ && k >= nA ? bB + (k - nA) : k; };
