@@ -217,6 +217,7 @@ __device__ __forceinline__ int wave_max_i(int x) {
 // n_i splits each); `total` is the workgroup count.
 struct ItemPlan {
     int nsplit, start, total;
+    int prefix;  // lane i: item i's prefix length (clamped into [0, cap])
 };
 template <int TK>
 __device__ __forceinline__ ItemPlan balanced_plan(const MfmaParams &p, int lane) {
@@ -240,6 +241,7 @@ __device__ __forceinline__ ItemPlan balanced_plan(const MfmaParams &p, int lane)
     }
     ItemPlan ip;
     ip.nsplit = has ? min(capi, (work + lo - 1) / lo) : 0;
+    ip.prefix = P;
     const int cnt = ip.nsplit * upi;
     int incl = cnt;  // inclusive prefix sum over the lanes
 #pragma unroll
@@ -404,12 +406,15 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     const int logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
     int unit, split, nsplit_b = 0;  // nsplit_b: the balanced plan's split count of this unit
     int pre0 = 0, pre1 = 0;  // paired halves: the prefix lengths of slots 2 L and 2 L + 1
-    if (PAIR) {
+    if constexpr (!SEQ && !KV8) {
         // Every kernel argument the prologue uses, fetched in one batch at
-        // entry rather than in several dependent round trips.
+        // entry rather than in several dependent round trips (not for E4M3,
+        // where the registers it keeps live would spill).
         asm volatile("" ::"s"(p.total_logical), "s"(p.max_splits), "s"(p.row_blocks), "s"(p.Hkv), "s"(p.G),
                      "s"(p.R), "s"(p.D), "s"(p.Hq), "s"(p.q), "s"(p.prefix), "s"(p.cap), "s"(p.tiles_per_split),
-                     "s"(p.mode), "s"(p.B), "s"(p.kc), "s"(p.vc), "s"(p.kb), "s"(p.vb), "s"(p.c));
+                     "s"(p.mode), "s"(p.B), "s"(p.kc), "s"(p.vc), "s"(p.kb), "s"(p.vb), "s"(p.c), "s"(p.balanced));
+    }
+    if (PAIR) {
         // Slot 2 L + hw of the list; a half past its end takes its partner's
         // unit for the addresses below and streams nothing.
         if (2 * logical >= p.total_logical) return;  // both halves: the whole workgroup
@@ -424,6 +429,7 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
             __builtin_amdgcn_ballot_w64(lane < p.n && logical >= ip.start && logical < ip.start + ip.nsplit * upi);
         const int item = __builtin_ctzll(hit);
         nsplit_b = __shfl(ip.nsplit, item, 64);
+        pre0 = __shfl(ip.prefix, item, 64);
         const int rloc = logical - __shfl(ip.start, item, 64);
         const int uin = rloc / nsplit_b;
         split = rloc - uin * nsplit_b;
@@ -464,17 +470,24 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
                 qf[kc] = bf16x8{};
         }
     }
+    // The prefix lengths this workgroup plans with (workgroup-uniform
+    // addresses) as scalar loads issued after the query loads and waited for
+    // on the scalar counter alone, so their round trip overlaps the query
+    // loads rather than following them (a vector load's wait would also wait
+    // for the queries).  Paired halves: slots 2 L and 2 L + 1; otherwise the
+    // item's own (the balanced plan has already read every item's).
     if constexpr (PAIR) {
-        // The two prefix lengths (workgroup-uniform addresses) as scalar loads
-        // issued after the query loads and waited for on the scalar counter
-        // alone, so their round trip overlaps the query loads rather than
-        // following them (a vector load's wait would also wait for the queries).
         const int32_t *a0 = p.prefix + (2 * logical) / p.max_splits / p.row_blocks / p.Hkv;
         const int32_t *a1 = p.prefix + min(2 * logical + 1, p.total_logical - 1) / p.max_splits / p.row_blocks / p.Hkv;
         asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
                      : "=s"(pre0), "=s"(pre1)
                      : "s"(a0), "s"(a1)
                      : "memory");
+    } else if constexpr (!SEQ) {
+        if (!p.balanced) {
+            const int32_t *a0 = p.prefix + __builtin_amdgcn_readfirstlane(it);
+            asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(pre0) : "s"(a0) : "memory");
+        }
     }
     // Transpose-load offsets of this lane in a V stage, per 32-column block mb.
     // In its group of 16 lanes (s = lane % 16), lane s fetches 8 bytes of row
@@ -500,7 +513,7 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     }
 
     // Prefix lengths are clamped into [0, cap] so that no access leaves the cache.
-    const int P = SEQ ? 0 : min(max(PAIR ? (hw ? pre1 : pre0) : p.prefix[it], 0), p.cap);
+    const int P = SEQ ? 0 : min(max(PAIR && hw ? pre1 : pre0, 0), p.cap);
     const int Pb = P & ~(TK - 1);  // cache positions in whole tiles
     int nsplit = 1, t0 = 0, nb_split = 0, tail_len = 0, ntail = 0;
     // Sequence mode: the workgroup's key tiles are segment A, tiles 0..nA-1 of
