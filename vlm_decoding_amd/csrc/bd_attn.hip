@@ -529,12 +529,20 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
             red[3] = 0;
         }
         bd_barrier_lds();
-        if (row_valid) {
-            atomicMin(&red[0], vis.hi1);
-            atomicMax(&red[1], vis.hi1);
-            if (vis.hi2 > vis.lo2) {
-                atomicMin(&red[2], vis.lo2);
-                atomicMax(&red[3], vis.hi2);
+        {
+            // Each wave reduces its rows' bounds first (rows that see no
+            // second range, and invalid rows, contribute the identities), so
+            // the workgroup's four LDS atomics are one per wave.
+            const bool two = row_valid && vis.hi2 > vis.lo2;
+            const int mn0 = wave_max_i(-(row_valid ? vis.hi1 : 0x7fffffff));
+            const int mx1 = wave_max_i(row_valid ? vis.hi1 : 0);
+            const int mn2 = wave_max_i(-(two ? vis.lo2 : 0x7fffffff));
+            const int mx3 = wave_max_i(two ? vis.hi2 : 0);
+            if (lane == 0) {
+                atomicMin(&red[0], -mn0);
+                atomicMax(&red[1], mx1);
+                atomicMin(&red[2], -mn2);
+                atomicMax(&red[3], mx3);
             }
         }
         bd_barrier_lds();
