@@ -52,6 +52,9 @@ def _check(got, ref, label):
 
 CASES = [
     # (label, overrides, mode, items checked against the oracle)
+    # the headline shape with ragged prefixes: more split slots than CUs, so the
+    # tile kernel runs paired halves (some slots absorbed, some units written out)
+    ("36_layers_paired_ragged", dict(n_items=36, prefix=("list", [4096 - 117 * i for i in range(36)])), BIDIR, [0, 35]),
     ("8_layers_prefix_4096", dict(n_items=8, prefix=("fixed", 4096)), BIDIR, [0, 7]),
     ("2_items_ragged_smaller", dict(n_items=2, prefix=("list", [700, 33])), CAUSAL, [0, 1]),
     # the balanced split plan (a mode flag): its exchange also holds each unit's split count
