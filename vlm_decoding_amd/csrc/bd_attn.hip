@@ -1248,8 +1248,11 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
         return pl;
     }
     // 8-wave workgroups (256 rows) only for d = 128: with d = 64 a tile has
-    // fewer 16-byte units than 8 waves have lanes.
-    pl.nw = (pl.rows <= 128 || d == 64) ? 4 : 8;
+    // fewer 16-byte units than 8 waves have lanes.  The two-stream mode keeps
+    // 4-wave workgroups (two per CU, so the two waves of a SIMD belong to
+    // different workgroups and their MFMA and softmax phases drift apart;
+    // its many units fill the GPU either way): 396-399 against 405-406 us.
+    pl.nw = (pl.rows <= 128 || d == 64 || seq) ? 4 : 8;
     pl.rows_per_group = pl.nw * 32;
     pl.row_blocks = (pl.rows + pl.rows_per_group - 1) / pl.rows_per_group;
     pl.units = n * Hkv * pl.row_blocks;
