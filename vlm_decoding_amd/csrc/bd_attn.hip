@@ -479,14 +479,16 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     if constexpr (PAIR) {
         const int32_t *a0 = p.prefix + (2 * logical) / p.max_splits / p.row_blocks / p.Hkv;
         const int32_t *a1 = p.prefix + min(2 * logical + 1, p.total_logical - 1) / p.max_splits / p.row_blocks / p.Hkv;
+        // Early-clobber outputs: the first load's destination must not share a
+        // register with the second load's address.
         asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
-                     : "=s"(pre0), "=s"(pre1)
+                     : "=&s"(pre0), "=&s"(pre1)
                      : "s"(a0), "s"(a1)
                      : "memory");
     } else if constexpr (!SEQ) {
         if (!p.balanced) {
             const int32_t *a0 = p.prefix + __builtin_amdgcn_readfirstlane(it);
-            asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(pre0) : "s"(a0) : "memory");
+            asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(pre0) : "s"(a0) : "memory");
         }
     }
     // Transpose-load offsets of this lane in a V stage, per 32-column block mb.
