@@ -55,6 +55,7 @@ struct MfmaParams {
     const int32_t *spans, *n_spans;
     int *unit_splits;  // [units]: split count of each unit, for the merge kernel
     int Lc, max_spans, Dblk;
+    int max_prefix;  // the host's longest prefix (<= cap): paired halves plan their first copies with it
 };
 
 // Block slots a query slot may attend to, as two half-open slot ranges
@@ -114,6 +115,21 @@ __device__ __forceinline__ SlotRanges seq_ranges(const MfmaParams &p, int it, in
     }
     return {0, 0, 0};
 }
+
+// A workgroup-uniform pointer, moved into scalar registers (an operand of a
+// scalar load written in inline assembly must be one).
+__device__ __forceinline__ const int32_t *bd_uniform_ptr(const int32_t *q) {
+    const uint64_t v = (uint64_t)q;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (const int32_t *)(((uint64_t)hi << 32) | lo);
+}
+
+// Paired halves: the plan of one list slot (see attn_mfma_kernel).
+struct SlotPlan {
+    bool valid;
+    int unit, nsplit, t0, nb, ntail;
+};
 
 // Row permutations of the K operand.  A-row rho (= lane % 32) of a 32-key
 // block loads key pi(rho).
@@ -381,7 +397,7 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     __shared__ __attribute__((aligned(16))) uint8_t lds_v2[SB * NH];
     __shared__ __attribute__((aligned(16))) uint8_t lds_v3[SB * NH];
     // This thread's half and its index within the half.
-    const int hw = PAIR ? (int)threadIdx.x / NT : 0;
+    const int hw = PAIR ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / NT) : 0;  // wave-uniform
     const int tid = (int)threadIdx.x - hw * NT;
     const int hoff = hw * SB;
     auto kraw = [&](int st) __attribute__((always_inline)) -> uint8_t * {
@@ -412,7 +428,8 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
         // where the registers it keeps live would spill).
         asm volatile("" ::"s"(p.total_logical), "s"(p.max_splits), "s"(p.row_blocks), "s"(p.Hkv), "s"(p.G),
                      "s"(p.R), "s"(p.D), "s"(p.Hq), "s"(p.q), "s"(p.prefix), "s"(p.cap), "s"(p.tiles_per_split),
-                     "s"(p.mode), "s"(p.B), "s"(p.kc), "s"(p.vc), "s"(p.kb), "s"(p.vb), "s"(p.c), "s"(p.balanced));
+                     "s"(p.mode), "s"(p.B), "s"(p.kc), "s"(p.vc), "s"(p.kb), "s"(p.vb), "s"(p.c), "s"(p.balanced),
+                     "s"(p.max_prefix));
     }
     if (PAIR) {
         // Slot 2 L + hw of the list; a half past its end takes its partner's
@@ -470,6 +487,81 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
                 qf[kc] = bf16x8{};
         }
     }
+    // Sequence mode: the workgroup's key tiles are segment A, tiles 0..nA-1 of
+    // the clean stream (the first nU of them seen whole by every row), then
+    // segment B, the noisy tiles from bB on; each row's ranges decide the rest.
+    int nU = 0, nA = 0, bB = 0;
+    // Key tile of list entry k (sequence mode) or bulk tile k.
+    auto tile_of = [&](int k) __attribute__((always_inline)) { return SEQ && k >= nA ? bB + (k - nA) : k; };
+
+    // Byte offset of this (item, KV head)'s K and V cache rows ([cap][HD] each).
+    const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD * EB;
+
+    // Bulk tiles are copied global -> LDS by the load units directly
+    // (global_load_lds_dwordx4): each instruction fills 64 consecutive 16-byte
+    // LDS slots, one per lane, so the XOR swizzle is applied by choosing every
+    // lane's source address.  No VGPRs hold tile data.
+    static_assert(K_UNITS % NT == 0, "tile units must split evenly over lanes");
+    auto issue_bulk = [&](int t, int st, bool real) __attribute__((always_inline)) {
+        const int key0 = tile_of(t) * TK;
+#pragma unroll
+        for (int j = 0; j < LK; ++j) {
+            const int base = (j * NW + w) * 64;
+            const int u = base + lane;
+            const int key = u / KU, pu = u % KU;
+            const int lu = pu ^ k_swz<HD, KV8>(key);
+            const uint8_t *src = real ? p.kc + kc_base + (size_t)(key0 + key) * HD * EB + lu * 16 : p.kc + kc_base;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&kbuf(st)[base * 16], 16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < LV; ++j) {
+            const int base = (j * NW + w) * 64;
+            const int u = base + lane;
+            const int key = u / KU, pu = u % KU;
+            const int lu = pu ^ v_swz<HD, KV8>(key);
+            const uint8_t *src = real ? p.vc + kc_base + (size_t)(key0 + key) * HD * EB + lu * 16 : p.kc + kc_base;
+            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 16], 16, 0, 0);
+        }
+    };
+    // Paired halves: the plan of list slot s for a prefix length.  The slots
+    // of an odd unit take its key ranges in reverse (slot s runs split
+    // nsplit - 1 - s), so with an odd slot count per unit the two tail splits
+    // of units 2k and 2k + 1 share a workgroup, which then steps through fewer
+    // bulk tiles, instead of each tail holding up a partner with a full share.
+    auto slot_plan = [&](int s, int raw_prefix) __attribute__((always_inline)) {
+        SlotPlan sp{false, -1, 1, 0, 0, 0};
+        if (s >= p.total_logical) return sp;
+        sp.unit = s / p.max_splits;
+        const int sl = s - sp.unit * p.max_splits;
+        const int Px = min(max(raw_prefix, 0), p.cap);
+        sp.nsplit = unit_nsplit<TK>(Px, p.D, p.tiles_per_split, p.max_splits);
+        if (sl >= sp.nsplit) return sp;
+        const int kx = (sp.unit & 1) ? sp.nsplit - 1 - sl : sl;
+        const UnitSplit u = unit_split_n<TK>(Px, p.D, sp.nsplit, kx);
+        sp.valid = true;
+        sp.t0 = u.t0;
+        sp.nb = u.nb;
+        sp.ntail = kx == sp.nsplit - 1 ? ((Px - (Px & ~(TK - 1))) + p.D + TK - 1) / TK : 0;
+        return sp;
+    };
+    // Paired halves: a half whose slot, planned with the host's max_prefix,
+    // streams bulk tiles only issues that plan's first NS - 1 tile copies now,
+    // before its prefix length is known (for a batch of equal prefixes the
+    // plan is exact); if the real plan differs, the half drains these copies
+    // and issues its own (below).  Not for E4M3 caches, where the extra live
+    // registers cost more than the earlier start gains.
+    bool spec = false;
+    int spec_t0 = 0, spec_nb = 0;
+    if constexpr (PAIR && !KV8) {
+        const SlotPlan sp = slot_plan(2 * logical + hw, p.max_prefix);
+        spec = sp.valid && sp.ntail == 0 && sp.nb > 0;
+        spec_t0 = sp.t0;
+        spec_nb = sp.nb;
+        if (spec) {
+#pragma unroll
+            for (int i = 0; i < NS - 1; ++i) issue_bulk(spec_t0 + i, i, i < spec_nb);
+        }
+    }
     // The prefix lengths this workgroup plans with (workgroup-uniform
     // addresses) as scalar loads issued after the query loads and waited for
     // on the scalar counter alone, so their round trip overlaps the query
@@ -477,8 +569,9 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     // for the queries).  Paired halves: slots 2 L and 2 L + 1; otherwise the
     // item's own (the balanced plan has already read every item's).
     if constexpr (PAIR) {
-        const int32_t *a0 = p.prefix + (2 * logical) / p.max_splits / p.row_blocks / p.Hkv;
-        const int32_t *a1 = p.prefix + min(2 * logical + 1, p.total_logical - 1) / p.max_splits / p.row_blocks / p.Hkv;
+        const int32_t *a0 = bd_uniform_ptr(p.prefix + (2 * logical) / p.max_splits / p.row_blocks / p.Hkv);
+        const int32_t *a1 =
+            bd_uniform_ptr(p.prefix + min(2 * logical + 1, p.total_logical - 1) / p.max_splits / p.row_blocks / p.Hkv);
         // Early-clobber outputs: the first load's destination must not share a
         // register with the second load's address.
         asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
@@ -487,7 +580,7 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
                      : "memory");
     } else if constexpr (!SEQ) {
         if (!p.balanced) {
-            const int32_t *a0 = p.prefix + __builtin_amdgcn_readfirstlane(it);
+            const int32_t *a0 = bd_uniform_ptr(p.prefix + it);
             asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=&s"(pre0) : "s"(a0) : "memory");
         }
     }
@@ -518,10 +611,6 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     const int P = SEQ ? 0 : min(max(PAIR && hw ? pre1 : pre0, 0), p.cap);
     const int Pb = P & ~(TK - 1);  // cache positions in whole tiles
     int nsplit = 1, t0 = 0, nb_split = 0, tail_len = 0, ntail = 0;
-    // Sequence mode: the workgroup's key tiles are segment A, tiles 0..nA-1 of
-    // the clean stream (the first nU of them seen whole by every row), then
-    // segment B, the noisy tiles from bB on; each row's ranges decide the rest.
-    int nU = 0, nA = 0, bB = 0;
     if constexpr (SEQ) {
         __shared__ int red[4];
         if (tid == 0) {
@@ -578,34 +667,10 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     // Paired halves: both halves' plans, computed alike by every wave from the
     // list slots and their prefix lengths alone, so the loop counts below (the
     // longer half's tail and bulk tile counts) and every branch around a
-    // barrier are the same in all eight waves; each half takes its own.  The
-    // slots of an odd unit take its key ranges in reverse (slot s runs split
-    // nsplit - 1 - s), so with an odd slot count per unit the two tail splits
-    // of units 2k and 2k + 1 share a workgroup, which then steps through fewer
-    // bulk tiles, instead of each tail holding up a partner with a full share.
+    // barrier are the same in all eight waves; each half takes its own.
     bool hvalid = true, merged = false;
     int ntail_all = ntail, nb_all = nb_split;
     if constexpr (PAIR) {
-        struct SlotPlan {
-            bool valid;
-            int unit, nsplit, t0, nb, ntail;
-        };
-        auto slot_plan = [&](int s, int raw_prefix) __attribute__((always_inline)) {
-            SlotPlan sp{false, -1, 1, 0, 0, 0};
-            if (s >= p.total_logical) return sp;
-            sp.unit = s / p.max_splits;
-            const int sl = s - sp.unit * p.max_splits;
-            const int Px = min(max(raw_prefix, 0), p.cap);
-            sp.nsplit = unit_nsplit<TK>(Px, p.D, p.tiles_per_split, p.max_splits);
-            if (sl >= sp.nsplit) return sp;
-            const int kx = (sp.unit & 1) ? sp.nsplit - 1 - sl : sl;
-            const UnitSplit u = unit_split_n<TK>(Px, p.D, sp.nsplit, kx);
-            sp.valid = true;
-            sp.t0 = u.t0;
-            sp.nb = u.nb;
-            sp.ntail = kx == sp.nsplit - 1 ? ((Px - (Px & ~(TK - 1))) + p.D + TK - 1) / TK : 0;
-            return sp;
-        };
         const SlotPlan s0 = slot_plan(2 * logical, pre0), s1 = slot_plan(2 * logical + 1, pre1);
         if (!s0.valid && !s1.valid) return;  // the whole workgroup
         const SlotPlan &me = hw == 0 ? s0 : s1;
@@ -619,44 +684,12 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
         nb_all = max(s0.nb, s1.nb);
         merged = s0.valid && s1.valid && s0.unit == s1.unit;
     }
-    // Key tile of list entry k (sequence mode) or bulk tile k.
-    auto tile_of = [&](int k) __attribute__((always_inline)) { return SEQ && k >= nA ? bB + (k - nA) : k; };
-
-    // Byte offset of this (item, KV head)'s K and V cache rows ([cap][HD] each).
-    const size_t kc_base = ((size_t)it * p.Hkv + g) * p.cap * HD * EB;
-
     floatx16 o[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) o[mb] = floatx16{};
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    // Bulk tiles are copied global -> LDS by the load units directly
-    // (global_load_lds_dwordx4): each instruction fills 64 consecutive 16-byte
-    // LDS slots, one per lane, so the XOR swizzle is applied by choosing every
-    // lane's source address.  No VGPRs hold tile data.
-    static_assert(K_UNITS % NT == 0, "tile units must split evenly over lanes");
-    auto issue_bulk = [&](int t, int st, bool real) __attribute__((always_inline)) {
-        const int key0 = tile_of(t) * TK;
-#pragma unroll
-        for (int j = 0; j < LK; ++j) {
-            const int base = (j * NW + w) * 64;
-            const int u = base + lane;
-            const int key = u / KU, pu = u % KU;
-            const int lu = pu ^ k_swz<HD, KV8>(key);
-            const uint8_t *src = real ? p.kc + kc_base + (size_t)(key0 + key) * HD * EB + lu * 16 : p.kc + kc_base;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&kbuf(st)[base * 16], 16, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < LV; ++j) {
-            const int base = (j * NW + w) * 64;
-            const int u = base + lane;
-            const int key = u / KU, pu = u % KU;
-            const int lu = pu ^ v_swz<HD, KV8>(key);
-            const uint8_t *src = real ? p.vc + kc_base + (size_t)(key0 + key) * HD * EB + lu * 16 : p.kc + kc_base;
-            __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)&vbuf(st)[base * 16], 16, 0, 0);
-        }
-    };
     // Tail tiles: the last P % TK cache positions followed by the D block slots,
     // zero past the end (in the unit's last split).  K and V rows, of the
     // cache or of the block ([slot][Hkv][d]), are gathered as 16-byte units
@@ -836,7 +869,9 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     if constexpr (PAIR) {
         // A half without a tail starts its bulk copies first and only keeps
         // step with its partner's tail barriers.
-        if (ntail == 0) first_fill();
+        const bool spec_hit = spec && hvalid && ntail == 0 && t0 == spec_t0 && nb_split == spec_nb;
+        if (spec && !spec_hit) bd_wait_vmcnt<0>();  // copies of another plan: let them land, then refill
+        if (ntail == 0 && !spec_hit) first_fill();
         for (int tt = 0; tt < ntail_all; ++tt) {
             if (tt > 0) bd_barrier_lds();
             if (tt < ntail) load_tail(NS - 1, tt, tt == 0);
@@ -1240,6 +1275,7 @@ __global__ __launch_bounds__(256) void attn_vec_kernel(const T *q, const T *kb, 
 AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max_prefix, bool seq, bool balanced) {
     AttnPlan pl{};
     pl.seq = seq;
+    pl.max_prefix = max_prefix;
     pl.mfma = (dtype == 1 || dtype == 2);
     pl.fp8 = (dtype == 2);
     pl.tk = pl.fp8 ? 2 * kTileKeys : kTileKeys;
@@ -1390,6 +1426,7 @@ hipError_t launch_attention_mfma(const AttnPlan &pl, const AttnArgs &a, hipStrea
     p.total_logical = pl.units * pl.max_splits;
     p.balanced = pl.balanced ? 1 : 0;
     p.balance_slots = pl.balance_slots;
+    p.max_prefix = pl.max_prefix;
     p.c = a.scale * BD_LOG2E;
     dim3 block(pl.nw * 64 * (pl.pair ? 2 : 1));
     const void *tile, *merge;

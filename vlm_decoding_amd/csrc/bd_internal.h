@@ -29,6 +29,7 @@ struct AttnPlan {
     bool balanced;        // ragged-batch plan: split counts from the device-side prefix lengths
     int balance_slots;    // ... workgroups it may use
     bool pair;            // one 8-wave workgroup runs two list slots (two 4-wave halves)
+    int max_prefix;       // the host's longest prefix
     int grid;             // workgroups launched
     size_t ws_ml_off, ws_o_off, ws_splits_off, ws_bytes;
 };
