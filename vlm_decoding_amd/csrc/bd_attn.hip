@@ -1023,10 +1023,11 @@ static_assert((4 * (4 / kMergeWaves)) % 8 == 0, "merge grid must be a multiple o
 // summed in split order.  The merged rows are staged in LDS and written out
 // as row segments of WPB * HD / NP contiguous elements.  Every split slot of a
 // lane is loaded at once, QPT * MAXS 16-byte units: NP = 4 with up to 16
-// splits, or one unit per split (NP = HD / 16) with up to 32.  With SW = 2
-// split waves a block holds up to 64 splits: wave w takes splits 32 w ..
-// 32 w + 31, both use the max over all splits, and wave 0 adds wave 1's sums
-// to its own (the sum over the first 32 splits, then the rest).
+// splits, or one unit per split (NP = HD / 16) with up to 32.  With SW > 1
+// split waves a block holds up to SW * MAXS splits: wave w takes splits
+// MAXS w .. MAXS w + MAXS - 1, all use the max over all splits, and wave 0
+// adds the other waves' sums to its own in wave order (the sum over its own
+// splits, then each later group's).
 // PAIRED: the partials of paired tile halves (some slots absorbed, see below).
 template <int HD, int NW, int TK, bool SEQ, int NP, int MAXS, int SW, bool PAIRED = false>
 __global__ __launch_bounds__(kMergeWaves * SW * 64) void attn_merge_kernel(MfmaParams p) {
@@ -1358,10 +1359,16 @@ AttnPlan plan_attention(int n, int D, int Hq, int Hkv, int d, int dtype, int max
 }
 
 namespace {
+// Split waves of the merge for plans beyond kWideSplits splits (one-item
+// calls): eight waves of kMaxSplits / 8 slots each, so a block has four times
+// the loads in flight that two 32-slot waves had (a step of 36 one-layer
+// calls of the 3B shape: 518 us with two waves, 493 with four, 487 with
+// eight, 492 with sixteen).
+constexpr int kMaxSplitWaves = 8;
 // The merge instance holds every split slot of a lane in registers: four
 // column parts for up to kNarrowSplits splits, one 16-byte unit per split
-// (HD / 16 parts) up to kWideSplits, and two such split waves per block
-// beyond.
+// (HD / 16 parts) up to kWideSplits, and kMaxSplitWaves split waves of such
+// units per block beyond.
 template <int HD, int NW, int TK, bool SEQ>
 const void *pick_merge(const AttnPlan &pl) {
     // Paired plans have more slots than CUs, so at most kNarrowSplits per unit.
@@ -1369,7 +1376,7 @@ const void *pick_merge(const AttnPlan &pl) {
         if (pl.pair) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, 4, kNarrowSplits, 1, true>;
     if (pl.max_splits <= kNarrowSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, 4, kNarrowSplits, 1>;
     if (pl.max_splits <= kWideSplits) return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kWideSplits, 1>;
-    return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kWideSplits, kMaxSplits / kWideSplits>;
+    return (const void *)attn_merge_kernel<HD, NW, TK, SEQ, HD / 16, kMaxSplits / kMaxSplitWaves, kMaxSplitWaves>;
 }
 template <bool KV8, bool SEQ>
 void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **merge, int *parts, int *waves) {
@@ -1387,7 +1394,7 @@ void pick_kernels(const AttnPlan &pl, int d, const void **tile, const void **mer
         *merge = pick_merge<64, 4, TK, SEQ>(pl);
     }
     *parts = pl.max_splits <= kNarrowSplits ? 4 : d / 16;
-    *waves = pl.max_splits <= kWideSplits ? 1 : kMaxSplits / kWideSplits;
+    *waves = pl.max_splits <= kWideSplits ? 1 : kMaxSplitWaves;
 }
 }  // namespace
 
