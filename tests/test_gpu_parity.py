@@ -229,11 +229,13 @@ def test_attention_balanced_at_the_item_limit(dev, n_items):
 
 # Few items with long prefixes: the plan gives such calls 32 or 64 splits per
 # unit (every workgroup on a CU of its own) and merges them with the 32-slot
-# merge instance or its two-split-wave form.  Ragged prefixes give units with
-# fewer splits than the plan's maximum.
+# merge instance or its form with eight split waves of 8 slots.  Ragged
+# prefixes give units with fewer splits than the plan's maximum (with 4096 and
+# 300, the short unit's few splits all fall to the first split wave).
 FEW_ITEM_CASES = [
     ("one_item_4096_64_splits", dict(n_items=1, prefix=("fixed", 4096))),
     ("two_items_ragged_64_splits", dict(n_items=2, prefix=("list", [4096, 2050]))),
+    ("two_items_4096_300_64_splits", dict(n_items=2, prefix=("list", [4096, 300]))),
     ("two_items_4133_tail", dict(n_items=2, prefix=("list", [4133, 4127]))),
     ("four_items_32_splits", dict(n_items=4, prefix=("list", [2048, 1100, 31, 2047]))),
     ("one_item_fp8_32_splits", dict(n_items=1, prefix=("fixed", 4096), dtype=FP8KV)),

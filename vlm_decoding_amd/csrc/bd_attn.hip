@@ -672,7 +672,10 @@ __global__ __launch_bounds__(NW * 64 * (PAIR ? 2 : 1), occupancy_for(HD)) void a
     int ntail_all = ntail, nb_all = nb_split;
     if constexpr (PAIR) {
         const SlotPlan s0 = slot_plan(2 * logical, pre0), s1 = slot_plan(2 * logical + 1, pre1);
-        if (!s0.valid && !s1.valid) return;  // the whole workgroup
+        if (!s0.valid && !s1.valid) {  // the whole workgroup
+            if (spec) bd_wait_vmcnt<0>();  // no copy into this workgroup's LDS outlives it
+            return;
+        }
         const SlotPlan &me = hw == 0 ? s0 : s1;
         hvalid = me.valid;
         nsplit = me.nsplit;
