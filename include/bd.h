@@ -96,6 +96,8 @@ enum { BD_BLOCK_BIDIR = 0, BD_BLOCK_CAUSAL = 1, BD_BLOCK_QUAD = 2 };
  *             queries and outputs, E4M3 keys and values: bd_attn_step_fp8kv)
  *  mode       BD_BLOCK_BIDIR, BD_BLOCK_CAUSAL or BD_BLOCK_QUAD, optionally | BD_PLAN_BALANCED
  *  max_prefix host-side upper bound of every prefix_len[i], 0..cap; sizes the grid
+ *             (and, for bf16 caches, the first tile copies a workgroup issues
+ *             before the device-side lengths arrive)
  *  scale      softmax scale (normally 1/sqrt(d)); finite and > 0
  * Size limits (BD_E_SHAPE otherwise), with S = block slots per item (D, or
  * B (B + 3) / 2 for BD_BLOCK_QUAD): S * Hq <= 2^20, cap * d <= 2^30, and the
